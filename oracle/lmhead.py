@@ -1,0 +1,62 @@
+"""Selective LM head with greedy confidence (test infrastructure only).
+
+The pages run the LM head only for sequences still denoising (JetEngine
+README, "Selective Logits"; developer notes, "ModelRunner": selective
+logits) and only on still-masked positions (developer notes, "Optimization
+History": sparse logits).  Each projected row gives the greedy token and its
+confidence, the largest probability of the softmax over the vocabulary
+(sampling at temperature 1 with greedy choice; SDAR page, generate.py runs
+greedy generation).
+
+Readings:
+  * logits l_v = sum_k h[k] W[k][v], W stored as its transpose [V][Hd];
+  * the mask token is never a candidate: its logit is treated as -inf, so it
+    is out of both the argmax and the normaliser;
+  * ties in the argmax go to the lowest token id;
+  * confidence max_p = exp(m - lse), m = max logit, lse = log-sum-exp.
+
+Also returns the runner-up probability p2, which the tests use only to
+decide which rows are near-ties.
+"""
+import numpy as np
+
+from .bf16 import widen
+
+
+def lmhead_logits(h_rows, w_vocab_bits, mask_id):
+    """float64 logits [M][V] with the mask column at -inf."""
+    W = widen(w_vocab_bits)                      # [V][Hd]
+    H = widen(h_rows)                            # [M][Hd]
+    logits = H @ W.T
+    logits[:, mask_id] = -np.inf
+    return logits
+
+
+def _reduce(logits):
+    m = logits.max(axis=1)
+    arg = logits.argmax(axis=1)                  # first maximum = lowest id
+    e = np.exp(logits - m[:, None])
+    ssum = e.sum(axis=1)
+    p1 = 1.0 / ssum                              # exp(m - lse)
+    part = np.partition(e, -2, axis=1)[:, -2]
+    p2 = part / ssum
+    return arg.astype(np.int64), p1, p2
+
+
+def lmhead_rows(h_rows, w_vocab_bits, mask_id, chunk=64):
+    """Greedy token, confidence and runner-up probability for each row.
+
+    h_rows: [M][Hd] bf16 bits; w_vocab_bits: [V][Hd] bf16 bits.
+    Returns (argmax [M] int64, p1 [M] float64, p2 [M] float64)."""
+    M = h_rows.shape[0]
+    W = widen(w_vocab_bits)
+    args = np.empty(M, dtype=np.int64)
+    p1 = np.empty(M)
+    p2 = np.empty(M)
+    for i in range(0, M, chunk):
+        H = widen(h_rows[i:i + chunk])
+        logits = H @ W.T
+        logits[:, mask_id] = -np.inf
+        a, x1, x2 = _reduce(logits)
+        args[i:i + chunk], p1[i:i + chunk], p2[i:i + chunk] = a, x1, x2
+    return args, p1, p2

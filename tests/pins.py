@@ -1,0 +1,479 @@
+"""Pins for the CPU oracle: checks against brute force, closed forms, library
+special cases and invariants.  Each check takes the implementation (a module
+exposing the oracle's functions) so that the same checks can be run on
+deliberately broken copies of the oracle (test_oracle_mutants.py) and shown
+to fail there.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+from block_diffusion_amd.synth import f32_to_bf16
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def bf(x):
+    return f32_to_bf16(np.asarray(x, dtype=np.float32))
+
+
+def wid(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------- attention
+
+def tiny_attn_case(seed=0, S=2, B=3, Hq=4, Hkv=2, D=8, P=4, L=(7, 0), extra_pages=2):
+    g = np.random.default_rng(seed)
+    npg = [-(-l // P) for l in L]
+    total = sum(npg) + extra_pages
+    perm = g.permutation(total)
+    maxp = max(max(npg), 1)
+    pt = np.full((S, maxp), -1, dtype=np.int32)
+    o = 0
+    for s, n in enumerate(npg):
+        pt[s, :n] = perm[o:o + n]
+        o += n
+    kc = bf(g.standard_normal((total, Hkv, P, D)))
+    vc = bf(g.standard_normal((total, Hkv, P, D)))
+    q = bf(g.standard_normal((S, B, Hq, D)))
+    kb = bf(g.standard_normal((S, B, Hkv, D)))
+    vb = bf(g.standard_normal((S, B, Hkv, D)))
+    return dict(q=q, k_blk=kb, v_blk=vb, k_cache=kc, v_cache=vc,
+                page_table=pt, prefix_len=np.asarray(L, dtype=np.int32))
+
+
+def attn_bruteforce(c, scale=None):
+    """Scalar loops and math.fsum, walking the page table token by token."""
+    q, kb, vb, kc, vc, pt, Ls = (c["q"], c["k_blk"], c["v_blk"], c["k_cache"],
+                                 c["v_cache"], c["page_table"], c["prefix_len"])
+    S, B, Hq, D = q.shape
+    Hkv = kb.shape[2]
+    P = kc.shape[2]
+    G = Hq // Hkv
+    sc = 1.0 / math.sqrt(D) if scale is None else scale
+    out = np.zeros((S, B, Hq, D))
+    for s in range(S):
+        for h in range(Hq):
+            g = h // G
+            keys, vals = [], []
+            for j in range(int(Ls[s])):
+                page = int(pt[s][j // P])
+                keys.append([float(x) for x in wid(kc[page, g, j % P])])
+                vals.append([float(x) for x in wid(vc[page, g, j % P])])
+            for j in range(B):
+                keys.append([float(x) for x in wid(kb[s, j, g])])
+                vals.append([float(x) for x in wid(vb[s, j, g])])
+            for i in range(B):
+                qi = [float(x) for x in wid(q[s, i, h])]
+                z = [math.fsum(a * b for a, b in zip(qi, k)) * sc for k in keys]
+                mz = max(z)
+                e = [math.exp(t - mz) for t in z]
+                den = math.fsum(e)
+                for d in range(D):
+                    out[s, i, h, d] = math.fsum(e[j] * vals[j][d] for j in range(len(keys))) / den
+    return out
+
+
+def _call_attn(impl, c, scale=None):
+    return impl.attention(c["q"], c["k_blk"], c["v_blk"], c["k_cache"], c["v_cache"],
+                          c["page_table"], c["prefix_len"], scale)
+
+
+def check_attn_bruteforce(impl):
+    for seed, L, P, B in [(0, (7, 0), 4, 3), (1, (16, 9), 4, 4), (2, (1, 13), 8, 2)]:
+        c = tiny_attn_case(seed=seed, L=L, P=P, B=B)
+        ref = attn_bruteforce(c)
+        got = _call_attn(impl, c)
+        assert np.max(np.abs(got - ref)) < 1e-12, (seed, np.max(np.abs(got - ref)))
+
+
+def check_attn_sdpa(impl):
+    """Library special case: after resolving pages, each sequence is plain
+    unmasked scaled-dot-product attention over [prefix ++ block], with kv
+    heads repeated for the query groups."""
+    import torch
+    import torch.nn.functional as F
+    c = tiny_attn_case(seed=5, S=3, B=4, Hq=6, Hkv=3, D=16, P=4, L=(9, 4, 0))
+    got = _call_attn(impl, c)
+    S, B, Hq, D = c["q"].shape
+    Hkv = c["k_blk"].shape[2]
+    P = c["k_cache"].shape[2]
+    for s in range(S):
+        L = int(c["prefix_len"][s])
+        ks, vs = [], []
+        for j in range(L):
+            p = c["page_table"][s][j // P]
+            ks.append(wid(c["k_cache"][p, :, j % P]))
+            vs.append(wid(c["v_cache"][p, :, j % P]))
+        K = np.concatenate([np.stack(ks, 0) if ks else np.zeros((0, Hkv, D)), wid(c["k_blk"][s])], 0)
+        Vv = np.concatenate([np.stack(vs, 0) if vs else np.zeros((0, Hkv, D)), wid(c["v_blk"][s])], 0)
+        qt = torch.from_numpy(wid(c["q"][s])).permute(1, 0, 2)[None]          # [1,Hq,B,D]
+        kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)[None]
+        vt = torch.from_numpy(Vv).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)[None]
+        ref = F.scaled_dot_product_attention(qt, kt, vt)[0].permute(1, 0, 2).numpy()
+        assert np.max(np.abs(got[s] - ref)) < 1e-12
+
+
+def check_attn_closed_forms(impl):
+    # Q = 0: uniform weights, the mean of all L+B value rows of the group.
+    c = tiny_attn_case(seed=3, L=(11, 5), P=4, B=3)
+    c["q"] = np.zeros_like(c["q"])
+    got = _call_attn(impl, c)
+    S, B, Hq, D = c["q"].shape
+    Hkv = c["k_blk"].shape[2]
+    P = c["k_cache"].shape[2]
+    for s in range(S):
+        L = int(c["prefix_len"][s])
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            rows = [wid(c["v_cache"][c["page_table"][s][j // P], g, j % P]) for j in range(L)]
+            rows += [wid(c["v_blk"][s, j, g]) for j in range(B)]
+            mean = np.mean(np.stack(rows), 0)
+            for i in range(B):
+                assert np.max(np.abs(got[s, i, h] - mean)) < 1e-12
+    # L = 0, B = 1: the only key is the token itself, O = its value row.
+    c = tiny_attn_case(seed=4, S=2, L=(0, 0), B=1)
+    got = _call_attn(impl, c)
+    G = c["q"].shape[2] // c["k_blk"].shape[2]
+    for h in range(c["q"].shape[2]):
+        assert np.array_equal(got[:, 0, h], wid(c["v_blk"][:, 0, h // G]))
+    # identical keys everywhere: weights uniform whatever q is.
+    c = tiny_attn_case(seed=6, L=(6, 3), P=4, B=2)
+    one = c["k_blk"][0, 0, 0].copy()
+    c["k_cache"][...] = one
+    c["k_blk"][...] = one
+    got = _call_attn(impl, c)
+    c0 = dict(c)
+    c0["q"] = np.zeros_like(c["q"])
+    assert np.max(np.abs(got - _call_attn(impl, c0))) < 1e-12
+
+
+def check_attn_block_permutation(impl):
+    """Bidirectional within the block: permuting the block's positions
+    (queries, keys and values together) permutes the outputs."""
+    c = tiny_attn_case(seed=7, L=(5, 10), P=4, B=4)
+    base = _call_attn(impl, c)
+    perm = np.array([2, 0, 3, 1])
+    c2 = dict(c)
+    for k in ("q", "k_blk", "v_blk"):
+        c2[k] = c[k][:, perm]
+    got = _call_attn(impl, c2)
+    assert np.max(np.abs(got - base[:, perm])) < 1e-12
+
+
+def check_attn_page_relabel(impl):
+    c = tiny_attn_case(seed=8, L=(13, 6), P=4, B=3, extra_pages=3)
+    base = _call_attn(impl, c)
+    n = c["k_cache"].shape[0]
+    pi = np.random.default_rng(9).permutation(n)
+    c2 = dict(c)
+    kc = np.empty_like(c["k_cache"]); vc = np.empty_like(c["v_cache"])
+    kc[pi] = c["k_cache"]; vc[pi] = c["v_cache"]
+    pt = c["page_table"].copy()
+    pt[pt >= 0] = pi[pt[pt >= 0]]
+    c2.update(k_cache=kc, v_cache=vc, page_table=pt)
+    assert np.array_equal(_call_attn(impl, c2), base)
+
+
+def check_attn_gqa_as_mha(impl):
+    c = tiny_attn_case(seed=10, S=2, B=3, Hq=6, Hkv=2, D=8, P=4, L=(9, 2))
+    base = _call_attn(impl, c)
+    G = 3
+    c2 = dict(c)
+    for k in ("k_blk", "v_blk"):
+        c2[k] = np.repeat(c[k], G, axis=2)
+    for k in ("k_cache", "v_cache"):
+        c2[k] = np.repeat(c[k], G, axis=1)
+    assert np.max(np.abs(_call_attn(impl, c2) - base)) < 1e-12
+
+
+def check_attn_golden(impl):
+    with open(os.path.join(GOLDEN, "closed_form_cases.json")) as f:
+        cases = json.load(f)["attention"]
+    for c in cases:
+        arr = {k: bf(np.array(c[k], dtype=np.float32)) for k in
+               ("q", "k_blk", "v_blk", "k_cache", "v_cache")}
+        got = impl.attention(arr["q"], arr["k_blk"], arr["v_blk"], arr["k_cache"],
+                             arr["v_cache"], np.array(c["page_table"], dtype=np.int32),
+                             np.array(c["prefix_len"], dtype=np.int32))
+        assert np.max(np.abs(got - np.array(c["expect"]))) < 1e-15, c["name"]
+
+
+ATTN_CHECKS = [check_attn_golden, check_attn_bruteforce, check_attn_sdpa, check_attn_closed_forms,
+               check_attn_block_permutation, check_attn_page_relabel,
+               check_attn_gqa_as_mha]
+
+
+# ------------------------------------------------------------------- LM head
+
+def lm_bruteforce(h_bits, w_bits, mask_id):
+    H = wid(h_bits); W = wid(w_bits)
+    out = []
+    for r in range(H.shape[0]):
+        logit = {}
+        for v in range(W.shape[0]):
+            if v == mask_id:
+                continue
+            logit[v] = math.fsum(float(a) * float(b) for a, b in zip(H[r], W[v]))
+        m = max(logit.values())
+        arg = min(v for v, x in logit.items() if x == m)
+        e = sorted((math.exp(x - m) for x in logit.values()), reverse=True)
+        den = math.fsum(e)
+        out.append((arg, 1.0 / den, e[1] / den))
+    return out
+
+
+def check_lm_bruteforce(impl):
+    g = np.random.default_rng(11)
+    for V, Hd, mask in [(12, 4, 11), (17, 8, 0), (9, 16, 4)]:
+        h = bf(g.standard_normal((5, Hd)) * 2)
+        w = bf(g.standard_normal((V, Hd)))
+        a, p1, p2 = impl.lmhead_rows(h, w, mask)
+        for r, (ea, e1, e2) in enumerate(lm_bruteforce(h, w, mask)):
+            assert a[r] == ea
+            assert abs(p1[r] - e1) < 1e-13 and abs(p2[r] - e2) < 1e-13
+
+
+def check_lm_zero_hidden(impl):
+    """h = 0: every candidate logit is 0, so max_p = 1/(V-1) and the argmax is
+    the smallest id that is not the mask."""
+    for V, mask in [(10, 9), (10, 0), (33, 5)]:
+        w = bf(np.random.default_rng(V).standard_normal((V, 8)))
+        h = np.zeros((3, 8), dtype=np.uint16)
+        a, p1, p2 = impl.lmhead_rows(h, w, mask)
+        assert np.all(a == (1 if mask == 0 else 0))
+        assert np.allclose(p1, 1.0 / (V - 1), rtol=0, atol=1e-15)
+        assert np.allclose(p2, 1.0 / (V - 1), rtol=0, atol=1e-15)
+
+
+def check_lm_one_hot(impl):
+    """W column t = c*e_k, every other column 0, h = e_k: logit c at t, 0
+    elsewhere, so max_p = e^c / (e^c + V - 2)."""
+    V, Hd, mask = 20, 6, 19
+    for t, k, c in [(3, 2, 2.5), (0, 5, 7.0), (18, 0, 0.75)]:
+        w = np.zeros((V, Hd), dtype=np.float32)
+        w[t, k] = c
+        h = np.zeros((1, Hd), dtype=np.float32)
+        h[0, k] = 1.0
+        a, p1, _ = impl.lmhead_rows(bf(h), bf(w), mask)
+        assert a[0] == t
+        assert abs(p1[0] - math.exp(c) / (math.exp(c) + V - 2)) < 1e-14
+
+
+def check_lm_vocab_permutation(impl):
+    g = np.random.default_rng(12)
+    V, Hd, mask = 40, 8, 7
+    h = bf(g.standard_normal((6, Hd)) * 3)
+    w = bf(g.standard_normal((V, Hd)))
+    a, p1, p2 = impl.lmhead_rows(h, w, mask)
+    pi = g.permutation(V)                    # new id of old id v is pi[v]
+    w2 = np.empty_like(w); w2[pi] = w
+    a2, q1, q2 = impl.lmhead_rows(h, w2, int(pi[mask]))
+    assert np.array_equal(a2, pi[a])
+    assert np.max(np.abs(q1 - p1)) < 1e-12 and np.max(np.abs(q2 - p2)) < 1e-12
+
+
+def check_lm_mask_never_chosen(impl):
+    g = np.random.default_rng(13)
+    V, Hd, mask = 30, 8, 12
+    h = g.standard_normal((4, Hd)).astype(np.float32)
+    w = g.standard_normal((V, Hd)).astype(np.float32) * 0.1
+    w[mask] = 50.0 * h[0] / np.linalg.norm(h[0])
+    a, p1, _ = impl.lmhead_rows(bf(h), bf(w), mask)
+    assert not np.any(a == mask)
+    # the normaliser leaves the mask out too (brute force skips its column).
+    ref = lm_bruteforce(bf(h), bf(w), mask)
+    for r, (ea, e1, _) in enumerate(ref):
+        assert a[r] == ea and abs(p1[r] - e1) < 1e-13
+
+
+def check_lm_ties_lowest(impl):
+    V, Hd, mask = 16, 4, 15
+    w = np.zeros((V, Hd), dtype=np.float32)
+    w[9, 1] = 3.0
+    w[4, 1] = 3.0
+    w[12, 1] = 3.0
+    h = np.zeros((1, Hd), dtype=np.float32); h[0, 1] = 1.0
+    a, p1, p2 = impl.lmhead_rows(bf(h), bf(w), mask)
+    assert a[0] == 4 and p1[0] == p2[0]
+
+
+def check_lm_scipy(impl):
+    from scipy.special import softmax
+    g = np.random.default_rng(14)
+    V, Hd, mask = 300, 32, 123
+    h = bf(g.standard_normal((8, Hd)) * 2)
+    w = bf(g.standard_normal((V, Hd)) / np.sqrt(Hd))
+    a, p1, p2 = impl.lmhead_rows(h, w, mask)
+    logit = wid(h) @ wid(w).T
+    keep = np.array([v for v in range(V) if v != mask])
+    p = softmax(logit[:, keep], axis=1)
+    assert np.array_equal(a, keep[np.argmax(p, axis=1)])
+    assert np.max(np.abs(p1 - p.max(1))) < 1e-14
+    assert np.max(np.abs(p2 - np.sort(p, 1)[:, -2])) < 1e-14
+
+
+def check_lm_golden(impl):
+    with open(os.path.join(GOLDEN, "closed_form_cases.json")) as f:
+        cases = json.load(f)["lmhead"]
+    for c in cases:
+        a, p1, p2 = impl.lmhead_rows(bf(np.array(c["hidden"], dtype=np.float32)),
+                                     bf(np.array(c["w_vocab"], dtype=np.float32)), c["mask_id"])
+        assert a.tolist() == c["expect_argmax"], c["name"]
+        assert np.max(np.abs(p1 - np.array(c["expect_p1"]))) < 1e-15, c["name"]
+        assert np.max(np.abs(p2 - np.array(c["expect_p2"]))) < 1e-15, c["name"]
+
+
+LM_CHECKS = [check_lm_golden, check_lm_bruteforce, check_lm_zero_hidden, check_lm_one_hot,
+             check_lm_vocab_permutation, check_lm_mask_never_chosen,
+             check_lm_ties_lowest, check_lm_scipy]
+
+
+# -------------------------------------------------------------------- remask
+
+DEN, SAV = 2, 3
+
+
+def remask_bruteforce(toks, state, conf, argm, mask_id, tau):
+    """Enumerate every subset C of the masked set and keep the one that the
+    rule characterises: if some masked confidence reaches tau, C is exactly
+    the set of those positions (every member reaches tau, and every position
+    that reaches tau is a member); otherwise C is a singleton {j} with conf_j
+    >= every masked confidence and j lower than any other position of equal
+    confidence."""
+    S, B = toks.shape
+    conf = np.asarray(conf).reshape(S, B)
+    argm = np.asarray(argm).reshape(S, B)
+    nt = toks.copy(); ns = state.copy()
+    for s in range(S):
+        if state[s] != DEN:
+            continue
+        M = [i for i in range(B) if toks[s, i] == mask_id]
+        sols = []
+        for r in range(1, len(M) + 1):
+            for C in itertools.combinations(M, r):
+                above = [i for i in M if conf[s, i] >= tau]
+                if above:
+                    ok = set(C) == set(above) and all(conf[s, i] >= tau for i in C)
+                else:
+                    j = C[0]
+                    ok = (len(C) == 1 and all(conf[s, j] >= conf[s, i] for i in M)
+                          and all(not (conf[s, i] == conf[s, j] and i < j) for i in M))
+                if ok:
+                    sols.append(C)
+        assert len(sols) == (1 if M else 0)
+        for C in sols:
+            for i in C:
+                nt[s, i] = argm[s, i]
+        if not np.any(nt[s] == mask_id):
+            ns[s] = SAV
+    return nt, ns
+
+
+def random_remask_case(g, S, B, mask_id, tau, exact=True):
+    toks = np.where(g.random((S, B)) < 0.7, mask_id, g.integers(0, mask_id, (S, B))).astype(np.int64)
+    state = np.where(g.random(S) < 0.85, DEN, SAV).astype(np.uint8)
+    levels = np.array([0.1, 0.3, tau, tau, 0.5, 0.95, 0.95, 0.2]) if exact else None
+    conf = (g.choice(levels, size=S * B) if exact else g.random(S * B))
+    argm = g.integers(0, mask_id, S * B)
+    return toks, state, conf, argm
+
+
+def check_remask_bruteforce(impl):
+    g = np.random.default_rng(15)
+    for B in (1, 2, 3, 4, 5, 6):
+        for _ in range(40):
+            tau = float(g.choice([0.5, 0.75, 0.9]))
+            toks, state, conf, argm = random_remask_case(g, 4, B, 99, tau)
+            et, es = remask_bruteforce(toks, state, conf, argm, 99, tau)
+            nt, ns, _ = impl.remask(toks, state, conf, argm, 99, tau)
+            assert np.array_equal(nt, et) and np.array_equal(ns, es)
+
+
+def check_remask_invariants(impl):
+    """Over whole blocks: committed tokens never change, each round of a
+    DENOISING sequence with a mask left commits at least one, the masked
+    count strictly falls, SAVING iff no mask is left, and a block finishes
+    within |M_1| rounds."""
+    g = np.random.default_rng(16)
+    mask = 50
+    for B in (1, 4, 16, 64):
+        S = 5
+        toks = np.where(g.random((S, B)) < 0.8, mask, g.integers(0, mask, (S, B))).astype(np.int64)
+        state = np.full(S, DEN, dtype=np.uint8)
+        m0 = (toks == mask).sum(1)
+        rounds = 0
+        while np.any(state == DEN):
+            conf = g.random(S * B)
+            argm = g.integers(0, mask, S * B)
+            nt, ns, com = impl.remask(toks, state, conf, argm, mask, 0.9)
+            was = toks != mask
+            assert np.array_equal(nt[was], toks[was])
+            for s in range(S):
+                if state[s] == DEN:
+                    before = (toks[s] == mask).sum(); after = (nt[s] == mask).sum()
+                    if before:
+                        assert after < before and com[s].sum() >= 1
+                    assert (ns[s] == SAV) == (after == 0)
+                else:
+                    assert np.array_equal(nt[s], toks[s]) and ns[s] == state[s]
+            toks, state = nt, ns
+            rounds += 1
+            assert rounds <= max(1, m0.max())
+
+
+def check_remask_special_thresholds(impl):
+    """tau > 1: exactly one commit per round, the most confident (the static
+    one-token-per-step schedule of block 4 / 4 steps); tau <= 0: every masked
+    position commits in the first round."""
+    g = np.random.default_rng(17)
+    mask, S, B = 77, 3, 4
+    toks = np.full((S, B), mask, dtype=np.int64)
+    state = np.full(S, DEN, dtype=np.uint8)
+    for r in range(B):
+        conf = g.random(S * B)
+        argm = g.integers(0, mask, S * B)
+        nt, ns, com = impl.remask(toks, state, conf, argm, mask, 1.5)
+        c2 = conf.reshape(S, B)
+        for s in range(S):
+            assert com[s].sum() == 1
+            M = np.where(toks[s] == mask)[0]
+            j = M[np.argmax(c2[s, M])]
+            assert com[s, j]
+        toks, state = nt, ns
+    assert np.all(state == SAV)
+    toks = np.full((S, B), mask, dtype=np.int64)
+    state = np.full(S, DEN, dtype=np.uint8)
+    nt, ns, com = impl.remask(toks, state, g.random(S * B), g.integers(0, mask, S * B), mask, 0.0)
+    assert com.all() and np.all(ns == SAV)
+
+
+def check_remask_golden(impl):
+    with open(os.path.join(GOLDEN, "remask_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        toks = np.array(c["block_tokens"], dtype=np.int64)
+        state = np.array(c["seq_state"], dtype=np.uint8)
+        nt, ns, _ = impl.remask(toks, state, np.array(c["conf"], dtype=np.float64),
+                                np.array(c["argmax"]), c["mask_id"], c["tau"],
+                                c.get("flags", 0))
+        assert nt.tolist() == c["expect_tokens"], c["name"]
+        assert ns.tolist() == c["expect_state"], c["name"]
+
+
+def check_compact_rows(impl):
+    mask = 9
+    toks = np.array([[9, 1, 9, 9], [2, 3, 4, 5], [9, 9, 0, 9], [9, 9, 9, 9]])
+    state = np.array([DEN, DEN, SAV, DEN], dtype=np.uint8)
+    assert impl.compact_rows(toks, state, mask).tolist() == [0, 2, 3, 12, 13, 14, 15]
+
+
+REMASK_CHECKS = [check_remask_bruteforce, check_remask_invariants,
+                 check_remask_special_thresholds, check_remask_golden,
+                 check_compact_rows]

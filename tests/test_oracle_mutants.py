@@ -1,0 +1,73 @@
+"""Plants plausible mistakes in copies of the oracle (on the CPU) and checks
+that at least one pin fails for each: the pins are strong enough to notice a
+dropped term, a wrong sign or index, or a swapped rule."""
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS
+
+ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
+
+# (file, original text, replacement, which pin family must catch it)
+MUTANTS = [
+    ("attention.py", "scale = 1.0 / np.sqrt(D)", "scale = 1.0 / D", "attn"),
+    ("attention.py", "h = g * G + gi", "h = gi * Hkv + g", "attn"),
+    ("attention.py", "reshape(npg * P, -1)[:L]", "reshape(npg * P, -1)[:max(L - 1, 0)]", "attn"),
+    ("attention.py", "z -= z.max(axis=1, keepdims=True)",
+     "z[:, L:] += np.triu(np.full((B, B), -np.inf), 1)\n        z -= z.max(axis=1, keepdims=True)", "attn"),
+    ("attention.py", "pages = np.asarray(page_table_s[:npg], dtype=np.int64)",
+     "pages = np.sort(np.asarray(page_table_s[:npg], dtype=np.int64))", "attn"),
+    ("attention.py", "out[:, gi, :] = p @ vals", "out[:, gi, :] = p @ keys", "attn"),
+    ("lmhead.py", "        logits[:, mask_id] = -np.inf\n        a, x1",
+     "        a, x1", "lm"),
+    ("lmhead.py", "arg = logits.argmax(axis=1)",
+     "arg = logits.shape[1] - 1 - logits[:, ::-1].argmax(axis=1)", "lm"),
+    ("lmhead.py", "logits = H @ W.T\n        logits[:, mask_id]",
+     "logits = (H @ W.T) / np.sqrt(H.shape[1])\n        logits[:, mask_id]", "lm"),
+    ("lmhead.py", "part = np.partition(e, -2, axis=1)[:, -2]",
+     "part = np.sort(e, axis=1)[:, -2] * 0 + np.sort(e, axis=1)[:, -3]", "lm"),
+    ("remask.py", "conf[s, i] >= tau", "conf[s, i] > tau", "remask"),
+    ("remask.py", "if conf[s, i] > conf[s, best]:", "if conf[s, i] >= conf[s, best]:", "remask"),
+    ("remask.py", "if flags & FALLBACK_LEFTMOST:", "if True:", "remask"),
+    ("remask.py", "            state[s] = SAVING", "            pass", "remask"),
+    ("remask.py", "for s in range(S) if seq_state[s] == DENOISING\n            for i in range(B)",
+     "for i in range(B) for s in range(S) if seq_state[s] == DENOISING", "remask"),
+]
+
+
+def load_mutant(fname, old, new):
+    pkg = types.ModuleType("oracle_mut")
+    pkg.__path__ = []
+    sys.modules["oracle_mut"] = pkg
+    for dep in ("bf16.py",):
+        spec = importlib.util.spec_from_file_location("oracle_mut." + dep[:-3], os.path.join(ORACLE, dep))
+        m = importlib.util.module_from_spec(spec)
+        sys.modules[spec.name] = m
+        spec.loader.exec_module(m)
+    src = open(os.path.join(ORACLE, fname)).read()
+    assert old in src, (fname, old)
+    src = src.replace(old, new)
+    name = "oracle_mut." + fname[:-3]
+    mod = types.ModuleType(name)
+    mod.__package__ = "oracle_mut"
+    sys.modules[name] = mod
+    exec(compile(src, f"<mutant {fname}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("mut", MUTANTS, ids=lambda m: f"{m[0]}:{m[1][:30]}")
+def test_mutant_is_caught(mut):
+    fname, old, new, fam = mut
+    mod = load_mutant(fname, old, new)
+    checks = {"attn": ATTN_CHECKS, "lm": LM_CHECKS, "remask": REMASK_CHECKS}[fam]
+    caught = []
+    for chk in checks:
+        try:
+            chk(mod)
+        except Exception:          # an assertion or a crash both count
+            caught.append(chk.__name__)
+    assert caught, f"no pin notices mutant {old!r} -> {new!r}"
