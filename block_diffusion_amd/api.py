@@ -1,0 +1,282 @@
+"""Thin Python binding of libdbd (ctypes).  Argument marshalling only: every
+step of the round runs in the library's HIP kernels.  PyTorch provides
+device memory and the current stream.
+
+The function names are those of the C ABI in include/dbd.h.  A missing or
+unloadable libdbd.so raises at import of the library (no fallback).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdbd.so")
+
+DBD_OK, DBD_ERR_INVALID_ARG, DBD_ERR_UNSUPPORTED, DBD_ERR_WORKSPACE, DBD_ERR_HIP = range(5)
+DBD_DENOISING, DBD_SAVING = 2, 3
+DBD_FALLBACK_LEFTMOST, DBD_COMPACT_ONLY = 1, 2
+
+_vp, _i32p, _u8p, _fp = C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p
+
+
+class dbd_round_args(C.Structure):
+    _fields_ = [(n, C.c_int) for n in
+                ("S", "B", "Hq", "Hkv", "D", "page_size", "max_pages_per_seq", "Hd", "V",
+                 "mask_token_id")] + [
+        ("dynamic_threshold", C.c_float), ("flags", C.c_uint32), ("softmax_scale", C.c_float),
+        ("q", _vp), ("k_blk", _vp), ("v_blk", _vp), ("k_cache", _vp), ("v_cache", _vp),
+        ("page_table", _vp), ("prefix_len", _vp), ("attn_out", _vp),
+        ("hidden", _vp), ("w_vocab", _vp), ("row_index", _vp), ("num_rows", _vp),
+        ("argmax_tok", _vp), ("conf", _vp), ("block_tokens", _vp), ("seq_state", _vp),
+        ("num_committed", _vp), ("workspace", _vp), ("workspace_bytes", C.c_size_t)]
+
+
+class DbdError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"libdbd status {status}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libdbd.so (once).  Raises if it is missing: build it with
+    ``python -m block_diffusion_amd.build``."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: run `python -m block_diffusion_amd.build` "
+                          "(there is no CPU fallback)")
+    L = C.CDLL(LIB_PATH)
+    i, f, u32, sz = C.c_int, C.c_float, C.c_uint32, C.c_size_t
+    L.dbd_attn_paged.argtypes = [i] * 7 + [_vp] * 7 + [f, _vp, _vp, sz, _vp]
+    L.dbd_attn_paged.restype = i
+    L.dbd_attn_workspace_size.argtypes = [i] * 7
+    L.dbd_attn_workspace_size.restype = sz
+    L.dbd_lmhead_conf.argtypes = [i] * 4 + [_vp] * 6 + [_vp, sz, _vp]
+    L.dbd_lmhead_conf.restype = i
+    L.dbd_lmhead_workspace_size.argtypes = [i, i]
+    L.dbd_lmhead_workspace_size.restype = sz
+    L.dbd_remask_commit.argtypes = [i, i, i, f, u32] + [_vp] * 7 + [_vp]
+    L.dbd_remask_commit.restype = i
+    L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
+    L.dbd_round.restype = i
+    L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
+    L.dbd_round_workspace_size.restype = sz
+    L.dbd_graph_create.argtypes = [C.POINTER(dbd_round_args), i, C.POINTER(_vp)]
+    L.dbd_graph_create.restype = i
+    L.dbd_graph_launch.argtypes = [_vp, _vp]
+    L.dbd_graph_launch.restype = i
+    L.dbd_graph_destroy.argtypes = [_vp]
+    L.dbd_graph_destroy.restype = None
+    L.dbd_validate_inputs.argtypes = [i] * 7 + [_vp] * 4
+    L.dbd_validate_inputs.restype = i
+    L.dbd_last_error.argtypes = []
+    L.dbd_last_error.restype = C.c_char_p
+    L.dbd_abi_version.argtypes = []
+    L.dbd_abi_version.restype = i
+    _lib = L
+    return L
+
+
+def _check(st):
+    if st != DBD_OK:
+        raise DbdError(st, lib().dbd_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def dbd_attn_workspace_size(S, B, Hq, Hkv, D, page_size, max_pages_per_seq):
+    return lib().dbd_attn_workspace_size(S, B, Hq, Hkv, D, page_size, max_pages_per_seq)
+
+
+def dbd_lmhead_workspace_size(max_rows, V):
+    return lib().dbd_lmhead_workspace_size(max_rows, V)
+
+
+def workspace(nbytes, device="cuda"):
+    """A device byte buffer (PyTorch's allocator aligns to 512 B)."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def dbd_attn_paged(q, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len, out,
+                   softmax_scale=0.0, ws=None, stream=None):
+    S, B, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    P = k_cache.shape[2]
+    maxp = page_table.shape[1]
+    for t, n in ((q, "q"), (k_blk, "k_blk"), (v_blk, "v_blk"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache"), (out, "out")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous bf16")
+    _need(k_blk, torch.bfloat16, (S, B, Hkv, D), "k_blk")
+    _need(v_blk, torch.bfloat16, (S, B, Hkv, D), "v_blk")
+    _need(v_cache, torch.bfloat16, tuple(k_cache.shape), "v_cache")
+    _need(out, torch.bfloat16, (S, B, Hq, D), "out")
+    _need(page_table, torch.int32, (S, maxp), "page_table")
+    _need(prefix_len, torch.int32, (S,), "prefix_len")
+    need = dbd_attn_workspace_size(S, B, Hq, Hkv, D, P, maxp)
+    if ws is None and need:
+        ws = workspace(need, q.device)
+    nbytes = ws.numel() if ws is not None else 0
+    _check(lib().dbd_attn_paged(S, B, Hq, Hkv, D, P, maxp, _ptr(q), _ptr(k_blk), _ptr(v_blk),
+                                _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                _ptr(prefix_len), float(softmax_scale), _ptr(out), _ptr(ws),
+                                nbytes, _stream(stream)))
+    return out
+
+
+def dbd_lmhead_conf(hidden, w_vocab, num_rows, argmax_tok, conf, mask_token_id,
+                    row_index=None, max_rows=None, ws=None, stream=None):
+    V, Hd = w_vocab.shape
+    if max_rows is None:
+        max_rows = row_index.shape[0] if row_index is not None else hidden.shape[0]
+    _need(hidden, torch.bfloat16, (hidden.shape[0], Hd), "hidden")
+    _need(w_vocab, torch.bfloat16, (V, Hd), "w_vocab")
+    _need(num_rows, torch.int32, (1,), "num_rows")
+    if row_index is not None:
+        if row_index.dtype != torch.int32 or row_index.numel() < max_rows:
+            raise ValueError("row_index must be int32 with at least max_rows entries")
+    need = dbd_lmhead_workspace_size(max_rows, V)
+    if ws is None and need:
+        ws = workspace(need, hidden.device)
+    _check(lib().dbd_lmhead_conf(max_rows, Hd, V, int(mask_token_id), _ptr(hidden),
+                                 _ptr(row_index), _ptr(num_rows), _ptr(w_vocab),
+                                 _ptr(argmax_tok), _ptr(conf), _ptr(ws),
+                                 ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def dbd_remask_commit(block_tokens, seq_state, argmax_tok, conf, row_index_out, num_rows_out,
+                      mask_token_id, dynamic_threshold, flags=0, num_committed=None,
+                      stream=None):
+    S, B = block_tokens.shape
+    _need(block_tokens, torch.int32, (S, B), "block_tokens")
+    _need(seq_state, torch.uint8, (S,), "seq_state")
+    _need(row_index_out, torch.int32, (S * B,), "row_index_out")
+    _need(num_rows_out, torch.int32, (1,), "num_rows_out")
+    _check(lib().dbd_remask_commit(S, B, int(mask_token_id), float(dynamic_threshold), int(flags),
+                                   _ptr(block_tokens), _ptr(seq_state), _ptr(argmax_tok),
+                                   _ptr(conf), _ptr(row_index_out), _ptr(num_rows_out),
+                                   _ptr(num_committed), _stream(stream)))
+
+
+@dataclass
+class RoundBuffers:
+    """Device state of the round that persists across rounds."""
+    row_index: torch.Tensor
+    num_rows: torch.Tensor
+    argmax_tok: torch.Tensor
+    conf: torch.Tensor
+    block_tokens: torch.Tensor
+    seq_state: torch.Tensor
+    num_committed: torch.Tensor
+    workspace: torch.Tensor
+
+
+def make_round_args(*, S, B, Hq, Hkv, D, page_size, max_pages_per_seq, Hd, V, mask_token_id,
+                    dynamic_threshold, q, k_blk, v_blk, k_cache, v_cache, page_table,
+                    prefix_len, attn_out, hidden, w_vocab, bufs: RoundBuffers, flags=0,
+                    softmax_scale=0.0) -> dbd_round_args:
+    a = dbd_round_args()
+    a.S, a.B, a.Hq, a.Hkv, a.D = S, B, Hq, Hkv, D
+    a.page_size, a.max_pages_per_seq, a.Hd, a.V = page_size, max_pages_per_seq, Hd, V
+    a.mask_token_id = mask_token_id
+    a.dynamic_threshold, a.flags, a.softmax_scale = dynamic_threshold, flags, softmax_scale
+    for n, t in (("q", q), ("k_blk", k_blk), ("v_blk", v_blk), ("k_cache", k_cache),
+                 ("v_cache", v_cache), ("page_table", page_table), ("prefix_len", prefix_len),
+                 ("attn_out", attn_out), ("hidden", hidden), ("w_vocab", w_vocab)):
+        setattr(a, n, _ptr(t))
+    for n in ("row_index", "num_rows", "argmax_tok", "conf", "block_tokens", "seq_state",
+              "num_committed", "workspace"):
+        setattr(a, n, _ptr(getattr(bufs, n)))
+    a.workspace_bytes = bufs.workspace.numel()
+    return a
+
+
+def dbd_round_workspace_size(args: dbd_round_args) -> int:
+    return lib().dbd_round_workspace_size(C.byref(args))
+
+
+def dbd_round(args: dbd_round_args, stream=None):
+    _check(lib().dbd_round(C.byref(args), _stream(stream)))
+
+
+class Graph:
+    """n_rounds captured rounds replayed with one launch (dbd_graph_*)."""
+
+    def __init__(self, args_list):
+        arr = (dbd_round_args * len(args_list))(*args_list)
+        h = C.c_void_p()
+        _check(lib().dbd_graph_create(arr, len(args_list), C.byref(h)))
+        self._h = h
+
+    def launch(self, stream=None):
+        _check(lib().dbd_graph_launch(self._h, _stream(stream)))
+
+    def close(self):
+        if self._h:
+            lib().dbd_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def dbd_graph_create(args_list):
+    return Graph(args_list)
+
+
+def dbd_validate_inputs(S, B, page_size, max_pages_per_seq, num_pages, V, mask_token_id,
+                        page_table=None, prefix_len=None, block_tokens=None, seq_state=None):
+    """Host-side check of host (numpy) copies; raises DbdError on a bad input."""
+    import numpy as np
+
+    def p(a, dt):
+        if a is None:
+            return None, None
+        a = np.ascontiguousarray(a, dtype=dt)
+        return a, a.ctypes.data
+    pt, ppt = p(page_table, np.int32)
+    pl, ppl = p(prefix_len, np.int32)
+    bt, pbt = p(block_tokens, np.int32)
+    ss, pss = p(seq_state, np.uint8)
+    _check(lib().dbd_validate_inputs(S, B, page_size, max_pages_per_seq, num_pages, V,
+                                     mask_token_id, ppt, ppl, pbt, pss))
+
+
+def dbd_abi_version():
+    return lib().dbd_abi_version()

@@ -1,0 +1,365 @@
+// libdbd C ABI: host-side validation, workspace carving, launches of the
+// denoise-round kernels, and graph capture of whole rounds.  The contract of
+// every entry point is in include/dbd.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/dbd.h"
+#include "dbd_internal.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+dbd_status fail(dbd_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+dbd_status hip_fail(hipError_t e, const char* where) {
+  return fail(DBD_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define REQUIRE(cond, ...)                                          \
+  do {                                                              \
+    if (!(cond)) return fail(DBD_ERR_INVALID_ARG, __VA_ARGS__);     \
+  } while (0)
+#define REQUIRE_PTR(p)                                                       \
+  do {                                                                       \
+    if ((p) == nullptr) return fail(DBD_ERR_INVALID_ARG, #p " is NULL");     \
+    if (!aligned((p), 16)) return fail(DBD_ERR_INVALID_ARG, #p " is not 16-byte aligned"); \
+  } while (0)
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+dbd_status check_attn(int S, int B, int Hq, int Hkv, int D, int page_size,
+                      int max_pages) {
+  REQUIRE(S >= 1, "S must be >= 1 (got %d)", S);
+  REQUIRE(B >= 1 && B <= 64, "block_length must be in [1,64] (got %d)", B);
+  REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  REQUIRE(page_size >= 16 && page_size % 16 == 0, "page_size must be a positive multiple of 16 (got %d)", page_size);
+  REQUIRE(max_pages >= 1, "max_pages_per_seq must be >= 1 (got %d)", max_pages);
+  REQUIRE(S <= 65535, "S must be <= 65535 (got %d)", S);
+  REQUIRE((long)Hkv * ((Hq / Hkv) * B + 63) / 64 <= 65535, "too many kv heads x row groups");
+  if (D != 64 && D != 128) return fail(DBD_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+  return DBD_OK;
+}
+
+dbd_status check_lm(int max_rows, int Hd, int V, int mask) {
+  REQUIRE(max_rows >= 0, "max_rows must be >= 0 (got %d)", max_rows);
+  REQUIRE(V >= 2, "vocab size must be >= 2 (got %d)", V);
+  REQUIRE(mask >= 0 && mask < V, "mask_token_id %d outside [0,%d)", mask, V);
+  REQUIRE(Hd >= 64 && Hd % 64 == 0, "hidden size must be a positive multiple of 64 (got %d)", Hd);
+  REQUIRE((long)V * Hd < (1L << 31), "V*Hd must fit in 31 bits");
+  REQUIRE((long)max_rows * Hd < (1L << 31), "max_rows*Hd must fit in 31 bits");
+  return DBD_OK;
+}
+
+dbd_status check_remask(int S, int B, float tau) {
+  REQUIRE(S >= 1 && S <= dbd::kRemaskMaxSeqs, "S must be in [1,%d] (got %d)", dbd::kRemaskMaxSeqs, S);
+  REQUIRE(B >= 1 && B <= 64, "block_length must be in [1,64] (got %d)", B);
+  REQUIRE(!isnan(tau), "dynamic_threshold is NaN");
+  return DBD_OK;
+}
+
+dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pages,
+                        const dbd_bf16* q, const dbd_bf16* k_blk, const dbd_bf16* v_blk,
+                        const dbd_bf16* k_cache, const dbd_bf16* v_cache,
+                        const int32_t* page_table, const int32_t* prefix_len,
+                        float scale, dbd_bf16* out, void* ws, size_t ws_bytes,
+                        hipStream_t st) {
+  dbd::AttnPlan plan = dbd::attn_plan(S, B, Hq, Hkv, D, P, max_pages);
+  if (plan.ws_bytes > 0) {
+    if (ws == nullptr || ws_bytes < plan.ws_bytes)
+      return fail(DBD_ERR_WORKSPACE, "attention workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
+    if (!aligned(ws, 256)) return fail(DBD_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  }
+  dbd::AttnArgs a{};
+  a.q = q; a.k_blk = k_blk; a.v_blk = v_blk; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.page_table = page_table; a.prefix_len = prefix_len; a.out = out;
+  const size_t slots = (size_t)S * Hkv * plan.n_rg * plan.n_chunk_max * 16 * plan.RT;
+  a.part_o = static_cast<float*>(ws);
+  a.part_ml = plan.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(ws) + round_up(slots * D * sizeof(float))) : nullptr;
+  a.S = S; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.P = P; a.max_pages = max_pages;
+  a.n_rg = plan.n_rg; a.chunk_keys = plan.chunk_keys; a.n_chunk_max = plan.n_chunk_max;
+  const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  hipError_t e = dbd::attn_launch(plan, a, st);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return DBD_OK;
+}
+
+dbd_status enqueue_lm(int max_rows, int Hd, int V, int mask, const dbd_bf16* hidden,
+                      const int32_t* row_index, const int32_t* num_rows,
+                      const dbd_bf16* w, int32_t* argmax_tok, float* conf,
+                      void* ws, size_t ws_bytes, hipStream_t st) {
+  if (max_rows == 0) return DBD_OK;
+  const size_t need = dbd::lmhead_ws_bytes(max_rows, V);
+  if (ws == nullptr || ws_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "LM-head workspace needs %zu bytes (got %zu)", need, ws_bytes);
+  if (!aligned(ws, 256)) return fail(DBD_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  dbd::LmArgs a{};
+  a.hidden = hidden; a.row_index = row_index; a.num_rows = num_rows; a.w = w;
+  a.Hd = Hd; a.V = V; a.mask_id = mask; a.max_rows = max_rows;
+  a.n_vt = (V + 127) / 128;
+  const size_t one = need / 3;
+  char* base = static_cast<char*>(ws);
+  a.pm = reinterpret_cast<float*>(base);
+  a.pa = reinterpret_cast<int32_t*>(base + one);
+  a.ps = reinterpret_cast<float*>(base + 2 * one);
+  a.argmax_tok = argmax_tok; a.conf = conf;
+  hipError_t e = dbd::lmhead_launch(a, st);
+  if (e != hipSuccess) return hip_fail(e, "LM-head launch");
+  return DBD_OK;
+}
+
+dbd_status enqueue_remask(int S, int B, int mask, float tau, uint32_t flags,
+                          int32_t* block_tokens, uint8_t* seq_state,
+                          const int32_t* argmax_tok, const float* conf,
+                          int32_t* row_index_out, int32_t* num_rows_out,
+                          int32_t* num_committed, hipStream_t st) {
+  dbd::RemaskArgs a{};
+  a.S = S; a.B = B; a.mask_id = mask; a.tau = tau; a.flags = flags;
+  a.block_tokens = block_tokens; a.seq_state = seq_state;
+  a.argmax_tok = argmax_tok; a.conf = conf;
+  a.row_index_out = row_index_out; a.num_rows_out = num_rows_out;
+  a.num_committed = num_committed;
+  hipError_t e = dbd::remask_launch(a, st);
+  if (e != hipSuccess) return hip_fail(e, "remask launch");
+  return DBD_OK;
+}
+
+dbd_status check_round(const dbd_round_args* a) {
+  REQUIRE(a != nullptr, "args is NULL");
+  dbd_status s = check_attn(a->S, a->B, a->Hq, a->Hkv, a->D, a->page_size, a->max_pages_per_seq);
+  if (s != DBD_OK) return s;
+  s = check_lm(a->S * a->B, a->Hd, a->V, a->mask_token_id);
+  if (s != DBD_OK) return s;
+  s = check_remask(a->S, a->B, a->dynamic_threshold);
+  if (s != DBD_OK) return s;
+  REQUIRE_PTR(a->q); REQUIRE_PTR(a->k_blk); REQUIRE_PTR(a->v_blk);
+  REQUIRE_PTR(a->k_cache); REQUIRE_PTR(a->v_cache);
+  REQUIRE_PTR(a->page_table); REQUIRE_PTR(a->prefix_len); REQUIRE_PTR(a->attn_out);
+  REQUIRE_PTR(a->hidden); REQUIRE_PTR(a->w_vocab); REQUIRE_PTR(a->row_index);
+  REQUIRE_PTR(a->num_rows); REQUIRE_PTR(a->argmax_tok); REQUIRE_PTR(a->conf);
+  REQUIRE_PTR(a->block_tokens); REQUIRE_PTR(a->seq_state);
+  const size_t need = dbd_round_workspace_size(a);
+  if (a->workspace == nullptr || a->workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "round workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
+  REQUIRE(aligned(a->workspace, 256), "workspace is not 256-byte aligned");
+  return DBD_OK;
+}
+
+dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
+  const dbd::AttnPlan plan = dbd::attn_plan(a->S, a->B, a->Hq, a->Hkv, a->D, a->page_size, a->max_pages_per_seq);
+  const size_t attn_ws = round_up(plan.ws_bytes);
+  char* ws = static_cast<char*>(a->workspace);
+  dbd_status s = enqueue_attn(a->S, a->B, a->Hq, a->Hkv, a->D, a->page_size, a->max_pages_per_seq,
+                              a->q, a->k_blk, a->v_blk, a->k_cache, a->v_cache, a->page_table,
+                              a->prefix_len, a->softmax_scale, a->attn_out, ws, plan.ws_bytes, st);
+  if (s != DBD_OK) return s;
+  const int max_rows = a->S * a->B;
+  s = enqueue_lm(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index, a->num_rows,
+                 a->w_vocab, a->argmax_tok, a->conf, ws + attn_ws, a->workspace_bytes - attn_ws, st);
+  if (s != DBD_OK) return s;
+  return enqueue_remask(a->S, a->B, a->mask_token_id, a->dynamic_threshold, a->flags & ~DBD_COMPACT_ONLY,
+                        a->block_tokens, a->seq_state, a->argmax_tok, a->conf, a->row_index,
+                        a->num_rows, a->num_committed, st);
+}
+
+}  // namespace
+
+struct dbd_graph {
+  hipStream_t stream;
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+extern "C" {
+
+int dbd_abi_version(void) { return DBD_ABI_VERSION; }
+
+const char* dbd_last_error(void) { return g_err.c_str(); }
+
+size_t dbd_attn_workspace_size(int S, int B, int Hq, int Hkv, int D, int page_size,
+                               int max_pages_per_seq) {
+  if (check_attn(S, B, Hq, Hkv, D, page_size, max_pages_per_seq) != DBD_OK) return 0;
+  return dbd::attn_plan(S, B, Hq, Hkv, D, page_size, max_pages_per_seq).ws_bytes;
+}
+
+size_t dbd_lmhead_workspace_size(int max_rows, int V) {
+  if (max_rows <= 0 || V < 2) return 0;
+  return dbd::lmhead_ws_bytes(max_rows, V);
+}
+
+size_t dbd_round_workspace_size(const dbd_round_args* a) {
+  if (a == nullptr) return 0;
+  const size_t attn = dbd_attn_workspace_size(a->S, a->B, a->Hq, a->Hkv, a->D, a->page_size,
+                                              a->max_pages_per_seq);
+  return round_up(attn) + dbd_lmhead_workspace_size(a->S * a->B, a->V);
+}
+
+dbd_status dbd_attn_paged(int S, int B, int Hq, int Hkv, int D, int page_size,
+                          int max_pages_per_seq, const dbd_bf16* q, const dbd_bf16* k_blk,
+                          const dbd_bf16* v_blk, const dbd_bf16* k_cache,
+                          const dbd_bf16* v_cache, const int32_t* page_table,
+                          const int32_t* prefix_len, float softmax_scale, dbd_bf16* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  dbd_status s = check_attn(S, B, Hq, Hkv, D, page_size, max_pages_per_seq);
+  if (s != DBD_OK) return s;
+  REQUIRE_PTR(q); REQUIRE_PTR(k_blk); REQUIRE_PTR(v_blk); REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache); REQUIRE_PTR(page_table); REQUIRE_PTR(prefix_len); REQUIRE_PTR(out);
+  REQUIRE(!isnan(softmax_scale), "softmax_scale is NaN");
+  return enqueue_attn(S, B, Hq, Hkv, D, page_size, max_pages_per_seq, q, k_blk, v_blk, k_cache,
+                      v_cache, page_table, prefix_len, softmax_scale, out, workspace,
+                      workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_lmhead_conf(int max_rows, int Hd, int V, int mask_token_id,
+                           const dbd_bf16* hidden, const int32_t* row_index,
+                           const int32_t* num_rows, const dbd_bf16* w_vocab,
+                           int32_t* argmax_tok, float* conf, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  dbd_status s = check_lm(max_rows, Hd, V, mask_token_id);
+  if (s != DBD_OK) return s;
+  REQUIRE_PTR(hidden); REQUIRE_PTR(num_rows); REQUIRE_PTR(w_vocab);
+  REQUIRE_PTR(argmax_tok); REQUIRE_PTR(conf);
+  if (row_index != nullptr) REQUIRE_PTR(row_index);
+  return enqueue_lm(max_rows, Hd, V, mask_token_id, hidden, row_index, num_rows, w_vocab,
+                    argmax_tok, conf, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_remask_commit(int S, int B, int mask_token_id, float dynamic_threshold,
+                             uint32_t flags, int32_t* block_tokens, uint8_t* seq_state,
+                             const int32_t* argmax_tok, const float* conf,
+                             int32_t* row_index_out, int32_t* num_rows_out,
+                             int32_t* num_committed, void* stream) {
+  dbd_status s = check_remask(S, B, dynamic_threshold);
+  if (s != DBD_OK) return s;
+  REQUIRE((flags & ~(DBD_FALLBACK_LEFTMOST | DBD_COMPACT_ONLY)) == 0, "unknown flags 0x%x", flags);
+  REQUIRE_PTR(block_tokens); REQUIRE_PTR(seq_state); REQUIRE_PTR(row_index_out);
+  REQUIRE_PTR(num_rows_out);
+  if (!(flags & DBD_COMPACT_ONLY)) {
+    REQUIRE_PTR(argmax_tok);
+    REQUIRE_PTR(conf);
+  }
+  if (num_committed != nullptr) REQUIRE_PTR(num_committed);
+  return enqueue_remask(S, B, mask_token_id, dynamic_threshold, flags, block_tokens, seq_state,
+                        argmax_tok, conf, row_index_out, num_rows_out, num_committed,
+                        static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_round(const dbd_round_args* a, void* stream) {
+  dbd_status s = check_round(a);
+  if (s != DBD_OK) return s;
+  return enqueue_round(a, static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_graph_create(const dbd_round_args* args, int n_rounds, dbd_graph** out) {
+  REQUIRE(out != nullptr, "out is NULL");
+  REQUIRE(args != nullptr && n_rounds >= 1, "need at least one round");
+  *out = nullptr;
+  for (int i = 0; i < n_rounds; ++i) {
+    dbd_status s = check_round(&args[i]);
+    if (s != DBD_OK) return s;
+  }
+  dbd_graph* g = new dbd_graph{};
+  hipError_t e = hipStreamCreateWithFlags(&g->stream, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete g;
+    return hip_fail(e, "hipStreamCreateWithFlags");
+  }
+  e = hipStreamBeginCapture(g->stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(g->stream);
+    delete g;
+    return hip_fail(e, "hipStreamBeginCapture");
+  }
+  dbd_status st = DBD_OK;
+  for (int i = 0; i < n_rounds && st == DBD_OK; ++i) st = enqueue_round(&args[i], g->stream);
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(g->stream, &graph);
+  if (st != DBD_OK || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(g->stream);
+    delete g;
+    return st != DBD_OK ? st : hip_fail(e, "hipStreamEndCapture");
+  }
+  g->graph = graph;
+  e = hipGraphInstantiate(&g->exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    (void)hipStreamDestroy(g->stream);
+    delete g;
+    return hip_fail(e, "hipGraphInstantiate");
+  }
+  *out = g;
+  return DBD_OK;
+}
+
+dbd_status dbd_graph_launch(dbd_graph* g, void* stream) {
+  REQUIRE(g != nullptr, "graph is NULL");
+  hipError_t e = hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hipGraphLaunch");
+  return DBD_OK;
+}
+
+void dbd_graph_destroy(dbd_graph* g) {
+  if (!g) return;
+  if (g->exec) (void)hipGraphExecDestroy(g->exec);
+  if (g->graph) (void)hipGraphDestroy(g->graph);
+  if (g->stream) (void)hipStreamDestroy(g->stream);
+  delete g;
+}
+
+dbd_status dbd_validate_inputs(int S, int B, int page_size, int max_pages_per_seq, int num_pages,
+                               int V, int mask_token_id, const int32_t* page_table,
+                               const int32_t* prefix_len, const int32_t* block_tokens,
+                               const uint8_t* seq_state) {
+  REQUIRE(S >= 1 && B >= 1 && B <= 64 && page_size >= 1 && max_pages_per_seq >= 1 && num_pages >= 0,
+          "bad sizes");
+  REQUIRE(V >= 2 && mask_token_id >= 0 && mask_token_id < V, "mask_token_id %d outside [0,%d)",
+          mask_token_id, V);
+  if (prefix_len) {
+    for (int s = 0; s < S; ++s) {
+      const long L = prefix_len[s];
+      if (L < 0 || L > (long)max_pages_per_seq * page_size)
+        return fail(DBD_ERR_INVALID_ARG, "prefix_len[%d] = %ld outside [0,%ld]", s, L,
+                    (long)max_pages_per_seq * page_size);
+      if (page_table) {
+        const long npg = (L + page_size - 1) / page_size;
+        for (long j = 0; j < npg; ++j) {
+          const int p = page_table[(size_t)s * max_pages_per_seq + j];
+          if (p < 0 || p >= num_pages)
+            return fail(DBD_ERR_INVALID_ARG, "page_table[%d][%ld] = %d outside [0,%d)", s, j, p,
+                        num_pages);
+        }
+      }
+    }
+  }
+  if (block_tokens) {
+    for (long i = 0; i < (long)S * B; ++i)
+      if (block_tokens[i] < 0 || block_tokens[i] >= V)
+        return fail(DBD_ERR_INVALID_ARG, "block_tokens[%ld] = %d outside [0,%d)", i, block_tokens[i], V);
+  }
+  if (seq_state) {
+    for (int s = 0; s < S; ++s)
+      if (seq_state[s] > DBD_FINISHED)
+        return fail(DBD_ERR_INVALID_ARG, "seq_state[%d] = %d is not a state", s, seq_state[s]);
+  }
+  return DBD_OK;
+}
+
+}  // extern "C"

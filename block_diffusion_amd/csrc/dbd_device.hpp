@@ -1,0 +1,61 @@
+// Device-side helpers shared by the gfx950 kernels of libdbd: vector types,
+// 16-byte loads, bf16 conversion and wave-level shuffles.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dbd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kWave = 64;
+
+// 16-byte global load (8 bf16) reinterpreted as an MFMA operand.
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+  u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x4 ld_u32x4(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// 2^x via the hardware exponential (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) {
+  return __shfl_xor(v, m, kWave);
+}
+__device__ __forceinline__ int shfl_xor_i(int v, int m) {
+  return __shfl_xor(v, m, kWave);
+}
+
+// Compiler-level ordering of LDS traffic among the lanes of one wave.  A
+// wave's LDS instructions execute in issue order, so a write by one lane is
+// seen by a later read of another lane of the same wave once the compiler
+// keeps the order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+}  // namespace dbd

@@ -1,0 +1,74 @@
+// Internal (non-ABI) declarations of libdbd: kernel argument blocks, launch
+// plans and launchers.  Host and device code both include this header.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dbd {
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k_blk;
+  const uint16_t* v_blk;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  const int32_t* prefix_len;
+  uint16_t* out;
+  float* part_o;   // [S][Hkv*n_rg][n_chunk_max][rows][D] unnormalised sums
+  float2* part_ml; // [S][Hkv*n_rg][n_chunk_max][rows] (max, sum), log2 units
+  int S, B, Hq, Hkv, G, P, max_pages;
+  int n_rg;        // row groups per kv head (rows = G*B split in 16*RT)
+  int chunk_keys;  // prefix keys per work item (multiple of 64)
+  int n_chunk_max; // chunk slots per (sequence, kv head, row group)
+  float scale_log2;
+};
+
+struct AttnPlan {
+  int D, RT, n_rg, chunk_keys, n_chunk_max;
+  size_t ws_bytes;
+};
+
+AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size,
+                   int max_pages);
+hipError_t attn_launch(const AttnPlan& plan, const AttnArgs& a,
+                       hipStream_t stream);
+
+// ------------------------------------------------------------------ LM head
+struct LmArgs {
+  const uint16_t* hidden;
+  const int32_t* row_index;
+  const int32_t* num_rows;
+  const uint16_t* w;
+  int Hd, V, mask_id, max_rows;
+  int n_vt;        // 128-column vocabulary tiles = partials per row
+  float* pm;       // [max_rows][n_vt] tile max logit
+  int32_t* pa;     // [max_rows][n_vt] tile argmax (lowest id on ties)
+  float* ps;       // [max_rows][n_vt] sum exp(l - tile max)
+  int32_t* argmax_tok;
+  float* conf;
+};
+
+size_t lmhead_ws_bytes(int max_rows, int V);
+hipError_t lmhead_launch(const LmArgs& a, hipStream_t stream);
+
+// ------------------------------------------------------------------- remask
+struct RemaskArgs {
+  int S, B, mask_id;
+  float tau;
+  uint32_t flags;
+  int32_t* block_tokens;
+  uint8_t* seq_state;
+  const int32_t* argmax_tok;
+  const float* conf;
+  int32_t* row_index_out;
+  int32_t* num_rows_out;
+  int32_t* num_committed;
+};
+
+constexpr int kRemaskMaxSeqs = 8192;
+hipError_t remask_launch(const RemaskArgs& a, hipStream_t stream);
+
+}  // namespace dbd

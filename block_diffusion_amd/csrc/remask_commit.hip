@@ -1,0 +1,112 @@
+// Threshold remask (low_confidence_dynamic) and row compaction, gfx950.
+//
+// The commit rule of JetEngine's low_confidence_dynamic strategy (developer
+// notes, "Remasking Strategies": unmask every position above the
+// threshold, with a fallback) on DENOISING sequences, and the state change
+// to SAVING once a block holds no mask (developer notes, "Scheduler").
+// Confidences and the threshold are compared in float32.
+//
+// One workgroup of 16 waves.  Pass 1: a wave per sequence, lane = block
+// position (B <= 64): ballot of the masked set and of the positions at or
+// above the threshold; if none qualifies, the most confident masked
+// position (wave max, then the lowest lane reaching it), or the leftmost
+// with DBD_FALLBACK_LEFTMOST.  The still-masked set of each sequence is kept
+// as a 64-bit mask in LDS.  Pass 2: exclusive scan of the per-sequence
+// counts.  Pass 3: each still-masked position writes s*B+i at its rank, so
+// the list is sequence-major and position-minor, the same on every run.
+#include "dbd_device.hpp"
+#include "dbd_internal.hpp"
+
+namespace dbd {
+
+constexpr uint32_t kFallbackLeftmost = 1u;
+constexpr uint32_t kCompactOnly = 2u;
+constexpr uint8_t kDenoising = 2, kSaving = 3;
+
+__global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
+  __shared__ unsigned long long s_left[kRemaskMaxSeqs];
+  __shared__ int s_off[kRemaskMaxSeqs];
+  __shared__ int s_wsum[16];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int S = a.S, B = a.B;
+
+  // pass 1: commit, state, still-masked set
+  for (int s = wave; s < S; s += 16) {
+    const uint8_t st = a.seq_state[s];  // same for every lane of the wave
+    const bool in = lane < B;
+    const bool den = st == kDenoising;
+    const bool masked = in && den && a.block_tokens[s * B + lane] == a.mask_id;
+    const unsigned long long mball = __ballot(masked);
+    bool still = masked;
+    if (den && !(a.flags & kCompactOnly)) {
+      const float c = masked ? a.conf[s * B + lane] : -INFINITY;
+      unsigned long long cball = __ballot(masked && c >= a.tau);
+      if (cball == 0ull && mball != 0ull) {
+        if (a.flags & kFallbackLeftmost) {
+          cball = mball & (~mball + 1ull);  // lowest set bit
+        } else {
+          float best = c;
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) best = fmaxf(best, shfl_xor_f(best, off));
+          const unsigned long long tie = __ballot(masked && c == best);
+          cball = tie & (~tie + 1ull);
+        }
+      }
+      const bool commit = (cball >> lane) & 1ull;
+      if (commit) a.block_tokens[s * B + lane] = a.argmax_tok[s * B + lane];
+      still = masked && !commit;
+      const unsigned long long sball = __ballot(still);
+      if (lane == 0) {
+        if (sball == 0ull) a.seq_state[s] = kSaving;
+        if (a.num_committed) a.num_committed[s] = __popcll(cball);
+      }
+    } else if (!(a.flags & kCompactOnly) && a.num_committed && lane == 0) {
+      a.num_committed[s] = 0;
+    }
+    const unsigned long long left = __ballot(still);
+    if (lane == 0) s_left[s] = left;
+  }
+  __syncthreads();
+
+  // pass 2: exclusive scan of per-sequence counts
+  const int per = (S + 1023) / 1024;
+  const int b0 = tid * per;
+  int local = 0;
+  for (int j = 0; j < per; ++j)
+    if (b0 + j < S) local += __popcll(s_left[b0 + j]);
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int wpre = 0;
+  for (int w = 0; w < wave; ++w) wpre += s_wsum[w];
+  int run = wpre + incl - local;
+  for (int j = 0; j < per; ++j)
+    if (b0 + j < S) {
+      s_off[b0 + j] = run;
+      run += __popcll(s_left[b0 + j]);
+    }
+  if (tid == 1023) *a.num_rows_out = wpre + incl;
+  __syncthreads();
+
+  // pass 3: scatter row ids
+  for (int s = wave; s < S; s += 16) {
+    const unsigned long long left = s_left[s];
+    if (lane < B && ((left >> lane) & 1ull)) {
+      const unsigned long long below = lane ? (left & ((1ull << lane) - 1ull)) : 0ull;
+      a.row_index_out[s_off[s] + __popcll(below)] = s * B + lane;
+    }
+  }
+}
+
+hipError_t remask_launch(const RemaskArgs& a, hipStream_t st) {
+  remask_kernel<<<1, 1024, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace dbd

@@ -1,0 +1,229 @@
+/*
+ * dbd.h -- C ABI of libdbd, one denoise round of block-diffusion decoding on
+ * an AMD Instinct MI355X (gfx950).
+ *
+ * A round (JetEngine README, "Block Diffusion Decoding"; JetEngine developer
+ * notes (CLAUDE.md), "Entry Point & Engine": step() runs the denoise batch,
+ * then postprocesses the logits) takes every active sequence's block of
+ * block_length tokens through three steps:
+ *   1. block-diffusion attention over the sequence's paged KV prefix and its
+ *      own block (bidirectional inside the block), grouped-query heads;
+ *   2. the selective LM head: only masked positions of DENOISING sequences
+ *      are projected to the vocabulary, fused with the softmax, giving each
+ *      such position its greedy token and confidence; logits never reach
+ *      device memory;
+ *   3. threshold remasking (low_confidence_dynamic), then the compact list
+ *      of still-masked rows that the next round's LM head projects.
+ *
+ * Conventions (every entry point):
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates or frees on these calls, never synchronises and never
+ *     reads device data from the host.  Work is enqueued on `stream` (a
+ *     hipStream_t passed as void*; NULL = the null stream) in stream order.
+ *   - Scalar arguments and pointer alignment are validated on the host
+ *     before anything is enqueued; a non-OK status means nothing was
+ *     enqueued, and dbd_last_error() returns a message (thread-local).
+ *     Device-resident data (page ids, prefix lengths, row lists, counts) is
+ *     trusted on these calls; dbd_validate_inputs() checks host copies.
+ *   - bf16 tensors are passed as raw 16-bit patterns (dbd_bf16).
+ *   - No exception crosses the ABI.
+ */
+#ifndef DBD_H
+#define DBD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DBD_ABI_VERSION 1
+
+typedef uint16_t dbd_bf16;
+
+typedef enum {
+  DBD_OK = 0,
+  DBD_ERR_INVALID_ARG = 1, /* a scalar or pointer failed host validation   */
+  DBD_ERR_UNSUPPORTED = 2, /* valid but outside what the kernels support   */
+  DBD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
+  DBD_ERR_HIP = 4          /* a HIP runtime call failed                    */
+} dbd_status;
+
+/* Sequence states, in the order of the scheduler's state machine (JetEngine
+ * developer notes, "Scheduler": WAITING -> PREFILLING -> DENOISING ->
+ * SAVING -> FINISHED).  A round reads DENOISING and writes SAVING. */
+enum { DBD_WAITING = 0, DBD_PREFILLING = 1, DBD_DENOISING = 2,
+       DBD_SAVING = 3, DBD_FINISHED = 4 };
+
+/* dbd_remask_commit flags */
+#define DBD_FALLBACK_LEFTMOST 1u /* fallback commits the leftmost masked position */
+#define DBD_COMPACT_ONLY 2u      /* no commit: only rebuild the row list           */
+
+/* ------------------------------------------------------------------------
+ * dbd_attn_paged -- block-diffusion attention over a paged KV cache.
+ *
+ * Defined by the denoise step's attention pattern (JetEngine developer
+ * notes, "ModelRunner": prefill and denoise use different attention
+ * patterns; "Layers": paged-KV denoise attention) over the paged cache with
+ * per-sequence block tables (README architecture tree, "Paged KV Cache";
+ * developer notes, "Chain Mechanism": positions/block tables).
+ *
+ * For sequence s, query head h (kv head g = h / (Hq/Hkv)), block position i:
+ *   keys   = the L_s = prefix_len[s] prefix tokens, token j in page
+ *            page_table[s*max_pages_per_seq + j/page_size] at slot
+ *            j % page_size, followed by the B block tokens (k_blk);
+ *   out    = softmax(q . keys^T * scale) . values, no mask inside the block.
+ *
+ * Layouts (row-major, bf16 unless noted):
+ *   q, out        [S][B][Hq][D]
+ *   k_blk, v_blk  [S][B][Hkv][D]
+ *   k_cache,
+ *   v_cache       [num_pages][Hkv][page_size][D]
+ *   page_table    int32 [S][max_pages_per_seq]; entries past a prefix's
+ *                 last page are not read
+ *   prefix_len    int32 [S], 0 <= L_s <= max_pages_per_seq*page_size
+ * softmax_scale <= 0 selects 1/sqrt(D).  Slots of a prefix's last page past
+ * its end are never used (they may hold anything, NaN included).
+ * Requirements: 1 <= B <= 64, D in {64,128}, Hq % Hkv == 0,
+ * page_size % 16 == 0, all pointers 16-byte aligned.
+ * workspace: at least dbd_attn_workspace_size(...) bytes of device memory,
+ * 256-byte aligned; contents on entry are ignored.
+ * ---------------------------------------------------------------------- */
+dbd_status dbd_attn_paged(int S, int B, int Hq, int Hkv, int D, int page_size,
+                          int max_pages_per_seq,
+                          const dbd_bf16* q, const dbd_bf16* k_blk,
+                          const dbd_bf16* v_blk, const dbd_bf16* k_cache,
+                          const dbd_bf16* v_cache, const int32_t* page_table,
+                          const int32_t* prefix_len, float softmax_scale,
+                          dbd_bf16* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+size_t dbd_attn_workspace_size(int S, int B, int Hq, int Hkv, int D,
+                               int page_size, int max_pages_per_seq);
+
+/* ------------------------------------------------------------------------
+ * dbd_lmhead_conf -- selective LM head fused with the softmax.
+ *
+ * Defined by selective logits (README, "Selective Logits": the LM head runs
+ * only for DENOISING sequences) restricted to masked positions (developer
+ * notes, "Optimization History": sparse logits), with greedy decoding
+ * (SDAR page, generate.py: greedy generation).
+ *
+ * For each r < *num_rows (device scalar), with row = row_index[r]
+ * (row_index == NULL: row = r):
+ *   l_v = sum_k hidden[row][k] * w_vocab[v][k]   (fp32 accumulation of the
+ *         bf16 products; logits are never rounded to bf16 or stored),
+ *   over every v != mask_token_id;
+ *   argmax_tok[row] = the smallest v with the largest l_v;
+ *   conf[row]       = exp(l_max - logsumexp_v l_v) = max probability.
+ * Rows not listed are not written.
+ * Layouts: hidden [rows][Hd] bf16 (row = s*B + position); w_vocab [V][Hd]
+ * bf16 (row v is column v of W in R^{Hd x V}); row_index int32 [max_rows];
+ * num_rows int32 device scalar, 0 <= *num_rows <= max_rows.
+ * Requirements: Hd % 64 == 0, V >= 2, 0 <= mask_token_id < V.
+ * workspace: dbd_lmhead_workspace_size(max_rows, V) bytes, 256-B aligned.
+ * ---------------------------------------------------------------------- */
+dbd_status dbd_lmhead_conf(int max_rows, int Hd, int V, int mask_token_id,
+                           const dbd_bf16* hidden, const int32_t* row_index,
+                           const int32_t* num_rows, const dbd_bf16* w_vocab,
+                           int32_t* argmax_tok, float* conf, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+size_t dbd_lmhead_workspace_size(int max_rows, int V);
+
+/* ------------------------------------------------------------------------
+ * dbd_remask_commit -- threshold remask (low_confidence_dynamic) and the
+ * next round's row list.
+ *
+ * Defined by the remasking strategy low_confidence_dynamic (developer notes,
+ * "Remasking Strategies": unmask every position above the threshold, with a
+ * fallback; README usage with dynamic_threshold) and the scheduler's state
+ * machine (developer notes, "Scheduler").
+ *
+ * For each DENOISING sequence s with masked set M = {i : block_tokens[s][i]
+ * == mask_token_id}:
+ *   C = {i in M : conf[s*B+i] >= dynamic_threshold}  (float32 compare);
+ *   if C is empty and M is not: C = {most confident i in M} (lowest i on
+ *   ties), or with DBD_FALLBACK_LEFTMOST the leftmost i in M;
+ *   block_tokens[s][i] = argmax_tok[s*B+i] for i in C;
+ *   if no mask is left: seq_state[s] = DBD_SAVING.
+ * Other states are untouched.  DBD_COMPACT_ONLY skips the commit and the
+ * state change.  Then row_index_out receives s*B+i for every still-masked
+ * position of every DENOISING sequence, sequence-major and position-minor,
+ * and *num_rows_out their count.  num_committed (may be NULL) receives the
+ * number committed per sequence.
+ * Layouts: block_tokens int32 [S][B] in/out; seq_state uint8 [S] in/out;
+ * conf float [S*B], argmax_tok int32 [S*B] (read only at masked positions
+ * of DENOISING sequences); row_index_out int32 [S*B].
+ * Requirements: 1 <= B <= 64, 1 <= S <= 8192, threshold not NaN.
+ * ---------------------------------------------------------------------- */
+dbd_status dbd_remask_commit(int S, int B, int mask_token_id,
+                             float dynamic_threshold, uint32_t flags,
+                             int32_t* block_tokens, uint8_t* seq_state,
+                             const int32_t* argmax_tok, const float* conf,
+                             int32_t* row_index_out, int32_t* num_rows_out,
+                             int32_t* num_committed, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dbd_round -- one whole denoise round: dbd_attn_paged, then
+ * dbd_lmhead_conf on the row list (row_index, *num_rows), then
+ * dbd_remask_commit, which overwrites (row_index, *num_rows) with the next
+ * round's list.  Build the first round's list with dbd_remask_commit and
+ * DBD_COMPACT_ONLY.  With no model in the loop, `hidden` is an input of the
+ * round (the state the model would have produced), not computed from
+ * attn_out.
+ * workspace: dbd_round_workspace_size(a) bytes.
+ * ---------------------------------------------------------------------- */
+typedef struct dbd_round_args {
+  int S, B, Hq, Hkv, D, page_size, max_pages_per_seq;
+  int Hd, V, mask_token_id;
+  float dynamic_threshold;
+  uint32_t flags;
+  float softmax_scale;
+  const dbd_bf16 *q, *k_blk, *v_blk, *k_cache, *v_cache;
+  const int32_t *page_table, *prefix_len;
+  dbd_bf16* attn_out;
+  const dbd_bf16 *hidden, *w_vocab;
+  int32_t* row_index; /* in: this round's rows; out: the next round's */
+  int32_t* num_rows;  /* device scalar, same in/out rule              */
+  int32_t* argmax_tok;
+  float* conf;
+  int32_t* block_tokens;
+  uint8_t* seq_state;
+  int32_t* num_committed; /* may be NULL */
+  void* workspace;
+  size_t workspace_bytes;
+} dbd_round_args;
+
+dbd_status dbd_round(const dbd_round_args* a, void* stream);
+size_t dbd_round_workspace_size(const dbd_round_args* a);
+
+/* Graph of n_rounds consecutive rounds (args[i] for round i, e.g. each with
+ * its own per-round inputs), captured once and replayed with one launch and
+ * no host work in between (dlmrt README, "Highlights": denoising loop on the
+ * device; JetEngine developer notes: CUDA-graph replay of the denoise
+ * batch).  The captured pointers and scalars are fixed at creation. */
+typedef struct dbd_graph dbd_graph;
+dbd_status dbd_graph_create(const dbd_round_args* args, int n_rounds,
+                            dbd_graph** out);
+dbd_status dbd_graph_launch(dbd_graph* g, void* stream);
+void dbd_graph_destroy(dbd_graph* g);
+
+/* Host-side check of host copies of the device-resident inputs: page ids in
+ * [0, num_pages), prefix lengths within the page table, mask id / tokens
+ * within the vocabulary, states within the enum.  Makes no HIP call. */
+dbd_status dbd_validate_inputs(int S, int B, int page_size,
+                               int max_pages_per_seq, int num_pages, int V,
+                               int mask_token_id, const int32_t* page_table,
+                               const int32_t* prefix_len,
+                               const int32_t* block_tokens,
+                               const uint8_t* seq_state);
+
+const char* dbd_last_error(void);
+int dbd_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DBD_H */

@@ -1,0 +1,136 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every
+symbol include/dbd.h declares, and rejects invalid arguments before any HIP
+call (so these run with no device)."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from block_diffusion_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dbd.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\**\s*(dbd_[a-z_0-9]+)\s*\(",
+                       src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_round_calls():
+    names = declared_functions()
+    for n in ("dbd_attn_paged", "dbd_lmhead_conf", "dbd_remask_commit", "dbd_round",
+              "dbd_graph_create", "dbd_graph_launch", "dbd_graph_destroy",
+              "dbd_attn_workspace_size", "dbd_lmhead_workspace_size",
+              "dbd_round_workspace_size", "dbd_validate_inputs", "dbd_last_error",
+              "dbd_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = api.lib()
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert api.dbd_abi_version() == 1
+
+
+def _attn(**kw):
+    a = dict(S=2, B=4, Hq=4, Hkv=2, D=64, P=16, maxp=3)
+    a.update(kw)
+    return api.lib().dbd_attn_paged(a["S"], a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["maxp"],
+                                    16, 16, 16, 16, 16, 16, 16, 0.0, 16, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), api.DBD_ERR_INVALID_ARG), (dict(B=65), api.DBD_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), api.DBD_ERR_INVALID_ARG), (dict(P=24), api.DBD_ERR_INVALID_ARG),
+    (dict(P=0), api.DBD_ERR_INVALID_ARG), (dict(D=96), api.DBD_ERR_UNSUPPORTED),
+    (dict(S=0), api.DBD_ERR_INVALID_ARG), (dict(maxp=0), api.DBD_ERR_INVALID_ARG)])
+def test_attn_rejects(kw, status):
+    assert _attn(**kw) == status
+    assert api.lib().dbd_last_error()
+
+
+def test_attn_null_and_misaligned_pointers():
+    L = api.lib()
+    st = L.dbd_attn_paged(2, 4, 4, 2, 64, 16, 3, None, 16, 16, 16, 16, 16, 16, 0.0, 16, None, 0, None)
+    assert st == api.DBD_ERR_INVALID_ARG and b"q is NULL" in L.dbd_last_error()
+    st = L.dbd_attn_paged(2, 4, 4, 2, 64, 16, 3, 16, 18, 16, 16, 16, 16, 16, 0.0, 16, None, 0, None)
+    assert st == api.DBD_ERR_INVALID_ARG and b"aligned" in L.dbd_last_error()
+    st = L.dbd_attn_paged(2, 4, 4, 2, 64, 16, 3, 16, 16, 16, 16, 16, 16, 16, float("nan"), 16, None, 0, None)
+    assert st == api.DBD_ERR_INVALID_ARG
+
+
+def test_attn_workspace_required():
+    L = api.lib()
+    need = api.dbd_attn_workspace_size(128, 4, 32, 8, 128, 256, 16)
+    assert need > 0
+    st = L.dbd_attn_paged(128, 4, 32, 8, 128, 256, 16, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, None, 0, None)
+    assert st == api.DBD_ERR_WORKSPACE
+    st = L.dbd_attn_paged(128, 4, 32, 8, 128, 256, 16, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, 16, need - 1, None)
+    assert st == api.DBD_ERR_WORKSPACE
+    # one chunk per sequence: no workspace needed
+    assert api.dbd_attn_workspace_size(2, 4, 4, 2, 64, 16, 3) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((16, 100, 1024, 5), api.DBD_ERR_INVALID_ARG),      # Hd not a multiple of 64
+    ((16, 128, 1, 0), api.DBD_ERR_INVALID_ARG),         # V < 2
+    ((16, 128, 1024, 1024), api.DBD_ERR_INVALID_ARG),   # mask id out of range
+    ((16, 128, 1024, -1), api.DBD_ERR_INVALID_ARG),
+    ((-1, 128, 1024, 5), api.DBD_ERR_INVALID_ARG)])
+def test_lmhead_rejects(args, status):
+    L = api.lib()
+    assert L.dbd_lmhead_conf(*args, 16, None, 16, 16, 16, 16, 256, 1 << 20, None) == status
+
+
+def test_lmhead_workspace_required():
+    L = api.lib()
+    assert L.dbd_lmhead_conf(16, 128, 1024, 5, 16, None, 16, 16, 16, 16, None, 0, None) == api.DBD_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("S,B,tau,flags,status", [
+    (0, 4, 0.9, 0, api.DBD_ERR_INVALID_ARG), (8193, 4, 0.9, 0, api.DBD_ERR_INVALID_ARG),
+    (2, 0, 0.9, 0, api.DBD_ERR_INVALID_ARG), (2, 65, 0.9, 0, api.DBD_ERR_INVALID_ARG),
+    (2, 4, float("nan"), 0, api.DBD_ERR_INVALID_ARG), (2, 4, 0.9, 8, api.DBD_ERR_INVALID_ARG)])
+def test_remask_rejects(S, B, tau, flags, status):
+    L = api.lib()
+    assert L.dbd_remask_commit(S, B, 5, tau, flags, 16, 16, 16, 16, 16, 16, None, None) == status
+
+
+def test_round_rejects():
+    a = api.dbd_round_args()
+    a.S, a.B, a.Hq, a.Hkv, a.D, a.page_size, a.max_pages_per_seq = 2, 4, 4, 2, 64, 16, 3
+    a.Hd, a.V, a.mask_token_id, a.dynamic_threshold = 256, 1024, 1023, 0.9
+    with pytest.raises(api.DbdError) as e:
+        api.dbd_round(a, stream=0)
+    assert e.value.status == api.DBD_ERR_INVALID_ARG
+    with pytest.raises(api.DbdError):
+        api.dbd_graph_create([a])
+
+
+def test_validate_inputs():
+    ok = dict(S=2, B=4, page_size=16, max_pages_per_seq=3, num_pages=4, V=1024, mask_token_id=1023)
+    pt = np.array([[1, -1, -1], [0, 3, 2]], np.int32)
+    api.dbd_validate_inputs(**ok, page_table=pt, prefix_len=[16, 37],
+                            block_tokens=np.full((2, 4), 1023), seq_state=[2, 2])
+    with pytest.raises(api.DbdError):
+        api.dbd_validate_inputs(**ok, page_table=pt, prefix_len=[17, 37])   # needs page 2 of seq 0
+    with pytest.raises(api.DbdError):
+        api.dbd_validate_inputs(**ok, page_table=pt, prefix_len=[16, 49])   # > 3 pages * 16
+    with pytest.raises(api.DbdError):
+        api.dbd_validate_inputs(**ok, block_tokens=np.full((2, 4), 1024))
+    with pytest.raises(api.DbdError):
+        api.dbd_validate_inputs(**ok, seq_state=[2, 7])
+    bad = dict(ok, mask_token_id=1024)
+    with pytest.raises(api.DbdError):
+        api.dbd_validate_inputs(**bad)

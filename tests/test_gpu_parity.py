@@ -1,0 +1,334 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on seeded
+inputs, element by element, at sizes the oracle finishes in seconds and, at
+the full SDAR-4B shapes, on sampled outputs.  Tolerances: attention max abs
+2e-2 and relative L2 5e-3 (bf16 output); confidence 1e-3 absolute; greedy
+tokens and committed sets exact outside the near-tie and near-threshold
+bands (tests/gpu_util.py)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_diffusion_amd import api, synth
+from block_diffusion_amd.workloads import (SDAR_1P7B, SDAR_4B, SDAR_4B_HIGHCONF, TINY,
+                                           Workload)
+from gpu_util import (ATTN_MAX_ABS, ATTN_REL_L2, RoundState, check_commits, check_lm_rows,
+                      compare_attn, dev_bf16, dev_i32, dev_u8, host_bits, oracle_attn_groups,
+                      round_inputs_dev, run_attn, tie_set, widen_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+def _custom(name, seed, **kw):
+    base = dict(name=name, seed_id=seed, S=1, B=4, Hq=4, Hkv=2, D=64, P=16, Hd=128, V=1000,
+                mask_id=999, prefix_lo=0, prefix_hi=0, tau=0.9, rounds=4, a_max=12.0)
+    base.update(kw)
+    return Workload(**base)
+
+
+ATTN_SMALL = [
+    TINY,
+    # several prefix chunks, an empty prefix and a one-token prefix; 9 rows (G=3, B=3)
+    _custom("multichunk_p16_d64", 101, S=3, B=3, Hq=6, Hkv=2, D=64, P=16,
+            prefix_fixed=(0, 1, 1500), prefix_hi=1500),
+    # 32 rows per kv head (two 16-row tiles), D=128
+    _custom("rows32_d128", 102, S=4, B=8, Hq=8, Hkv=2, D=128, P=32,
+            prefix_fixed=(33, 700, 0, 1025), prefix_hi=1025),
+    # 128 rows per kv head: two row groups of 64
+    _custom("rows128_two_groups", 103, S=2, B=16, Hq=16, Hkv=2, D=128, P=16,
+            prefix_fixed=(2100, 17), prefix_hi=2100),
+    # MHA with the largest block, 64 rows
+    _custom("mha_b64", 104, S=2, B=64, Hq=4, Hkv=4, D=128, P=256,
+            prefix_fixed=(3000, 255), prefix_hi=3000),
+    # block of one token, D=64, 64 rows from G=64
+    _custom("g64_b1", 105, S=2, B=1, Hq=64, Hkv=1, D=64, P=64,
+            prefix_fixed=(64, 129), prefix_hi=129),
+]
+
+
+@pytest.mark.parametrize("w", ATTN_SMALL, ids=lambda w: w.name)
+def test_attention_parity_small(w):
+    fx = synth.make_fixed(w, with_w=False)
+    rin = synth.make_round(w, 1, None)
+    out = run_attn(fx, rin)
+    groups = [(s, g) for s in range(w.S) for g in range(w.Hkv)]
+    ref = oracle_attn_groups(fx, rin, groups)
+    mx, rl2 = compare_attn(out, ref, w.G)
+    print(f"{w.name}: max abs {mx:.3e} rel L2 {rl2:.3e}")
+    assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2
+
+
+def test_attention_parity_sdar1p7b_full():
+    w = SDAR_1P7B
+    fx = synth.make_fixed(w, with_w=False)
+    rin = synth.make_round(w, 1, None)
+    out = run_attn(fx, rin)
+    ref = oracle_attn_groups(fx, rin, [(s, g) for s in range(w.S) for g in range(w.Hkv)])
+    mx, rl2 = compare_attn(out, ref, w.G)
+    print(f"{w.name}: max abs {mx:.3e} rel L2 {rl2:.3e}")
+    assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2
+
+
+@pytest.fixture(scope="module")
+def sdar4b_fixed():
+    return synth.make_fixed(SDAR_4B)
+
+
+def test_attention_parity_sdar4b_sampled(sdar4b_fixed):
+    w, fx = SDAR_4B, sdar4b_fixed
+    rin = synth.make_round(w, 1, None)
+    out = run_attn(fx, rin)
+    g = np.random.default_rng(7)
+    L = fx.prefix_len
+    # the longest and shortest prefixes plus a random sample
+    ss = sorted(set([int(np.argmax(L)), int(np.argmin(L))] + g.choice(w.S, 22, replace=False).tolist()))
+    groups = [(s, int(k)) for s in ss for k in g.choice(w.Hkv, 3, replace=False)]
+    ref = oracle_attn_groups(fx, rin, groups)
+    mx, rl2 = compare_attn(out, ref, w.G)
+    print(f"{w.name}: {len(groups)} groups, max abs {mx:.3e} rel L2 {rl2:.3e}")
+    assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2
+    assert np.all(np.isfinite(widen_bits(out)))
+
+
+def test_attention_page_relabel_bitwise():
+    """Physical page ids do not change the traversal order, so relabelling
+    the pages gives the same bits."""
+    w = ATTN_SMALL[1]
+    fx = synth.make_fixed(w, with_w=False)
+    rin = synth.make_round(w, 1, None)
+    base = run_attn(fx, rin)
+    n = fx.k_cache.shape[0]
+    pi = np.random.default_rng(3).permutation(n)
+    kc = np.empty_like(fx.k_cache); vc = np.empty_like(fx.v_cache)
+    kc[pi] = fx.k_cache; vc[pi] = fx.v_cache
+    pt = fx.page_table.copy()
+    pt[pt >= 0] = pi[pt[pt >= 0]]
+    fx2 = synth.Fixed(fx.prefix_len, pt, kc, vc, None, fx.block_tokens0, fx.seq_state0)
+    assert np.array_equal(run_attn(fx2, rin), base)
+
+
+def test_attention_deterministic():
+    w = ATTN_SMALL[3]
+    fx = synth.make_fixed(w, with_w=False)
+    rin = synth.make_round(w, 1, None)
+    assert np.array_equal(run_attn(fx, rin), run_attn(fx, rin))
+
+
+# ------------------------------------------------------------------- LM head
+
+def _lm_run(hidden_bits, w_bits, mask_id, rows, max_rows=None, use_index=True):
+    n = hidden_bits.shape[0]
+    h = dev_bf16(hidden_bits)
+    wv = dev_bf16(w_bits)
+    M = len(rows)
+    if max_rows is None:
+        max_rows = M
+    ri = np.zeros(max(max_rows, 1), np.int32)
+    ri[:M] = rows
+    ri_d = dev_i32(ri) if use_index else None
+    nr = dev_i32([M])
+    arg = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    conf = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    api.dbd_lmhead_conf(h, wv, nr, arg, conf, mask_id, row_index=ri_d, max_rows=max_rows)
+    torch.cuda.synchronize()
+    return arg.cpu().numpy(), conf.cpu().numpy()
+
+
+def test_lmhead_parity_tiny_all_rows():
+    w = TINY
+    fx = synth.make_fixed(w)
+    rin = synth.make_round(w, 1, fx.w_vocab)
+    rows = np.arange(w.S * w.B)
+    arg, conf = _lm_run(rin.hidden, fx.w_vocab, w.mask_id, rows, use_index=False)
+    _, p1, _, nt = check_lm_rows(rows, arg, conf, rin.hidden, fx.w_vocab, w.mask_id)
+    print("tiny p1:", np.round(p1, 3), "tie-exempt", nt)
+
+
+@pytest.mark.parametrize("V,Hd,mask,n,M,max_rows", [
+    (1000, 128, 500, 64, 37, 50),      # ragged last vocab tile, listed rows < max_rows
+    (300, 64, 0, 300, 300, 300),       # two row tiles (256 + 44), mask id 0
+    (2048, 256, 2047, 40, 0, 40),      # no rows this round
+    (129, 64, 128, 5, 5, 5),           # one column past a 128 tile
+])
+def test_lmhead_parity_ragged(V, Hd, mask, n, M, max_rows):
+    g = np.random.default_rng(V + M)
+    wv = synth.normal_bf16(g, (V, Hd), std=1.0 / np.sqrt(Hd))
+    t = g.integers(0, V, n)
+    a = g.uniform(0, 10, n)
+    wt = widen_bits(wv[t]); wt /= np.linalg.norm(wt, axis=1, keepdims=True)
+    h = synth.f32_to_bf16((g.standard_normal((n, Hd)) + a[:, None] * wt).astype(np.float32))
+    rows = g.permutation(n)[:M]
+    arg, conf = _lm_run(h, wv, mask, rows, max_rows=max_rows)
+    if M:
+        check_lm_rows(rows, arg, conf, h, wv, mask)
+    untouched = np.setdiff1d(np.arange(n), rows)
+    assert np.all(arg[untouched] == -7) and np.all(np.isnan(conf[untouched]))
+
+
+def test_lmhead_parity_sdar1p7b_all_rows():
+    w = SDAR_1P7B
+    fx = synth.make_fixed(w)
+    rin = synth.make_round(w, 1, fx.w_vocab)
+    rows = np.arange(w.S * w.B)
+    arg, conf = _lm_run(rin.hidden, fx.w_vocab, w.mask_id, rows)
+    _, p1, _, nt = check_lm_rows(rows, arg, conf, rin.hidden, fx.w_vocab, w.mask_id)
+    print(f"{w.name}: {(p1 >= w.tau).sum()} rows >= tau, tie-exempt {nt}")
+
+
+@pytest.mark.parametrize("w", [SDAR_4B, SDAR_4B_HIGHCONF], ids=lambda w: w.name)
+def test_lmhead_parity_sdar4b_sampled(w, sdar4b_fixed):
+    fx = sdar4b_fixed
+    rin = synth.make_round(w, 1, fx.w_vocab)
+    for M in (512, 384):
+        rows = np.arange(M)
+        arg, conf = _lm_run(rin.hidden, fx.w_vocab, w.mask_id, rows, max_rows=512)
+        g = np.random.default_rng(M)
+        samp = np.sort(np.concatenate([g.choice(M, 40, replace=False), [0, M - 1]]))
+        samp = np.unique(samp)
+        check_lm_rows(samp, arg, conf, rin.hidden, fx.w_vocab, w.mask_id)
+        assert np.all(arg[M:] == -7)
+
+
+# -------------------------------------------------------------------- remask
+
+@pytest.mark.parametrize("S,B,flags", [(1, 1, 0), (3, 4, 0), (128, 4, 0), (64, 16, 0),
+                                       (8, 64, 0), (50, 7, 1), (8192, 4, 0), (1000, 64, 0)])
+def test_remask_parity(S, B, flags):
+    g = np.random.default_rng(S * 131 + B)
+    mask = 151669
+    tau = np.float32(0.9)
+    levels = np.array([0.1, 0.5, 0.9, 0.9, 0.95, 0.3, 0.3], dtype=np.float32)
+    toks = np.where(g.random((S, B)) < 0.7, mask, g.integers(0, mask, (S, B))).astype(np.int32)
+    state = g.choice(np.array([2, 2, 2, 3, 0, 4], np.uint8), size=S)
+    conf = np.where(g.random(S * B) < 0.5, g.choice(levels, S * B), g.random(S * B)).astype(np.float32)
+    argm = g.integers(0, mask, S * B).astype(np.int32)
+    t_d, s_d = dev_i32(toks), dev_u8(state)
+    ri = torch.full((S * B,), -1, dtype=torch.int32, device="cuda")
+    nr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nc = torch.full((S,), -1, dtype=torch.int32, device="cuda")
+    api.dbd_remask_commit(t_d, s_d, dev_i32(argm), torch.from_numpy(conf).cuda(), ri, nr, mask,
+                          float(tau), flags=flags, num_committed=nc)
+    torch.cuda.synchronize()
+    et, es, com = oracle.remask(toks, state, conf.astype(np.float64), argm, mask,
+                                float(tau), flags)
+    assert np.array_equal(t_d.cpu().numpy(), et)
+    assert np.array_equal(s_d.cpu().numpy(), es)
+    rows = oracle.compact_rows(et, es, mask)
+    assert nr.item() == rows.size
+    assert np.array_equal(ri.cpu().numpy()[:rows.size], rows)
+    den = state == 2
+    assert np.array_equal(nc.cpu().numpy()[den], com.sum(1)[den])
+
+
+def test_remask_compact_only():
+    S, B, mask = 37, 5, 9
+    g = np.random.default_rng(1)
+    toks = np.where(g.random((S, B)) < 0.5, mask, 1).astype(np.int32)
+    state = g.choice(np.array([2, 3], np.uint8), size=S)
+    t_d, s_d = dev_i32(toks), dev_u8(state)
+    ri = torch.full((S * B,), -1, dtype=torch.int32, device="cuda")
+    nr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.dbd_remask_commit(t_d, s_d, None, None, ri, nr, mask, 0.9, flags=api.DBD_COMPACT_ONLY)
+    rows = oracle.compact_rows(toks, state, mask)
+    assert nr.item() == rows.size and np.array_equal(ri.cpu().numpy()[:rows.size], rows)
+    assert np.array_equal(t_d.cpu().numpy(), toks) and np.array_equal(s_d.cpu().numpy(), state)
+
+
+# --------------------------------------------------------------- whole round
+
+def _setup_rounds(w, fx, n_rounds):
+    st = RoundState(w, fx)
+    st.init_rows()
+    attn_out = torch.empty((w.S, w.B, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    rins = [synth.make_round(w, r, fx.w_vocab) for r in range(1, n_rounds + 1)]
+    devs = [round_inputs_dev(r) for r in rins]
+    args = [st.args(d, attn_out) for d in devs]
+    return st, rins, devs, args, attn_out
+
+
+def _run_rounds(w, fx, n_rounds, check_lm_full):
+    """Eager rounds with teacher forcing: each round is checked from the
+    GPU's state at its start."""
+    st, rins, devs, args, _ = _setup_rounds(w, fx, n_rounds)
+    history = []
+    toks = fx.block_tokens0.copy()
+    state = fx.seq_state0.copy()
+    for r in range(n_rounds):
+        rows0 = oracle.compact_rows(toks, state, w.mask_id)
+        assert st.bufs.num_rows.item() == rows0.size
+        assert np.array_equal(st.bufs.row_index.cpu().numpy()[:rows0.size], rows0)
+        api.dbd_round(args[r])
+        torch.cuda.synchronize()
+        t1 = st.bufs.block_tokens.cpu().numpy()
+        s1 = st.bufs.seq_state.cpu().numpy()
+        arg = st.bufs.argmax_tok.cpu().numpy()
+        conf = st.bufs.conf.cpu().numpy()
+        history.append((t1.copy(), s1.copy()))
+        if rows0.size:
+            if check_lm_full:
+                a, p1, p2, _ = check_lm_rows(rows0, arg, conf, rins[r].hidden, fx.w_vocab, w.mask_id)
+                p1_by_row = np.full(w.S * w.B, np.nan); p1_by_row[rows0] = p1
+                a_by_row = np.full(w.S * w.B, -1); a_by_row[rows0] = a
+                p2_by_row = np.full(w.S * w.B, np.nan); p2_by_row[rows0] = p2
+                hid = rins[r].hidden
+
+                def arg_ok(row, tok):
+                    if p1_by_row[row] - p2_by_row[row] >= 1e-4:
+                        return tok == a_by_row[row]
+                    return tok in tie_set(hid[row], fx.w_vocab, w.mask_id, p1_by_row[row])
+                check_commits(toks, state, t1, s1, p1_by_row, arg_ok, w.mask_id, w.tau)
+            # exact: the commit rule applied by the oracle to the GPU's own
+            # float32 confidences and tokens gives the GPU's result
+            et, es, _ = oracle.remask(toks, state, conf.astype(np.float64), arg, w.mask_id,
+                                      float(np.float32(w.tau)))
+            assert np.array_equal(t1, et) and np.array_equal(s1, es)
+        else:
+            assert np.array_equal(t1, toks)
+        toks, state = t1, s1       # teacher forcing: the next round starts from the GPU state
+    return st, history
+
+
+@pytest.mark.parametrize("w", [TINY, SDAR_1P7B], ids=lambda w: w.name)
+def test_round_parity_teacher_forced(w):
+    fx = synth.make_fixed(w)
+    st, hist = _run_rounds(w, fx, w.rounds, check_lm_full=True)
+    assert np.all(hist[-1][1] == oracle.SAVING)
+
+
+def test_round_sdar4b_rounds(sdar4b_fixed):
+    """Full SDAR-4B shapes: four rounds; every round's commits are exactly
+    the rule applied to the GPU's confidences; sampled confidences are checked
+    against the oracle in the LM-head test above."""
+    w, fx = SDAR_4B, sdar4b_fixed
+    st, hist = _run_rounds(w, fx, w.rounds, check_lm_full=False)
+    assert np.all(hist[-1][1] == oracle.SAVING)
+    assert (hist[0][0] != w.mask_id).sum() >= w.S
+
+
+@pytest.mark.parametrize("w", [TINY, SDAR_1P7B], ids=lambda w: w.name)
+def test_graph_matches_eager(w):
+    """One graph of all rounds, replayed three times with eager resets and
+    host syncs in between; every replay equals the eager rounds bit for bit."""
+    fx = synth.make_fixed(w)
+    st_e, hist = _run_rounds(w, fx, w.rounds, check_lm_full=False)
+    ref = [st_e.bufs.block_tokens.cpu().numpy(), st_e.bufs.seq_state.cpu().numpy(),
+           st_e.bufs.conf.cpu().numpy(), st_e.bufs.argmax_tok.cpu().numpy()]
+    st, rins, devs, args, attn_out = _setup_rounds(w, fx, w.rounds)
+    gr = api.dbd_graph_create(args)
+    try:
+        for rep in range(3):
+            st.bufs.block_tokens.copy_(dev_i32(fx.block_tokens0))
+            st.bufs.seq_state.copy_(dev_u8(fx.seq_state0))
+            st.bufs.conf.fill_(float("nan"))
+            st.bufs.argmax_tok.fill_(-1)
+            st.init_rows()
+            torch.cuda.synchronize()
+            gr.launch()
+            torch.cuda.synchronize()
+            got = [st.bufs.block_tokens.cpu().numpy(), st.bufs.seq_state.cpu().numpy(),
+                   st.bufs.conf.cpu().numpy(), st.bufs.argmax_tok.cpu().numpy()]
+            for a, b in zip(got, ref):
+                assert np.array_equal(a, b, equal_nan=True), rep
+            assert st.bufs.num_rows.item() == st_e.bufs.num_rows.item()
+    finally:
+        gr.close()
