@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Denoise-round throughput on one MI355X at SDAR-4B shapes (block_length 4,
+batch 128, 32/8 heads, head dim 128, hidden 2560, vocab 151936, KV pages of
+256, prefixes U[256,4096], threshold 0.9).
+
+One step = one whole block: the initial all-masked state is restored and
+the block's rounds (4) run as one captured graph, each round being paged
+attention over every sequence, the selective fused LM head on the masked
+rows and the threshold remask.  value = block-tokens per second =
+batch * block_length * rounds * steps / elapsed.  All inputs (prefix cache,
+LM-head weight, per-round queries/keys/values/hidden states) are seeded,
+synthetic and resident in HBM before the timed region.
+
+Prints one JSON line (rank 0).  Also times each entry point on its own with
+HIP events on the launch stream for the roofline object, and the CPU oracle
+on a bounded sample for the CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sdar4b_b4_bs128")
+    ap.add_argument("--kernel-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=128,
+                    help="sequences in the CPU oracle's bounded sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the denoise round shards by sequence with no exchange, so one GPU's share is "
+              "the measured unit", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_diffusion_amd import api, synth
+    from block_diffusion_amd.workloads import BY_NAME
+
+    api.lib()
+    w = BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def dbf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t0 = time.time()
+    fx = synth.make_fixed(w)
+    rins = [synth.make_round(w, r, fx.w_vocab) for r in range(1, w.rounds + 1)]
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+
+    n = w.S * w.B
+    fixed = dict(k_cache=dbf(fx.k_cache), v_cache=dbf(fx.v_cache),
+                 page_table=torch.from_numpy(fx.page_table).to(dev),
+                 prefix_len=torch.from_numpy(fx.prefix_len).to(dev), w_vocab=dbf(fx.w_vocab))
+    per_round = [dict(q=dbf(r.q), k_blk=dbf(r.k_blk), v_blk=dbf(r.v_blk), hidden=dbf(r.hidden))
+                 for r in rins]
+    tok0 = torch.from_numpy(fx.block_tokens0).to(dev)
+    st0 = torch.from_numpy(fx.seq_state0).to(dev)
+    bufs = api.RoundBuffers(
+        row_index=torch.zeros(n, dtype=torch.int32, device=dev),
+        num_rows=torch.zeros(1, dtype=torch.int32, device=dev),
+        argmax_tok=torch.zeros(n, dtype=torch.int32, device=dev),
+        conf=torch.zeros(n, dtype=torch.float32, device=dev),
+        block_tokens=tok0.clone(), seq_state=st0.clone(),
+        num_committed=torch.zeros(w.S, dtype=torch.int32, device=dev),
+        workspace=torch.empty(1, dtype=torch.uint8, device=dev))
+    attn_out = torch.empty((w.S, w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    shape = dict(S=w.S, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, page_size=w.P,
+                 max_pages_per_seq=w.max_pages, Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
+                 dynamic_threshold=w.tau)
+
+    def round_args():
+        return [api.make_round_args(**shape, **pr, **fixed, attn_out=attn_out, bufs=bufs)
+                for pr in per_round]
+
+    need = api.dbd_round_workspace_size(round_args()[0])
+    bufs.workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    graph = api.dbd_graph_create(round_args())
+
+    def reset():
+        bufs.block_tokens.copy_(tok0)
+        bufs.seq_state.copy_(st0)
+        api.dbd_remask_commit(bufs.block_tokens, bufs.seq_state, None, None, bufs.row_index,
+                              bufs.num_rows, w.mask_id, w.tau, flags=api.DBD_COMPACT_ONLY)
+
+    def step():
+        reset()
+        graph.launch()
+
+    # rows per round (for the LM-head breakdown), from one untimed block
+    reset()
+    rows_per_round = []
+    for a in round_args():
+        rows_per_round.append(int(bufs.num_rows.item()))
+        api.dbd_round(a)
+    torch.cuda.synchronize()
+    saving = int((bufs.seq_state == 3).sum().item())
+    log(f"rows per round {rows_per_round}, sequences SAVING after the block: {saving}/{w.S}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    block_tokens = w.S * w.B * w.rounds * args.steps
+    value = block_tokens / elapsed
+    log(f"{args.steps} steps in {elapsed * 1e3:.2f} ms: {ms_per_step:.3f} ms/step, "
+        f"{value:.0f} block-tokens/s")
+
+    # ---- per entry point, HIP events on the launch stream
+    stream = torch.cuda.current_stream()
+    it = args.kernel_iters
+
+    def ev_time(fn):
+        for _ in range(3):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(it):
+            fn()
+        e.record(stream)
+        e.synchronize()
+        return s.elapsed_time(e) * 1e3 / it     # microseconds per launch
+
+    r1 = per_round[0]
+    t_attn = ev_time(lambda: api.dbd_attn_paged(r1["q"], r1["k_blk"], r1["v_blk"],
+                                                fixed["k_cache"], fixed["v_cache"],
+                                                fixed["page_table"], fixed["prefix_len"],
+                                                attn_out, ws=bufs.workspace))
+    lm_rows = torch.arange(n, dtype=torch.int32, device=dev)
+    lm_times = {}
+    for M in sorted(set(rows_per_round) | {n}, reverse=True):
+        if M == 0:
+            continue
+        nr = torch.tensor([M], dtype=torch.int32, device=dev)
+        lm_times[M] = ev_time(lambda: api.dbd_lmhead_conf(
+            r1["hidden"], fixed["w_vocab"], nr, bufs.argmax_tok, bufs.conf, w.mask_id,
+            row_index=lm_rows, max_rows=n, ws=bufs.workspace))
+    conf_r = torch.rand(n, device=dev)
+    arg_r = torch.zeros(n, dtype=torch.int32, device=dev)
+    tk, ss = tok0.clone(), st0.clone()
+    ri, nr2 = torch.zeros(n, dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev)
+    t_remask = ev_time(lambda: api.dbd_remask_commit(tk, ss, arg_r, conf_r, ri, nr2, w.mask_id,
+                                                     2.0))   # tau > 1: one commit each, no state change until full
+    log(f"attention {t_attn:.1f} us, LM head {', '.join(f'M={m}: {t:.1f} us' for m, t in lm_times.items())}, "
+        f"remask {t_remask:.1f} us")
+
+    # algorithmic work
+    L = fx.prefix_len.astype(np.int64)
+    npages = -(-L // w.P)
+    attn_bytes = int(L.sum() * w.Hkv * w.D * 2 * 2                 # prefix K and V
+                     + 2 * w.S * w.B * w.Hq * w.D * 2              # q in, out
+                     + 2 * w.S * w.B * w.Hkv * w.D * 2             # block K and V
+                     + w.S * 4 + npages.sum() * 4)                 # prefix lengths, page ids
+    M1 = rows_per_round[0]
+    lm_flops = 2.0 * M1 * w.Hd * w.V
+    t_lm1 = lm_times[M1]
+    step_attn = t_attn * w.rounds
+    step_lm = sum(lm_times.get(m, 0.0) for m in rows_per_round)
+    attn_roof = dict(bound="hbm", achieved=attn_bytes / (t_attn * 1e-6) / 1e9, peak=PEAK_HBM_GBS,
+                     unit="GB/s")
+    lm_roof = dict(bound="mfma", achieved=lm_flops / (t_lm1 * 1e-6) / 1e12, peak=PEAK_BF16_TFLOPS,
+                   unit="TFLOP/s")
+    for r in (attn_roof, lm_roof):
+        r["frac"] = r["achieved"] / r["peak"]
+        r["traffic"] = None
+    dominant = "attention" if step_attn >= step_lm else "lmhead"
+    roof = dict(attn_roof if dominant == "attention" else lm_roof)
+    roof["kernel"] = "dbd_attn_paged" if dominant == "attention" else "dbd_lmhead_conf"
+
+    out = {
+        "metric": "denoise-round block-tokens/sec at SDAR-4B shapes, B=4, batch 128; % HBM/MFMA peak",
+        "value": round(value, 1), "unit": "block-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.S, "block_length": w.B, "rounds_per_step": w.rounds,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D, "hidden": w.Hd,
+                   "vocab": w.V, "page_size": w.P, "prefix": [w.prefix_lo, w.prefix_hi],
+                   "threshold": w.tau, "rows_per_round": rows_per_round, "parallelism": "none"},
+        "roofline": roof,
+        "breakdown_us": {"attention": round(t_attn, 2),
+                         "lmhead": {str(m): round(t, 2) for m, t in lm_times.items()},
+                         "remask": round(t_remask, 2),
+                         "attention_roofline": {k: (round(v, 4) if isinstance(v, float) else v)
+                                                for k, v in attn_roof.items()},
+                         "lmhead_roofline_M%d" % M1: {k: (round(v, 4) if isinstance(v, float) else v)
+                                                      for k, v in lm_roof.items()}},
+    }
+    graph.close()
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, fx, rins[0], args.cpu_seqs)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(w, fx, rin, n_seq):
+    """The oracle, as it stands, on a bounded sample: the first n_seq
+    sequences' round 1 (attention for all their heads, the LM head on their
+    masked rows, the remask)."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    S = n_seq
+    t0 = time.perf_counter()
+    for s in range(S):
+        for g in range(w.Hkv):
+            oracle.attention_group(s, g, rin.q, rin.k_blk, rin.v_blk, fx.k_cache, fx.v_cache,
+                                   fx.page_table, fx.prefix_len)
+    toks, state = fx.block_tokens0[:S], fx.seq_state0[:S]
+    rows = oracle.compact_rows(toks, state, w.mask_id)
+    a, p1, _ = oracle.lmhead_rows(rin.hidden[rows], fx.w_vocab, w.mask_id)
+    conf = np.full(S * w.B, np.nan); conf[rows] = p1
+    arg = np.full(S * w.B, -1); arg[rows] = a
+    oracle.remask(toks, state, conf, arg, w.mask_id, w.tau)
+    dt = time.perf_counter() - t0
+    return {"value": round(S * w.B / dt, 3), "unit": "block-tokens/s",
+            "cores": blas_threads if blas_threads else cores, "kind": "oracle",
+            "sample": f"round 1 of the first {S} of {w.S} sequences ({S * w.B} block tokens): "
+                      f"float64 attention over all their heads, full-vocabulary LM head on "
+                      f"{rows.size} masked rows, remask; {dt:.1f} s on {cores} host cores "
+                      f"(BLAS threads {blas_threads})"}
+
+
+if __name__ == "__main__":
+    main()

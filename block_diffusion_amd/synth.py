@@ -6,13 +6,14 @@ bf16 encoding of those draws, the paged layout of the prefix cache and the
 planted-token construction of the hidden states; it holds none of the
 round's arithmetic (no attention, no softmax, no commit rule).
 
-Every stream is ``numpy.random.default_rng([1234, seed_id, round, stream])``
-so any array can be regenerated on its own.  Values are drawn in float32
+Every stream is keyed ``[1234, seed_id, round, stream]`` (large arrays add
+a block index, see normal_bf16) so any array can be regenerated on its own.  Values are drawn in float32
 and rounded to bf16 (round to nearest even); both sides consume the same
 16-bit patterns.
 """
 from __future__ import annotations
 
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -33,9 +34,12 @@ def rng(w: Workload, rnd: int, stream: int) -> np.random.Generator:
 def f32_to_bf16(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns, round to nearest even (NaN -> qNaN)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    out = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
     nan = np.isnan(x)
+    if nan.any():
+        u = np.where(nan, np.uint32(0), u)
+    # finite inputs: u + 0x7FFF + lsb cannot wrap past 0xFF807FFF
+    out = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     if nan.any():
         out[nan] = BF16_QNAN
     return out
@@ -46,19 +50,49 @@ def bf16_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def normal_bf16(g: np.random.Generator, shape, std: float = 1.0,
-                chunk: int = 1 << 24) -> np.ndarray:
-    """N(0, std^2) draws in float32, rounded to bf16, generated in chunks so
-    multi-GB caches do not need a float32 copy of the whole array."""
+CHUNK = 1 << 22
+
+
+def _fill_chunk(out, key, i, std):
+    n = out.size
+    lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
+    v = np.random.default_rng(key + [i]).standard_normal(hi - lo, dtype=np.float32)
+    if std != 1.0:
+        v *= np.float32(std)
+    out[lo:hi] = f32_to_bf16(v)
+
+
+def normal_bf16(g, shape, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) draws in float32, rounded to bf16.
+
+    g is either a Generator (one sequential stream) or a seed key (list of
+    ints): then element block i (of CHUNK elements) is drawn from
+    default_rng(key + [i]), block by block on a thread pool, so multi-GB
+    caches are generated in parallel and still the same on every run."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    for i in range(0, n, chunk):
-        m = min(chunk, n - i)
-        v = g.standard_normal(m, dtype=np.float32)
-        if std != 1.0:
-            v *= np.float32(std)
-        out[i:i + m] = f32_to_bf16(v)
+    if isinstance(g, np.random.Generator):
+        for i in range(0, n, CHUNK):
+            m = min(CHUNK, n - i)
+            v = g.standard_normal(m, dtype=np.float32)
+            if std != 1.0:
+                v *= np.float32(std)
+            out[i:i + m] = f32_to_bf16(v)
+        return out.reshape(shape)
+    nchunks = -(-n // CHUNK)
+    if nchunks <= 2:
+        for i in range(nchunks):
+            _fill_chunk(out, list(g), i, std)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        workers = min(16, len(os.sched_getaffinity(0)), nchunks)
+        with ThreadPoolExecutor(workers) as ex:
+            list(ex.map(lambda i: _fill_chunk(out, list(g), i, std), range(nchunks)))
     return out.reshape(shape)
+
+
+def key(w: Workload, rnd: int, stream: int) -> list:
+    return [1234, w.seed_id, rnd, stream]
 
 
 @dataclass
@@ -108,8 +142,8 @@ def make_fixed(w: Workload, poison_tail: bool = True, with_w: bool = True) -> Fi
     L = prefix_lengths(w)
     table, npages = page_layout(w, L)
     shape = (npages, w.Hkv, w.P, w.D)
-    kc = normal_bf16(rng(w, 0, ST_KCACHE), shape)
-    vc = normal_bf16(rng(w, 0, ST_VCACHE), shape)
+    kc = normal_bf16(key(w, 0, ST_KCACHE), shape)
+    vc = normal_bf16(key(w, 0, ST_VCACHE), shape)
     if poison_tail:
         # slots past a prefix's end inside its last page are never part of
         # the prefix; fill them with NaN so any read of them shows up.
@@ -120,7 +154,7 @@ def make_fixed(w: Workload, poison_tail: bool = True, with_w: bool = True) -> Fi
                 p = table[s, n - 1]
                 kc[p, :, tail:, :] = BF16_QNAN
                 vc[p, :, tail:, :] = BF16_QNAN
-    wv = normal_bf16(rng(w, 0, ST_W), (w.V, w.Hd), std=1.0 / np.sqrt(w.Hd)) if with_w else None
+    wv = normal_bf16(key(w, 0, ST_W), (w.V, w.Hd), std=1.0 / np.sqrt(w.Hd)) if with_w else None
     toks = np.full((w.S, w.B), w.mask_id, dtype=np.int32)
     if w.init_committed_max > 0:
         g = rng(w, 0, ST_INIT)
@@ -150,8 +184,8 @@ def make_hidden(w: Workload, rnd: int, w_vocab: np.ndarray) -> np.ndarray:
 
 
 def make_round(w: Workload, rnd: int, w_vocab: np.ndarray | None) -> RoundInputs:
-    q = normal_bf16(rng(w, rnd, ST_Q), (w.S, w.B, w.Hq, w.D))
-    kb = normal_bf16(rng(w, rnd, ST_KBLK), (w.S, w.B, w.Hkv, w.D))
-    vb = normal_bf16(rng(w, rnd, ST_VBLK), (w.S, w.B, w.Hkv, w.D))
+    q = normal_bf16(key(w, rnd, ST_Q), (w.S, w.B, w.Hq, w.D))
+    kb = normal_bf16(key(w, rnd, ST_KBLK), (w.S, w.B, w.Hkv, w.D))
+    vb = normal_bf16(key(w, rnd, ST_VBLK), (w.S, w.B, w.Hkv, w.D))
     h = make_hidden(w, rnd, w_vocab) if w_vocab is not None else None
     return RoundInputs(q, kb, vb, h)
