@@ -61,7 +61,7 @@ dbd_status check_lm(int max_rows, int Hd, int V, int mask) {
   REQUIRE(max_rows >= 0, "max_rows must be >= 0 (got %d)", max_rows);
   REQUIRE(V >= 2, "vocab size must be >= 2 (got %d)", V);
   REQUIRE(mask >= 0 && mask < V, "mask_token_id %d outside [0,%d)", mask, V);
-  REQUIRE(Hd >= 64 && Hd % 64 == 0, "hidden size must be a positive multiple of 64 (got %d)", Hd);
+  REQUIRE(Hd >= 128 && Hd % 128 == 0, "hidden size must be a positive multiple of 128 (got %d)", Hd);
   REQUIRE((long)V * Hd < (1L << 31), "V*Hd must fit in 31 bits");
   REQUIRE((long)max_rows * Hd < (1L << 31), "max_rows*Hd must fit in 31 bits");
   return DBD_OK;
@@ -113,7 +113,6 @@ dbd_status enqueue_lm(int max_rows, int Hd, int V, int mask, const dbd_bf16* hid
   dbd::LmArgs a{};
   a.hidden = hidden; a.row_index = row_index; a.num_rows = num_rows; a.w = w;
   a.Hd = Hd; a.V = V; a.mask_id = mask; a.max_rows = max_rows;
-  a.n_vt = (V + 127) / 128;
   const size_t one = need / 3;
   char* base = static_cast<char*>(ws);
   a.pm = reinterpret_cast<float*>(base);

@@ -37,16 +37,19 @@ hipError_t attn_launch(const AttnPlan& plan, const AttnArgs& a,
                        hipStream_t stream);
 
 // ------------------------------------------------------------------ LM head
+// workgroups of the persistent LM-head kernel (one per CU of an MI355X) and
+// the number of (max, id, sum) partials it leaves per row
+constexpr int kLmGrid = 256;
+
 struct LmArgs {
   const uint16_t* hidden;
   const int32_t* row_index;
   const int32_t* num_rows;
   const uint16_t* w;
   int Hd, V, mask_id, max_rows;
-  int n_vt;        // 128-column vocabulary tiles = partials per row
-  float* pm;       // [max_rows][n_vt] tile max logit
-  int32_t* pa;     // [max_rows][n_vt] tile argmax (lowest id on ties)
-  float* ps;       // [max_rows][n_vt] sum exp(l - tile max)
+  float* pm;       // [max_rows][kLmGrid] partial max logit
+  int32_t* pa;     // [max_rows][kLmGrid] partial argmax (lowest id on ties)
+  float* ps;       // [max_rows][kLmGrid] partial sum exp(l - max)
   int32_t* argmax_tok;
   float* conf;
 };

@@ -121,7 +121,7 @@ size_t dbd_attn_workspace_size(int S, int B, int Hq, int Hkv, int D,
  * Layouts: hidden [rows][Hd] bf16 (row = s*B + position); w_vocab [V][Hd]
  * bf16 (row v is column v of W in R^{Hd x V}); row_index int32 [max_rows];
  * num_rows int32 device scalar, 0 <= *num_rows <= max_rows.
- * Requirements: Hd % 64 == 0, V >= 2, 0 <= mask_token_id < V.
+ * Requirements: Hd % 128 == 0, V >= 2, 0 <= mask_token_id < V.
  * workspace: dbd_lmhead_workspace_size(max_rows, V) bytes, 256-B aligned.
  * ---------------------------------------------------------------------- */
 dbd_status dbd_lmhead_conf(int max_rows, int Hd, int V, int mask_token_id,

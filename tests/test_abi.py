@@ -83,7 +83,8 @@ def test_attn_workspace_required():
 
 
 @pytest.mark.parametrize("args,status", [
-    ((16, 100, 1024, 5), api.DBD_ERR_INVALID_ARG),      # Hd not a multiple of 64
+    ((16, 100, 1024, 5), api.DBD_ERR_INVALID_ARG),      # Hd not a multiple of 128
+    ((16, 192, 1024, 5), api.DBD_ERR_INVALID_ARG),
     ((16, 128, 1, 0), api.DBD_ERR_INVALID_ARG),         # V < 2
     ((16, 128, 1024, 1024), api.DBD_ERR_INVALID_ARG),   # mask id out of range
     ((16, 128, 1024, -1), api.DBD_ERR_INVALID_ARG),

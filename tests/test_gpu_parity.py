@@ -146,9 +146,9 @@ def test_lmhead_parity_tiny_all_rows():
 
 @pytest.mark.parametrize("V,Hd,mask,n,M,max_rows", [
     (1000, 128, 500, 64, 37, 50),      # ragged last vocab tile, listed rows < max_rows
-    (300, 64, 0, 300, 300, 300),       # two row tiles (256 + 44), mask id 0
+    (300, 128, 0, 300, 300, 300),      # two row tiles (256 + 44), mask id 0
     (2048, 256, 2047, 40, 0, 40),      # no rows this round
-    (129, 64, 128, 5, 5, 5),           # one column past a 128 tile
+    (129, 128, 128, 5, 5, 5),          # one column past a 128 tile
 ])
 def test_lmhead_parity_ragged(V, Hd, mask, n, M, max_rows):
     g = np.random.default_rng(V + M)
