@@ -5,27 +5,32 @@
 // sequence's block attends to all of that sequence's prefix tokens, found
 // through its page table, and to every token of its own block, with no mask
 // inside the block.  Grouped-query heads: the G = Hq/Hkv query heads of kv
-// head g share its keys and values.
+// head g share its keys and values; their G*B query rows form MFMA tiles of
+// 16 rows (RT tiles per row group).
 //
-// Work decomposition (split-KV): one workgroup per (prefix chunk, kv head,
-// row group, sequence).  The G*B query rows of a kv head form MFMA tiles of
-// 16 rows (RT tiles per row group).  Chunk 0 also takes the block's own keys.
-// The four waves of a workgroup stream disjoint 16-key tiles of the chunk
-// without workgroup barriers:
-//   * K tile: each lane loads 16 contiguous bytes of one key row straight
-//     into the A operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16);
-//   * V tile: coalesced 16-byte loads into a wave-private LDS tile, read back
-//     transposed as the A operand of O^T += V^T P^T (16x16x16 bf16 MFMA);
-//   * the score tile's accumulator layout (lane = query row, 4 keys) is
-//     exactly the B operand layout of the PV product, so probabilities go
-//     from the softmax to the MFMA without a shuffle;
-//   * online softmax in fp32 with base-2 exponentials (scores pre-scaled by
-//     scale*log2(e)); probabilities are rounded to bf16 for the MFMA and the
-//     row sum uses the rounded values.
-// Loads of the wave's next tile are issued before the current tile's math.
-// At the end the four waves merge (max, sum, acc) through LDS; a sequence
-// with one chunk writes bf16 output directly, otherwise the chunk writes an
-// fp32 partial and attn_combine_kernel merges the chunks.
+// Work decomposition.  A segment is (sequence s, kv head g, row group rg); it
+// owns ceil(L_s/16) prefix tiles of 16 keys plus ceil(B/16) tiles of the
+// block's own keys.  All segments, in order, form one global tile stream,
+// which is cut into equal contiguous ranges, one per single-wave workgroup:
+// every wave streams the same number of tiles whatever the prefix lengths.
+// A wave finishes each segment it touches with (max, sum, unnormalised
+// output); a segment split over several waves leaves fp32 partials that
+// attn_combine_kernel merges, one that fits in one wave is written directly.
+// attn_plan_kernel first turns prefix lengths into tile prefix sums.
+//
+// Per wave, tiles go straight from global memory into a three-slot LDS ring
+// (global_load_lds_dwordx4: 16 keys of K and of V, plus the segment's query
+// rows when the tile starts one), two tiles in flight while the third is
+// computed.  Rows are stored with their 16-byte chunks XOR-permuted by row so
+// fragment reads hit distinct banks.  Per tile:
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (lane: query row, 4 keys);
+//   * online softmax in fp32, base 2 (scores pre-scaled by scale*log2 e),
+//     probabilities rounded to bf16 for the MFMA, the row sum taken over the
+//     rounded values;
+//   * the score accumulator layout is exactly the B operand of
+//     O^T += V^T P^T (v_mfma_f32_16x16x16bf16_1k), V^T read from the ring.
+// Keys past the end of a prefix or block are masked to -inf; their loads
+// re-read the last valid key, so nothing past a page or buffer is touched.
 #include <algorithm>
 
 #include "dbd_device.hpp"
@@ -35,143 +40,305 @@ namespace dbd {
 
 namespace {
 
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+#define INL __attribute__((always_inline))
+
+constexpr int NR = 3;          // ring slots per wave
+constexpr int kCUs = 256;      // MI355X compute units
+constexpr int kLdsPerCU = 160 * 1024;
+
+// chunk permutation of row r (D=128: 16 chunks per row; D=64: 8)
 template <int D>
-struct TileRegs {
-  static constexpr int KS = D / 32;          // 16-byte K pieces per lane
-  static constexpr int VN = (16 * D / 8) / 64; // 16-byte V pieces per lane
-  bf16x8 k[KS];
-  u32x4 v[VN];
+__device__ __forceinline__ int rswz(int r) {
+  return D == 128 ? (r & 15) : (((r >> 1) ^ ((r & 1) << 2)) & 7);
+}
+// element offset of logical 16-byte chunk c of row r
+template <int D>
+__device__ __forceinline__ int eoff(int r, int c) {
+  return r * D + ((c ^ rswz<D>(r)) << 3);
+}
+
+template <int D, int RT>
+struct Geo {
+  static constexpr int ROWS = 16 * RT;
+  static constexpr int KS = D / 32;
+  static constexpr int DT = D / 16;
+  static constexpr int KV = 16 * D;                 // elements of one K (or V) tile
+  static constexpr int SLOT = 2 * KV + ROWS * D;    // K, V, Q
+  static constexpr int LPR = D / 8;                 // lanes per row in a 1 KB load
+  static constexpr int RPI = 64 / LPR;              // rows per 1 KB load
 };
 
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const AttnArgs& a,
-                                          int s, int g, int t, int n_ptiles,
-                                          int kbeg, int kend, int lane,
-                                          int& nvalid) {
-  const uint16_t* kb;
-  const uint16_t* vb;
-  int stride;
-  if (t < n_ptiles) {
-    const int j0 = kbeg + 16 * t;
-    const int page = a.page_table[(size_t)s * a.max_pages + j0 / a.P];
-    const size_t base = ((size_t)(page * a.Hkv + g) * a.P + (j0 % a.P)) * D;
-    kb = a.k_cache + base;
-    vb = a.v_cache + base;
-    stride = D;
-    nvalid = min(16, kend - j0);
-  } else {
-    const int j0 = 16 * (t - n_ptiles);
-    const size_t base = ((size_t)(s * a.B + j0) * a.Hkv + g) * D;
-    kb = a.k_blk + base;
-    vb = a.v_blk + base;
-    stride = a.Hkv * D;
-    nvalid = min(16, a.B - j0);
-  }
-  const int lr = lane & 15, lg = lane >> 4;
-  const int kr = min(lr, nvalid - 1);  // clamp: never read past the tile
+// One direct-to-LDS load: lane l copies 16 bytes from its own global address
+// to lds + 16*l.  Issued as inline assembly so that the compiler neither
+// pairs it with its own vmcnt bookkeeping nor moves LDS accesses across it
+// (the memory clobber); the ring's waits are explicit (wait_vm).  M0 carries
+// the LDS base; the s_nop is the wait state a fresh M0 needs before an LDS
+// DMA reads it.
+__device__ __forceinline__ void dma16(const void* g, const lds_u16* lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(g), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
+}
+
+// Copy 16 rows (row i from src0 + min(i, nvalid-1)*stride) into a region of
+// the ring, permuting chunks; lane l of each 1 KB load fills row
+// r0 + l/LPR, physical chunk l%LPR.
+template <int D, int RT>
+__device__ __forceinline__ void dma_rows16(lds_u16* dst, const uint16_t* src0, int stride,
+                                           int nvalid, int lane) {
+  using Gm = Geo<D, RT>;
 #pragma unroll
-  for (int ks = 0; ks < TileRegs<D>::KS; ++ks)
-    r.k[ks] = ld_bf16x8(kb + (size_t)kr * stride + 8 * lg + 32 * ks);
-#pragma unroll
-  for (int i = 0; i < TileRegs<D>::VN; ++i) {
-    const int c = lane + 64 * i;
-    const int key = c / (D / 8), dch = c % (D / 8);
-    const int kc = min(key, nvalid - 1);
-    u32x4 v = ld_u32x4(vb + (size_t)kc * stride + dch * 8);
-    if (key >= nvalid) v = u32x4{0u, 0u, 0u, 0u};
-    r.v[i] = v;
+  for (int r0 = 0; r0 < 16; r0 += Gm::RPI) {
+    const int row = r0 + lane / Gm::LPR;
+    const int lc = (lane % Gm::LPR) ^ rswz<D>(row);
+    const int srow = min(row, nvalid - 1);
+    dma16(src0 + (size_t)srow * stride + lc * 8, dst + r0 * D);
   }
 }
 
+// Uniform loads of read-only metadata through the scalar cache (constant
+// address space), so they never join the vector-memory counter that paces
+// the LDS ring.
+__device__ __forceinline__ int ldc(const int32_t* p, size_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
+
+// s_waitcnt vmcnt(n), also a compiler barrier for memory accesses
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// all of this wave's LDS reads (and scalar loads) have returned
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+struct Dec {      // a position in the tile stream
+  int s, hg, j;   // sequence, segment within the sequence, tile within the segment
+  int L, nP, tiles;
+};
+
 }  // namespace
 
-template <int D, int RT>
-__global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
-  constexpr int ROWS = 16 * RT;
-  constexpr int KS = D / 32;
-  constexpr int DT = D / 16;
-  constexpr int VSTR = D + 4;  // bf16 elements per V row in LDS (bank spread)
-  constexpr int MSTR = D + 4;  // floats per row of the merge buffer
-
-  __shared__ __align__(16) uint16_t s_v[4][16 * VSTR];
-  __shared__ __align__(16) float s_o[4][16 * MSTR];
-  __shared__ float s_m[4][16];
-  __shared__ float s_l[4][16];
-
-  const int s = blockIdx.z;
-  const int gy = blockIdx.y;
-  const int g = gy / a.n_rg, rg = gy % a.n_rg;
-  const int c = blockIdx.x;
-  const int L = a.prefix_len[s];
-  const int n_chunks = max(1, (L + a.chunk_keys - 1) / a.chunk_keys);
-  if (c >= n_chunks) return;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int R = a.G * a.B;
-
-  // Q^T as the B operand: lane holds query row lr, dims 8*lg + 32*ks.
-  bf16x8 qf[RT][KS];
+// Tile prefix sums: plan[s] = sum over s' < s of (ceil(L_s'/16) + ceil(B/16)).
+__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
+  __shared__ int s_wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = a.S, nB = (a.B + 15) / 16;
+  const int per = (S + 1023) / 1024;
+  const int b0 = tid * per;
+  int local = 0;
+  for (int j = 0; j < per; ++j)
+    if (b0 + j < S) local += (a.prefix_len[b0 + j] + 15) / 16 + nB;
+  int incl = local;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int r = rg * ROWS + rt * 16 + lr;
-    if (r < R) {
-      const int pos = r / a.G, gi = r % a.G;
-      const uint16_t* qp = a.q + ((size_t)(s * a.B + pos) * a.Hq + g * a.G + gi) * D + 8 * lg;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = ld_bf16x8(qp + 32 * ks);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = bf16x8{};
-    }
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
   }
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  int run = 0;
+  for (int w = 0; w < wave; ++w) run += s_wsum[w];
+  run += incl - local;
+  for (int j = 0; j < per; ++j)
+    if (b0 + j < S) {
+      a.plan[b0 + j] = run;
+      run += (a.prefix_len[b0 + j] + 15) / 16 + nB;
+    }
+  if (tid == 1023) {
+    int tot = 0;
+    for (int w = 0; w < 16; ++w) tot += s_wsum[w];
+    a.plan[S] = tot;
+  }
+}
 
+template <int D, int RT>
+__global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
+  using Gm = Geo<D, RT>;
+  constexpr int ROWS = Gm::ROWS, KS = Gm::KS, DT = Gm::DT, KV = Gm::KV;
+  __shared__ __align__(16) uint16_t R0_[Gm::SLOT];
+  __shared__ __align__(16) uint16_t R1_[Gm::SLOT];
+  __shared__ __align__(16) uint16_t R2_[Gm::SLOT];
+  lds_u16* const R0 = (lds_u16*)R0_;
+  lds_u16* const R1 = (lds_u16*)R1_;
+  lds_u16* const R2 = (lds_u16*)R2_;
+
+  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const int S = a.S, NHG = a.Hkv * a.n_rg, nB = (a.B + 15) / 16;
+  const int R = a.G * a.B;
+  const long T = (long)NHG * ldc(a.plan, S);
+  const long NWe = min((long)a.grid, max(1L, T / 64));
+  const long w = blockIdx.x;
+  if (w >= NWe) return;
+  const long t0 = w * T / NWe, t1 = (w + 1) * T / NWe;
+  const int n = (int)(t1 - t0);
+  if (n <= 0) return;
+
+  // locate t0: largest s with NHG*plan[s] <= t0 (64-way search)
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = min(lo + lane * step, hi);
+    const bool pred = idx < hi && (long)NHG * a.plan[idx] <= t0;
+    const unsigned long long bal = __ballot(pred);
+    const int k = 63 - __clzll(bal);
+    lo = __builtin_amdgcn_readfirstlane(lo + k * step);
+    hi = min(hi, lo + step);
+  }
+  auto load_seq = [&](Dec& d) INL {
+    d.L = ldc(a.prefix_len, d.s);
+    d.nP = (d.L + 15) / 16;
+    d.tiles = d.nP + nB;
+  };
+  Dec dc;
+  dc.s = lo;
+  load_seq(dc);
+  {
+    const long rem = t0 - (long)NHG * ldc(a.plan, lo);
+    dc.hg = (int)(rem / dc.tiles);
+    dc.j = (int)(rem % dc.tiles);
+  }
+  Dec dd = dc;                 // stream position of the next tile to load
+  auto advance = [&](Dec& d) INL {
+    if (++d.j == d.tiles) {
+      d.j = 0;
+      if (++d.hg == NHG) {
+        d.hg = 0;
+        if (++d.s < S) load_seq(d);
+      }
+    }
+  };
+
+  // load tile `d` (and the segment's query rows if with_q) into `slot`
+  auto dma_tile = [&](lds_u16* slot, const Dec& d, bool with_q) INL {
+    wait_lgkm0();   // the slot's previous tile has been read out
+    const int g = d.hg / a.n_rg, rg = d.hg % a.n_rg;
+    const uint16_t* sk;
+    const uint16_t* sv;
+    int stride, nvalid;
+    if (d.j < d.nP) {
+      const int key0 = 16 * d.j;
+      const int page = ldc(a.page_table, (size_t)d.s * a.max_pages + key0 / a.P);
+      const size_t base = (((size_t)page * a.Hkv + g) * a.P + key0 % a.P) * D;
+      sk = a.k_cache + base;
+      sv = a.v_cache + base;
+      stride = D;
+      nvalid = min(16, d.L - key0);
+    } else {
+      const int key0 = 16 * (d.j - d.nP);
+      const size_t base = ((size_t)(d.s * a.B + key0) * a.Hkv + g) * D;
+      sk = a.k_blk + base;
+      sv = a.v_blk + base;
+      stride = a.Hkv * D;
+      nvalid = min(16, a.B - key0);
+    }
+    dma_rows16<D, RT>(slot, sk, stride, nvalid, lane);
+    dma_rows16<D, RT>(slot + KV, sv, stride, nvalid, lane);
+    if (with_q) {
+      // query row r = rg*ROWS + i -> (pos, gi) = (r / G, r % G); rows past
+      // G*B re-read the last real row (their outputs are never written)
+#pragma unroll
+      for (int r0 = 0; r0 < ROWS; r0 += Gm::RPI) {
+        const int row = r0 + lane / Gm::LPR;
+        const int lc = (lane % Gm::LPR) ^ rswz<D>(row);
+        const int rr = min(rg * ROWS + row, R - 1);
+        const int pos = rr / a.G, gi = rr % a.G;
+        const uint16_t* src = a.q + ((size_t)(d.s * a.B + pos) * a.Hq + g * a.G + gi) * D + lc * 8;
+        dma16(src, slot + 2 * KV + r0 * D);
+      }
+    }
+  };
+
+  // per-segment state
+  bf16x8 qf[RT][KS];
   float m_run[RT], l_run[RT];
   f32x4 acc[RT][DT];
+
+  auto finalize = [&](const Dec& d) INL {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    m_run[rt] = -INFINITY;
-    l_run[rt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int kbeg = c * a.chunk_keys;
-  const int kend = min(L, kbeg + a.chunk_keys);
-  const int n_ptiles = kend > kbeg ? (kend - kbeg + 15) / 16 : 0;
-  const int n_btiles = c == 0 ? (a.B + 15) / 16 : 0;
-  const int n_tiles = n_ptiles + n_btiles;
-
-  uint16_t* vt = s_v[wave];
-  TileRegs<D> nxt;
-  int nv_next = 0;
-  if (wave < n_tiles) load_tile<D>(nxt, a, s, g, wave, n_ptiles, kbeg, kend, lane, nv_next);
-
-  for (int t = wave; t < n_tiles; t += 4) {
-    TileRegs<D> cur = nxt;
-    const int nvalid = nv_next;
-    if (t + 4 < n_tiles) load_tile<D>(nxt, a, s, g, t + 4, n_ptiles, kbeg, kend, lane, nv_next);
-
-    // V tile -> wave-private LDS, row-major [key][d]
-#pragma unroll
-    for (int i = 0; i < TileRegs<D>::VN; ++i) {
-      const int cidx = lane + 64 * i;
-      const int key = cidx / (D / 8), dch = cidx % (D / 8);
-      u32x2* dst = reinterpret_cast<u32x2*>(vt + key * VSTR + dch * 8);
-      dst[0] = u32x2{cur.v[i].x, cur.v[i].y};
-      dst[1] = u32x2{cur.v[i].z, cur.v[i].w};
+    for (int rt = 0; rt < RT; ++rt) {
+      l_run[rt] += shfl_xor_f(l_run[rt], 16);
+      l_run[rt] += shfl_xor_f(l_run[rt], 32);
     }
+    const int g = d.hg / a.n_rg, rg = d.hg % a.n_rg;
+    const long ts = (long)NHG * ldc(a.plan, d.s) + (long)d.hg * d.tiles;
+    const long w0 = ((ts + 1) * NWe - 1) / T;
+    const long w1 = ((ts + d.tiles) * NWe - 1) / T;
+    if (w0 == w1) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int rr = rg * ROWS + rt * 16 + lr;
+        if (rr < R) {
+          const float inv = 1.f / l_run[rt];
+          const int pos = rr / a.G, gi = rr % a.G;
+          uint16_t* op = a.out + ((size_t)(d.s * a.B + pos) * a.Hq + g * a.G + gi) * D + 4 * lg;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            u32x2 v;
+            v.x = (uint32_t)f2bf(acc[rt][dt].x * inv) | ((uint32_t)f2bf(acc[rt][dt].y * inv) << 16);
+            v.y = (uint32_t)f2bf(acc[rt][dt].z * inv) | ((uint32_t)f2bf(acc[rt][dt].w * inv) << 16);
+            *reinterpret_cast<u32x2*>(op + 16 * dt) = v;
+          }
+        }
+      }
+    } else {
+      const size_t slot = ((size_t)(d.s * NHG + d.hg) * a.maxp + (size_t)(w - w0)) * ROWS;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const size_t row = slot + rt * 16 + lr;
+        float* po = a.part_o + row * D + 4 * lg;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt) = acc[rt][dt];
+        if (lg == 0) a.part_ml[row] = make_float2(m_run[rt], l_run[rt]);
+      }
+    }
+  };
 
-    // scores S^T[key][row] (lane: row lr, keys 4*lg+i)
+  auto consume = [&](const lds_u16* slot, int k) INL {
+    // every tile issues at least 2*D/32 loads (K and V) and two tiles were
+    // issued after this one: waiting down to that many leaves this slot done
+    wait_vm<4 * Gm::KV / 512>();
+    if (k > 0 && dc.j == 0) {
+      // the previous tile closed a segment
+      Dec prev = dc;
+      if (prev.hg == 0) {
+        --prev.s;
+        load_seq(prev);
+        prev.hg = NHG - 1;
+      } else {
+        --prev.hg;
+      }
+      finalize(prev);
+    }
+    if (k == 0 || dc.j == 0) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qf[rt][ks] = __builtin_bit_cast(
+              bf16x8, *(const lds_u32x4*)(slot + 2 * KV + eoff<D>(rt * 16 + lr, lg + 4 * ks)));
+        m_run[rt] = -INFINITY;
+        l_run[rt] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    const int nvalid = dc.j < dc.nP ? min(16, dc.L - 16 * dc.j) : min(16, a.B - 16 * (dc.j - dc.nP));
+
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(slot + eoff<D>(lr, lg + 4 * ks)));
     f32x4 sc[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       sc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.k[ks], qf[rt][ks], sc[rt], 0, 0, 0);
+        sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], sc[rt], 0, 0, 0);
     }
-
     i16x4 pb[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -200,114 +367,108 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(AttnArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
     }
-
-    wave_lds_sync();
-    // O^T[d][row] += V^T[d][key] P^T[key][row]
+    // O^T[d][row] += V^T[d][key] P^T[key][row]; lane reads d = 16*dt + lr of
+    // keys 4*lg .. 4*lg+3
+    const lds_u16* vt = slot + KV;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint16_t* vp = vt + (4 * lg) * VSTR + 16 * dt + lr;
-      const i16x4 va = i16x4{(short)vp[0], (short)vp[VSTR], (short)vp[2 * VSTR], (short)vp[3 * VSTR]};
+      const int c = 2 * dt + (lr >> 3), e = lr & 7;
+      const i16x4 va = i16x4{(short)vt[eoff<D>(4 * lg + 0, c) + e], (short)vt[eoff<D>(4 * lg + 1, c) + e],
+                             (short)vt[eoff<D>(4 * lg + 2, c) + e], (short)vt[eoff<D>(4 * lg + 3, c) + e]};
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
     }
-    wave_lds_sync();
-  }
+  };
 
-  // row sums: the four lanes of a row each hold part of it
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    l_run[rt] += shfl_xor_f(l_run[rt], 16);
-    l_run[rt] += shfl_xor_f(l_run[rt], 32);
-  }
-
-  const size_t pbase = ((size_t)(s * (a.Hkv * a.n_rg) + gy) * a.n_chunk_max + c) * ROWS;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    __syncthreads();
-    if (lg == 0) {
-      s_m[wave][lr] = m_run[rt];
-      s_l[wave][lr] = l_run[rt];
+  // the stream: tiles 0..n-1; loads run two tiles ahead (past the end they
+  // repeat the last tile into the idle slot)
+  bool first_dma = true;
+  auto next_dma = [&](lds_u16* slot, int kt) INL {
+    if (kt < n) {
+      dma_tile(slot, dd, first_dma || dd.j == 0);
+      first_dma = false;
+      if (kt + 1 < n) advance(dd);
+    } else {
+      dma_tile(slot, dd, false);
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4*>(&s_o[wave][lr * MSTR + 16 * dt + 4 * lg]) = acc[rt][dt];
-    __syncthreads();
-    for (int idx = tid; idx < 16 * (D / 8); idx += 256) {
-      const int row = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
-      const int r = rg * ROWS + rt * 16 + row;
-      if (r >= R) continue;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][row]);
-      float wgt[4], Ls = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        wgt[w] = fast_exp2(s_m[w][row] - M);
-        Ls += s_l[w][row] * wgt[w];
-      }
-      float o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(&s_o[w][row * MSTR + d0]);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(&s_o[w][row * MSTR + d0 + 4]);
-        o[0] += wgt[w] * lo.x; o[1] += wgt[w] * lo.y; o[2] += wgt[w] * lo.z; o[3] += wgt[w] * lo.w;
-        o[4] += wgt[w] * hi.x; o[5] += wgt[w] * hi.y; o[6] += wgt[w] * hi.z; o[7] += wgt[w] * hi.w;
-      }
-      if (n_chunks == 1) {
-        const float inv = 1.f / Ls;
-        const int pos = r / a.G, gi = r % a.G;
-        uint16_t* op = a.out + ((size_t)(s * a.B + pos) * a.Hq + g * a.G + gi) * D + d0;
-        u32x4 packed;
-        packed.x = (uint32_t)f2bf(o[0] * inv) | ((uint32_t)f2bf(o[1] * inv) << 16);
-        packed.y = (uint32_t)f2bf(o[2] * inv) | ((uint32_t)f2bf(o[3] * inv) << 16);
-        packed.z = (uint32_t)f2bf(o[4] * inv) | ((uint32_t)f2bf(o[5] * inv) << 16);
-        packed.w = (uint32_t)f2bf(o[6] * inv) | ((uint32_t)f2bf(o[7] * inv) << 16);
-        *reinterpret_cast<u32x4*>(op) = packed;
+  };
+  next_dma(R0, 0);
+  next_dma(R1, 1);
+  for (int k = 0; k < n; k += 3) {
+    next_dma(R2, k + 2);
+    consume(R0, k);
+    advance(dc);
+    next_dma(R0, k + 3);
+    if (k + 1 < n) {
+      consume(R1, k + 1);
+      advance(dc);
+    }
+    next_dma(R1, k + 4);
+    if (k + 2 < n) {
+      consume(R2, k + 2);
+      advance(dc);
+    }
+  }
+  // close the last segment: dc now points one past the last tile
+  {
+    Dec prev = dc;
+    if (prev.j == 0) {
+      if (prev.hg == 0) {
+        --prev.s;
+        load_seq(prev);
+        prev.hg = NHG - 1;
       } else {
-        float* po = a.part_o + (pbase + rt * 16 + row) * D + d0;
-        *reinterpret_cast<f32x4*>(po) = f32x4{o[0], o[1], o[2], o[3]};
-        *reinterpret_cast<f32x4*>(po + 4) = f32x4{o[4], o[5], o[6], o[7]};
-        if (d0 == 0) a.part_ml[pbase + rt * 16 + row] = make_float2(M, Ls);
+        --prev.hg;
       }
+      prev.j = prev.tiles - 1;
+    } else {
+      --prev.j;
     }
+    finalize(prev);
   }
+  wait_vm<0>();   // no load may land in LDS after the wave is gone
 }
 
-// Merge the chunk partials of one (sequence, kv head, row group).
+// Merge the partials of segments split over several waves.
 template <int D, int RT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int ROWS = 16 * RT;
-  const int s = blockIdx.y, gy = blockIdx.x;
-  const int g = gy / a.n_rg, rg = gy % a.n_rg;
-  const int L = a.prefix_len[s];
-  const int n_chunks = max(1, (L + a.chunk_keys - 1) / a.chunk_keys);
-  if (n_chunks == 1) return;
+  const int NHG = a.Hkv * a.n_rg, nB = (a.B + 15) / 16;
+  const int seg = blockIdx.x;
+  const int s = seg / NHG, hg = seg % NHG;
+  const int g = hg / a.n_rg, rg = hg % a.n_rg;
+  const long T = (long)NHG * a.plan[a.S];
+  const long NW = min((long)a.grid, max(1L, T / 64));
+  const int tiles = (a.prefix_len[s] + 15) / 16 + nB;
+  const long ts = (long)NHG * a.plan[s] + (long)hg * tiles;
+  const long w0 = ((ts + 1) * NW - 1) / T;
+  const long w1 = ((ts + tiles) * NW - 1) / T;
+  const int pieces = (int)(w1 - w0 + 1);
+  if (pieces == 1) return;
   const int R = a.G * a.B;
-  const size_t base0 = (size_t)(s * (a.Hkv * a.n_rg) + gy) * a.n_chunk_max;
+  const size_t base = (size_t)seg * a.maxp;
   for (int idx = threadIdx.x; idx < ROWS * (D / 8); idx += 256) {
     const int row = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
-    const int r = rg * ROWS + row;
-    if (r >= R) continue;
+    const int rr = rg * ROWS + row;
+    if (rr >= R) continue;
     float M = -INFINITY;
-    for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, a.part_ml[(base0 + c) * ROWS + row].x);
+    for (int p = 0; p < pieces; ++p) M = fmaxf(M, a.part_ml[(base + p) * ROWS + row].x);
     float Ls = 0.f, o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float2 ml = a.part_ml[(base0 + c) * ROWS + row];
-      const float w = fast_exp2(ml.x - M);
-      Ls += ml.y * w;
-      const float* po = a.part_o + ((base0 + c) * ROWS + row) * D + d0;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(po);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(po + 4);
-      o[0] += w * lo.x; o[1] += w * lo.y; o[2] += w * lo.z; o[3] += w * lo.w;
-      o[4] += w * hi.x; o[5] += w * hi.y; o[6] += w * hi.z; o[7] += w * hi.w;
+    for (int p = 0; p < pieces; ++p) {
+      const float2 ml = a.part_ml[(base + p) * ROWS + row];
+      const float wgt = fast_exp2(ml.x - M);
+      Ls += ml.y * wgt;
+      const float* po = a.part_o + ((base + p) * ROWS + row) * D + d0;
+      const f32x4 lo4 = *reinterpret_cast<const f32x4*>(po);
+      const f32x4 hi4 = *reinterpret_cast<const f32x4*>(po + 4);
+      o[0] += wgt * lo4.x; o[1] += wgt * lo4.y; o[2] += wgt * lo4.z; o[3] += wgt * lo4.w;
+      o[4] += wgt * hi4.x; o[5] += wgt * hi4.y; o[6] += wgt * hi4.z; o[7] += wgt * hi4.w;
     }
     const float inv = 1.f / Ls;
-    const int pos = r / a.G, gi = r % a.G;
+    const int pos = rr / a.G, gi = rr % a.G;
     uint16_t* op = a.out + ((size_t)(s * a.B + pos) * a.Hq + g * a.G + gi) * D + d0;
     u32x4 packed;
     packed.x = (uint32_t)f2bf(o[0] * inv) | ((uint32_t)f2bf(o[1] * inv) << 16);
@@ -318,35 +479,30 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   }
 }
 
-AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size,
-                   int max_pages) {
+AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_pages) {
   AttnPlan p{};
   p.D = D;
   const int G = Hq / Hkv;
   const int R = G * B;
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   p.n_rg = (R + 16 * p.RT - 1) / (16 * p.RT);
-  p.chunk_keys = p.RT >= 4 ? 1024 : 512;
-  const long max_prefix = (long)max_pages * page_size;
-  p.n_chunk_max = (int)std::max<long>(1, (max_prefix + p.chunk_keys - 1) / p.chunk_keys);
-  if (p.n_chunk_max > 1) {
-    const size_t slots = (size_t)S * Hkv * p.n_rg * p.n_chunk_max * 16 * p.RT;
-    const size_t o_bytes = (slots * D * sizeof(float) + 255) & ~(size_t)255;
-    p.ws_bytes = o_bytes + slots * sizeof(float2);
-  } else {
-    p.ws_bytes = 0;
-  }
+  const long max_seg_tiles = ((long)max_pages * page_size + 15) / 16 + (B + 15) / 16;
+  p.maxp = (int)((max_seg_tiles + 63) / 64 + 1);
+  const int slot_bytes = (2 * 16 * D + 16 * p.RT * D) * 2;
+  const int waves_per_cu = std::max(1, std::min(8, kLdsPerCU / (NR * slot_bytes)));
+  p.grid = kCUs * waves_per_cu;
+  p.plan_bytes = ((size_t)(S + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  const size_t slots = (size_t)S * Hkv * p.n_rg * p.maxp * 16 * p.RT;
+  p.o_bytes = (slots * D * sizeof(float) + 255) & ~(size_t)255;
+  p.ws_bytes = p.plan_bytes + p.o_bytes + slots * sizeof(float2);
   return p;
 }
 
 template <int D, int RT>
 static hipError_t launch_dr(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
-  dim3 grid(p.n_chunk_max, a.Hkv * p.n_rg, a.S);
-  attn_chunk_kernel<D, RT><<<grid, 256, 0, st>>>(a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_chunk_max == 1) return e;
-  dim3 g2(a.Hkv * p.n_rg, a.S);
-  attn_combine_kernel<D, RT><<<g2, 256, 0, st>>>(a);
+  attn_plan_kernel<<<1, 1024, 0, st>>>(a);
+  attn_stream_kernel<D, RT><<<p.grid, 64, 0, st>>>(a);
+  attn_combine_kernel<D, RT><<<a.S * a.Hkv * p.n_rg, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

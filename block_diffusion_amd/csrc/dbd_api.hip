@@ -52,7 +52,8 @@ dbd_status check_attn(int S, int B, int Hq, int Hkv, int D, int page_size,
   REQUIRE(page_size >= 16 && page_size % 16 == 0, "page_size must be a positive multiple of 16 (got %d)", page_size);
   REQUIRE(max_pages >= 1, "max_pages_per_seq must be >= 1 (got %d)", max_pages);
   REQUIRE(S <= 65535, "S must be <= 65535 (got %d)", S);
-  REQUIRE((long)Hkv * ((Hq / Hkv) * B + 63) / 64 <= 65535, "too many kv heads x row groups");
+  REQUIRE((long)S * ((long)max_pages * page_size / 16 + 4) < (1L << 31),
+          "S x max_pages_per_seq x page_size too large for 32-bit tile counts");
   if (D != 64 && D != 128) return fail(DBD_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
   return DBD_OK;
 }
@@ -81,19 +82,18 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
                         float scale, dbd_bf16* out, void* ws, size_t ws_bytes,
                         hipStream_t st) {
   dbd::AttnPlan plan = dbd::attn_plan(S, B, Hq, Hkv, D, P, max_pages);
-  if (plan.ws_bytes > 0) {
-    if (ws == nullptr || ws_bytes < plan.ws_bytes)
-      return fail(DBD_ERR_WORKSPACE, "attention workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
-    if (!aligned(ws, 256)) return fail(DBD_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  }
+  if (ws == nullptr || ws_bytes < plan.ws_bytes)
+    return fail(DBD_ERR_WORKSPACE, "attention workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
+  if (!aligned(ws, 256)) return fail(DBD_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   dbd::AttnArgs a{};
   a.q = q; a.k_blk = k_blk; a.v_blk = v_blk; a.k_cache = k_cache; a.v_cache = v_cache;
   a.page_table = page_table; a.prefix_len = prefix_len; a.out = out;
-  const size_t slots = (size_t)S * Hkv * plan.n_rg * plan.n_chunk_max * 16 * plan.RT;
-  a.part_o = static_cast<float*>(ws);
-  a.part_ml = plan.ws_bytes ? reinterpret_cast<float2*>(static_cast<char*>(ws) + round_up(slots * D * sizeof(float))) : nullptr;
+  char* w = static_cast<char*>(ws);
+  a.plan = reinterpret_cast<int32_t*>(w);
+  a.part_o = reinterpret_cast<float*>(w + plan.plan_bytes);
+  a.part_ml = reinterpret_cast<float2*>(w + plan.plan_bytes + plan.o_bytes);
   a.S = S; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.P = P; a.max_pages = max_pages;
-  a.n_rg = plan.n_rg; a.chunk_keys = plan.chunk_keys; a.n_chunk_max = plan.n_chunk_max;
+  a.n_rg = plan.n_rg; a.maxp = plan.maxp; a.grid = plan.grid;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
   hipError_t e = dbd::attn_launch(plan, a, st);

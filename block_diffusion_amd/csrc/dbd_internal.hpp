@@ -17,18 +17,19 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* prefix_len;
   uint16_t* out;
-  float* part_o;   // [S][Hkv*n_rg][n_chunk_max][rows][D] unnormalised sums
-  float2* part_ml; // [S][Hkv*n_rg][n_chunk_max][rows] (max, sum), log2 units
+  int32_t* plan;   // [S+1] exclusive prefix sums of tiles per sequence
+  float* part_o;   // [S*NHG*maxp][rows][D] unnormalised sums of split segments
+  float2* part_ml; // [S*NHG*maxp][rows] (max, sum), log2 units
   int S, B, Hq, Hkv, G, P, max_pages;
   int n_rg;        // row groups per kv head (rows = G*B split in 16*RT)
-  int chunk_keys;  // prefix keys per work item (multiple of 64)
-  int n_chunk_max; // chunk slots per (sequence, kv head, row group)
+  int maxp;        // partial slots per segment
+  int grid;        // workgroups (single waves) of the stream kernel
   float scale_log2;
 };
 
 struct AttnPlan {
-  int D, RT, n_rg, chunk_keys, n_chunk_max;
-  size_t ws_bytes;
+  int D, RT, n_rg, maxp, grid;
+  size_t plan_bytes, o_bytes, ws_bytes;  // workspace: plan | part_o | part_ml
 };
 
 AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size,

@@ -78,8 +78,11 @@ def test_attn_workspace_required():
     assert st == api.DBD_ERR_WORKSPACE
     st = L.dbd_attn_paged(128, 4, 32, 8, 128, 256, 16, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, 16, need - 1, None)
     assert st == api.DBD_ERR_WORKSPACE
-    # one chunk per sequence: no workspace needed
-    assert api.dbd_attn_workspace_size(2, 4, 4, 2, 64, 16, 3) == 0
+    # the tile plan and the split-segment partials always need some space
+    small = api.dbd_attn_workspace_size(2, 4, 4, 2, 64, 16, 3)
+    assert 0 < small < need
+    st = L.dbd_attn_paged(2, 4, 4, 2, 64, 16, 3, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, None, 0, None)
+    assert st == api.DBD_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("args,status", [
