@@ -42,9 +42,35 @@ def parse():
     ap.add_argument("--workload", default="sdar4b_b4_bs128")
     ap.add_argument("--kernel-iters", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=128,
-                    help="sequences in the CPU oracle's bounded sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="the CPU oracle repeats whole blocks until this much time has passed")
+    ap.add_argument("--only", choices=["attention", "lmhead", "remask"],
+                    help="launch only this entry point (warmup + steps times, round-1 inputs) and "
+                         "print its mean launch time: the run that rocprofv3 counters are taken on")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB",
+                    help="copy MIB MiB device-to-device (warmup + steps times) and exit: the plain "
+                         "copy kernel of known size that scales FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
+
+
+def traffic_table(workload):
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE
+    (scaled by the copy calibration), keyed by entry point and row count.
+    An entry counts only while the kernel source it was taken on is
+    unchanged (sha256 recorded beside it); otherwise the figure is None."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    table = {}
+    if not os.path.exists(path):
+        return table
+    pat = re.compile(r"<!-- traffic (\S+) rows=(\d+) bytes=(\d+) src=(\S+) sha256=([0-9a-f]+) -->")
+    for m in pat.finditer(open(path).read()):
+        name, rows, nbytes, src, sha = m.groups()
+        src_path = os.path.join(ROOT, "block_diffusion_amd", "csrc", src)
+        ok = os.path.exists(src_path) and hashlib.sha256(open(src_path, "rb").read()).hexdigest() == sha
+        table[(name, int(rows))] = int(nbytes) if ok else None
+    return table
 
 
 def main():
@@ -66,6 +92,16 @@ def main():
     w = BY_NAME[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": nbytes, "launches": args.warmup + args.steps}))
+        return
 
     def dbf(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -113,6 +149,11 @@ def main():
     def step():
         reset()
         graph.launch()
+
+    if args.only:
+        only(args, w, api, fixed, per_round[0], attn_out, bufs, tok0, st0)
+        graph.close()
+        return
 
     # rows per round (for the LM-head breakdown), from one untimed block
     reset()
@@ -192,9 +233,11 @@ def main():
                      unit="GB/s")
     lm_roof = dict(bound="mfma", achieved=lm_flops / (t_lm1 * 1e-6) / 1e12, peak=PEAK_BF16_TFLOPS,
                    unit="TFLOP/s")
+    traffic = traffic_table(w.name)
+    attn_roof["traffic"] = traffic.get(("dbd_attn_paged", n))
+    lm_roof["traffic"] = traffic.get(("dbd_lmhead_conf", M1))
     for r in (attn_roof, lm_roof):
         r["frac"] = r["achieved"] / r["peak"]
-        r["traffic"] = None
     dominant = "attention" if step_attn >= step_lm else "lmhead"
     roof = dict(attn_roof if dominant == "attention" else lm_roof)
     roof["kernel"] = "dbd_attn_paged" if dominant == "attention" else "dbd_lmhead_conf"
@@ -220,14 +263,51 @@ def main():
     graph.close()
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, fx, rins[0], args.cpu_seqs)
+        out["cpu_baseline"] = cpu_baseline(w, fx, rins, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(w, fx, rin, n_seq):
-    """The oracle, as it stands, on a bounded sample: the first n_seq
-    sequences' round 1 (attention for all their heads, the LM head on their
-    masked rows, the remask)."""
+def only(args, w, api, fixed, r1, attn_out, bufs, tok0, st0):
+    """One entry point alone on the round-1 inputs (all S*B rows masked, so
+    the LM head projects S*B rows), for counter runs."""
+    import torch
+    dev = attn_out.device
+    n = w.S * w.B
+    if args.only == "attention":
+        fn = lambda: api.dbd_attn_paged(r1["q"], r1["k_blk"], r1["v_blk"], fixed["k_cache"],
+                                        fixed["v_cache"], fixed["page_table"], fixed["prefix_len"],
+                                        attn_out, ws=bufs.workspace)
+    elif args.only == "lmhead":
+        rows = torch.arange(n, dtype=torch.int32, device=dev)
+        nr = torch.tensor([n], dtype=torch.int32, device=dev)
+        fn = lambda: api.dbd_lmhead_conf(r1["hidden"], fixed["w_vocab"], nr, bufs.argmax_tok,
+                                         bufs.conf, w.mask_id, row_index=rows, max_rows=n,
+                                         ws=bufs.workspace)
+    else:
+        conf_r = torch.rand(n, device=dev)
+        arg_r = torch.zeros(n, dtype=torch.int32, device=dev)
+        tk, ss = tok0.clone(), st0.clone()
+        ri = torch.zeros(n, dtype=torch.int32, device=dev)
+        nr2 = torch.zeros(1, dtype=torch.int32, device=dev)
+        fn = lambda: api.dbd_remask_commit(tk, ss, arg_r, conf_r, ri, nr2, w.mask_id, 2.0)
+    for _ in range(args.warmup):
+        fn()
+    stream = torch.cuda.current_stream()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(args.steps):
+        fn()
+    e.record(stream)
+    e.synchronize()
+    print(json.dumps({"only": args.only, "workload": w.name, "rows": n, "launches": args.steps,
+                      "us_per_launch": round(s.elapsed_time(e) * 1e3 / args.steps, 2)}), flush=True)
+
+
+def cpu_baseline(w, fx, rins, min_seconds):
+    """The oracle, as it stands, on the same job: whole blocks (every round
+    of every sequence: float64 attention over all heads, the full-vocabulary
+    LM head on the masked rows, the remask), repeated until at least
+    min_seconds have passed; value in the same unit as the GPU figure."""
     import numpy as np
 
     import oracle
@@ -237,25 +317,24 @@ def cpu_baseline(w, fx, rin, n_seq):
     except Exception:
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    S = n_seq
+    blocks = 0
     t0 = time.perf_counter()
-    for s in range(S):
-        for g in range(w.Hkv):
-            oracle.attention_group(s, g, rin.q, rin.k_blk, rin.v_blk, fx.k_cache, fx.v_cache,
-                                   fx.page_table, fx.prefix_len)
-    toks, state = fx.block_tokens0[:S], fx.seq_state0[:S]
-    rows = oracle.compact_rows(toks, state, w.mask_id)
-    a, p1, _ = oracle.lmhead_rows(rin.hidden[rows], fx.w_vocab, w.mask_id)
-    conf = np.full(S * w.B, np.nan); conf[rows] = p1
-    arg = np.full(S * w.B, -1); arg[rows] = a
-    oracle.remask(toks, state, conf, arg, w.mask_id, w.tau)
-    dt = time.perf_counter() - t0
-    return {"value": round(S * w.B / dt, 3), "unit": "block-tokens/s",
+    while True:
+        toks, state = fx.block_tokens0, fx.seq_state0
+        for rin in rins:
+            r = oracle.denoise_round(rin, fx, w.mask_id, w.tau, block_tokens=toks, seq_state=state)
+            toks, state = r["tokens"], r["state"]
+        blocks += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    n_tok = w.S * w.B * len(rins) * blocks
+    return {"value": round(n_tok / dt, 3), "unit": "block-tokens/s",
             "cores": blas_threads if blas_threads else cores, "kind": "oracle",
-            "sample": f"round 1 of the first {S} of {w.S} sequences ({S * w.B} block tokens): "
-                      f"float64 attention over all their heads, full-vocabulary LM head on "
-                      f"{rows.size} masked rows, remask; {dt:.1f} s on {cores} host cores "
-                      f"(BLAS threads {blas_threads})"}
+            "sample": f"{blocks} whole block(s) of the same workload ({len(rins)} rounds x {w.S} "
+                      f"sequences x {w.B} positions = {n_tok} block tokens): float64 attention "
+                      f"over every head, full-vocabulary LM head on the masked rows, remask; "
+                      f"{dt:.1f} s on {cores} host cores (BLAS threads {blas_threads})"}
 
 
 if __name__ == "__main__":
