@@ -23,11 +23,17 @@ import numpy as np
 from .bf16 import widen
 
 
-def lmhead_logits(h_rows, w_vocab_bits, mask_id):
-    """float64 logits [M][V] with the mask column at -inf."""
-    W = widen(w_vocab_bits)                      # [V][Hd]
+def lmhead_logits(h_rows, w_vocab_bits, mask_id, vchunk=512):
+    """float64 logits [M][V] with the mask column at -inf.
+
+    W is widened a few hundred vocabulary rows at a time (each logit is the
+    same dot product; this only bounds the float64 copy of W in memory)."""
     H = widen(h_rows)                            # [M][Hd]
-    logits = H @ W.T
+    V = w_vocab_bits.shape[0]
+    logits = np.empty((H.shape[0], V))
+    for v0 in range(0, V, vchunk):
+        W = widen(w_vocab_bits[v0:v0 + vchunk])  # [vchunk][Hd]
+        logits[:, v0:v0 + vchunk] = H @ W.T
     logits[:, mask_id] = -np.inf
     return logits
 
@@ -43,20 +49,17 @@ def _reduce(logits):
     return arg.astype(np.int64), p1, p2
 
 
-def lmhead_rows(h_rows, w_vocab_bits, mask_id, chunk=64):
+def lmhead_rows(h_rows, w_vocab_bits, mask_id, chunk=256):
     """Greedy token, confidence and runner-up probability for each row.
 
     h_rows: [M][Hd] bf16 bits; w_vocab_bits: [V][Hd] bf16 bits.
     Returns (argmax [M] int64, p1 [M] float64, p2 [M] float64)."""
     M = h_rows.shape[0]
-    W = widen(w_vocab_bits)
     args = np.empty(M, dtype=np.int64)
     p1 = np.empty(M)
     p2 = np.empty(M)
     for i in range(0, M, chunk):
-        H = widen(h_rows[i:i + chunk])
-        logits = H @ W.T
-        logits[:, mask_id] = -np.inf
+        logits = lmhead_logits(h_rows[i:i + chunk], w_vocab_bits, mask_id)
         a, x1, x2 = _reduce(logits)
         args[i:i + chunk], p1[i:i + chunk], p2[i:i + chunk] = a, x1, x2
     return args, p1, p2

@@ -10,8 +10,8 @@ import torch
 
 import oracle
 from block_diffusion_amd import api, synth
-from block_diffusion_amd.workloads import (SDAR_1P7B, SDAR_4B, SDAR_4B_HIGHCONF, TINY,
-                                           Workload)
+from block_diffusion_amd.workloads import (LLADA_LONG, SDAR_1P7B, SDAR_4B, SDAR_4B_HIGHCONF,
+                                           SDAR_8B, TINY, Workload)
 from gpu_util import (ATTN_MAX_ABS, ATTN_REL_L2, RoundState, check_commits, check_lm_rows,
                       compare_attn, dev_bf16, dev_i32, dev_u8, host_bits, oracle_attn_groups,
                       round_inputs_dev, run_attn, tie_set, widen_bits)
@@ -114,6 +114,43 @@ def test_attention_deterministic():
     assert np.array_equal(run_attn(fx, rin), run_attn(fx, rin))
 
 
+@pytest.fixture(scope="module")
+def big_fixed():
+    """Fixed inputs of the SDAR-8B (B=16) and LLaDA (B=64, 16K-32K prefix)
+    shapes, generated once per module."""
+    cache = {}
+
+    def get(w):
+        if w.name not in cache:
+            cache.clear()                    # one multi-GB workload at a time
+            cache[w.name] = synth.make_fixed(w)
+        return cache[w.name]
+    return get
+
+
+def _sample_groups(w, L, n_seq, n_head, seed):
+    g = np.random.default_rng(seed)
+    ss = sorted(set([int(np.argmax(L)), int(np.argmin(L))] +
+                    g.choice(w.S, min(n_seq, w.S), replace=False).tolist()))
+    return [(s, int(k)) for s in ss for k in g.choice(w.Hkv, min(n_head, w.Hkv), replace=False)]
+
+
+@pytest.mark.parametrize("w", [SDAR_8B, LLADA_LONG], ids=lambda w: w.name)
+def test_attention_parity_large_sampled(w, big_fixed):
+    """Full-size SDAR-8B (64 rows per kv head, prefixes to 8K) and LLaDA
+    (MHA, 64 rows, prefixes to 32K) attention on sampled (sequence, head)
+    groups, always including the longest and shortest prefixes."""
+    fx = big_fixed(w)
+    rin = synth.make_round(w, 1, None)
+    out = run_attn(fx, rin)
+    groups = _sample_groups(w, fx.prefix_len, 6, 3, 11)
+    ref = oracle_attn_groups(fx, rin, groups)
+    mx, rl2 = compare_attn(out, ref, w.G)
+    print(f"{w.name}: {len(groups)} groups, max abs {mx:.3e} rel L2 {rl2:.3e}")
+    assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2
+    assert np.all(np.isfinite(widen_bits(out)))
+
+
 # ------------------------------------------------------------------- LM head
 
 def _lm_run(hidden_bits, w_bits, mask_id, rows, max_rows=None, use_index=True):
@@ -187,6 +224,24 @@ def test_lmhead_parity_sdar4b_sampled(w, sdar4b_fixed):
         samp = np.unique(samp)
         check_lm_rows(samp, arg, conf, rin.hidden, fx.w_vocab, w.mask_id)
         assert np.all(arg[M:] == -7)
+
+
+@pytest.mark.parametrize("w", [SDAR_8B, LLADA_LONG], ids=lambda w: w.name)
+def test_lmhead_parity_large_sampled(w, big_fixed):
+    """Round-1 masked rows of the SDAR-8B shapes (about 640 rows: two row
+    tiles of the LM head, hidden 4096) and of LLaDA (512 rows, vocabulary
+    126464), through the compact row list; sampled rows against the oracle."""
+    fx = big_fixed(w)
+    rin = synth.make_round(w, 1, fx.w_vocab)
+    rows = oracle.compact_rows(fx.block_tokens0, fx.seq_state0, w.mask_id)
+    M = rows.size
+    arg, conf = _lm_run(rin.hidden, fx.w_vocab, w.mask_id, rows, max_rows=w.S * w.B)
+    g = np.random.default_rng(M)
+    samp = np.unique(np.concatenate([rows[g.choice(M, 24, replace=False)], rows[[0, M - 1]]]))
+    _, p1, _, nt = check_lm_rows(samp, arg, conf, rin.hidden, fx.w_vocab, w.mask_id)
+    print(f"{w.name}: M={M}, {len(samp)} sampled rows, tie-exempt {nt}")
+    untouched = np.setdiff1d(np.arange(w.S * w.B), rows)
+    assert np.all(arg[untouched] == -7)
 
 
 # -------------------------------------------------------------------- remask
@@ -303,6 +358,18 @@ def test_round_sdar4b_rounds(sdar4b_fixed):
     st, hist = _run_rounds(w, fx, w.rounds, check_lm_full=False)
     assert np.all(hist[-1][1] == oracle.SAVING)
     assert (hist[0][0] != w.mask_id).sum() >= w.S
+
+
+@pytest.mark.parametrize("w,n_rounds", [(SDAR_8B, 3), (LLADA_LONG, 2)], ids=lambda x: getattr(x, "name", str(x)))
+def test_round_large_rounds(w, n_rounds, big_fixed):
+    """First rounds of the SDAR-8B (initial commits, threshold 0.75) and
+    LLaDA shapes: every round's commits are exactly the rule applied to the
+    GPU's confidences, from the GPU's own state."""
+    fx = big_fixed(w)
+    st, hist = _run_rounds(w, fx, n_rounds, check_lm_full=False)
+    masked0 = (fx.block_tokens0 == w.mask_id).sum()
+    masked = [(h[0] == w.mask_id).sum() for h in hist]
+    assert masked[0] < masked0 and all(b < a for a, b in zip(masked, masked[1:]))
 
 
 @pytest.mark.parametrize("w", [TINY, SDAR_1P7B], ids=lambda w: w.name)

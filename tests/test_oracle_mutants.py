@@ -22,12 +22,12 @@ MUTANTS = [
     ("attention.py", "pages = np.asarray(page_table_s[:npg], dtype=np.int64)",
      "pages = np.sort(np.asarray(page_table_s[:npg], dtype=np.int64))", "attn"),
     ("attention.py", "out[:, gi, :] = p @ vals", "out[:, gi, :] = p @ keys", "attn"),
-    ("lmhead.py", "        logits[:, mask_id] = -np.inf\n        a, x1",
-     "        a, x1", "lm"),
+    ("lmhead.py", "    logits[:, mask_id] = -np.inf\n    return logits",
+     "    return logits", "lm"),
     ("lmhead.py", "arg = logits.argmax(axis=1)",
      "arg = logits.shape[1] - 1 - logits[:, ::-1].argmax(axis=1)", "lm"),
-    ("lmhead.py", "logits = H @ W.T\n        logits[:, mask_id]",
-     "logits = (H @ W.T) / np.sqrt(H.shape[1])\n        logits[:, mask_id]", "lm"),
+    ("lmhead.py", "logits[:, v0:v0 + vchunk] = H @ W.T",
+     "logits[:, v0:v0 + vchunk] = (H @ W.T) / np.sqrt(H.shape[1])", "lm"),
     ("lmhead.py", "part = np.partition(e, -2, axis=1)[:, -2]",
      "part = np.sort(e, axis=1)[:, -2] * 0 + np.sort(e, axis=1)[:, -3]", "lm"),
     ("remask.py", "conf[s, i] >= tau", "conf[s, i] > tau", "remask"),
