@@ -18,9 +18,9 @@
 // attn_combine_kernel merges, one that fits in one wave is written directly.
 // attn_plan_kernel first turns prefix lengths into tile prefix sums.
 //
-// Per wave, tiles go straight from global memory into a three-slot LDS ring
-// (global_load_lds_dwordx4: 16 keys of K and of V, plus the segment's query
-// rows when the tile starts one), two tiles in flight while the third is
+// Per wave, tiles go straight from global memory into a ring of kRing LDS
+// slots (global_load_lds_dwordx4: 16 keys of K and of V, plus the segment's
+// query rows when the tile starts one), kRing-1 tiles in flight while one is
 // computed.  Rows are stored with their 16-byte chunks XOR-permuted by row so
 // fragment reads hit distinct banks.  Per tile:
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (lane: query row, 4 keys);
@@ -44,7 +44,7 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #define INL __attribute__((always_inline))
 
-constexpr int NR = 3;          // ring slots per wave
+constexpr int kRing = 3;       // ring slots per wave
 constexpr int kCUs = 256;      // MI355X compute units
 constexpr int kLdsPerCU = 160 * 1024;
 
@@ -154,16 +154,12 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int RT>
+template <int D, int RT, int NR>
 __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   using Gm = Geo<D, RT>;
   constexpr int ROWS = Gm::ROWS, KS = Gm::KS, DT = Gm::DT, KV = Gm::KV;
-  __shared__ __align__(16) uint16_t R0_[Gm::SLOT];
-  __shared__ __align__(16) uint16_t R1_[Gm::SLOT];
-  __shared__ __align__(16) uint16_t R2_[Gm::SLOT];
-  lds_u16* const R0 = (lds_u16*)R0_;
-  lds_u16* const R1 = (lds_u16*)R1_;
-  lds_u16* const R2 = (lds_u16*)R2_;
+  __shared__ __align__(16) uint16_t ring_[NR * Gm::SLOT];
+  lds_u16* const ring = (lds_u16*)ring_;
 
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int S = a.S, NHG = a.Hkv * a.n_rg, nB = (a.B + 15) / 16;
@@ -297,9 +293,9 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   };
 
   auto consume = [&](const lds_u16* slot, int k) INL {
-    // every tile issues at least 2*D/32 loads (K and V) and two tiles were
+    // every tile issues at least 2*D/32 loads (K and V) and NR-1 tiles were
     // issued after this one: waiting down to that many leaves this slot done
-    wait_vm<4 * Gm::KV / 512>();
+    wait_vm<(NR - 1) * 2 * Gm::KV / 512>();
     if (k > 0 && dc.j == 0) {
       // the previous tile closed a segment
       Dec prev = dc;
@@ -381,8 +377,8 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
     }
   };
 
-  // the stream: tiles 0..n-1; loads run two tiles ahead (past the end they
-  // repeat the last tile into the idle slot)
+  // the stream: tiles 0..n-1; loads run NR-1 tiles ahead (past the end
+  // they repeat the last tile into the idle slot)
   bool first_dma = true;
   auto next_dma = [&](lds_u16* slot, int kt) INL {
     if (kt < n) {
@@ -393,21 +389,16 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       dma_tile(slot, dd, false);
     }
   };
-  next_dma(R0, 0);
-  next_dma(R1, 1);
-  for (int k = 0; k < n; k += 3) {
-    next_dma(R2, k + 2);
-    consume(R0, k);
-    advance(dc);
-    next_dma(R0, k + 3);
-    if (k + 1 < n) {
-      consume(R1, k + 1);
-      advance(dc);
-    }
-    next_dma(R1, k + 4);
-    if (k + 2 < n) {
-      consume(R2, k + 2);
-      advance(dc);
+#pragma unroll
+  for (int u = 0; u + 1 < NR; ++u) next_dma(ring + u * Gm::SLOT, u);
+  for (int k = 0; k < n; k += NR) {
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      next_dma(ring + ((u + NR - 1) % NR) * Gm::SLOT, k + u + NR - 1);
+      if (u == 0 || k + u < n) {
+        consume(ring + u * Gm::SLOT, k + u);
+        advance(dc);
+      }
     }
   }
   // close the last segment: dc now points one past the last tile
@@ -489,7 +480,7 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
   const long max_seg_tiles = ((long)max_pages * page_size + 15) / 16 + (B + 15) / 16;
   p.maxp = (int)((max_seg_tiles + 63) / 64 + 1);
   const int slot_bytes = (2 * 16 * D + 16 * p.RT * D) * 2;
-  const int waves_per_cu = std::max(1, std::min(8, kLdsPerCU / (NR * slot_bytes)));
+  const int waves_per_cu = std::max(1, std::min(8, kLdsPerCU / (kRing * slot_bytes)));
   p.grid = kCUs * waves_per_cu;
   p.plan_bytes = ((size_t)(S + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   const size_t slots = (size_t)S * Hkv * p.n_rg * p.maxp * 16 * p.RT;
@@ -501,7 +492,7 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
 template <int D, int RT>
 static hipError_t launch_dr(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
   attn_plan_kernel<<<1, 1024, 0, st>>>(a);
-  attn_stream_kernel<D, RT><<<p.grid, 64, 0, st>>>(a);
+  attn_stream_kernel<D, RT, kRing><<<p.grid, 64, 0, st>>>(a);
   attn_combine_kernel<D, RT><<<a.S * a.Hkv * p.n_rg, 256, 0, st>>>(a);
   return hipGetLastError();
 }

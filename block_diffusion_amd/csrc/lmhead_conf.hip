@@ -141,14 +141,18 @@ __device__ __forceinline__ void lm_rowtile(const LmArgs& a, int M, int mt, uint1
   for (int mb = 0; mb < 4; ++mb) run[mb] = Part{-INFINITY, 0x7fffffff, 0.f};
 
   for (int n0 = v_lo; n0 < v_hi; n0 += NT) {
-    const int vlim = v_hi - 1 - n0;   // W rows past the range re-read its last row (never used)
+    // W rows past the range re-read one of the tile's first 16 rows (their
+    // products are never used): spread over 16 rows rather than all on the
+    // last one, so that a ragged tile does not hammer one cache line
+    const int vlim = v_hi - 1 - n0;
     auto dma = [&](uint16_t* buf, int kt) {
       const char* wbase = reinterpret_cast<const char*>(a.w + (size_t)n0 * a.Hd + kt * TK);
       const char* hbase = reinterpret_cast<const char*>(a.hidden + kt * TK);
 #pragma unroll
       for (int i = 0; i < WPW; ++i) {
         const int q = wave * WPW + i;                        // LDS block (16 rows)
-        const int row = min(16 * q + lrow, vlim);
+        const int r0 = 16 * q + lrow;
+        const int row = r0 <= vlim ? r0 : min(r0 & 15, vlim);
         __builtin_amdgcn_global_load_lds((const void*)(wbase + (uint32_t)(row * hdb) + woffb[i]),
                                          LDS_PTR(buf + q * 512), 16, 0, 0);
       }
