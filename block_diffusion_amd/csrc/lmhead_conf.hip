@@ -7,44 +7,56 @@
 // generate.py runs greedy generation).  No logit is ever stored: a tile of
 // logits lives in MFMA accumulators and is reduced there.
 //
-// lmhead_tile_kernel (persistent, kLmGrid workgroups of four waves, one per
-// CU): C^T[v][m] = W[v][:] . h[m][:] with v_mfma_f32_32x32x16_bf16, each wave
-// owning a 128 (vocab) x 128 (row) block.  The workgroup tile adapts to the
-// row count M read on the device, so W streams from HBM exactly once while
-// every wave has work:  M <= 128: 512 vocab x 128 rows;  M <= 256: 256 x 256;
-// otherwise 128 x 512 (and row tiles of 512 in turn past 512 rows).  W and
-// the gathered hidden rows stream in k-stages of 32 straight from global
-// memory into four LDS buffers (16-byte chunks XOR-swizzled by row, so the
-// fragment reads are bank-conflict free); stages k+1..k+3 are in flight
-// while stage k is multiplied.  Each workgroup owns a contiguous vocabulary
-// range (32-column blocks split evenly), tiled NT columns at a time.  After each tile a wave reduces its accumulators per row
-// -- the largest logit (mask id and columns past V excluded), the lowest id
-// reaching it, sum(exp(l - max)) in fp32 -- and folds that into a running
-// (max, id, sum) per row; at the end the waves sharing rows fold through LDS
-// and the workgroup writes one partial per row.
+// lmhead_tile_kernel: persistent, one workgroup of four waves per CU.  The M
+// rows (read on the device) are split among the G members of a *team* of
+// workgroups that sit on the same XCD (workgroup b runs on XCD b % 8), with
+// G = 1, 2 or 4 for M <= 256, 512 or 1024 (larger M loops over passes of
+// 1024 rows).  Each team owns a contiguous range of the vocabulary; each
+// member streams that range of W against its own <= 256 rows.  The members
+// read the same W tile at about the same time, so W comes from HBM once per
+// XCD and from L2 for the other members.
 //
-// lmhead_merge_kernel: one wave per row folds the kLmGrid partials,
+// A tile is 256 vocabulary columns x R <= 256 rows, four waves of 128 x R/2
+// computing C^T[v][m] = W[v].h[m] with v_mfma_f32_32x32x16_bf16.  K streams
+// in stages of 64 (one 128-byte line per row) straight from global memory
+// into LDS (global_load_lds_dwordx4; 16-byte chunks XOR-permuted by row so
+// fragment reads are bank-conflict free):
+//   * waves 0-1 load W into a 3-slot ring, two stages ahead (HBM latency),
+//   * waves 2-3 load hidden rows into a 2-slot ring, one stage ahead (L2),
+// each with its own vmcnt, so a slow W line never holds up a hidden stage.
+// Stages run back to back across tiles.  Within a stage, the fragment reads
+// of k-step j+1 are interleaved with the MFMAs of k-step j.  After a tile,
+// each wave reduces its accumulators per row -- the largest logit (mask id
+// and columns past the range excluded), the lowest id reaching it, and
+// sum(exp(l - max)) -- and folds that into a running (max, id, sum) per row;
+// at the end the two waves sharing rows fold through LDS and the workgroup
+// writes one partial per (row, team).
+//
+// lmhead_merge_kernel: one wave per row folds the partials of all teams,
 // (m,a,s) + (m',a',s') = (max, id of the larger max or the lower id on equal
 // maxima, s*e^(m-max) + s'*e^(m'-max)), in a fixed order, and writes the
 // greedy token and the confidence 1/s = exp(max - logsumexp).
-#include <type_traits>
-
 #include "dbd_device.hpp"
 #include "dbd_internal.hpp"
 
 namespace dbd {
 
 namespace {
-constexpr int TK = 32;           // k depth of one stage
-constexpr int MAXR = 640;        // rows of the largest stage (128 + 512)
 
-// Physical 16-byte slot of logical k-chunk kc of a 64-byte LDS row: XOR with
-// ((row>>1) ^ (row>>3)) & 3, so that the 32 rows one fragment read touches
-// fall in distinct slots of every 128-byte and every 256-byte bank window.
-__device__ __forceinline__ int slot_xor(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
-__device__ __forceinline__ int swz(int row, int kc) {
-  return row * TK + ((kc ^ slot_xor(row)) << 3);
-}
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+constexpr int TK = 64;               // k per stage: one 128-byte line per row
+constexpr int NT = 256;              // vocabulary columns per tile
+constexpr int RMAX = 256;            // hidden rows per workgroup per pass
+constexpr int WSLOT = NT * TK;       // elements of one W stage (32 KB)
+constexpr int HSLOT = RMAX * TK;     // elements of one hidden stage (32 KB)
+constexpr int NWS = 3;               // W ring slots (two stages in flight)
+constexpr int NHS = 2;               // hidden ring slots (one stage in flight)
+constexpr int WPW = NT / 8 / 2;      // 1 KB W loads per W wave per stage
+
+// chunk permutation of LDS row r: rows 2i and 2i+1 (one 256-byte bank window)
+// and any 8 consecutive rows (one 128-byte window per row) use distinct slots
+__device__ __forceinline__ int rswz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 struct Part {
   float m;
@@ -65,290 +77,361 @@ __device__ __forceinline__ void fold(Part& x, float m2, int a2, float s2) {
   x.a = a;
 }
 
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+// One 1 KB direct-to-LDS load: lane l copies the 16 bytes at base + off to
+// lds + 16*l.  Inline assembly, so that the compiler neither adds its own
+// vmcnt waits for the LDS it writes nor moves LDS accesses across it; the
+// rings are paced by explicit waits.  M0 carries the LDS address (the s_nop
+// is the wait state a freshly written M0 needs before an LDS DMA).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, const lds_u16* lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
+}
 
-// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
-
-// vmcnt(n) and lgkmcnt(0).
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
-}
-
-// Workgroup barrier without the release fence of __syncthreads(): that fence
-// would also wait for every load still streaming into LDS.  The empty asm
-// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// One workgroup's share of the vocabulary for row tile mt, with tile shape
-// NT (vocab) x MT (rows); WN x WM waves of 128 x 128.  Stages of TK=32 go
-// straight from global memory into LDS (global_load_lds_dwordx4: lane l of
-// a wave instruction fills bytes 16*l of a 1 KB block, i.e. 16 rows of 64 B),
-// four buffers deep, so stages k+1..k+3 stream in while stage k is multiplied.
-template <int NT, int MT>
-__device__ __forceinline__ void lm_rowtile(const LmArgs& a, int M, int mt, uint16_t* B0,
-                                           uint16_t* B1, uint16_t* B2, uint16_t* B3) {
-  constexpr int WN = NT / 128;
-  constexpr int CHW = (NT + MT) / 64;   // 1 KB wave loads per stage per wave
+// rows per pass member: G = 1, 2, 4 by row count
+__device__ __forceinline__ int team_size(int M) { return M <= 256 ? 1 : (M <= 512 ? 2 : 4); }
+
+// One pass of one workgroup: rows [m_base, m_end) of the compact row list
+// (R = 64*MB row slots, two waves of 32*MB rows) against vocabulary columns
+// [v_lo, v_hi), as seen by one wave; WL: this wave streams W (else hidden
+// rows).  Writes one partial per valid row into slot `team`.
+template <int MB, bool WL>
+__device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
+                                        int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
+  constexpr int R = 64 * MB, RH = 32 * MB;
+  constexpr int HPW = R / 16;                  // 1 KB hidden loads per hidden wave per stage
+  constexpr int NLD = WL ? WPW : HPW;          // this wave's loads per stage
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS bases in SGPRs
-  const int wn = wave % WN, wm = wave / WN;
-  const int m0 = mt * MT;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
   const int nk = a.Hd / TK;
-  // this workgroup's contiguous vocabulary range [v_lo, v_hi), in 32-column
-  // blocks split evenly over the grid, so every workgroup streams the same
-  // share of W whatever the tile count
-  const int nblk = (a.V + 31) / 32;
-  const int v_lo = min(a.V, (int)(((long)blockIdx.x * nblk) / gridDim.x) * 32);
-  const int v_hi = min(a.V, (int)(((long)(blockIdx.x + 1) * nblk) / gridDim.x) * 32);
+  const int ntile = (v_hi - v_lo + NT - 1) / NT;
+  const uint32_t hdb = (uint32_t)a.Hd * 2;     // row bytes
 
-  // Each wave fills WPW 1 KB blocks of W rows and HPW of gathered hidden
-  // rows per stage (a block = 16 rows of 64 B).  Lane l writes row R + l/4,
-  // LDS slot l%4, which must hold logical k-chunk (l%4) ^ slot_xor(row).
-  constexpr int WPW = NT / 64, HPW = MT / 64;
-  const int lrow = lane >> 2;
-  const int hdb = a.Hd * 2;                                  // row bytes
-  uint32_t hoffb[HPW];
+  // Lane l of a 1 KB load fills LDS row 8*blk + l/8, physical chunk l%8,
+  // which holds logical chunk (l%8) ^ rswz(row).  off[i]: byte offset of the
+  // lane's 16 bytes for this wave's i-th load, relative to the stage's
+  // first W row (W waves) or to the hidden matrix (hidden waves).
+  const int lr = lane >> 3;
+  uint32_t off[NLD];
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) {
-    const int r = 16 * (wave * HPW + j) + lrow;              // row within the hidden part
-    const int m = m0 + r;
-    const int hr = m < M ? (a.row_index ? a.row_index[m] : m) : 0;  // rows past M: any valid row
-    hoffb[j] = (uint32_t)hr * (uint32_t)hdb + (((lane & 3) ^ slot_xor(NT + r)) << 4);
-  }
-  uint32_t woffb[WPW];
-#pragma unroll
-  for (int i = 0; i < WPW; ++i) {
-    const int r = 16 * (wave * WPW + i) + lrow;
-    woffb[i] = (uint32_t)(((lane & 3) ^ slot_xor(r)) << 4);
+  for (int i = 0; i < NLD; ++i) {
+    const int blk = wn * NLD + i;
+    const int row = 8 * blk + lr;                       // LDS row
+    const uint32_t ch = (uint32_t)(((lane & 7) ^ rswz(row)) << 4);
+    if (WL) {
+      off[i] = (uint32_t)row * hdb + ch;
+    } else {
+      const int m = m_base + row;
+      const int mm = m < m_end ? m : m_base;            // rows past the list: any listed row
+      const int hr = a.row_index ? a.row_index[mm] : mm;
+      off[i] = (uint32_t)hr * hdb + ch;
+    }
   }
 
-  int mbv = (M - (m0 + wm * 128) + 31) >> 5;  // valid 32-row blocks of this wave
-  mbv = mbv < 0 ? 0 : (mbv > 4 ? 4 : mbv);
-
-  Part run[4];
+  // Issue cursor: the next stage this wave loads (tile it_t, k-stage it_k);
+  // past the last stage it keeps loading the last one (never used).
+  int it_t = 0, it_k = 0;
+  auto issue = [&](lds_u16* slot) {
+    const char* kb = reinterpret_cast<const char*>(WL ? a.w : a.hidden) + (size_t)it_k * (TK * 2);
+    if (WL) {
+      const int n0 = v_lo + min(it_t, ntile - 1) * NT;
+      const char* tb = kb + (size_t)n0 * hdb;
+      const int lim = v_hi - n0;                       // valid rows of this tile
+      // rows past the range re-read a row of the tile's first 8
+      const uint32_t back = (uint32_t)min(lr, lim - 1) * hdb;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) run[mb] = Part{-INFINITY, 0x7fffffff, 0.f};
-
-  for (int n0 = v_lo; n0 < v_hi; n0 += NT) {
-    // W rows past the range re-read one of the tile's first 16 rows (their
-    // products are never used): spread over 16 rows rather than all on the
-    // last one, so that a ragged tile does not hammer one cache line
-    const int vlim = v_hi - 1 - n0;
-    auto dma = [&](uint16_t* buf, int kt) {
-      const char* wbase = reinterpret_cast<const char*>(a.w + (size_t)n0 * a.Hd + kt * TK);
-      const char* hbase = reinterpret_cast<const char*>(a.hidden + kt * TK);
-#pragma unroll
-      for (int i = 0; i < WPW; ++i) {
-        const int q = wave * WPW + i;                        // LDS block (16 rows)
-        const int r0 = 16 * q + lrow;
-        const int row = r0 <= vlim ? r0 : min(r0 & 15, vlim);
-        __builtin_amdgcn_global_load_lds((const void*)(wbase + (uint32_t)(row * hdb) + woffb[i]),
-                                         LDS_PTR(buf + q * 512), 16, 0, 0);
+      for (int i = 0; i < NLD; ++i) {
+        const int row = 8 * (wn * NLD + i) + lr;
+        const uint32_t o = row < lim ? off[i] : back + (off[i] & 0x70);
+        dma16(tb, o, slot + (wn * NLD + i) * 512);
       }
+    } else {
 #pragma unroll
-      for (int j = 0; j < HPW; ++j) {
-        const int q = NT / 16 + wave * HPW + j;
-        __builtin_amdgcn_global_load_lds((const void*)(hbase + hoffb[j]),
-                                         LDS_PTR(buf + q * 512), 16, 0, 0);
+      for (int i = 0; i < NLD; ++i) dma16(kb, off[i], slot + (wn * NLD + i) * 512);
+    }
+    if (it_t < ntile) {
+      if (++it_k == nk) {
+        it_k = 0;
+        if (it_t + 1 < ntile) ++it_t;
+        else it_k = nk - 1, it_t = ntile;              // hold at the last stage
       }
-    };
+    }
+  };
+  // the stage about to be read has landed for this wave's stream, and this
+  // wave's fragment reads are done; then the whole workgroup syncs
+  auto sync = [&]() {
+    wait_vm<WL ? WPW * (NWS - 2) : HPW * (NHS - 2)>();
+    wait_lgkm0();
+    barrier_only();
+  };
 
-    // Accumulators start at 0, or at -inf on columns that are not candidates
-    // (the mask id, columns past this workgroup's range): MFMA accumulation
-    // keeps them at -inf, so the reduction below needs no per-value test.
+  // fragment reads: lane row (lane & 31) of a 32-row block, logical chunk
+  // 2j + lane/32 of k-step j; the permutation depends on the row mod 16 only,
+  // so blocks 32 rows apart share it
+  const int fr = lane & 31;
+  int chk[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) chk[j] = ((2 * j + (lane >> 5)) ^ rswz(fr)) << 3;
+  const lds_u16* const wfr = Wr + (wn * 128 + fr) * TK;
+  const lds_u16* const hfr = Hr + (wm * RH + fr) * TK;
+  auto read_frags = [&](int ws, int hs, int j, bf16x8* af, bf16x8* bfr) {
+    const lds_u16* w = wfr + ws * WSLOT + chk[j];
+    const lds_u16* h = hfr + hs * HSLOT + chk[j];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      af[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(w + nb * 32 * TK));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      bfr[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(h + mb * 32 * TK));
+  };
+
+  f32x16 acc[4][MB];
+  auto mfma_rows = [&](const bf16x8* af, const bf16x8* bfr, int mb) {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[nb], bfr[mb], acc[nb][mb], 0, 0, 0);
+  };
+  // one k-step's MFMAs with the next step's fragment reads interleaved
+  auto step = [&](const bf16x8* af, const bf16x8* bfr, int ws, int hs, int jn, bf16x8* an, bf16x8* bn) {
+    read_frags(ws, hs, jn, an, bn);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) mfma_rows(af, bfr, mb);
+    constexpr int NPAIR = 4 * MB < 4 + MB ? 4 * MB : 4 + MB;
+#pragma unroll
+    for (int r = 0; r < NPAIR; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+    if (4 * MB > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, 4 * MB - NPAIR, 0);
+    if (4 + MB > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, 4 + MB - NPAIR, 0);
+  };
+
+  Part run[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) run[mb] = Part{-INFINITY, 0x7fffffff, 0.f};
+
+  // Accumulators start at 0, or at -inf on columns that are not candidates
+  // (the mask id, columns past the range): MFMA accumulation keeps them at
+  // -inf, so the reduction needs no per-value test.
+  auto init_acc = [&](int n0) {
     const int vbase = n0 + wn * 128;
     const bool plain = (vbase + 128 <= v_hi) && (a.mask_id < vbase || a.mask_id >= vbase + 128);
-    f32x16 acc[4][4];
     if (plain) {
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16{};
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = f32x16{};
     } else {
+      // column vbase + loff + c of value c: compare the lane part against
+      // uniform bounds so that no per-value column index is kept in registers
+      const int loff = 4 * (lane >> 5), lim = v_hi - vbase, mk = a.mask_id - vbase;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
         f32x16 b;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int v = vbase + nb * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          b[i] = (v < v_hi && v != a.mask_id) ? 0.f : -INFINITY;
+          const int c = nb * 32 + 8 * (i >> 2) + (i & 3);
+          b[i] = (loff < lim - c && loff != mk - c) ? 0.f : -INFINITY;
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = b;
+        for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = b;
       }
     }
+  };
 
-    // fragments of one k-step (16): A = 4 blocks of W rows, B = 4 of hidden rows
-    auto read_frags = [&](const uint16_t* buf, int kk, bf16x8* af, bf16x8* bfr) {
-      const int kc = kk * 2 + (lane >> 5);
+  // reduce a finished tile: lane holds row (lane & 31) of each row block mb
+  // and vocabulary rows 8*(i/4) + 4*(lane/32) + (i%4) of each 32-block nb
+  auto reduce_tile = [&](int n0) {
+    const int vbase = n0 + wn * 128;
+    if (vbase >= v_hi) return;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        af[nb] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&buf[swz(wn * 128 + nb * 32 + (lane & 31), kc)]));
+    for (int mb = 0; mb < MB; ++mb) {
+      // block-online reduction of the lane's 64 values of this row, 16 at a
+      // time: block max, lowest id reaching it, sum(2^(x - m)) rescaled once
+      // per block.  Values are in log2 units; non-candidates are -inf.
+      float m = -INFINITY, sum = 0.f;
+      int idx = 0x7fffffff;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        bfr[mb] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(&buf[swz(NT + wm * 128 + mb * 32 + (lane & 31), kc)]));
-    };
-    auto mfmas = [&](const bf16x8* af, const bf16x8* bfr) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[nb], bfr[mb], acc[nb][mb], 0, 0, 0);
-    };
-    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-    // Stage kt (buffer `cur`, first k-step already in fa0/fb0): start the
-    // load of stage kt+3 into `nxt3` (read in stage kt-1, released by that
-    // stage's barrier), read the second k-step while the first multiplies,
-    // then wait for stage kt+1, sync in the middle of the stage, and read its
-    // first k-step while the second multiplies.  Every stage is the same code:
-    // past the last stage the loads repeat the last stage into the idle
-    // buffer and the final fragment read is unused.  Fragment reads complete
-    // (lgkmcnt 0) before each barrier, so a buffer is never refilled under a
-    // read still in flight.
-    auto step = [&](int kt, const uint16_t* cur, const uint16_t* nxt, uint16_t* nxt3) {
-      dma(nxt3, min(kt + 3, nk - 1));
-      read_frags(cur, 1, fa1, fb1);
-      mfmas(fa0, fb0);
-      wait_vm_lgkm0<2 * CHW>();
-      barrier_only();
-      read_frags(nxt, 0, fa0, fb0);
-      mfmas(fa1, fb1);
-    };
-
-    // nk is a multiple of 4 (Hd % 128 == 0), so the loop body is straight-line
-    dma(B0, 0);
-    dma(B1, 1);
-    dma(B2, 2);
-    wait_vm_lgkm0<2 * CHW>();
-    barrier_only();
-    read_frags(B0, 0, fa0, fb0);
-    for (int kt = 0; kt < nk; kt += 4) {
-      step(kt, B0, B1, B3);
-      step(kt + 1, B1, B2, B0);
-      step(kt + 2, B2, B3, B1);
-      step(kt + 3, B3, B0, B2);
-    }
-    // the next tile's first loads must not overtake this tile's last reads
-    wait_vm_lgkm0<0>();
-    barrier_only();
-
-    // reduce this tile: lane holds column (lane & 31) = one row per mb and
-    // vocab rows 8*(i/4) + 4*(lane/32) + (i%4) of each 32-block nb.
-    if (vbase < v_hi) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        // Block-online reduction of the lane's 64 values of this row, 16 at a
-        // time (one 32x32 block nb): block max, lowest id reaching it, and
-        // sum(2^(x - m)) rescaled once per block.  Values are in log2 units;
-        // non-candidates are -inf and contribute 0.
-        float m = -INFINITY, sum = 0.f;
-        int idx = 0x7fffffff;
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          __builtin_amdgcn_sched_barrier(0);
-          const int vb0 = vbase + nb * 32 + 4 * (lane >> 5);
-          float x[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            // read the accumulator from its AGPR here, not in one burst at the
-            // loop exit (which would need all 256 values in VGPRs at once)
-            float r;
-            asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(acc[nb][mb][i]));
-            x[i] = r * kLog2e;
-          }
-          float bm = x[0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) bm = fmaxf(bm, x[i]);
-          int bi = 0x7fffffff;   // lowest id reaching the block max (ids grow with i)
-#pragma unroll
-          for (int i = 15; i >= 0; --i) bi = (x[i] == bm) ? vb0 + 8 * (i >> 2) + (i & 3) : bi;
-          const float mn = fmaxf(m, bm);
-          float sb = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sb += fast_exp2(x[i] - mn);
-          sb = (mn == -INFINITY) ? 0.f : sb;            // all -inf so far: -inf - -inf
-          const float scale = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
-          sum = fmaf(sum, scale, sb);
-          idx = (bm > m) ? bi : idx;   // equal maxima keep the earlier, lower id
-          m = mn;
-        }
+      for (int nb = 0; nb < 4; ++nb) {
         __builtin_amdgcn_sched_barrier(0);
-        // combine with the lane holding the other half of the row's values
-        const float pm = shfl_xor_f(m, 32);
-        const int pi = shfl_xor_i(idx, 32);
-        const float ps = shfl_xor_f(sum, 32);
-        const float mx = fmaxf(m, pm);
-        const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mx);
-        const float w2 = pm == -INFINITY ? 0.f : fast_exp2(pm - mx);
-        sum = sum * w1 + ps * w2;
-        idx = (pm > m || (pm == m && pi < idx)) ? pi : idx;
-        fold(run[mb], mx * (1.0f / kLog2e), idx, sum);
+        const int vb0 = vbase + nb * 32 + 4 * (lane >> 5);
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          // read the accumulator from its AGPR here, not in one burst at the
+          // loop exit (which would need all of them in VGPRs at once)
+          float r;
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(acc[nb][mb][i]));
+          x[i] = r * kLog2e;
+        }
+        float bm = x[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) bm = fmaxf(bm, x[i]);
+        int bi = 0;   // offset of the lowest id reaching the block max (ids grow with i)
+#pragma unroll
+        for (int i = 15; i >= 0; --i) bi = (x[i] == bm) ? 8 * (i >> 2) + (i & 3) : bi;
+        bi += vb0;
+        const float mn = fmaxf(m, bm);
+        float sb = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sb += fast_exp2(x[i] - mn);
+        sb = (mn == -INFINITY) ? 0.f : sb;            // all -inf so far: -inf - -inf
+        const float scale = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+        sum = fmaf(sum, scale, sb);
+        idx = (bm > m) ? bi : idx;   // equal maxima keep the earlier, lower id
+        m = mn;
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // combine with the lane holding the other half of the row's values
+      const float pm = shfl_xor_f(m, 32);
+      const int pi = shfl_xor_i(idx, 32);
+      const float ps = shfl_xor_f(sum, 32);
+      const float mx = fmaxf(m, pm);
+      const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mx);
+      const float w2 = pm == -INFINITY ? 0.f : fast_exp2(pm - mx);
+      sum = sum * w1 + ps * w2;
+      idx = (pm > m || (pm == m && pi < idx)) ? pi : idx;
+      fold(run[mb], mx * (1.0f / kLog2e), idx, sum);
     }
+  };
+
+  // prologue: stages 0..slots-2 in flight, then wait for stage 0
+  constexpr int NS = WL ? NWS : NHS;
+#pragma unroll
+  for (int j = 0; j + 1 < NS; ++j) issue(WL ? Wr + j * WSLOT : Hr + j * HSLOT);
+  sync();
+  int ws = 0, hs = 0;      // ring slots of the stage being computed
+  issue(WL ? Wr + (NWS - 1) * WSLOT : Hr + (NHS - 1) * HSLOT);
+  bf16x8 fa0[4], fb0[MB], fa1[4], fb1[MB];
+  read_frags(ws, hs, 0, fa0, fb0);
+
+  for (int tile = 0; tile < ntile; ++tile) {
+    const int n0 = v_lo + tile * NT;
+    init_acc(n0);
+    for (int kt = 0; kt < nk; ++kt) {
+      step(fa0, fb0, ws, hs, 1, fa1, fb1);
+      step(fa1, fb1, ws, hs, 2, fa0, fb0);
+      step(fa0, fb0, ws, hs, 3, fa1, fb1);
+      // k-step 3: half its MFMAs, then the sync for the next stage, the load
+      // of a later stage into the slot just read, the next stage's first
+      // fragments, and the other half under them
+#pragma unroll
+      for (int mb = 0; mb < MB / 2; ++mb) mfma_rows(fa1, fb1, mb);
+      sync();
+      issue(WL ? Wr + ws * WSLOT : Hr + hs * HSLOT);
+      ws = ws == NWS - 1 ? 0 : ws + 1;
+      hs = hs == NHS - 1 ? 0 : hs + 1;
+      read_frags(ws, hs, 0, fa0, fb0);
+#pragma unroll
+      for (int mb = MB / 2; mb < MB; ++mb) mfma_rows(fa1, fb1, mb);
+      constexpr int NM2 = 4 * (MB - MB / 2), NP2 = NM2 < 4 + MB ? NM2 : 4 + MB;
+#pragma unroll
+      for (int r = 0; r < NP2; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      }
+      if (4 + MB > NP2) __builtin_amdgcn_sched_group_barrier(0x100, 4 + MB - NP2, 0);
+      if (NM2 > NP2) __builtin_amdgcn_sched_group_barrier(0x008, NM2 - NP2, 0);
+    }
+    reduce_tile(n0);
   }
 
-  // fold the waves that share rows, then one partial per row (the row
-  // partials use the first stage buffer, idle after the last barrier)
-  Part* s_part = reinterpret_cast<Part*>(B0);
-  if (WN > 1) {
-    if (lane < 32) {
+  // all loads have landed and every wave is past its last fragment read
+  wait_vm<0>();
+  wait_lgkm0();
+  barrier_only();
+
+  // fold the two waves that share rows, then one partial per row
+  typedef __attribute__((address_space(3))) float lds_f32;
+  typedef __attribute__((address_space(3))) int lds_i32;
+  lds_f32* const s_m = (lds_f32*)Hr;
+  lds_i32* const s_a = (lds_i32*)(Hr + 2 * 256);
+  lds_f32* const s_s = (lds_f32*)(Hr + 4 * 256);
+  if (wn == 1 && lane < 32) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) s_part[(wave * 4 + mb) * 32 + lane] = run[mb];
+    for (int mb = 0; mb < MB; ++mb) {
+      const int k = (wm * MB + mb) * 32 + lane;
+      s_m[k] = run[mb].m;
+      s_a[k] = run[mb].a;
+      s_s[k] = run[mb].s;
     }
-    __syncthreads();
-    if (wn == 0 && lane < 32) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        for (int o = 1; o < WN; ++o) {
-          const Part p = s_part[((wave + o) * 4 + mb) * 32 + lane];
-          fold(run[mb], p.m, p.a, p.s);
-        }
-    }
-    __syncthreads();
   }
+  __syncthreads();
   if (wn == 0 && lane < 32) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 128 + mb * 32 + lane;
-      if (m < M) {
-        const size_t o = (size_t)m * kLmGrid + blockIdx.x;
+    for (int mb = 0; mb < MB; ++mb) {
+      const int k = (wm * MB + mb) * 32 + lane;
+      fold(run[mb], s_m[k], s_a[k], s_s[k]);
+      const int m = m_base + wm * RH + mb * 32 + lane;
+      if (m < m_end) {
+        const size_t o = (size_t)m * nteam + team;
         a.pm[o] = run[mb].m;
         a.pa[o] = run[mb].a;
         a.ps[o] = run[mb].s;
       }
     }
   }
+  __syncthreads();   // the partial scratch is read before the next pass loads
+}
+
+template <int MB>
+__device__ __forceinline__ void lm_pass_any(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
+                                            int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
+  if (v_hi <= v_lo) {
+    // an empty vocabulary range still leaves a neutral partial for its rows
+    for (int m = m_base + (int)threadIdx.x; m < m_end; m += blockDim.x) {
+      const size_t o = (size_t)m * nteam + team;
+      a.pm[o] = -INFINITY;
+      a.pa[o] = 0x7fffffff;
+      a.ps[o] = 0.f;
+    }
+    return;
+  }
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 2)
+    lm_pass<MB, true>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
+  else
+    lm_pass<MB, false>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
 }
 }  // namespace
 
-// One kernel per tile shape; each exits unless the row count on the device
-// selects its shape, so the launch sequence stays fixed for graph capture.
-template <int NT, int MT>
 __global__ __launch_bounds__(256, 1) void lmhead_tile_kernel(LmArgs a) {
-  __shared__ __align__(16) uint16_t B0[MAXR * TK];
-  __shared__ __align__(16) uint16_t B1[MAXR * TK];
-  __shared__ __align__(16) uint16_t B2[MAXR * TK];
-  __shared__ __align__(16) uint16_t B3[MAXR * TK];
+  __shared__ __align__(16) uint16_t Wr_[NWS * WSLOT];
+  __shared__ __align__(16) uint16_t Hr_[NHS * HSLOT];
+  lds_u16* const Wr = (lds_u16*)Wr_;
+  lds_u16* const Hr = (lds_u16*)Hr_;
   const int M = *a.num_rows;
-  const int want = M <= 0 ? 0 : (M <= 128 ? 512 : (M <= 256 ? 256 : 128));
-  if (want != NT) return;
-  const int n_mt = (M + MT - 1) / MT;
-  for (int mt = 0; mt < n_mt; ++mt) {
-    lm_rowtile<NT, MT>(a, M, mt, B0, B1, B2, B3);
-    __syncthreads();   // row partials in B0 are read before the next row tile loads
+  if (M <= 0) return;
+  const int G = team_size(M), nteam = kLmGrid / G;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;       // 32 workgroups per XCD
+  const int member = local % G, team = xcd * (32 / G) + local / G;
+  const int nblk = (a.V + 31) / 32;
+  const int v_lo = min(a.V, (int)(((long)team * nblk) / nteam) * 32);
+  const int v_hi = min(a.V, (int)(((long)(team + 1) * nblk) / nteam) * 32);
+  const int pass_rows = RMAX * G;
+  for (int p0 = 0; p0 < M; p0 += pass_rows) {
+    const int Mp = min(pass_rows, M - p0);
+    const int R = min(RMAX, (((Mp + G - 1) / G) + 63) / 64 * 64);
+    const int m_base = p0 + member * R;
+    const int m_end = min(m_base + R, p0 + Mp);
+    if (m_base >= m_end) continue;
+    switch (R / 64) {
+      case 1: lm_pass_any<1>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      case 2: lm_pass_any<2>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      case 3: lm_pass_any<3>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      default: lm_pass_any<4>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+    }
   }
 }
 
@@ -357,19 +440,10 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(LmArgs a) {
   const int r = blockIdx.x * 4 + wave;
   const int M = *a.num_rows;
   if (r >= M) return;
-  constexpr int PER = kLmGrid / 64;
-  const size_t base = (size_t)r * kLmGrid;
-  float pm[PER], ps[PER];
-  int pa[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    pm[j] = a.pm[base + lane + 64 * j];
-    pa[j] = a.pa[base + lane + 64 * j];
-    ps[j] = a.ps[base + lane + 64 * j];
-  }
+  const int nteam = kLmGrid / team_size(M);
+  const size_t base = (size_t)r * nteam;
   Part x{-INFINITY, 0x7fffffff, 0.f};
-#pragma unroll
-  for (int j = 0; j < PER; ++j) fold(x, pm[j], pa[j], ps[j]);
+  for (int t = lane; t < nteam; t += 64) fold(x, a.pm[base + t], a.pa[base + t], a.ps[base + t]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = shfl_xor_f(x.m, off);
@@ -391,9 +465,7 @@ size_t lmhead_ws_bytes(int max_rows, int V) {
 }
 
 hipError_t lmhead_launch(const LmArgs& a, hipStream_t st) {
-  lmhead_tile_kernel<512, 128><<<kLmGrid, 256, 0, st>>>(a);
-  lmhead_tile_kernel<256, 256><<<kLmGrid, 256, 0, st>>>(a);
-  lmhead_tile_kernel<128, 512><<<kLmGrid, 256, 0, st>>>(a);
+  lmhead_tile_kernel<<<kLmGrid, 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   lmhead_merge_kernel<<<(a.max_rows + 3) / 4, 256, 0, st>>>(a);
