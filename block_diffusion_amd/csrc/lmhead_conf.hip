@@ -36,6 +36,8 @@
 // (m,a,s) + (m',a',s') = (max, id of the larger max or the lower id on equal
 // maxima, s*e^(m-max) + s'*e^(m'-max)), in a fixed order, and writes the
 // greedy token and the confidence 1/s = exp(max - logsumexp).
+#include <type_traits>
+
 #include "dbd_device.hpp"
 #include "dbd_internal.hpp"
 
@@ -143,7 +145,9 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   // Issue cursor: the next stage this wave loads (tile it_t, k-stage it_k);
   // past the last stage it keeps loading the last one (never used).
   int it_t = 0, it_k = 0;
-  auto issue = [&](lds_u16* slot) {
+  // loads [I0, I1) of this wave's share of the cursor's stage into `slot`
+  auto issue_part = [&](lds_u16* slot, auto i0c, auto i1c) {
+    constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
     const char* kb = reinterpret_cast<const char*>(WL ? a.w : a.hidden) + (size_t)it_k * (TK * 2);
     if (WL) {
       const int n0 = v_lo + min(it_t, ntile - 1) * NT;
@@ -152,15 +156,17 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       // rows past the range re-read a row of the tile's first 8
       const uint32_t back = (uint32_t)min(lr, lim - 1) * hdb;
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) {
+      for (int i = I0; i < I1; ++i) {
         const int row = 8 * (wn * NLD + i) + lr;
         const uint32_t o = row < lim ? off[i] : back + (off[i] & 0x70);
         dma16(tb, o, slot + (wn * NLD + i) * 512);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) dma16(kb, off[i], slot + (wn * NLD + i) * 512);
+      for (int i = I0; i < I1; ++i) dma16(kb, off[i], slot + (wn * NLD + i) * 512);
     }
+  };
+  auto advance = [&]() {
     if (it_t < ntile) {
       if (++it_k == nk) {
         it_k = 0;
@@ -168,6 +174,10 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
         else it_k = nk - 1, it_t = ntile;              // hold at the last stage
       }
     }
+  };
+  auto issue = [&](lds_u16* slot) {
+    issue_part(slot, std::integral_constant<int, 0>{}, std::integral_constant<int, NLD>{});
+    advance();
   };
   // the stage about to be read has landed for this wave's stream, and this
   // wave's fragment reads are done; then the whole workgroup syncs
@@ -203,8 +213,10 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
     for (int nb = 0; nb < 4; ++nb)
       acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[nb], bfr[mb], acc[nb][mb], 0, 0, 0);
   };
-  // one k-step's MFMAs with the next step's fragment reads interleaved
+  // one k-step's MFMAs with the next step's fragment reads interleaved,
+  // fenced so that nothing else is scheduled into it
   auto step = [&](const bf16x8* af, const bf16x8* bfr, int ws, int hs, int jn, bf16x8* an, bf16x8* bn) {
+    __builtin_amdgcn_sched_barrier(0);
     read_frags(ws, hs, jn, an, bn);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) mfma_rows(af, bfr, mb);
@@ -216,6 +228,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
     }
     if (4 * MB > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, 4 * MB - NPAIR, 0);
     if (4 + MB > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, 4 + MB - NPAIR, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   Part run[MB];
@@ -307,13 +320,21 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
     }
   };
 
-  // prologue: stages 0..slots-2 in flight, then wait for stage 0
-  constexpr int NS = WL ? NWS : NHS;
-#pragma unroll
-  for (int j = 0; j + 1 < NS; ++j) issue(WL ? Wr + j * WSLOT : Hr + j * HSLOT);
+  // Ring schedule.  W waves: stages 0 and 1 up front; during stage s they
+  // load stage s+2 into the slot released by the sync before stage s, a
+  // quarter at the start of each k-step.  Hidden waves: stage 0 up front,
+  // then right after the sync that ends stage s, stage s+2 into the slot of
+  // stage s (a whole stage to land; the hidden rows are L2 hits).
+  using I = std::integral_constant<int, 0>;
+  if (WL) {
+    issue(Wr);
+    issue(Wr + WSLOT);
+  } else {
+    issue(Hr);
+  }
   sync();
+  if (!WL) issue(Hr + HSLOT);
   int ws = 0, hs = 0;      // ring slots of the stage being computed
-  issue(WL ? Wr + (NWS - 1) * WSLOT : Hr + (NHS - 1) * HSLOT);
   bf16x8 fa0[4], fb0[MB], fa1[4], fb1[MB];
   read_frags(ws, hs, 0, fa0, fb0);
 
@@ -321,18 +342,29 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
     const int n0 = v_lo + tile * NT;
     init_acc(n0);
     for (int kt = 0; kt < nk; ++kt) {
+      lds_u16* const wt = Wr + (ws == 0 ? NWS - 1 : ws - 1) * WSLOT;
+      constexpr int Q = WPW / 4;
+      if (WL) issue_part(wt, I{}, std::integral_constant<int, Q>{});
       step(fa0, fb0, ws, hs, 1, fa1, fb1);
+      if (WL) issue_part(wt, std::integral_constant<int, Q>{}, std::integral_constant<int, 2 * Q>{});
       step(fa1, fb1, ws, hs, 2, fa0, fb0);
+      if (WL) issue_part(wt, std::integral_constant<int, 2 * Q>{}, std::integral_constant<int, 3 * Q>{});
       step(fa0, fb0, ws, hs, 3, fa1, fb1);
-      // k-step 3: half its MFMAs, then the sync for the next stage, the load
-      // of a later stage into the slot just read, the next stage's first
-      // fragments, and the other half under them
+      if (WL) {
+        issue_part(wt, std::integral_constant<int, 3 * Q>{}, std::integral_constant<int, 4 * Q>{});
+        advance();
+      }
+      // k-step 3: half its MFMAs, the sync for the next stage, the hidden
+      // loads, and the other half under the next stage's first fragments
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mb = 0; mb < MB / 2; ++mb) mfma_rows(fa1, fb1, mb);
+      __builtin_amdgcn_sched_barrier(0);
       sync();
-      issue(WL ? Wr + ws * WSLOT : Hr + hs * HSLOT);
+      if (!WL) issue(Hr + hs * HSLOT);
       ws = ws == NWS - 1 ? 0 : ws + 1;
       hs = hs == NHS - 1 ? 0 : hs + 1;
+      __builtin_amdgcn_sched_barrier(0);
       read_frags(ws, hs, 0, fa0, fb0);
 #pragma unroll
       for (int mb = MB / 2; mb < MB; ++mb) mfma_rows(fa1, fb1, mb);
@@ -344,6 +376,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       }
       if (4 + MB > NP2) __builtin_amdgcn_sched_group_barrier(0x100, 4 + MB - NP2, 0);
       if (NM2 > NP2) __builtin_amdgcn_sched_group_barrier(0x008, NM2 - NP2, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     reduce_tile(n0);
   }
