@@ -9,7 +9,7 @@
 // 16 rows (RT tiles per row group).
 //
 // Work decomposition.  A segment is (sequence s, kv head g, row group rg); it
-// owns ceil(L_s/16) prefix tiles of 16 keys plus ceil(B/16) tiles of the
+// owns ceil(L_s/kKT) prefix tiles of kKT keys plus ceil(B/kKT) tiles of the
 // block's own keys.  All segments, in order, form one global tile stream,
 // which is cut into equal contiguous ranges, one per single-wave workgroup:
 // every wave streams the same number of tiles whatever the prefix lengths.
@@ -19,18 +19,21 @@
 // attn_plan_kernel first turns prefix lengths into tile prefix sums.
 //
 // Per wave, tiles go straight from global memory into a ring of kRing LDS
-// slots (global_load_lds_dwordx4: 16 keys of K and of V, plus the segment's
-// query rows when the tile starts one), kRing-1 tiles in flight while one is
-// computed.  Rows are stored with their 16-byte chunks XOR-permuted by row so
-// fragment reads hit distinct banks.  Per tile:
+// slots (global_load_lds_dwordx4: kKT keys of K and of V in runs of 16 that
+// never cross a page, plus the segment's query rows when the tile starts
+// one), kRing-1 tiles in flight while one is computed.  Rows are stored with
+// their 16-byte chunks XOR-permuted by row so fragment reads hit distinct
+// banks.  Per run of 16 keys:
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (lane: query row, 4 keys);
 //   * online softmax in fp32, base 2 (scores pre-scaled by scale*log2 e),
 //     probabilities rounded to bf16 for the MFMA, the row sum taken over the
 //     rounded values;
 //   * the score accumulator layout is exactly the B operand of
-//     O^T += V^T P^T (v_mfma_f32_16x16x16bf16_1k), V^T read from the ring.
+//     O^T += V^T P^T (v_mfma_f32_16x16x16bf16_1k); the V^T operand comes
+//     straight from the row-major V rows with the LDS transpose read
+//     ds_read_b64_tr_b16.
 // Keys past the end of a prefix or block are masked to -inf; their loads
-// re-read the last valid key, so nothing past a page or buffer is touched.
+// re-read a valid key, so nothing past a page or buffer is touched.
 #include <algorithm>
 
 #include "dbd_device.hpp"
@@ -44,7 +47,18 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #define INL __attribute__((always_inline))
 
-constexpr int kRing = 3;       // ring slots per wave
+#ifndef ATTN_RING
+#define ATTN_RING 2
+#endif
+#ifndef ATTN_WAVES
+#define ATTN_WAVES 4
+#endif
+#ifndef ATTN_KT
+#define ATTN_KT 32
+#endif
+constexpr int kKT = ATTN_KT;   // keys per tile (a multiple of 16)
+constexpr int kRing = ATTN_RING;       // ring slots per wave
+constexpr int kMaxWavesPerCU = ATTN_WAVES;
 constexpr int kCUs = 256;      // MI355X compute units
 constexpr int kLdsPerCU = 160 * 1024;
 
@@ -64,7 +78,7 @@ struct Geo {
   static constexpr int ROWS = 16 * RT;
   static constexpr int KS = D / 32;
   static constexpr int DT = D / 16;
-  static constexpr int KV = 16 * D;                 // elements of one K (or V) tile
+  static constexpr int KV = kKT * D;                // elements of one K (or V) tile
   static constexpr int SLOT = 2 * KV + ROWS * D;    // K, V, Q
   static constexpr int LPR = D / 8;                 // lanes per row in a 1 KB load
   static constexpr int RPI = 64 / LPR;              // rows per 1 KB load
@@ -125,12 +139,12 @@ struct Dec {      // a position in the tile stream
 __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
   __shared__ int s_wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = a.S, nB = (a.B + 15) / 16;
+  const int S = a.S, nB = (a.B + kKT - 1) / kKT;
   const int per = (S + 1023) / 1024;
   const int b0 = tid * per;
   int local = 0;
   for (int j = 0; j < per; ++j)
-    if (b0 + j < S) local += (a.prefix_len[b0 + j] + 15) / 16 + nB;
+    if (b0 + j < S) local += (a.prefix_len[b0 + j] + kKT - 1) / kKT + nB;
   int incl = local;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -145,7 +159,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
   for (int j = 0; j < per; ++j)
     if (b0 + j < S) {
       a.plan[b0 + j] = run;
-      run += (a.prefix_len[b0 + j] + 15) / 16 + nB;
+      run += (a.prefix_len[b0 + j] + kKT - 1) / kKT + nB;
     }
   if (tid == 1023) {
     int tot = 0;
@@ -162,7 +176,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   lds_u16* const ring = (lds_u16*)ring_;
 
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
-  const int S = a.S, NHG = a.Hkv * a.n_rg, nB = (a.B + 15) / 16;
+  const int S = a.S, NHG = a.Hkv * a.n_rg, nB = (a.B + kKT - 1) / kKT;
   const int R = a.G * a.B;
   const long T = (long)NHG * ldc(a.plan, S);
   const long NWe = min((long)a.grid, max(1L, T / 64));
@@ -185,7 +199,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   }
   auto load_seq = [&](Dec& d) INL {
     d.L = ldc(a.prefix_len, d.s);
-    d.nP = (d.L + 15) / 16;
+    d.nP = (d.L + kKT - 1) / kKT;
     d.tiles = d.nP + nB;
   };
   Dec dc;
@@ -211,27 +225,35 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   auto dma_tile = [&](lds_u16* slot, const Dec& d, bool with_q) INL {
     wait_lgkm0();   // the slot's previous tile has been read out
     const int g = d.hg / a.n_rg, rg = d.hg % a.n_rg;
-    const uint16_t* sk;
-    const uint16_t* sv;
-    int stride, nvalid;
-    if (d.j < d.nP) {
-      const int key0 = 16 * d.j;
-      const int page = ldc(a.page_table, (size_t)d.s * a.max_pages + key0 / a.P);
-      const size_t base = (((size_t)page * a.Hkv + g) * a.P + key0 % a.P) * D;
-      sk = a.k_cache + base;
-      sv = a.v_cache + base;
-      stride = D;
-      nvalid = min(16, d.L - key0);
-    } else {
-      const int key0 = 16 * (d.j - d.nP);
-      const size_t base = ((size_t)(d.s * a.B + key0) * a.Hkv + g) * D;
-      sk = a.k_blk + base;
-      sv = a.v_blk + base;
-      stride = a.Hkv * D;
-      nvalid = min(16, a.B - key0);
+    // kKT/16 runs of 16 keys; a run never crosses a page (the page size is a
+    // multiple of 16).  A run wholly past the end re-reads the tile's first
+    // key (its scores are masked).
+#pragma unroll
+    for (int hh = 0; hh < kKT / 16; ++hh) {
+      const uint16_t* sk;
+      const uint16_t* sv;
+      int stride, nvalid;
+      if (d.j < d.nP) {
+        int key0 = kKT * d.j + 16 * hh;
+        nvalid = min(16, d.L - key0);
+        if (nvalid <= 0) key0 = kKT * d.j, nvalid = 1;
+        const int page = ldc(a.page_table, (size_t)d.s * a.max_pages + key0 / a.P);
+        const size_t base = (((size_t)page * a.Hkv + g) * a.P + key0 % a.P) * D;
+        sk = a.k_cache + base;
+        sv = a.v_cache + base;
+        stride = D;
+      } else {
+        int key0 = kKT * (d.j - d.nP) + 16 * hh;
+        nvalid = min(16, a.B - key0);
+        if (nvalid <= 0) key0 = kKT * (d.j - d.nP), nvalid = 1;
+        const size_t base = ((size_t)(d.s * a.B + key0) * a.Hkv + g) * D;
+        sk = a.k_blk + base;
+        sv = a.v_blk + base;
+        stride = a.Hkv * D;
+      }
+      dma_rows16<D, RT>(slot + hh * 16 * D, sk, stride, nvalid, lane);
+      dma_rows16<D, RT>(slot + KV + hh * 16 * D, sv, stride, nvalid, lane);
     }
-    dma_rows16<D, RT>(slot, sk, stride, nvalid, lane);
-    dma_rows16<D, RT>(slot + KV, sv, stride, nvalid, lane);
     if (with_q) {
       // query row r = rg*ROWS + i -> (pos, gi) = (r / G, r % G); rows past
       // G*B re-read the last real row (their outputs are never written)
@@ -321,59 +343,68 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
-    const int nvalid = dc.j < dc.nP ? min(16, dc.L - 16 * dc.j) : min(16, a.B - 16 * (dc.j - dc.nP));
-
-    bf16x8 kf[KS];
+    const int nvalid_t = dc.j < dc.nP ? dc.L - kKT * dc.j : a.B - kKT * (dc.j - dc.nP);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(slot + eoff<D>(lr, lg + 4 * ks)));
-    f32x4 sc[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      sc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < kKT / 16; ++hh) {
+      const int nvalid = nvalid_t - 16 * hh;   // valid keys of this run (may be <= 0)
+      const lds_u16* kt16 = slot + hh * 16 * D;
+      bf16x8 kf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], sc[rt], 0, 0, 0);
-    }
-    i16x4 pb[RT];
+        kf[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kt16 + eoff<D>(lr, lg + 4 * ks)));
+      f32x4 sc[RT];
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float x[4];
-      float tmax = -INFINITY;
+      for (int rt = 0; rt < RT; ++rt) {
+        sc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = (4 * lg + i < nvalid) ? sc[rt][i] * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[i]);
+        for (int ks = 0; ks < KS; ++ks)
+          sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], sc[rt], 0, 0, 0);
       }
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-      const float m_new = fmaxf(m_run[rt], tmax);
-      const float alpha = fast_exp2(m_run[rt] - m_new);
-      m_run[rt] = m_new;
-      float psum = 0.f;
-      short pbits[4];
+      i16x4 pb[RT];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t b = f2bf(fast_exp2(x[i] - m_new));
-        pbits[i] = (short)b;
-        psum += bf2f(b);
+      for (int rt = 0; rt < RT; ++rt) {
+        float x[4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = (4 * lg + i < nvalid) ? sc[rt][i] * a.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, x[i]);
+        }
+        tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        // a run with no valid key leaves the state as it is (m_run is finite
+        // once the segment's first key has been seen)
+        const float m_new = fmaxf(m_run[rt], tmax);
+        const float alpha = fast_exp2(m_run[rt] - m_new);
+        m_run[rt] = m_new;
+        float psum = 0.f;
+        short pbits[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t b = f2bf(fast_exp2(x[i] - m_new));
+          pbits[i] = (short)b;
+          psum += bf2f(b);
+        }
+        pb[rt] = i16x4{pbits[0], pbits[1], pbits[2], pbits[3]};
+        l_run[rt] = l_run[rt] * alpha + psum;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
       }
-      pb[rt] = i16x4{pbits[0], pbits[1], pbits[2], pbits[3]};
-      l_run[rt] = l_run[rt] * alpha + psum;
+      // O^T[d][row] += V^T[d][key] P^T[key][row]: lane 16*lg + lr needs
+      // V[keys 4*lg .. 4*lg+3][d = 16*dt + lr].  ds_read_b64_tr_b16 hands
+      // lane i of each 16-lane group element i%4 of the 8-byte words read by
+      // lanes i/4 + 4k (k = 0..3) of its group, so lane w of group lg reads
+      // V[4*lg + w/4][16*dt + 4*(w%4) .. +3].
+      const lds_u16* vt = slot + KV + hh * 16 * D;
+      const int vrow = 4 * lg + (lr >> 2), vsub = 4 * (lr & 1), vch = (lr & 3) >> 1;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
-    }
-    // O^T[d][row] += V^T[d][key] P^T[key][row]; lane reads d = 16*dt + lr of
-    // keys 4*lg .. 4*lg+3
-    const lds_u16* vt = slot + KV;
+      for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vt + eoff<D>(vrow, 2 * dt + vch) + vsub));
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int c = 2 * dt + (lr >> 3), e = lr & 7;
-      const i16x4 va = i16x4{(short)vt[eoff<D>(4 * lg + 0, c) + e], (short)vt[eoff<D>(4 * lg + 1, c) + e],
-                             (short)vt[eoff<D>(4 * lg + 2, c) + e], (short)vt[eoff<D>(4 * lg + 3, c) + e]};
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
+        for (int rt = 0; rt < RT; ++rt)
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
+      }
     }
   };
 
@@ -425,13 +456,13 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
 template <int D, int RT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int ROWS = 16 * RT;
-  const int NHG = a.Hkv * a.n_rg, nB = (a.B + 15) / 16;
+  const int NHG = a.Hkv * a.n_rg, nB = (a.B + kKT - 1) / kKT;
   const int seg = blockIdx.x;
   const int s = seg / NHG, hg = seg % NHG;
   const int g = hg / a.n_rg, rg = hg % a.n_rg;
   const long T = (long)NHG * a.plan[a.S];
   const long NW = min((long)a.grid, max(1L, T / 64));
-  const int tiles = (a.prefix_len[s] + 15) / 16 + nB;
+  const int tiles = (a.prefix_len[s] + kKT - 1) / kKT + nB;
   const long ts = (long)NHG * a.plan[s] + (long)hg * tiles;
   const long w0 = ((ts + 1) * NW - 1) / T;
   const long w1 = ((ts + tiles) * NW - 1) / T;
@@ -477,10 +508,10 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
   const int R = G * B;
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   p.n_rg = (R + 16 * p.RT - 1) / (16 * p.RT);
-  const long max_seg_tiles = ((long)max_pages * page_size + 15) / 16 + (B + 15) / 16;
+  const long max_seg_tiles = ((long)max_pages * page_size + kKT - 1) / kKT + (B + kKT - 1) / kKT;
   p.maxp = (int)((max_seg_tiles + 63) / 64 + 1);
-  const int slot_bytes = (2 * 16 * D + 16 * p.RT * D) * 2;
-  const int waves_per_cu = std::max(1, std::min(8, kLdsPerCU / (kRing * slot_bytes)));
+  const int slot_bytes = (2 * kKT * D + 16 * p.RT * D) * 2;
+  const int waves_per_cu = std::max(1, std::min(kMaxWavesPerCU, kLdsPerCU / (kRing * slot_bytes)));
   p.grid = kCUs * waves_per_cu;
   p.plan_bytes = ((size_t)(S + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   const size_t slots = (size_t)S * Hkv * p.n_rg * p.maxp * 16 * p.RT;
