@@ -17,10 +17,12 @@ here is "parity unpinned".
 """
 from .bf16 import widen
 from .attention import attention, attention_group
-from .lmhead import lmhead_rows, lmhead_logits
-from .remask import remask, compact_rows, DENOISING, SAVING
+from .lmhead import lmhead_rows, lmhead_logits, lmhead_entropy
+from .remask import (remask, remask_rule, compact_rows, DENOISING, SAVING,
+                     RULE_DYNAMIC, RULE_STATIC, RULE_SEQUENTIAL, RULE_ENTROPY)
 from .round import denoise_round
 
 __all__ = ["widen", "attention", "attention_group", "lmhead_rows",
-           "lmhead_logits", "remask", "compact_rows", "denoise_round",
-           "DENOISING", "SAVING"]
+           "lmhead_logits", "lmhead_entropy", "remask", "remask_rule",
+           "compact_rows", "denoise_round", "DENOISING", "SAVING",
+           "RULE_DYNAMIC", "RULE_STATIC", "RULE_SEQUENTIAL", "RULE_ENTROPY"]

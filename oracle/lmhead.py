@@ -17,6 +17,11 @@ Readings:
 
 Also returns the runner-up probability p2, which the tests use only to
 decide which rows are near-ties.
+
+lmhead_entropy gives each row's entropy -sum_v p_v ln p_v over the same
+distribution (mask token excluded); the entropy-bounded commit rule
+(developer notes, "Remasking Strategies": unmask by cumulative entropy
+budget) orders positions by it.
 """
 import numpy as np
 
@@ -63,3 +68,22 @@ def lmhead_rows(h_rows, w_vocab_bits, mask_id, chunk=256):
         a, x1, x2 = _reduce(logits)
         args[i:i + chunk], p1[i:i + chunk], p2[i:i + chunk] = a, x1, x2
     return args, p1, p2
+
+
+def lmhead_entropy(h_rows, w_vocab_bits, mask_id, chunk=256):
+    """Entropy in nats of each row's softmax over the vocabulary without the
+    mask token: H = -sum_v p_v ln p_v, written as lse - sum_v p_v l_v.
+
+    h_rows: [M][Hd] bf16 bits; w_vocab_bits: [V][Hd] bf16 bits.
+    Returns H [M] float64."""
+    M = h_rows.shape[0]
+    H = np.empty(M)
+    for i in range(0, M, chunk):
+        logits = lmhead_logits(h_rows[i:i + chunk], w_vocab_bits, mask_id)
+        m = logits.max(axis=1, keepdims=True)
+        z = logits - m                            # -inf at the mask column
+        e = np.exp(z)
+        ssum = e.sum(axis=1)
+        zfin = np.where(np.isfinite(z), z, 0.0)   # the mask column has p = 0
+        H[i:i + chunk] = np.log(ssum) - (e * zfin).sum(axis=1) / ssum
+    return H

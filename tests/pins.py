@@ -330,7 +330,63 @@ def check_lm_golden(impl):
         assert np.max(np.abs(p2 - np.array(c["expect_p2"]))) < 1e-15, c["name"]
 
 
-LM_CHECKS = [check_lm_golden, check_lm_bruteforce, check_lm_zero_hidden, check_lm_one_hot,
+def lm_entropy_bruteforce(h_bits, w_bits, mask_id):
+    H = wid(h_bits); W = wid(w_bits)
+    out = []
+    for r in range(H.shape[0]):
+        logit = [math.fsum(float(a) * float(b) for a, b in zip(H[r], W[v]))
+                 for v in range(W.shape[0]) if v != mask_id]
+        m = max(logit)
+        e = [math.exp(x - m) for x in logit]
+        den = math.fsum(e)
+        out.append(-math.fsum((t / den) * math.log(t / den) for t in e if t > 0))
+    return out
+
+
+def check_lm_entropy_bruteforce(impl):
+    g = np.random.default_rng(21)
+    for V, Hd, mask in [(12, 4, 11), (17, 8, 0), (9, 16, 4)]:
+        h = bf(g.standard_normal((5, Hd)) * 2)
+        w = bf(g.standard_normal((V, Hd)))
+        H = impl.lmhead_entropy(h, w, mask)
+        for r, e in enumerate(lm_entropy_bruteforce(h, w, mask)):
+            assert abs(H[r] - e) < 1e-12
+
+
+def check_lm_entropy_closed_forms(impl):
+    """h = 0: uniform over the V-1 candidates, H = ln(V-1).  One-hot W with
+    logit c at t: p_t = e^c/(e^c+V-2), the rest share 1-p_t equally, so
+    H = -p_t ln p_t - (1-p_t) ln((1-p_t)/(V-2))."""
+    for V, mask in [(10, 9), (33, 5)]:
+        w = bf(np.random.default_rng(V).standard_normal((V, 8)))
+        H = impl.lmhead_entropy(np.zeros((2, 8), dtype=np.uint16), w, mask)
+        assert np.allclose(H, math.log(V - 1), rtol=0, atol=1e-13)
+    V, Hd, mask = 20, 6, 19
+    for t, k, c in [(3, 2, 2.5), (0, 5, 7.0)]:
+        w = np.zeros((V, Hd), dtype=np.float32)
+        w[t, k] = c
+        h = np.zeros((1, Hd), dtype=np.float32)
+        h[0, k] = 1.0
+        pt = math.exp(c) / (math.exp(c) + V - 2)
+        want = -pt * math.log(pt) - (1 - pt) * math.log((1 - pt) / (V - 2))
+        assert abs(impl.lmhead_entropy(bf(h), bf(w), mask)[0] - want) < 1e-13
+
+
+def check_lm_entropy_scipy(impl):
+    from scipy.special import softmax
+    from scipy.stats import entropy
+    g = np.random.default_rng(22)
+    V, Hd, mask = 300, 32, 123
+    h = bf(g.standard_normal((8, Hd)) * 2)
+    w = bf(g.standard_normal((V, Hd)) / np.sqrt(Hd))
+    logit = wid(h) @ wid(w).T
+    keep = np.array([v for v in range(V) if v != mask])
+    p = softmax(logit[:, keep], axis=1)
+    assert np.max(np.abs(impl.lmhead_entropy(h, w, mask) - entropy(p, axis=1))) < 1e-12
+
+
+LM_CHECKS = [check_lm_entropy_bruteforce, check_lm_entropy_closed_forms, check_lm_entropy_scipy,
+             check_lm_golden, check_lm_bruteforce, check_lm_zero_hidden, check_lm_one_hot,
              check_lm_vocab_permutation, check_lm_mask_never_chosen,
              check_lm_ties_lowest, check_lm_scipy]
 
@@ -477,3 +533,135 @@ def check_compact_rows(impl):
 REMASK_CHECKS = [check_remask_bruteforce, check_remask_invariants,
                  check_remask_special_thresholds, check_remask_golden,
                  check_compact_rows]
+
+
+# -------------------------------------------------------------- commit rules
+
+def rule_bruteforce(toks, state, conf, ent, argm, mask_id, rule, k, eb):
+    """Enumerate every subset C of the masked set and keep the ones the
+    rule's characterisation admits:
+      static:     |C| = min(k,|M|), and no position outside C beats one in C
+                  (higher confidence, or equal and lower position);
+      sequential: |C| = min(k,|M|), and no position outside C lies left of
+                  one in C;
+      entropy:    C is a leading run of M sorted by (entropy, position), its
+                  running sum (float32, in that order) is within eb unless
+                  |C| = 1, and adding the next position would exceed eb.
+    Exactly one subset must qualify."""
+    S, B = toks.shape
+    conf = np.asarray(conf).reshape(S, B)
+    ent = np.asarray(ent, dtype=np.float32).reshape(S, B)
+    argm = np.asarray(argm).reshape(S, B)
+    nt = toks.copy(); ns = state.copy()
+    for s in range(S):
+        if state[s] != DEN:
+            continue
+        M = [i for i in range(B) if toks[s, i] == mask_id]
+        kk = min(max(k, 1), len(M))
+        order = sorted(M, key=lambda i: (ent[s, i], i))
+        sols = []
+        for r in range(1, len(M) + 1):
+            for C in itertools.combinations(M, r):
+                out = [i for i in M if i not in C]
+                if rule == 1:
+                    ok = r == kk and not any(
+                        conf[s, o] > conf[s, c] or (conf[s, o] == conf[s, c] and o < c)
+                        for o in out for c in C)
+                elif rule == 2:
+                    ok = r == kk and not any(o < c for o in out for c in C)
+                else:
+                    ok = sorted(C, key=lambda i: (ent[s, i], i)) == order[:r]
+                    run = np.float32(0)
+                    for i in order[:r]:
+                        run = np.float32(run + ent[s, i])
+                    ok = ok and (r == 1 or run <= np.float32(eb))
+                    if ok and r < len(M):
+                        ok = np.float32(run + ent[s, order[r]]) > np.float32(eb)
+                if ok:
+                    sols.append(C)
+        assert len(sols) == (1 if M else 0), (rule, sols)
+        for C in sols:
+            for i in C:
+                nt[s, i] = argm[s, i]
+        if not np.any(nt[s] == mask_id):
+            ns[s] = SAV
+    return nt, ns
+
+
+def _rule_case(g, S, B, mask_id):
+    toks, state, conf, argm = random_remask_case(g, S, B, mask_id, 0.5)
+    ent = g.choice(np.array([0.05, 0.3, 0.3, 1.2, 2.5, 0.7], dtype=np.float32), size=S * B)
+    return toks, state, conf, ent, argm
+
+
+def check_rule_bruteforce(impl):
+    g = np.random.default_rng(23)
+    for rule in (1, 2, 3):
+        for B in (1, 2, 3, 4, 5, 6):
+            for _ in range(25):
+                toks, state, conf, ent, argm = _rule_case(g, 3, B, 99)
+                k = int(g.integers(1, 4))
+                eb = float(g.choice([0.0, 0.35, 1.0, 3.0, 100.0]))
+                et, es = rule_bruteforce(toks, state, conf, ent, argm, 99, rule, k, eb)
+                nt, ns, _ = impl.remask_rule(toks, state, conf, argm, 99, rule,
+                                             tokens_per_step=k, eb=eb, entropy=ent)
+                assert np.array_equal(nt, et) and np.array_equal(ns, es), (rule, B)
+
+
+def check_rule_special_cases(impl):
+    """static with k = 1 is the dynamic rule with tau > 1; sequential with
+    k = 1 is the dynamic rule with tau > 1 and the leftmost fallback; an
+    unbounded entropy budget commits every masked position, a negative one
+    exactly the lowest-entropy position."""
+    g = np.random.default_rng(24)
+    for _ in range(30):
+        toks, state, conf, ent, argm = _rule_case(g, 5, 6, 77)
+        a = impl.remask_rule(toks, state, conf, argm, 77, 1, tokens_per_step=1)
+        b = impl.remask(toks, state, conf, argm, 77, 1.5)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+        a = impl.remask_rule(toks, state, conf, argm, 77, 2, tokens_per_step=1)
+        b = impl.remask(toks, state, conf, argm, 77, 1.5, 1)
+        assert all(np.array_equal(x, y) for x, y in zip(a, b))
+        nt, ns, com = impl.remask_rule(toks, state, conf, argm, 77, 3, eb=1e30, entropy=ent)
+        den = state == DEN
+        assert np.array_equal(com[den], toks[den] == 77)
+        nt, ns, com = impl.remask_rule(toks, state, conf, argm, 77, 3, eb=-1.0, entropy=ent)
+        e2 = ent.reshape(5, 6)
+        for s in np.where(den)[0]:
+            M = np.where(toks[s] == 77)[0]
+            if M.size:
+                j = min(M, key=lambda i: (e2[s, i], i))
+                assert com[s].sum() == 1 and com[s, j]
+
+
+def check_rule_invariants(impl):
+    """Whole blocks under each rule: committed tokens never change, at least
+    one commit per round while a mask is left, SAVING iff no mask left,
+    static / sequential commit exactly min(k, |M|)."""
+    g = np.random.default_rng(25)
+    mask = 50
+    for rule in (1, 2, 3):
+        for B in (1, 4, 16, 64):
+            S = 4
+            toks = np.where(g.random((S, B)) < 0.8, mask, g.integers(0, mask, (S, B))).astype(np.int64)
+            state = np.full(S, DEN, dtype=np.uint8)
+            while np.any(state == DEN):
+                conf = g.random(S * B)
+                ent = (g.random(S * B) * 3).astype(np.float32)
+                k = int(g.integers(1, 5))
+                nt, ns, com = impl.remask_rule(toks, state, conf, g.integers(0, mask, S * B), mask,
+                                               rule, tokens_per_step=k, eb=2.0, entropy=ent)
+                assert np.array_equal(nt[toks != mask], toks[toks != mask])
+                for s in range(S):
+                    if state[s] != DEN:
+                        continue
+                    before = (toks[s] == mask).sum()
+                    if before:
+                        assert com[s].sum() >= 1
+                        if rule in (1, 2):
+                            assert com[s].sum() == min(k, before)
+                    assert (ns[s] == SAV) == ((nt[s] == mask).sum() == 0)
+                toks, state = nt, ns
+
+
+RULE_CHECKS = [check_rule_bruteforce, check_rule_special_cases, check_rule_invariants]

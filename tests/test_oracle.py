@@ -3,7 +3,7 @@ special cases, invariants, hand-worked fixtures)."""
 import pytest
 
 import oracle
-from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS
+from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS
 
 
 @pytest.mark.parametrize("check", ATTN_CHECKS, ids=lambda f: f.__name__)
@@ -18,6 +18,11 @@ def test_lmhead_pins(check):
 
 @pytest.mark.parametrize("check", REMASK_CHECKS, ids=lambda f: f.__name__)
 def test_remask_pins(check):
+    check(oracle)
+
+
+@pytest.mark.parametrize("check", RULE_CHECKS, ids=lambda f: f.__name__)
+def test_rule_pins(check):
     check(oracle)
 
 

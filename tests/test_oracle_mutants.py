@@ -8,7 +8,7 @@ import types
 
 import pytest
 
-from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS
+from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS
 
 ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 
@@ -36,6 +36,21 @@ MUTANTS = [
     ("remask.py", "            state[s] = SAVING", "            pass", "remask"),
     ("remask.py", "for s in range(S) if seq_state[s] == DENOISING\n            for i in range(B)",
      "for i in range(B) for s in range(S) if seq_state[s] == DENOISING", "remask"),
+    ("lmhead.py", "H[i:i + chunk] = np.log(ssum) - (e * zfin).sum(axis=1) / ssum",
+     "H[i:i + chunk] = np.log(ssum) + (e * zfin).sum(axis=1) / ssum", "lm"),
+    ("lmhead.py", "H[i:i + chunk] = np.log(ssum) - (e * zfin).sum(axis=1) / ssum",
+     "H[i:i + chunk] = np.log2(ssum) - (e * zfin).sum(axis=1) / ssum", "lm"),
+    ("lmhead.py", "zfin = np.where(np.isfinite(z), z, 0.0)   # the mask column has p = 0",
+     "zfin = np.where(np.isfinite(z), z, 0.0); ssum = ssum + np.exp(-1.0)", "lm"),
+    ("remask.py", "chosen = masked[:k]", "chosen = masked[-k:]", "rule"),
+    ("remask.py", "k = min(max(int(tokens_per_step), 1), len(masked))",
+     "k = max(min(max(int(tokens_per_step), 1), len(masked)) - 1, 1)", "rule"),
+    ("remask.py", "                        if conf[s, i] > conf[s, best]:\n                            best = i\n                    chosen.append(best)",
+     "                        if conf[s, i] < conf[s, best]:\n                            best = i\n                    chosen.append(best)", "rule"),
+    ("remask.py", "if chosen and nxt > budget:", "if nxt > budget:", "rule"),
+    ("remask.py", "if chosen and nxt > budget:", "if chosen and nxt >= budget:", "rule"),
+    ("remask.py", "order = sorted(masked, key=lambda i: (ent[s, i], i))",
+     "order = sorted(masked, key=lambda i: (ent[s, i], -i))", "rule"),
 ]
 
 
@@ -63,7 +78,7 @@ def load_mutant(fname, old, new):
 def test_mutant_is_caught(mut):
     fname, old, new, fam = mut
     mod = load_mutant(fname, old, new)
-    checks = {"attn": ATTN_CHECKS, "lm": LM_CHECKS, "remask": REMASK_CHECKS}[fam]
+    checks = {"attn": ATTN_CHECKS, "lm": LM_CHECKS, "remask": REMASK_CHECKS, "rule": RULE_CHECKS}[fam]
     caught = []
     for chk in checks:
         try:
