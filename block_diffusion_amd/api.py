@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(HERE, "libdbd.so")
 DBD_OK, DBD_ERR_INVALID_ARG, DBD_ERR_UNSUPPORTED, DBD_ERR_WORKSPACE, DBD_ERR_HIP = range(5)
 DBD_DENOISING, DBD_SAVING = 2, 3
 DBD_FALLBACK_LEFTMOST, DBD_COMPACT_ONLY = 1, 2
+(DBD_RULE_LOW_CONF_DYNAMIC, DBD_RULE_LOW_CONF_STATIC, DBD_RULE_SEQUENTIAL,
+ DBD_RULE_ENTROPY_BOUNDED) = 0, 1, 2, 3
 
 _vp, _i32p, _u8p, _fp = C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p
 
@@ -32,7 +34,9 @@ class dbd_round_args(C.Structure):
         ("page_table", _vp), ("prefix_len", _vp), ("attn_out", _vp),
         ("hidden", _vp), ("w_vocab", _vp), ("row_index", _vp), ("num_rows", _vp),
         ("argmax_tok", _vp), ("conf", _vp), ("block_tokens", _vp), ("seq_state", _vp),
-        ("num_committed", _vp), ("workspace", _vp), ("workspace_bytes", C.c_size_t)]
+        ("num_committed", _vp), ("workspace", _vp), ("workspace_bytes", C.c_size_t),
+        ("rule", C.c_int), ("tokens_per_step", C.c_int), ("eb_threshold", C.c_float),
+        ("entropy", _vp)]
 
 
 class DbdError(RuntimeError):
@@ -65,6 +69,10 @@ def lib() -> C.CDLL:
     L.dbd_lmhead_workspace_size.restype = sz
     L.dbd_remask_commit.argtypes = [i, i, i, f, u32] + [_vp] * 7 + [_vp]
     L.dbd_remask_commit.restype = i
+    L.dbd_lmhead_conf_entropy.argtypes = [i] * 4 + [_vp] * 7 + [_vp, sz, _vp]
+    L.dbd_lmhead_conf_entropy.restype = i
+    L.dbd_remask_commit_rule.argtypes = [i, i, i, i, f, i, f, u32] + [_vp] * 8 + [_vp]
+    L.dbd_remask_commit_rule.restype = i
     L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
     L.dbd_round.restype = i
     L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
@@ -158,7 +166,9 @@ def dbd_attn_paged(q, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len, ou
 
 
 def dbd_lmhead_conf(hidden, w_vocab, num_rows, argmax_tok, conf, mask_token_id,
-                    row_index=None, max_rows=None, ws=None, stream=None):
+                    row_index=None, max_rows=None, ws=None, stream=None, entropy=None):
+    """entropy (float32, optional): also each listed row's softmax entropy
+    (dbd_lmhead_conf_entropy)."""
     V, Hd = w_vocab.shape
     if max_rows is None:
         max_rows = row_index.shape[0] if row_index is not None else hidden.shape[0]
@@ -171,10 +181,19 @@ def dbd_lmhead_conf(hidden, w_vocab, num_rows, argmax_tok, conf, mask_token_id,
     need = dbd_lmhead_workspace_size(max_rows, V)
     if ws is None and need:
         ws = workspace(need, hidden.device)
-    _check(lib().dbd_lmhead_conf(max_rows, Hd, V, int(mask_token_id), _ptr(hidden),
-                                 _ptr(row_index), _ptr(num_rows), _ptr(w_vocab),
-                                 _ptr(argmax_tok), _ptr(conf), _ptr(ws),
-                                 ws.numel() if ws is not None else 0, _stream(stream)))
+    nb = ws.numel() if ws is not None else 0
+    if entropy is None:
+        _check(lib().dbd_lmhead_conf(max_rows, Hd, V, int(mask_token_id), _ptr(hidden),
+                                     _ptr(row_index), _ptr(num_rows), _ptr(w_vocab),
+                                     _ptr(argmax_tok), _ptr(conf), _ptr(ws), nb,
+                                     _stream(stream)))
+    else:
+        if entropy.dtype != torch.float32:
+            raise ValueError("entropy must be float32")
+        _check(lib().dbd_lmhead_conf_entropy(max_rows, Hd, V, int(mask_token_id), _ptr(hidden),
+                                             _ptr(row_index), _ptr(num_rows), _ptr(w_vocab),
+                                             _ptr(argmax_tok), _ptr(conf), _ptr(entropy),
+                                             _ptr(ws), nb, _stream(stream)))
 
 
 def dbd_remask_commit(block_tokens, seq_state, argmax_tok, conf, row_index_out, num_rows_out,
@@ -189,6 +208,23 @@ def dbd_remask_commit(block_tokens, seq_state, argmax_tok, conf, row_index_out, 
                                    _ptr(block_tokens), _ptr(seq_state), _ptr(argmax_tok),
                                    _ptr(conf), _ptr(row_index_out), _ptr(num_rows_out),
                                    _ptr(num_committed), _stream(stream)))
+
+
+def dbd_remask_commit_rule(block_tokens, seq_state, argmax_tok, conf, row_index_out,
+                           num_rows_out, mask_token_id, rule, dynamic_threshold=0.9,
+                           tokens_per_step=1, eb_threshold=0.0, entropy=None, flags=0,
+                           num_committed=None, stream=None):
+    S, B = block_tokens.shape
+    _need(block_tokens, torch.int32, (S, B), "block_tokens")
+    _need(seq_state, torch.uint8, (S,), "seq_state")
+    _need(row_index_out, torch.int32, (S * B,), "row_index_out")
+    _need(num_rows_out, torch.int32, (1,), "num_rows_out")
+    _check(lib().dbd_remask_commit_rule(S, B, int(mask_token_id), int(rule),
+                                        float(dynamic_threshold), int(tokens_per_step),
+                                        float(eb_threshold), int(flags), _ptr(block_tokens),
+                                        _ptr(seq_state), _ptr(argmax_tok), _ptr(conf),
+                                        _ptr(entropy), _ptr(row_index_out), _ptr(num_rows_out),
+                                        _ptr(num_committed), _stream(stream)))
 
 
 @dataclass
@@ -207,7 +243,8 @@ class RoundBuffers:
 def make_round_args(*, S, B, Hq, Hkv, D, page_size, max_pages_per_seq, Hd, V, mask_token_id,
                     dynamic_threshold, q, k_blk, v_blk, k_cache, v_cache, page_table,
                     prefix_len, attn_out, hidden, w_vocab, bufs: RoundBuffers, flags=0,
-                    softmax_scale=0.0) -> dbd_round_args:
+                    softmax_scale=0.0, rule=0, tokens_per_step=1, eb_threshold=0.0,
+                    entropy=None) -> dbd_round_args:
     a = dbd_round_args()
     a.S, a.B, a.Hq, a.Hkv, a.D = S, B, Hq, Hkv, D
     a.page_size, a.max_pages_per_seq, a.Hd, a.V = page_size, max_pages_per_seq, Hd, V
@@ -221,6 +258,8 @@ def make_round_args(*, S, B, Hq, Hkv, D, page_size, max_pages_per_seq, Hd, V, ma
               "num_committed", "workspace"):
         setattr(a, n, _ptr(getattr(bufs, n)))
     a.workspace_bytes = bufs.workspace.numel()
+    a.rule, a.tokens_per_step, a.eb_threshold = rule, tokens_per_step, eb_threshold
+    a.entropy = _ptr(entropy)
     return a
 
 

@@ -103,7 +103,7 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
 
 dbd_status enqueue_lm(int max_rows, int Hd, int V, int mask, const dbd_bf16* hidden,
                       const int32_t* row_index, const int32_t* num_rows,
-                      const dbd_bf16* w, int32_t* argmax_tok, float* conf,
+                      const dbd_bf16* w, int32_t* argmax_tok, float* conf, float* entropy,
                       void* ws, size_t ws_bytes, hipStream_t st) {
   if (max_rows == 0) return DBD_OK;
   const size_t need = dbd::lmhead_ws_bytes(max_rows, V);
@@ -113,30 +113,41 @@ dbd_status enqueue_lm(int max_rows, int Hd, int V, int mask, const dbd_bf16* hid
   dbd::LmArgs a{};
   a.hidden = hidden; a.row_index = row_index; a.num_rows = num_rows; a.w = w;
   a.Hd = Hd; a.V = V; a.mask_id = mask; a.max_rows = max_rows;
-  const size_t one = need / 3;
+  const size_t one = need / 4;
   char* base = static_cast<char*>(ws);
   a.pm = reinterpret_cast<float*>(base);
   a.pa = reinterpret_cast<int32_t*>(base + one);
   a.ps = reinterpret_cast<float*>(base + 2 * one);
-  a.argmax_tok = argmax_tok; a.conf = conf;
+  a.pt = reinterpret_cast<float*>(base + 3 * one);
+  a.argmax_tok = argmax_tok; a.conf = conf; a.entropy = entropy;
   hipError_t e = dbd::lmhead_launch(a, st);
   if (e != hipSuccess) return hip_fail(e, "LM-head launch");
   return DBD_OK;
 }
 
-dbd_status enqueue_remask(int S, int B, int mask, float tau, uint32_t flags,
+dbd_status enqueue_remask(int S, int B, int mask, float tau, uint32_t flags, int rule, int k,
+                          float eb, const float* entropy,
                           int32_t* block_tokens, uint8_t* seq_state,
                           const int32_t* argmax_tok, const float* conf,
                           int32_t* row_index_out, int32_t* num_rows_out,
                           int32_t* num_committed, hipStream_t st) {
   dbd::RemaskArgs a{};
   a.S = S; a.B = B; a.mask_id = mask; a.tau = tau; a.flags = flags;
+  a.rule = rule; a.k = k < 1 ? 1 : k; a.eb = eb; a.entropy = entropy;
   a.block_tokens = block_tokens; a.seq_state = seq_state;
   a.argmax_tok = argmax_tok; a.conf = conf;
   a.row_index_out = row_index_out; a.num_rows_out = num_rows_out;
   a.num_committed = num_committed;
   hipError_t e = dbd::remask_launch(a, st);
   if (e != hipSuccess) return hip_fail(e, "remask launch");
+  return DBD_OK;
+}
+
+// entropy is needed (and checked) only when the rule commits by entropy
+dbd_status check_rule(int rule, float eb, const float* entropy, bool commits) {
+  REQUIRE(rule >= DBD_RULE_LOW_CONF_DYNAMIC && rule <= DBD_RULE_ENTROPY_BOUNDED, "unknown rule %d", rule);
+  REQUIRE(!isnan(eb), "eb_threshold is NaN");
+  if (commits && rule == DBD_RULE_ENTROPY_BOUNDED) REQUIRE_PTR(entropy);
   return DBD_OK;
 }
 
@@ -147,6 +158,8 @@ dbd_status check_round(const dbd_round_args* a) {
   s = check_lm(a->S * a->B, a->Hd, a->V, a->mask_token_id);
   if (s != DBD_OK) return s;
   s = check_remask(a->S, a->B, a->dynamic_threshold);
+  if (s != DBD_OK) return s;
+  s = check_rule(a->rule, a->eb_threshold, a->entropy, true);
   if (s != DBD_OK) return s;
   REQUIRE_PTR(a->q); REQUIRE_PTR(a->k_blk); REQUIRE_PTR(a->v_blk);
   REQUIRE_PTR(a->k_cache); REQUIRE_PTR(a->v_cache);
@@ -170,10 +183,12 @@ dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
                               a->prefix_len, a->softmax_scale, a->attn_out, ws, plan.ws_bytes, st);
   if (s != DBD_OK) return s;
   const int max_rows = a->S * a->B;
+  float* ent = a->rule == DBD_RULE_ENTROPY_BOUNDED ? a->entropy : nullptr;
   s = enqueue_lm(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index, a->num_rows,
-                 a->w_vocab, a->argmax_tok, a->conf, ws + attn_ws, a->workspace_bytes - attn_ws, st);
+                 a->w_vocab, a->argmax_tok, a->conf, ent, ws + attn_ws, a->workspace_bytes - attn_ws, st);
   if (s != DBD_OK) return s;
   return enqueue_remask(a->S, a->B, a->mask_token_id, a->dynamic_threshold, a->flags & ~DBD_COMPACT_ONLY,
+                        a->rule, a->tokens_per_step, a->eb_threshold, ent,
                         a->block_tokens, a->seq_state, a->argmax_tok, a->conf, a->row_index,
                         a->num_rows, a->num_committed, st);
 }
@@ -237,7 +252,23 @@ dbd_status dbd_lmhead_conf(int max_rows, int Hd, int V, int mask_token_id,
   REQUIRE_PTR(argmax_tok); REQUIRE_PTR(conf);
   if (row_index != nullptr) REQUIRE_PTR(row_index);
   return enqueue_lm(max_rows, Hd, V, mask_token_id, hidden, row_index, num_rows, w_vocab,
-                    argmax_tok, conf, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+                    argmax_tok, conf, nullptr, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_lmhead_conf_entropy(int max_rows, int Hd, int V, int mask_token_id,
+                                   const dbd_bf16* hidden, const int32_t* row_index,
+                                   const int32_t* num_rows, const dbd_bf16* w_vocab,
+                                   int32_t* argmax_tok, float* conf, float* entropy,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  dbd_status s = check_lm(max_rows, Hd, V, mask_token_id);
+  if (s != DBD_OK) return s;
+  REQUIRE_PTR(hidden); REQUIRE_PTR(num_rows); REQUIRE_PTR(w_vocab);
+  REQUIRE_PTR(argmax_tok); REQUIRE_PTR(conf); REQUIRE_PTR(entropy);
+  if (row_index != nullptr) REQUIRE_PTR(row_index);
+  return enqueue_lm(max_rows, Hd, V, mask_token_id, hidden, row_index, num_rows, w_vocab,
+                    argmax_tok, conf, entropy, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream));
 }
 
 dbd_status dbd_remask_commit(int S, int B, int mask_token_id, float dynamic_threshold,
@@ -255,8 +286,34 @@ dbd_status dbd_remask_commit(int S, int B, int mask_token_id, float dynamic_thre
     REQUIRE_PTR(conf);
   }
   if (num_committed != nullptr) REQUIRE_PTR(num_committed);
-  return enqueue_remask(S, B, mask_token_id, dynamic_threshold, flags, block_tokens, seq_state,
-                        argmax_tok, conf, row_index_out, num_rows_out, num_committed,
+  return enqueue_remask(S, B, mask_token_id, dynamic_threshold, flags, DBD_RULE_LOW_CONF_DYNAMIC, 1,
+                        0.f, nullptr, block_tokens, seq_state, argmax_tok, conf, row_index_out,
+                        num_rows_out, num_committed, static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_remask_commit_rule(int S, int B, int mask_token_id, int rule,
+                                  float dynamic_threshold, int tokens_per_step,
+                                  float eb_threshold, uint32_t flags, int32_t* block_tokens,
+                                  uint8_t* seq_state, const int32_t* argmax_tok,
+                                  const float* conf, const float* entropy,
+                                  int32_t* row_index_out, int32_t* num_rows_out,
+                                  int32_t* num_committed, void* stream) {
+  dbd_status s = check_remask(S, B, dynamic_threshold);
+  if (s != DBD_OK) return s;
+  REQUIRE((flags & ~(DBD_FALLBACK_LEFTMOST | DBD_COMPACT_ONLY)) == 0, "unknown flags 0x%x", flags);
+  const bool commit = !(flags & DBD_COMPACT_ONLY);
+  s = check_rule(rule, eb_threshold, entropy, commit);
+  if (s != DBD_OK) return s;
+  REQUIRE_PTR(block_tokens); REQUIRE_PTR(seq_state); REQUIRE_PTR(row_index_out);
+  REQUIRE_PTR(num_rows_out);
+  if (commit) {
+    REQUIRE_PTR(argmax_tok);
+    if (rule == DBD_RULE_LOW_CONF_DYNAMIC || rule == DBD_RULE_LOW_CONF_STATIC) REQUIRE_PTR(conf);
+  }
+  if (num_committed != nullptr) REQUIRE_PTR(num_committed);
+  return enqueue_remask(S, B, mask_token_id, dynamic_threshold, flags, rule, tokens_per_step,
+                        eb_threshold, entropy, block_tokens, seq_state, argmax_tok, conf,
+                        row_index_out, num_rows_out, num_committed,
                         static_cast<hipStream_t>(stream));
 }
 

@@ -51,8 +51,10 @@ struct LmArgs {
   float* pm;       // [max_rows][kLmGrid] partial max logit
   int32_t* pa;     // [max_rows][kLmGrid] partial argmax (lowest id on ties)
   float* ps;       // [max_rows][kLmGrid] partial sum exp(l - max)
+  float* pt;       // [max_rows][kLmGrid] partial sum exp(l - max) (l - max)
   int32_t* argmax_tok;
   float* conf;
+  float* entropy;  // may be NULL: softmax entropy per listed row (nats)
 };
 
 size_t lmhead_ws_bytes(int max_rows, int V);
@@ -63,6 +65,10 @@ struct RemaskArgs {
   int S, B, mask_id;
   float tau;
   uint32_t flags;
+  int rule;           // 0 dynamic threshold, 1 static top-k, 2 sequential, 3 entropy-bounded
+  int k;              // tokens per step (rules 1 and 2)
+  float eb;           // entropy budget (rule 3)
+  const float* entropy;  // [S*B] (rule 3)
   int32_t* block_tokens;
   uint8_t* seq_state;
   const int32_t* argmax_tok;

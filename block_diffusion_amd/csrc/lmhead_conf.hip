@@ -60,21 +60,29 @@ constexpr int WPW = NT / 8 / 2;      // 1 KB W loads per W wave per stage
 // and any 8 consecutive rows (one 128-byte window per row) use distinct slots
 __device__ __forceinline__ int rswz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
+// Running reduction of a row's logits l over the columns seen so far, in
+// natural units: m = max l, a = lowest id reaching m, s = sum e^(l-m),
+// t = sum e^(l-m) (l-m).  The softmax entropy is ln s - t/s.
 struct Part {
   float m;
   int a;
   float s;
+  float t;
 };
 
-__device__ __forceinline__ void fold(Part& x, float m2, int a2, float s2) {
+// (m,a,s,t) + (m2,a2,s2,t2): rescale both to M = max(m, m2):
+// s -> s e^(m-M), t -> e^(m-M) (t + (m-M) s).
+__device__ __forceinline__ void fold(Part& x, float m2, int a2, float s2, float t2) {
   if (m2 == -INFINITY) return;
   if (x.m == -INFINITY) {
-    x.m = m2; x.a = a2; x.s = s2;
+    x.m = m2; x.a = a2; x.s = s2; x.t = t2;
     return;
   }
   const float M = fmaxf(x.m, m2);
   const int a = (m2 > x.m || (m2 == x.m && a2 < x.a)) ? a2 : x.a;
-  x.s = x.s * fast_exp2((x.m - M) * kLog2e) + s2 * fast_exp2((m2 - M) * kLog2e);
+  const float w1 = fast_exp2((x.m - M) * kLog2e), w2 = fast_exp2((m2 - M) * kLog2e);
+  x.t = w1 * fmaf(x.m - M, x.s, x.t) + w2 * fmaf(m2 - M, s2, t2);
+  x.s = x.s * w1 + s2 * w2;
   x.m = M;
   x.a = a;
 }
@@ -107,8 +115,9 @@ __device__ __forceinline__ int team_size(int M) { return M <= 256 ? 1 : (M <= 51
 // One pass of one workgroup: rows [m_base, m_end) of the compact row list
 // (R = 64*MB row slots, two waves of 32*MB rows) against vocabulary columns
 // [v_lo, v_hi), as seen by one wave; WL: this wave streams W (else hidden
-// rows).  Writes one partial per valid row into slot `team`.
-template <int MB, bool WL>
+// rows); ENT: also accumulate sum e^(l-m)(l-m) for the entropy.  Writes one
+// partial per valid row into slot `team`.
+template <int MB, bool WL, bool ENT>
 __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
                                         int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
   constexpr int R = 64 * MB, RH = 32 * MB;
@@ -233,7 +242,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
 
   Part run[MB];
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) run[mb] = Part{-INFINITY, 0x7fffffff, 0.f};
+  for (int mb = 0; mb < MB; ++mb) run[mb] = Part{-INFINITY, 0x7fffffff, 0.f, 0.f};
 
   // Accumulators start at 0, or at -inf on columns that are not candidates
   // (the mask id, columns past the range): MFMA accumulation keeps them at
@@ -274,7 +283,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       // block-online reduction of the lane's 64 values of this row, 16 at a
       // time: block max, lowest id reaching it, sum(2^(x - m)) rescaled once
       // per block.  Values are in log2 units; non-candidates are -inf.
-      float m = -INFINITY, sum = 0.f;
+      float m = -INFINITY, sum = 0.f, tt = 0.f;   // tt: sum 2^(x-m) (x-m)
       int idx = 0x7fffffff;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) {
@@ -297,11 +306,24 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
         for (int i = 15; i >= 0; --i) bi = (x[i] == bm) ? 8 * (i >> 2) + (i & 3) : bi;
         bi += vb0;
         const float mn = fmaxf(m, bm);
-        float sb = 0.f;
+        float sb = 0.f, tb = 0.f;
+        if (ENT) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sb += fast_exp2(x[i] - mn);
+          for (int i = 0; i < 16; ++i) {
+            // d >= -200: 2^d is then 0 in fp32 and d*2^d too (also for -inf)
+            const float d = fmaxf(x[i] - mn, -200.f);
+            const float e = fast_exp2(d);
+            sb += e;
+            tb = fmaf(e, d, tb);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sb += fast_exp2(x[i] - mn);
+        }
         sb = (mn == -INFINITY) ? 0.f : sb;            // all -inf so far: -inf - -inf
+        tb = (mn == -INFINITY) ? 0.f : tb;
         const float scale = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+        if (ENT) tt = (m == -INFINITY) ? tb : fmaf(scale, fmaf(m - mn, sum, tt), tb);
         sum = fmaf(sum, scale, sb);
         idx = (bm > m) ? bi : idx;   // equal maxima keep the earlier, lower id
         m = mn;
@@ -311,12 +333,17 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       const float pm = shfl_xor_f(m, 32);
       const int pi = shfl_xor_i(idx, 32);
       const float ps = shfl_xor_f(sum, 32);
+      const float pt = ENT ? shfl_xor_f(tt, 32) : 0.f;
       const float mx = fmaxf(m, pm);
       const float w1 = m == -INFINITY ? 0.f : fast_exp2(m - mx);
       const float w2 = pm == -INFINITY ? 0.f : fast_exp2(pm - mx);
+      const float t1 = (!ENT || m == -INFINITY) ? 0.f : w1 * fmaf(m - mx, sum, tt);
+      const float t2 = (!ENT || pm == -INFINITY) ? 0.f : w2 * fmaf(pm - mx, ps, pt);
       sum = sum * w1 + ps * w2;
+      tt = t1 + t2;
       idx = (pm > m || (pm == m && pi < idx)) ? pi : idx;
-      fold(run[mb], mx * (1.0f / kLog2e), idx, sum);
+      // to natural units: t = tt * ln 2
+      fold(run[mb], mx * (1.0f / kLog2e), idx, sum, tt * (1.0f / kLog2e));
     }
   };
 
@@ -392,6 +419,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   lds_f32* const s_m = (lds_f32*)Hr;
   lds_i32* const s_a = (lds_i32*)(Hr + 2 * 256);
   lds_f32* const s_s = (lds_f32*)(Hr + 4 * 256);
+  lds_f32* const s_t = (lds_f32*)(Hr + 6 * 256);
   if (wn == 1 && lane < 32) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -399,6 +427,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       s_m[k] = run[mb].m;
       s_a[k] = run[mb].a;
       s_s[k] = run[mb].s;
+      s_t[k] = run[mb].t;
     }
   }
   __syncthreads();
@@ -406,20 +435,21 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int k = (wm * MB + mb) * 32 + lane;
-      fold(run[mb], s_m[k], s_a[k], s_s[k]);
+      fold(run[mb], s_m[k], s_a[k], s_s[k], s_t[k]);
       const int m = m_base + wm * RH + mb * 32 + lane;
       if (m < m_end) {
         const size_t o = (size_t)m * nteam + team;
         a.pm[o] = run[mb].m;
         a.pa[o] = run[mb].a;
         a.ps[o] = run[mb].s;
+        if (ENT) a.pt[o] = run[mb].t;
       }
     }
   }
   __syncthreads();   // the partial scratch is read before the next pass loads
 }
 
-template <int MB>
+template <int MB, bool ENT>
 __device__ __forceinline__ void lm_pass_any(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
                                             int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
   if (v_hi <= v_lo) {
@@ -429,16 +459,18 @@ __device__ __forceinline__ void lm_pass_any(const LmArgs& a, int m_base, int m_e
       a.pm[o] = -INFINITY;
       a.pa[o] = 0x7fffffff;
       a.ps[o] = 0.f;
+      a.pt[o] = 0.f;
     }
     return;
   }
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 2)
-    lm_pass<MB, true>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
+    lm_pass<MB, true, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
   else
-    lm_pass<MB, false>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
+    lm_pass<MB, false, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
 }
 }  // namespace
 
+template <bool ENT>
 __global__ __launch_bounds__(256, 1) void lmhead_tile_kernel(LmArgs a) {
   __shared__ __align__(16) uint16_t Wr_[NWS * WSLOT];
   __shared__ __align__(16) uint16_t Hr_[NHS * HSLOT];
@@ -460,10 +492,10 @@ __global__ __launch_bounds__(256, 1) void lmhead_tile_kernel(LmArgs a) {
     const int m_end = min(m_base + R, p0 + Mp);
     if (m_base >= m_end) continue;
     switch (R / 64) {
-      case 1: lm_pass_any<1>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
-      case 2: lm_pass_any<2>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
-      case 3: lm_pass_any<3>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
-      default: lm_pass_any<4>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      case 1: lm_pass_any<1, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      case 2: lm_pass_any<2, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      case 3: lm_pass_any<3, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      default: lm_pass_any<4, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
     }
   }
 }
@@ -475,30 +507,36 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(LmArgs a) {
   if (r >= M) return;
   const int nteam = kLmGrid / team_size(M);
   const size_t base = (size_t)r * nteam;
-  Part x{-INFINITY, 0x7fffffff, 0.f};
-  for (int t = lane; t < nteam; t += 64) fold(x, a.pm[base + t], a.pa[base + t], a.ps[base + t]);
+  Part x{-INFINITY, 0x7fffffff, 0.f, 0.f};
+  const bool ent = a.entropy != nullptr;
+  for (int t = lane; t < nteam; t += 64)
+    fold(x, a.pm[base + t], a.pa[base + t], a.ps[base + t], ent ? a.pt[base + t] : 0.f);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = shfl_xor_f(x.m, off);
     const int a2 = shfl_xor_i(x.a, off);
     const float s2 = shfl_xor_f(x.s, off);
-    fold(x, m2, a2, s2);
+    const float t2 = shfl_xor_f(x.t, off);
+    fold(x, m2, a2, s2, t2);
   }
   if (lane == 0) {
     const int row = a.row_index ? a.row_index[r] : r;
     a.argmax_tok[row] = x.a;
     a.conf[row] = 1.f / x.s;
+    if (a.entropy) a.entropy[row] = __logf(x.s) - x.t / x.s;
   }
 }
 
 size_t lmhead_ws_bytes(int max_rows, int V) {
   (void)V;
   const size_t one = ((size_t)max_rows * kLmGrid * 4 + 255) & ~(size_t)255;
-  return 3 * one;
+  return 4 * one;
 }
 
 hipError_t lmhead_launch(const LmArgs& a, hipStream_t st) {
-  lmhead_tile_kernel<<<kLmGrid, 256, 0, st>>>(a);
+  // the entropy sums only when a caller wants the entropy
+  if (a.entropy) lmhead_tile_kernel<true><<<kLmGrid, 256, 0, st>>>(a);
+  else lmhead_tile_kernel<false><<<kLmGrid, 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   lmhead_merge_kernel<<<(a.max_rows + 3) / 4, 256, 0, st>>>(a);

@@ -1,19 +1,27 @@
-// Threshold remask (low_confidence_dynamic) and row compaction, gfx950.
+// Remask by a commit rule, and row compaction, gfx950.
 //
-// The commit rule of JetEngine's low_confidence_dynamic strategy (developer
-// notes, "Remasking Strategies": unmask every position above the
-// threshold, with a fallback) on DENOISING sequences, and the state change
-// to SAVING once a block holds no mask (developer notes, "Scheduler").
-// Confidences and the threshold are compared in float32.
+// The remasking strategies of JetEngine's scheduler (developer notes,
+// "Remasking Strategies"), applied to DENOISING sequences, and the state
+// change to SAVING once a block holds no mask (developer notes,
+// "Scheduler"):
+//   rule 0, low_confidence_dynamic: every masked position with confidence
+//     >= the threshold; if none, the most confident (lowest position on
+//     ties), or the leftmost with DBD_FALLBACK_LEFTMOST;
+//   rule 1, low_confidence_static: the k most confident masked positions
+//     (lower position first on ties);
+//   rule 2, sequential: the k leftmost masked positions;
+//   rule 3, entropy_bounded: masked positions in ascending entropy (lower
+//     position first on ties), the longest leading run whose float32 running
+//     sum stays within the budget, at least one.
+// Confidences, entropies and the threshold are compared in float32.
 //
 // One workgroup of 16 waves.  Pass 1: a wave per sequence, lane = block
-// position (B <= 64): ballot of the masked set and of the positions at or
-// above the threshold; if none qualifies, the most confident masked
-// position (wave max, then the lowest lane reaching it), or the leftmost
-// with DBD_FALLBACK_LEFTMOST.  The still-masked set of each sequence is kept
-// as a 64-bit mask in LDS.  Pass 2: exclusive scan of the per-sequence
-// counts.  Pass 3: each still-masked position writes s*B+i at its rank, so
-// the list is sequence-major and position-minor, the same on every run.
+// position (B <= 64): ballots of the masked set; the rule's choice is built
+// one wave-wide selection at a time (max or min, then the lowest lane).
+// The still-masked set of each sequence is kept as a 64-bit mask in LDS.
+// Pass 2: exclusive scan of the per-sequence counts.  Pass 3: each
+// still-masked position writes s*B+i at its rank, so the list is
+// sequence-major and position-minor, the same on every run.
 #include "dbd_device.hpp"
 #include "dbd_internal.hpp"
 
@@ -40,17 +48,62 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
     const unsigned long long mball = __ballot(masked);
     bool still = masked;
     if (den && !(a.flags & kCompactOnly)) {
-      const float c = masked ? a.conf[s * B + lane] : -INFINITY;
-      unsigned long long cball = __ballot(masked && c >= a.tau);
-      if (cball == 0ull && mball != 0ull) {
-        if (a.flags & kFallbackLeftmost) {
-          cball = mball & (~mball + 1ull);  // lowest set bit
-        } else {
-          float best = c;
+      unsigned long long cball = 0ull;
+      if (a.rule == 0) {
+        const float c = masked ? a.conf[s * B + lane] : -INFINITY;
+        cball = __ballot(masked && c >= a.tau);
+        if (cball == 0ull && mball != 0ull) {
+          if (a.flags & kFallbackLeftmost) {
+            cball = mball & (~mball + 1ull);  // lowest set bit
+          } else {
+            float best = c;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) best = fmaxf(best, shfl_xor_f(best, off));
+            const unsigned long long tie = __ballot(masked && c == best);
+            cball = tie & (~tie + 1ull);
+          }
+        }
+      } else if (a.rule == 2) {
+        // the k lowest set bits of the masked set
+        unsigned long long rest = mball;
+        for (int r = 0; r < a.k && rest != 0ull; ++r) {
+          const unsigned long long low = rest & (~rest + 1ull);
+          cball |= low;
+          rest ^= low;
+        }
+      } else if (a.rule == 1) {
+        // k times: the most confident remaining position, lowest lane on ties
+        const float c = masked ? a.conf[s * B + lane] : -INFINITY;
+        unsigned long long rest = mball;
+        for (int r = 0; r < a.k && rest != 0ull; ++r) {
+          const bool cand = (rest >> lane) & 1ull;
+          float best = cand ? c : -INFINITY;
 #pragma unroll
           for (int off = 32; off >= 1; off >>= 1) best = fmaxf(best, shfl_xor_f(best, off));
-          const unsigned long long tie = __ballot(masked && c == best);
-          cball = tie & (~tie + 1ull);
+          unsigned long long tie = __ballot(cand && c == best);
+          if (tie == 0ull) tie = rest;   // every remaining value is -inf or NaN
+          const unsigned long long pick = tie & (~tie + 1ull);
+          cball |= pick;
+          rest ^= pick;
+        }
+      } else {
+        // ascending entropy; stop before the running sum passes the budget
+        const float e = masked ? a.entropy[s * B + lane] : INFINITY;
+        unsigned long long rest = mball;
+        float run = 0.f;
+        while (rest != 0ull) {
+          const bool cand = (rest >> lane) & 1ull;
+          float lo = cand ? e : INFINITY;
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) lo = fminf(lo, shfl_xor_f(lo, off));
+          unsigned long long tie = __ballot(cand && e == lo);
+          if (tie == 0ull) tie = rest;   // every remaining value is +inf or NaN
+          const unsigned long long pick = tie & (~tie + 1ull);
+          const float nxt = run + lo;
+          if (cball != 0ull && nxt > a.eb) break;
+          cball |= pick;
+          rest ^= pick;
+          run = nxt;
         }
       }
       const bool commit = (cball >> lane) & 1ull;

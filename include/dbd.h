@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define DBD_ABI_VERSION 1
+#define DBD_ABI_VERSION 2
 
 typedef uint16_t dbd_bf16;
 
@@ -59,6 +59,11 @@ enum { DBD_WAITING = 0, DBD_PREFILLING = 1, DBD_DENOISING = 2,
 /* dbd_remask_commit flags */
 #define DBD_FALLBACK_LEFTMOST 1u /* fallback commits the leftmost masked position */
 #define DBD_COMPACT_ONLY 2u      /* no commit: only rebuild the row list           */
+
+/* Commit rules: the remasking strategies the JetEngine developer notes list
+ * ("Remasking Strategies"); see dbd_remask_commit_rule. */
+enum { DBD_RULE_LOW_CONF_DYNAMIC = 0, DBD_RULE_LOW_CONF_STATIC = 1,
+       DBD_RULE_SEQUENTIAL = 2, DBD_RULE_ENTROPY_BOUNDED = 3 };
 
 /* ------------------------------------------------------------------------
  * dbd_attn_paged -- block-diffusion attention over a paged KV cache.
@@ -132,6 +137,22 @@ dbd_status dbd_lmhead_conf(int max_rows, int Hd, int V, int mask_token_id,
 
 size_t dbd_lmhead_workspace_size(int max_rows, int V);
 
+/* dbd_lmhead_conf plus each listed row's softmax entropy, the quantity the
+ * entropy-bounded commit rule orders positions by (developer notes,
+ * "Remasking Strategies": unmask by cumulative entropy budget):
+ *   entropy[row] = -sum_{v != mask} p_v ln p_v   (nats, float32),
+ * from the same fused pass (a running sum of e^(l-m) (l-m) merged like the
+ * normaliser).  entropy: float [rows], written only at listed rows; every
+ * other argument as dbd_lmhead_conf. */
+dbd_status dbd_lmhead_conf_entropy(int max_rows, int Hd, int V,
+                                   int mask_token_id, const dbd_bf16* hidden,
+                                   const int32_t* row_index,
+                                   const int32_t* num_rows,
+                                   const dbd_bf16* w_vocab,
+                                   int32_t* argmax_tok, float* conf,
+                                   float* entropy, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * dbd_remask_commit -- threshold remask (low_confidence_dynamic) and the
  * next round's row list.
@@ -166,6 +187,40 @@ dbd_status dbd_remask_commit(int S, int B, int mask_token_id,
                              int32_t* num_committed, void* stream);
 
 /* ------------------------------------------------------------------------
+ * dbd_remask_commit_rule -- dbd_remask_commit with the commit set chosen by
+ * one of the remasking strategies of the developer notes ("Remasking
+ * Strategies": sequential unmasks left to right, low_confidence_static the
+ * top k by confidence, low_confidence_dynamic above a threshold with a
+ * fallback, entropy_bounded by a cumulative entropy budget).  The notes
+ * give one phrase per strategy; the readings taken, for a DENOISING
+ * sequence with masked set M and k = min(max(tokens_per_step,1), |M|):
+ *   DBD_RULE_LOW_CONF_DYNAMIC: as dbd_remask_commit (dynamic_threshold,
+ *       flags);
+ *   DBD_RULE_LOW_CONF_STATIC:  the k most confident positions of M (lower
+ *       position first on equal confidence);
+ *   DBD_RULE_SEQUENTIAL:       the k leftmost positions of M;
+ *   DBD_RULE_ENTROPY_BOUNDED:  M in ascending entropy[s*B+i] (lower position
+ *       first on ties); the longest leading run whose float32 running sum is
+ *       <= eb_threshold, and at least its first position.
+ * Then as dbd_remask_commit: committed positions take argmax_tok, SAVING
+ * once no mask is left, the next round's row list.  entropy (float [S*B],
+ * read at masked positions of DENOISING sequences) is required for
+ * DBD_RULE_ENTROPY_BOUNDED and ignored otherwise.
+ * Requirements: as dbd_remask_commit; rule one of DBD_RULE_*; eb_threshold
+ * not NaN.
+ * ---------------------------------------------------------------------- */
+dbd_status dbd_remask_commit_rule(int S, int B, int mask_token_id, int rule,
+                                  float dynamic_threshold,
+                                  int tokens_per_step, float eb_threshold,
+                                  uint32_t flags, int32_t* block_tokens,
+                                  uint8_t* seq_state,
+                                  const int32_t* argmax_tok, const float* conf,
+                                  const float* entropy,
+                                  int32_t* row_index_out,
+                                  int32_t* num_rows_out,
+                                  int32_t* num_committed, void* stream);
+
+/* ------------------------------------------------------------------------
  * dbd_round -- one whole denoise round: dbd_attn_paged, then
  * dbd_lmhead_conf on the row list (row_index, *num_rows), then
  * dbd_remask_commit, which overwrites (row_index, *num_rows) with the next
@@ -194,6 +249,11 @@ typedef struct dbd_round_args {
   int32_t* num_committed; /* may be NULL */
   void* workspace;
   size_t workspace_bytes;
+  /* commit rule (dbd_remask_commit_rule); rule 0 is the threshold rule */
+  int rule;
+  int tokens_per_step;
+  float eb_threshold;
+  float* entropy; /* float [S*B]; required for DBD_RULE_ENTROPY_BOUNDED */
 } dbd_round_args;
 
 dbd_status dbd_round(const dbd_round_args* a, void* stream);

@@ -25,6 +25,7 @@ def declared_functions():
 def test_header_declares_the_round_calls():
     names = declared_functions()
     for n in ("dbd_attn_paged", "dbd_lmhead_conf", "dbd_remask_commit", "dbd_round",
+              "dbd_lmhead_conf_entropy", "dbd_remask_commit_rule",
               "dbd_graph_create", "dbd_graph_launch", "dbd_graph_destroy",
               "dbd_attn_workspace_size", "dbd_lmhead_workspace_size",
               "dbd_round_workspace_size", "dbd_validate_inputs", "dbd_last_error",
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(lib, n)
-    assert api.dbd_abi_version() == 1
+    assert api.dbd_abi_version() == 2
 
 
 def _attn(**kw):
@@ -111,6 +112,27 @@ def test_remask_rejects(S, B, tau, flags, status):
     assert L.dbd_remask_commit(S, B, 5, tau, flags, 16, 16, 16, 16, 16, 16, None, None) == status
 
 
+@pytest.mark.parametrize("rule,eb,entropy,flags,status", [
+    (4, 0.0, 16, 0, api.DBD_ERR_INVALID_ARG),                 # unknown rule
+    (-1, 0.0, 16, 0, api.DBD_ERR_INVALID_ARG),
+    (3, float("nan"), 16, 0, api.DBD_ERR_INVALID_ARG),        # NaN budget
+    (3, 1.0, None, 0, api.DBD_ERR_INVALID_ARG),               # entropy rule needs entropy
+    (3, 1.0, 18, 0, api.DBD_ERR_INVALID_ARG),                 # misaligned entropy
+    (1, 0.0, None, 4, api.DBD_ERR_INVALID_ARG)])              # unknown flag
+def test_remask_rule_rejects(rule, eb, entropy, flags, status):
+    L = api.lib()
+    st = L.dbd_remask_commit_rule(2, 4, 5, rule, 0.9, 1, eb, flags, 16, 16, 16, 16, entropy,
+                                  16, 16, None, None)
+    assert st == status and L.dbd_last_error()
+
+
+def test_lmhead_entropy_requires_output():
+    L = api.lib()
+    st = L.dbd_lmhead_conf_entropy(16, 128, 1024, 5, 16, None, 16, 16, 16, 16, None, 256,
+                                   1 << 20, None)
+    assert st == api.DBD_ERR_INVALID_ARG and b"entropy is NULL" in L.dbd_last_error()
+
+
 def test_round_rejects():
     a = api.dbd_round_args()
     a.S, a.B, a.Hq, a.Hkv, a.D, a.page_size, a.max_pages_per_seq = 2, 4, 4, 2, 64, 16, 3
@@ -120,6 +142,10 @@ def test_round_rejects():
     assert e.value.status == api.DBD_ERR_INVALID_ARG
     with pytest.raises(api.DbdError):
         api.dbd_graph_create([a])
+    a.rule, a.eb_threshold = 3, 1.0          # entropy rule without an entropy buffer
+    with pytest.raises(api.DbdError) as e:
+        api.dbd_round(a, stream=0)
+    assert e.value.status == api.DBD_ERR_INVALID_ARG
 
 
 def test_validate_inputs():
