@@ -8,7 +8,8 @@ Plain, slow, float64 numpy written from the pages' description of the
 round (JetEngine README: "Block Diffusion Decoding", "Selective Logits";
 JetEngine developer notes (CLAUDE.md): "Remasking Strategies",
 "Scheduler", "ModelRunner"; dlmrt README: "Highlights" on rounds run on
-the device).  It shares no code with the HIP path: it decodes bf16 bit
+the device; developer notes, "Important Patterns" and "Sequence" on the
+SAVING forward and the block commit).  It shares no code with the HIP path: it decodes bf16 bit
 patterns itself and reads nothing from ``block_diffusion_amd``.
 
 Every function is pinned by CPU tests against brute force, closed forms,
@@ -21,8 +22,10 @@ from .lmhead import lmhead_rows, lmhead_logits, lmhead_entropy
 from .remask import (remask, remask_rule, compact_rows, DENOISING, SAVING,
                      RULE_DYNAMIC, RULE_STATIC, RULE_SEQUENTIAL, RULE_ENTROPY)
 from .round import denoise_round
+from .block_commit import kv_save, commit_block, step_commit, FINISHED
 
 __all__ = ["widen", "attention", "attention_group", "lmhead_rows",
            "lmhead_logits", "lmhead_entropy", "remask", "remask_rule",
            "compact_rows", "denoise_round", "DENOISING", "SAVING",
-           "RULE_DYNAMIC", "RULE_STATIC", "RULE_SEQUENTIAL", "RULE_ENTROPY"]
+           "RULE_DYNAMIC", "RULE_STATIC", "RULE_SEQUENTIAL", "RULE_ENTROPY",
+           "kv_save", "commit_block", "step_commit", "FINISHED"]

@@ -665,3 +665,186 @@ def check_rule_invariants(impl):
 
 
 RULE_CHECKS = [check_rule_bruteforce, check_rule_special_cases, check_rule_invariants]
+
+
+# ------------------------------------------------- SAVING step, block commit
+# The checks take the implementation for kv_save / commit_block / step_commit
+# and the real (separately pinned) oracle for attention and the rules.
+
+FIN = 4
+
+
+def _saving_case(seed, S=3, B=3, Hq=4, Hkv=2, D=8, P=4, L=(7, 0, 5), blocks=2):
+    """A paged cache whose tables already cover `blocks` more blocks, with
+    the slots past each prefix filled with NaN."""
+    g = np.random.default_rng(seed)
+    npg = [-(-(l + blocks * B) // P) for l in L]
+    total = sum(npg) + 2
+    perm = g.permutation(total)
+    pt = np.full((S, max(npg)), -1, dtype=np.int32)
+    o = 0
+    for s, n in enumerate(npg):
+        pt[s, :n] = perm[o:o + n]
+        o += n
+    kc = bf(g.standard_normal((total, Hkv, P, D)))
+    vc = bf(g.standard_normal((total, Hkv, P, D)))
+    for s in range(S):
+        for p in range(L[s], npg[s] * P):
+            kc[pt[s, p // P], :, p % P] = 0x7FC0
+            vc[pt[s, p // P], :, p % P] = 0x7FC0
+
+    def blk():
+        return (bf(g.standard_normal((S, B, Hq, D))), bf(g.standard_normal((S, B, Hkv, D))),
+                bf(g.standard_normal((S, B, Hkv, D))))
+    return g, dict(k_cache=kc, v_cache=vc, page_table=pt, prefix_len=np.asarray(L, np.int32)), blk
+
+
+def _attn_lists(q, keys, vals, sc):
+    """Attention of q [B][Hq][D] (float64) over explicit per-kv-head key and
+    value lists keys[g] = [n][D]: scalar loops and math.fsum."""
+    B, Hq, D = q.shape
+    G = Hq // len(keys)
+    out = np.zeros((B, Hq, D))
+    for h in range(Hq):
+        K, V = keys[h // G], vals[h // G]
+        for i in range(B):
+            z = [math.fsum(a * b for a, b in zip(q[i, h], k)) * sc for k in K]
+            mz = max(z)
+            e = [math.exp(t - mz) for t in z]
+            den = math.fsum(e)
+            for d in range(D):
+                out[i, h, d] = math.fsum(e[j] * V[j][d] for j in range(len(K))) / den
+    return out
+
+
+def check_kvsave_attention(impl):
+    """After the SAVING step and the commit, the next block's attention over
+    the cache equals attention over an explicit key list: the old prefix
+    (walked through the page table), the saved block, the new block; for a
+    sequence that was not SAVING, the old prefix and the new block."""
+    import oracle as real
+    for seed, L, P, B in [(0, (7, 0, 5), 4, 3), (1, (3, 8, 1), 4, 2), (2, (16, 9, 4), 8, 4)]:
+        g, c, blk = _saving_case(seed, B=B, P=P, L=L)
+        S = len(L)
+        state = np.array([SAV, SAV, DEN], dtype=np.uint8)
+        q1, kb1, vb1 = blk()
+        kc2, vc2 = impl.kv_save(c["k_cache"], c["v_cache"], c["page_table"], c["prefix_len"],
+                                state, kb1, vb1)
+        toks = g.integers(0, 50, (S, B))
+        toks[2, 0] = 99
+        t2, s2, L2, _ = impl.commit_block(toks, state, c["prefix_len"], 99)
+        q2, kb2, vb2 = blk()
+        got = real.attention(q2, kb2, vb2, kc2, vc2, c["page_table"], L2)
+        Hkv, D = kb1.shape[2], kb1.shape[3]
+        for s in range(S):
+            keys, vals = [], []
+            for gk in range(Hkv):
+                K, V = [], []
+                for j in range(int(L[s])):
+                    page = int(c["page_table"][s][j // P])
+                    K.append(list(wid(c["k_cache"][page, gk, j % P])))
+                    V.append(list(wid(c["v_cache"][page, gk, j % P])))
+                if state[s] == SAV:
+                    K += [list(wid(kb1[s, j, gk])) for j in range(B)]
+                    V += [list(wid(vb1[s, j, gk])) for j in range(B)]
+                K += [list(wid(kb2[s, j, gk])) for j in range(B)]
+                V += [list(wid(vb2[s, j, gk])) for j in range(B)]
+                keys.append(K)
+                vals.append(V)
+            ref = _attn_lists(wid(q2[s]), keys, vals, 1.0 / math.sqrt(D))
+            assert np.max(np.abs(got[s] - ref)) < 1e-12, (seed, s)
+
+
+def check_kvsave_untouched(impl):
+    """Exactly the slots at positions prefix_len..prefix_len+B-1 of SAVING
+    sequences change, to the block's bits; every other bit (NaN tails
+    included) is unchanged; the inputs are not modified."""
+    for seed, L, P, B in [(3, (7, 0, 5), 4, 3), (4, (4, 12, 2), 4, 4), (5, (0, 1, 30), 16, 5)]:
+        g, c, blk = _saving_case(seed, B=B, P=P, L=L)
+        for state in ([SAV, DEN, SAV], [DEN, DEN, DEN], [SAV, SAV, SAV], [0, SAV, FIN]):
+            state = np.array(state, dtype=np.uint8)
+            _, kb, vb = blk()
+            k0, v0 = c["k_cache"].copy(), c["v_cache"].copy()
+            kc2, vc2 = impl.kv_save(c["k_cache"], c["v_cache"], c["page_table"], c["prefix_len"],
+                                    state, kb, vb)
+            assert np.array_equal(c["k_cache"], k0) and np.array_equal(c["v_cache"], v0)
+            touched = np.zeros(k0.shape[:1] + k0.shape[2:3], dtype=bool)   # [page][slot]
+            for s in np.where(state == SAV)[0]:
+                for j in range(B):
+                    p = int(L[s]) + j
+                    pg = int(c["page_table"][s][p // P])
+                    touched[pg, p % P] = True
+                    assert np.array_equal(kc2[pg, :, p % P], kb[s, j])
+                    assert np.array_equal(vc2[pg, :, p % P], vb[s, j])
+            assert touched.sum() == (state == SAV).sum() * B
+            keep = ~touched
+            assert np.array_equal(kc2.transpose(0, 2, 1, 3)[keep], k0.transpose(0, 2, 1, 3)[keep])
+            assert np.array_equal(vc2.transpose(0, 2, 1, 3)[keep], v0.transpose(0, 2, 1, 3)[keep])
+
+
+def check_commit_block_worked(impl):
+    """A hand-worked case.  Sequence 0 SAVING commits its block at 5..7 and
+    restarts; 1 DENOISING is untouched; 2 SAVING reaches its end length
+    (8 + 3 >= 11) and finishes, keeping its block; 3 WAITING is untouched;
+    4 SAVING near the stream's end keeps only the positions that fit."""
+    toks = np.array([[4, 5, 6], [9, 9, 1], [7, 8, 2], [9, 9, 9], [3, 1, 4]])
+    state = np.array([SAV, DEN, SAV, 0, SAV], dtype=np.uint8)
+    L = np.array([5, 2, 8, 0, 11], dtype=np.int32)
+    ts = np.full((5, 13), -1, dtype=np.int64)
+    end = np.array([100, 100, 11, 100, 100], dtype=np.int32)
+    nt, ns, nL, nts = impl.commit_block(toks, state, L, 9, ts, end)
+    assert np.array_equal(nt, [[9, 9, 9], [9, 9, 1], [7, 8, 2], [9, 9, 9], [9, 9, 9]])
+    assert np.array_equal(ns, [DEN, DEN, FIN, 0, DEN])
+    assert np.array_equal(nL, [8, 2, 11, 0, 14])
+    exp = np.full((5, 13), -1)
+    exp[0, 5:8] = [4, 5, 6]
+    exp[2, 8:11] = [7, 8, 2]
+    exp[4, 11:13] = [3, 1]
+    assert np.array_equal(nts, exp)
+    # without a stream or end lengths nothing finishes
+    nt, ns, nL, nts = impl.commit_block(toks, state, L, 9)
+    assert nts is None and np.array_equal(ns, [DEN, DEN, DEN, 0, DEN])
+
+
+def check_step_commit_order(impl):
+    """One step commits the sequences that were SAVING on entry, and only
+    those: a sequence that the rule fills in this step stays SAVING (its
+    SAVING forward comes first); the next row list holds the fresh blocks."""
+    B, mask = 4, 99
+    toks = np.array([[1, 2, 3, 4], [mask, 5, 6, 7], [mask, mask, 8, 9]])
+    state = np.array([SAV, DEN, DEN], dtype=np.uint8)
+    L = np.array([8, 4, 0], dtype=np.int32)
+    conf = np.full(3 * B, 0.5)
+    argm = np.arange(3 * B) + 100
+    nt, ns, nL, _, com, rows = impl.step_commit(toks, state, L, conf, argm, mask, 2,
+                                                tokens_per_step=1)
+    assert np.array_equal(ns, [DEN, SAV, DEN])
+    assert np.array_equal(nL, [12, 4, 0])
+    assert np.array_equal(nt, [[mask] * 4, [104, 5, 6, 7], [108, mask, 8, 9]])
+    assert np.array_equal(rows, [0, 1, 2, 3, 9])
+    assert com.sum() == 2
+
+
+def check_multiblock_stream(impl):
+    """Several whole blocks, each B rounds of the sequential rule (k = 1)
+    and one SAVING step, with argmax = 1000*step + row: position j of block
+    b is committed at step (B+1)*b + j, so the stream holds a closed form."""
+    S, B, mask, L0, nb = 3, 3, 999, np.array([2, 5, 0], np.int32), 3
+    toks = np.full((S, B), mask)
+    state = np.full(S, DEN, dtype=np.uint8)
+    L = L0.copy()
+    ts = np.full((S, 20), -1, dtype=np.int64)
+    for t in range((B + 1) * nb):
+        argm = 1000 * t + np.arange(S * B)
+        toks, state, L, ts, _, _ = impl.step_commit(toks, state, L, np.zeros(S * B), argm, mask, 2,
+                                                    tokens_per_step=1, token_stream=ts)
+    assert np.all(state == DEN) and np.array_equal(L, L0 + nb * B)
+    for s in range(S):
+        for b in range(nb):
+            for j in range(B):
+                assert ts[s, L0[s] + b * B + j] == 1000 * ((B + 1) * b + j) + s * B + j
+        assert np.all(ts[s, :L0[s]] == -1) and np.all(ts[s, L0[s] + nb * B:] == -1)
+
+
+SAVE_CHECKS = [check_kvsave_attention, check_kvsave_untouched, check_commit_block_worked,
+               check_step_commit_order, check_multiblock_stream]

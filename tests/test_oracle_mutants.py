@@ -8,7 +8,7 @@ import types
 
 import pytest
 
-from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS
+from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS, SAVE_CHECKS
 
 ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 
@@ -51,6 +51,18 @@ MUTANTS = [
     ("remask.py", "if chosen and nxt > budget:", "if chosen and nxt >= budget:", "rule"),
     ("remask.py", "order = sorted(masked, key=lambda i: (ent[s, i], i))",
      "order = sorted(masked, key=lambda i: (ent[s, i], -i))", "rule"),
+    ("block_commit.py", "            p = L + j\n", "            p = L + j + 1\n", "save"),
+    ("block_commit.py", "kc[page, :, p % P, :] = k_blk[s, j]", "kc[page, :, j % P, :] = k_blk[s, j]", "save"),
+    ("block_commit.py", "page = int(page_table[s][p // P])", "page = int(page_table[s][j // P])", "save"),
+    ("block_commit.py", "vc[page, :, p % P, :] = v_blk[s, j]", "vc[page, :, p % P, :] = k_blk[s, j]", "save"),
+    ("block_commit.py", "        if seq_state[s] != SAVING:\n            continue\n        L = int",
+     "        if seq_state[s] == 0:\n            continue\n        L = int", "save"),
+    ("block_commit.py", "        L[s] += B\n", "        L[s] += B - 1\n", "save"),
+    ("block_commit.py", "            toks[s, :] = mask_id\n", "            pass\n", "save"),
+    ("block_commit.py", "if end_len is not None and L[s] >= end_len[s]:",
+     "if end_len is not None and L[s] > end_len[s]:", "save"),
+    ("block_commit.py", "ts[s, L[s] + j] = toks[s, j]", "ts[s, L[s] + j] = toks[s, B - 1 - j]", "save"),
+    ("block_commit.py", "only = np.where(saving0, SAVING, 0).astype(state.dtype)", "only = state", "save"),
 ]
 
 
@@ -58,7 +70,9 @@ def load_mutant(fname, old, new):
     pkg = types.ModuleType("oracle_mut")
     pkg.__path__ = []
     sys.modules["oracle_mut"] = pkg
-    for dep in ("bf16.py",):
+    for dep in ("bf16.py", "remask.py"):
+        if dep == fname:
+            continue
         spec = importlib.util.spec_from_file_location("oracle_mut." + dep[:-3], os.path.join(ORACLE, dep))
         m = importlib.util.module_from_spec(spec)
         sys.modules[spec.name] = m
@@ -78,7 +92,8 @@ def load_mutant(fname, old, new):
 def test_mutant_is_caught(mut):
     fname, old, new, fam = mut
     mod = load_mutant(fname, old, new)
-    checks = {"attn": ATTN_CHECKS, "lm": LM_CHECKS, "remask": REMASK_CHECKS, "rule": RULE_CHECKS}[fam]
+    checks = {"attn": ATTN_CHECKS, "lm": LM_CHECKS, "remask": REMASK_CHECKS, "rule": RULE_CHECKS,
+              "save": SAVE_CHECKS}[fam]
     caught = []
     for chk in checks:
         try:
