@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdbd.so")
 
 DBD_OK, DBD_ERR_INVALID_ARG, DBD_ERR_UNSUPPORTED, DBD_ERR_WORKSPACE, DBD_ERR_HIP = range(5)
-DBD_DENOISING, DBD_SAVING = 2, 3
+DBD_WAITING, DBD_PREFILLING, DBD_DENOISING, DBD_SAVING, DBD_FINISHED = range(5)
 DBD_FALLBACK_LEFTMOST, DBD_COMPACT_ONLY = 1, 2
 (DBD_RULE_LOW_CONF_DYNAMIC, DBD_RULE_LOW_CONF_STATIC, DBD_RULE_SEQUENTIAL,
  DBD_RULE_ENTROPY_BOUNDED) = 0, 1, 2, 3
@@ -36,7 +36,8 @@ class dbd_round_args(C.Structure):
         ("argmax_tok", _vp), ("conf", _vp), ("block_tokens", _vp), ("seq_state", _vp),
         ("num_committed", _vp), ("workspace", _vp), ("workspace_bytes", C.c_size_t),
         ("rule", C.c_int), ("tokens_per_step", C.c_int), ("eb_threshold", C.c_float),
-        ("entropy", _vp)]
+        ("entropy", _vp), ("save_kv", C.c_int), ("num_pages", C.c_int),
+        ("token_stream", _vp), ("stream_cap", C.c_int), ("end_len", _vp)]
 
 
 class DbdError(RuntimeError):
@@ -73,6 +74,10 @@ def lib() -> C.CDLL:
     L.dbd_lmhead_conf_entropy.restype = i
     L.dbd_remask_commit_rule.argtypes = [i, i, i, i, f, i, f, u32] + [_vp] * 8 + [_vp]
     L.dbd_remask_commit_rule.restype = i
+    L.dbd_attn_paged_save.argtypes = [i] * 8 + [_vp] * 8 + [f, _vp, _vp, sz, _vp]
+    L.dbd_attn_paged_save.restype = i
+    L.dbd_commit_block.argtypes = [i, i, i] + [_vp] * 4 + [i] + [_vp] * 3 + [_vp]
+    L.dbd_commit_block.restype = i
     L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
     L.dbd_round.restype = i
     L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
@@ -165,6 +170,54 @@ def dbd_attn_paged(q, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len, ou
     return out
 
 
+def dbd_attn_paged_save(q, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len, seq_state,
+                        out, softmax_scale=0.0, ws=None, stream=None):
+    """dbd_attn_paged, and the block K/V of SAVING sequences written into
+    k_cache / v_cache (in place) at positions prefix_len + j."""
+    S, B, Hq, D = q.shape
+    Hkv = k_blk.shape[2]
+    npages, _, P, _ = k_cache.shape
+    maxp = page_table.shape[1]
+    for t, n in ((q, "q"), (k_cache, "k_cache")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous bf16")
+    _need(k_blk, torch.bfloat16, (S, B, Hkv, D), "k_blk")
+    _need(v_blk, torch.bfloat16, (S, B, Hkv, D), "v_blk")
+    _need(v_cache, torch.bfloat16, tuple(k_cache.shape), "v_cache")
+    _need(out, torch.bfloat16, (S, B, Hq, D), "out")
+    _need(page_table, torch.int32, (S, maxp), "page_table")
+    _need(prefix_len, torch.int32, (S,), "prefix_len")
+    _need(seq_state, torch.uint8, (S,), "seq_state")
+    need = dbd_attn_workspace_size(S, B, Hq, Hkv, D, P, maxp)
+    if ws is None and need:
+        ws = workspace(need, q.device)
+    nbytes = ws.numel() if ws is not None else 0
+    _check(lib().dbd_attn_paged_save(S, B, Hq, Hkv, D, P, maxp, npages, _ptr(q), _ptr(k_blk),
+                                     _ptr(v_blk), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                     _ptr(prefix_len), _ptr(seq_state), float(softmax_scale),
+                                     _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def dbd_commit_block(block_tokens, seq_state, prefix_len, row_index_out, num_rows_out,
+                     mask_token_id, token_stream=None, end_len=None, stream=None):
+    S, B = block_tokens.shape
+    _need(block_tokens, torch.int32, (S, B), "block_tokens")
+    _need(seq_state, torch.uint8, (S,), "seq_state")
+    _need(prefix_len, torch.int32, (S,), "prefix_len")
+    _need(row_index_out, torch.int32, (S * B,), "row_index_out")
+    _need(num_rows_out, torch.int32, (1,), "num_rows_out")
+    cap = 0
+    if token_stream is not None:
+        _need(token_stream, torch.int32, (S, token_stream.shape[1]), "token_stream")
+        cap = token_stream.shape[1]
+    if end_len is not None:
+        _need(end_len, torch.int32, (S,), "end_len")
+    _check(lib().dbd_commit_block(S, B, int(mask_token_id), _ptr(block_tokens), _ptr(seq_state),
+                                  _ptr(prefix_len), _ptr(token_stream), cap, _ptr(end_len),
+                                  _ptr(row_index_out), _ptr(num_rows_out), _stream(stream)))
+
+
 def dbd_lmhead_conf(hidden, w_vocab, num_rows, argmax_tok, conf, mask_token_id,
                     row_index=None, max_rows=None, ws=None, stream=None, entropy=None):
     """entropy (float32, optional): also each listed row's softmax entropy
@@ -244,7 +297,10 @@ def make_round_args(*, S, B, Hq, Hkv, D, page_size, max_pages_per_seq, Hd, V, ma
                     dynamic_threshold, q, k_blk, v_blk, k_cache, v_cache, page_table,
                     prefix_len, attn_out, hidden, w_vocab, bufs: RoundBuffers, flags=0,
                     softmax_scale=0.0, rule=0, tokens_per_step=1, eb_threshold=0.0,
-                    entropy=None) -> dbd_round_args:
+                    entropy=None, save_kv=False, token_stream=None,
+                    end_len=None) -> dbd_round_args:
+    """save_kv: the round is a whole step for a batch with SAVING sequences
+    (their block K/V go into the cache, their blocks are committed)."""
     a = dbd_round_args()
     a.S, a.B, a.Hq, a.Hkv, a.D = S, B, Hq, Hkv, D
     a.page_size, a.max_pages_per_seq, a.Hd, a.V = page_size, max_pages_per_seq, Hd, V
@@ -260,6 +316,11 @@ def make_round_args(*, S, B, Hq, Hkv, D, page_size, max_pages_per_seq, Hd, V, ma
     a.workspace_bytes = bufs.workspace.numel()
     a.rule, a.tokens_per_step, a.eb_threshold = rule, tokens_per_step, eb_threshold
     a.entropy = _ptr(entropy)
+    a.save_kv = int(bool(save_kv))
+    a.num_pages = int(k_cache.shape[0]) if save_kv else 0
+    a.token_stream = _ptr(token_stream)
+    a.stream_cap = int(token_stream.shape[1]) if token_stream is not None else 0
+    a.end_len = _ptr(end_len)
     return a
 
 

@@ -34,6 +34,15 @@
 //     ds_read_b64_tr_b16.
 // Keys past the end of a prefix or block are masked to -inf; their loads
 // re-read a valid key, so nothing past a page or buffer is touched.
+//
+// SAVING forward (the SAVE instances): the forward over a finished block
+// also stores the block's keys and values into the sequence's pages at
+// positions prefix_len + j (JetEngine developer notes, "Important
+// Patterns": the SAVING forward writes the final block into the KV cache;
+// "Optimization History": one kernel both writes the cache and attends).
+// The wave that consumes a block tile of row group 0 copies the tile's
+// valid rows from LDS to the cache after computing on it.  Nothing in the
+// same launch reads those slots: prefix reads stop below prefix_len.
 #include <algorithm>
 
 #include "dbd_device.hpp"
@@ -61,6 +70,7 @@ constexpr int kRing = ATTN_RING;       // ring slots per wave
 constexpr int kMaxWavesPerCU = ATTN_WAVES;
 constexpr int kCUs = 256;      // MI355X compute units
 constexpr int kLdsPerCU = 160 * 1024;
+constexpr int kSavingState = 3;   // sequence state SAVING
 
 // chunk permutation of row r (D=128: 16 chunks per row; D=64: 8)
 template <int D>
@@ -128,6 +138,14 @@ __device__ __forceinline__ void wait_vm() {
 // all of this wave's LDS reads (and scalar loads) have returned
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// state of sequence s through the scalar cache: the aligned dword holding
+// byte s (the state array is 16-byte aligned, so that dword never crosses
+// the end of the page holding byte s)
+__device__ __forceinline__ int state_of(const uint8_t* st, int s) {
+  const uint32_t w = (uint32_t)ldc(reinterpret_cast<const int32_t*>(st), (size_t)(s >> 2));
+  return (int)((w >> (8 * (s & 3))) & 0xFFu);
+}
+
 struct Dec {      // a position in the tile stream
   int s, hg, j;   // sequence, segment within the sequence, tile within the segment
   int L, nP, tiles;
@@ -168,7 +186,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int RT, int NR>
+template <int D, int RT, int NR, bool SAVE>
 __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   using Gm = Geo<D, RT>;
   constexpr int ROWS = Gm::ROWS, KS = Gm::KS, DT = Gm::DT, KV = Gm::KV;
@@ -314,6 +332,32 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
     }
   };
 
+  // SAVING forward: copy the valid rows of block tile dc (K and V, in LDS)
+  // to the cache at positions L + key; lane l moves 16-byte chunks l,
+  // l+64, ... of each run of 16 rows
+  auto save_tile = [&](const lds_u16* slot) {
+    const int g = dc.hg / a.n_rg;
+    const int kb = kKT * (dc.j - dc.nP);
+#pragma unroll
+    for (int hh = 0; hh < kKT / 16; ++hh) {
+      const int nvalid = min(16, a.B - (kb + 16 * hh));
+#pragma unroll
+      for (int i = lane; i < 16 * Gm::LPR; i += 64) {
+        const int r = i / Gm::LPR, c = i % Gm::LPR;
+        if (r >= nvalid) continue;
+        const int pos = dc.L + kb + 16 * hh + r;
+        const int pidx = pos / a.P;
+        if (pidx >= a.max_pages) continue;
+        const int page = a.page_table[(size_t)dc.s * a.max_pages + pidx];
+        if (page < 0 || page >= a.num_pages) continue;
+        const size_t dst = (((size_t)page * a.Hkv + g) * a.P + pos % a.P) * D + c * 8;
+        const int src = hh * 16 * D + eoff<D>(r, c);
+        *reinterpret_cast<u32x4*>(a.k_cache_out + dst) = *(const lds_u32x4*)(slot + src);
+        *reinterpret_cast<u32x4*>(a.v_cache_out + dst) = *(const lds_u32x4*)(slot + KV + src);
+      }
+    }
+  };
+
   auto consume = [&](const lds_u16* slot, int k) INL {
     // every tile issues at least 2*D/32 loads (K and V) and NR-1 tiles were
     // issued after this one: waiting down to that many leaves this slot done
@@ -405,6 +449,9 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
         for (int rt = 0; rt < RT; ++rt)
           acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
       }
+    }
+    if constexpr (SAVE) {
+      if (dc.j >= dc.nP && dc.hg % a.n_rg == 0 && state_of(a.save_state, dc.s) == kSavingState) save_tile(slot);
     }
   };
 
@@ -523,7 +570,10 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
 template <int D, int RT>
 static hipError_t launch_dr(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
   attn_plan_kernel<<<1, 1024, 0, st>>>(a);
-  attn_stream_kernel<D, RT, kRing><<<p.grid, 64, 0, st>>>(a);
+  if (a.save_state != nullptr)
+    attn_stream_kernel<D, RT, kRing, true><<<p.grid, 64, 0, st>>>(a);
+  else
+    attn_stream_kernel<D, RT, kRing, false><<<p.grid, 64, 0, st>>>(a);
   attn_combine_kernel<D, RT><<<a.S * a.Hkv * p.n_rg, 256, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -80,7 +80,9 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
                         const dbd_bf16* k_cache, const dbd_bf16* v_cache,
                         const int32_t* page_table, const int32_t* prefix_len,
                         float scale, dbd_bf16* out, void* ws, size_t ws_bytes,
-                        hipStream_t st) {
+                        hipStream_t st, const uint8_t* save_state = nullptr,
+                        dbd_bf16* kc_out = nullptr, dbd_bf16* vc_out = nullptr,
+                        int num_pages = 0) {
   dbd::AttnPlan plan = dbd::attn_plan(S, B, Hq, Hkv, D, P, max_pages);
   if (ws == nullptr || ws_bytes < plan.ws_bytes)
     return fail(DBD_ERR_WORKSPACE, "attention workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
@@ -96,6 +98,8 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
   a.n_rg = plan.n_rg; a.maxp = plan.maxp; a.grid = plan.grid;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
+  a.save_state = save_state; a.k_cache_out = kc_out; a.v_cache_out = vc_out;
+  a.num_pages = num_pages;
   hipError_t e = dbd::attn_launch(plan, a, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return DBD_OK;
@@ -130,7 +134,9 @@ dbd_status enqueue_remask(int S, int B, int mask, float tau, uint32_t flags, int
                           int32_t* block_tokens, uint8_t* seq_state,
                           const int32_t* argmax_tok, const float* conf,
                           int32_t* row_index_out, int32_t* num_rows_out,
-                          int32_t* num_committed, hipStream_t st) {
+                          int32_t* num_committed, hipStream_t st,
+                          int32_t* prefix_len = nullptr, int32_t* token_stream = nullptr,
+                          int stream_cap = 0, const int32_t* end_len = nullptr) {
   dbd::RemaskArgs a{};
   a.S = S; a.B = B; a.mask_id = mask; a.tau = tau; a.flags = flags;
   a.rule = rule; a.k = k < 1 ? 1 : k; a.eb = eb; a.entropy = entropy;
@@ -138,6 +144,8 @@ dbd_status enqueue_remask(int S, int B, int mask, float tau, uint32_t flags, int
   a.argmax_tok = argmax_tok; a.conf = conf;
   a.row_index_out = row_index_out; a.num_rows_out = num_rows_out;
   a.num_committed = num_committed;
+  a.prefix_len = prefix_len; a.token_stream = token_stream; a.stream_cap = stream_cap;
+  a.end_len = end_len;
   hipError_t e = dbd::remask_launch(a, st);
   if (e != hipSuccess) return hip_fail(e, "remask launch");
   return DBD_OK;
@@ -167,6 +175,14 @@ dbd_status check_round(const dbd_round_args* a) {
   REQUIRE_PTR(a->hidden); REQUIRE_PTR(a->w_vocab); REQUIRE_PTR(a->row_index);
   REQUIRE_PTR(a->num_rows); REQUIRE_PTR(a->argmax_tok); REQUIRE_PTR(a->conf);
   REQUIRE_PTR(a->block_tokens); REQUIRE_PTR(a->seq_state);
+  if (a->save_kv) {
+    REQUIRE(a->num_pages >= 1, "num_pages must be >= 1 with save_kv (got %d)", a->num_pages);
+    if (a->token_stream != nullptr) {
+      REQUIRE_PTR(a->token_stream);
+      REQUIRE(a->stream_cap >= 1, "stream_cap must be >= 1 (got %d)", a->stream_cap);
+    }
+    if (a->end_len != nullptr) REQUIRE_PTR(a->end_len);
+  }
   const size_t need = dbd_round_workspace_size(a);
   if (a->workspace == nullptr || a->workspace_bytes < need)
     return fail(DBD_ERR_WORKSPACE, "round workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
@@ -178,19 +194,28 @@ dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
   const dbd::AttnPlan plan = dbd::attn_plan(a->S, a->B, a->Hq, a->Hkv, a->D, a->page_size, a->max_pages_per_seq);
   const size_t attn_ws = round_up(plan.ws_bytes);
   char* ws = static_cast<char*>(a->workspace);
+  // with save_kv the caller's cache and prefix lengths are writable (dbd.h)
+  const bool save = a->save_kv != 0;
   dbd_status s = enqueue_attn(a->S, a->B, a->Hq, a->Hkv, a->D, a->page_size, a->max_pages_per_seq,
                               a->q, a->k_blk, a->v_blk, a->k_cache, a->v_cache, a->page_table,
-                              a->prefix_len, a->softmax_scale, a->attn_out, ws, plan.ws_bytes, st);
+                              a->prefix_len, a->softmax_scale, a->attn_out, ws, plan.ws_bytes, st,
+                              save ? a->seq_state : nullptr,
+                              save ? const_cast<dbd_bf16*>(a->k_cache) : nullptr,
+                              save ? const_cast<dbd_bf16*>(a->v_cache) : nullptr, a->num_pages);
   if (s != DBD_OK) return s;
   const int max_rows = a->S * a->B;
   float* ent = a->rule == DBD_RULE_ENTROPY_BOUNDED ? a->entropy : nullptr;
   s = enqueue_lm(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index, a->num_rows,
                  a->w_vocab, a->argmax_tok, a->conf, ent, ws + attn_ws, a->workspace_bytes - attn_ws, st);
   if (s != DBD_OK) return s;
-  return enqueue_remask(a->S, a->B, a->mask_token_id, a->dynamic_threshold, a->flags & ~DBD_COMPACT_ONLY,
+  const uint32_t fl = (a->flags & ~DBD_COMPACT_ONLY) | (save ? dbd::kCommitSaving : 0u);
+  return enqueue_remask(a->S, a->B, a->mask_token_id, a->dynamic_threshold, fl,
                         a->rule, a->tokens_per_step, a->eb_threshold, ent,
                         a->block_tokens, a->seq_state, a->argmax_tok, a->conf, a->row_index,
-                        a->num_rows, a->num_committed, st);
+                        a->num_rows, a->num_committed, st,
+                        save ? const_cast<int32_t*>(a->prefix_len) : nullptr,
+                        save ? a->token_stream : nullptr, a->stream_cap,
+                        save ? a->end_len : nullptr);
 }
 
 }  // namespace
@@ -239,6 +264,46 @@ dbd_status dbd_attn_paged(int S, int B, int Hq, int Hkv, int D, int page_size,
   return enqueue_attn(S, B, Hq, Hkv, D, page_size, max_pages_per_seq, q, k_blk, v_blk, k_cache,
                       v_cache, page_table, prefix_len, softmax_scale, out, workspace,
                       workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_attn_paged_save(int S, int B, int Hq, int Hkv, int D, int page_size,
+                               int max_pages_per_seq, int num_pages, const dbd_bf16* q,
+                               const dbd_bf16* k_blk, const dbd_bf16* v_blk, dbd_bf16* k_cache,
+                               dbd_bf16* v_cache, const int32_t* page_table,
+                               const int32_t* prefix_len, const uint8_t* seq_state,
+                               float softmax_scale, dbd_bf16* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  dbd_status s = check_attn(S, B, Hq, Hkv, D, page_size, max_pages_per_seq);
+  if (s != DBD_OK) return s;
+  REQUIRE(num_pages >= 1, "num_pages must be >= 1 (got %d)", num_pages);
+  REQUIRE_PTR(q); REQUIRE_PTR(k_blk); REQUIRE_PTR(v_blk); REQUIRE_PTR(k_cache);
+  REQUIRE_PTR(v_cache); REQUIRE_PTR(page_table); REQUIRE_PTR(prefix_len);
+  REQUIRE_PTR(seq_state); REQUIRE_PTR(out);
+  REQUIRE(!isnan(softmax_scale), "softmax_scale is NaN");
+  return enqueue_attn(S, B, Hq, Hkv, D, page_size, max_pages_per_seq, q, k_blk, v_blk, k_cache,
+                      v_cache, page_table, prefix_len, softmax_scale, out, workspace,
+                      workspace_bytes, static_cast<hipStream_t>(stream), seq_state, k_cache,
+                      v_cache, num_pages);
+}
+
+dbd_status dbd_commit_block(int S, int B, int mask_token_id, int32_t* block_tokens,
+                            uint8_t* seq_state, int32_t* prefix_len, int32_t* token_stream,
+                            int stream_cap, const int32_t* end_len, int32_t* row_index_out,
+                            int32_t* num_rows_out, void* stream) {
+  dbd_status s = check_remask(S, B, 0.f);
+  if (s != DBD_OK) return s;
+  REQUIRE_PTR(block_tokens); REQUIRE_PTR(seq_state); REQUIRE_PTR(prefix_len);
+  REQUIRE_PTR(row_index_out); REQUIRE_PTR(num_rows_out);
+  if (token_stream != nullptr) {
+    REQUIRE_PTR(token_stream);
+    REQUIRE(stream_cap >= 1, "stream_cap must be >= 1 (got %d)", stream_cap);
+  }
+  if (end_len != nullptr) REQUIRE_PTR(end_len);
+  return enqueue_remask(S, B, mask_token_id, 0.f, DBD_COMPACT_ONLY | dbd::kCommitSaving,
+                        DBD_RULE_LOW_CONF_DYNAMIC, 1, 0.f, nullptr, block_tokens, seq_state,
+                        nullptr, nullptr, row_index_out, num_rows_out, nullptr,
+                        static_cast<hipStream_t>(stream), prefix_len, token_stream, stream_cap,
+                        end_len);
 }
 
 dbd_status dbd_lmhead_conf(int max_rows, int Hd, int V, int mask_token_id,

@@ -25,6 +25,13 @@ struct AttnArgs {
   int maxp;        // partial slots per segment
   int grid;        // workgroups (single waves) of the stream kernel
   float scale_log2;
+  // SAVING forward: when save_state is set, the block keys and values of
+  // every sequence whose state is SAVING are also written into its pages at
+  // positions prefix_len + j (pages outside [0, num_pages) are skipped)
+  const uint8_t* save_state;
+  uint16_t* k_cache_out;   // the same buffers as k_cache, v_cache
+  uint16_t* v_cache_out;
+  int num_pages;
 };
 
 struct AttnPlan {
@@ -76,9 +83,17 @@ struct RemaskArgs {
   int32_t* row_index_out;
   int32_t* num_rows_out;
   int32_t* num_committed;
+  // block commit of sequences SAVING on entry (flags & kCommitSaving)
+  int32_t* prefix_len;        // in/out
+  int32_t* token_stream;      // [S][stream_cap], may be NULL
+  int stream_cap;
+  const int32_t* end_len;     // [S], may be NULL
 };
 
 constexpr int kRemaskMaxSeqs = 8192;
+// internal remask flag (beside the public DBD_FALLBACK_LEFTMOST = 1 and
+// DBD_COMPACT_ONLY = 2): commit the blocks of sequences SAVING on entry
+constexpr uint32_t kCommitSaving = 4u;
 hipError_t remask_launch(const RemaskArgs& a, hipStream_t stream);
 
 }  // namespace dbd

@@ -15,6 +15,16 @@
 //     sum stays within the budget, at least one.
 // Confidences, entropies and the threshold are compared in float32.
 //
+// Block commit (kCommitSaving): a sequence that is SAVING on entry has had
+// its SAVING forward (the attention launch wrote its block into the KV
+// cache), so its block is committed (developer notes, "Sequence":
+// commit_block puts the block into the token stream): the block goes to
+// token_stream[s][prefix_len .. prefix_len+B-1] (positions past the
+// stream's capacity are dropped), prefix_len grows by B, and the sequence
+// starts a new all-mask block in DENOISING, or is FINISHED (keeping its
+// block) once prefix_len reaches end_len[s].  A sequence that the rule
+// fills in this launch stays SAVING until its own SAVING forward.
+//
 // One workgroup of 16 waves.  Pass 1: a wave per sequence, lane = block
 // position (B <= 64): ballots of the masked set; the rule's choice is built
 // one wave-wide selection at a time (max or min, then the lowest lane).
@@ -29,7 +39,7 @@ namespace dbd {
 
 constexpr uint32_t kFallbackLeftmost = 1u;
 constexpr uint32_t kCompactOnly = 2u;
-constexpr uint8_t kDenoising = 2, kSaving = 3;
+constexpr uint8_t kDenoising = 2, kSaving = 3, kFinished = 4;
 
 __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
   __shared__ unsigned long long s_left[kRemaskMaxSeqs];
@@ -43,6 +53,22 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
   for (int s = wave; s < S; s += 16) {
     const uint8_t st = a.seq_state[s];  // same for every lane of the wave
     const bool in = lane < B;
+    if (st == kSaving && (a.flags & kCommitSaving)) {
+      const int L = a.prefix_len[s];
+      if (a.token_stream != nullptr && in && L + lane >= 0 && L + lane < a.stream_cap)
+        a.token_stream[(size_t)s * a.stream_cap + L + lane] = a.block_tokens[s * B + lane];
+      const int L2 = L + B;
+      const bool fin = a.end_len != nullptr && L2 >= a.end_len[s];
+      if (in && !fin) a.block_tokens[s * B + lane] = a.mask_id;
+      if (lane == 0) {
+        a.prefix_len[s] = L2;
+        a.seq_state[s] = fin ? kFinished : kDenoising;
+        if (a.num_committed && !(a.flags & kCompactOnly)) a.num_committed[s] = 0;
+      }
+      const unsigned long long fresh = __ballot(in && !fin);
+      if (lane == 0) s_left[s] = fresh;
+      continue;
+    }
     const bool den = st == kDenoising;
     const bool masked = in && den && a.block_tokens[s * B + lane] == a.mask_id;
     const unsigned long long mball = __ballot(masked);

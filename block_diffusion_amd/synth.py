@@ -124,13 +124,15 @@ def prefix_lengths(w: Workload) -> np.ndarray:
     return g.integers(w.prefix_lo, w.prefix_hi + 1, size=w.S).astype(np.int32)
 
 
-def page_layout(w: Workload, prefix_len: np.ndarray):
+def page_layout(w: Workload, prefix_len: np.ndarray, reserve_tokens: int = 0):
     """Physical page ids: a seeded permutation of all pages the prefixes
-    need, so that logical order and physical order differ."""
-    npg = [(-(-int(L) // w.P)) for L in prefix_len]
+    need (plus room for reserve_tokens more tokens per sequence, for blocks
+    that later steps append), so that logical order and physical order
+    differ."""
+    npg = [(-(-(int(L) + reserve_tokens) // w.P)) for L in prefix_len]
     total = int(sum(npg))
     perm = rng(w, 0, ST_PAGES).permutation(total).astype(np.int32)
-    table = np.full((w.S, w.max_pages), -1, dtype=np.int32)
+    table = np.full((w.S, max(w.max_pages, max(npg))), -1, dtype=np.int32)
     o = 0
     for s, n in enumerate(npg):
         table[s, :n] = perm[o:o + n]
@@ -138,15 +140,17 @@ def page_layout(w: Workload, prefix_len: np.ndarray):
     return table, total
 
 
-def make_fixed(w: Workload, poison_tail: bool = True, with_w: bool = True) -> Fixed:
+def make_fixed(w: Workload, poison_tail: bool = True, with_w: bool = True,
+               reserve_tokens: int = 0) -> Fixed:
     L = prefix_lengths(w)
-    table, npages = page_layout(w, L)
+    table, npages = page_layout(w, L, reserve_tokens)
     shape = (npages, w.Hkv, w.P, w.D)
     kc = normal_bf16(key(w, 0, ST_KCACHE), shape)
     vc = normal_bf16(key(w, 0, ST_VCACHE), shape)
     if poison_tail:
-        # slots past a prefix's end inside its last page are never part of
-        # the prefix; fill them with NaN so any read of them shows up.
+        # slots past a prefix's end (the rest of its last page and any
+        # reserved page) are not part of the prefix; fill them with NaN so
+        # any read of them shows up.
         for s in range(w.S):
             n = (-(-int(L[s]) // w.P))
             tail = int(L[s]) - (n - 1) * w.P
@@ -154,6 +158,10 @@ def make_fixed(w: Workload, poison_tail: bool = True, with_w: bool = True) -> Fi
                 p = table[s, n - 1]
                 kc[p, :, tail:, :] = BF16_QNAN
                 vc[p, :, tail:, :] = BF16_QNAN
+            for p in table[s, n:]:
+                if p >= 0:
+                    kc[p] = BF16_QNAN
+                    vc[p] = BF16_QNAN
     wv = normal_bf16(key(w, 0, ST_W), (w.V, w.Hd), std=1.0 / np.sqrt(w.Hd)) if with_w else None
     toks = np.full((w.S, w.B), w.mask_id, dtype=np.int32)
     if w.init_committed_max > 0:

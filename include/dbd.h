@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define DBD_ABI_VERSION 2
+#define DBD_ABI_VERSION 3
 
 typedef uint16_t dbd_bf16;
 
@@ -106,6 +106,42 @@ dbd_status dbd_attn_paged(int S, int B, int Hq, int Hkv, int D, int page_size,
 
 size_t dbd_attn_workspace_size(int S, int B, int Hq, int Hkv, int D,
                                int page_size, int max_pages_per_seq);
+
+/* ------------------------------------------------------------------------
+ * dbd_attn_paged_save -- dbd_attn_paged for a batch that holds SAVING
+ * sequences: the same attention for every sequence, and, in the same
+ * kernel, the block keys and values of every sequence whose seq_state is
+ * DBD_SAVING written into its pages.
+ *
+ * Defined by the SAVING forward (JetEngine developer notes, "Important
+ * Patterns": a finished block runs one more forward that writes its final
+ * representations into the KV cache, and skipping it corrupts the cache;
+ * "Optimization History": the FA3 kernel writes the cache and attends in
+ * one kernel) and the cache addressing of dbd_attn_paged:
+ *   for s with seq_state[s] == DBD_SAVING, j < B, p = prefix_len[s] + j:
+ *     k_cache[page_table[s][p / page_size]][g][p % page_size][:] = k_blk[s][j][g][:]
+ *     v_cache[...same...]                                         = v_blk[s][j][g][:]
+ *   for every kv head g.  prefix_len is not changed (dbd_commit_block
+ *   advances it).
+ * The caller assigns the pages that cover positions prefix_len[s] ..
+ * prefix_len[s]+B-1 of each SAVING sequence before the call; a position
+ * whose page index reaches max_pages_per_seq or whose page id lies outside
+ * [0, num_pages) is not written (the kernel never writes outside the
+ * cache).  The attention reads no slot at or past prefix_len, so the writes
+ * do not affect this call's out.  seq_state: uint8 [S], read only.  Every
+ * other argument, layout and requirement as dbd_attn_paged; workspace size
+ * dbd_attn_workspace_size(...).
+ * ---------------------------------------------------------------------- */
+dbd_status dbd_attn_paged_save(int S, int B, int Hq, int Hkv, int D,
+                               int page_size, int max_pages_per_seq,
+                               int num_pages, const dbd_bf16* q,
+                               const dbd_bf16* k_blk, const dbd_bf16* v_blk,
+                               dbd_bf16* k_cache, dbd_bf16* v_cache,
+                               const int32_t* page_table,
+                               const int32_t* prefix_len,
+                               const uint8_t* seq_state, float softmax_scale,
+                               dbd_bf16* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * dbd_lmhead_conf -- selective LM head fused with the softmax.
@@ -221,6 +257,37 @@ dbd_status dbd_remask_commit_rule(int S, int B, int mask_token_id, int rule,
                                   int32_t* num_committed, void* stream);
 
 /* ------------------------------------------------------------------------
+ * dbd_commit_block -- commit the blocks of SAVING sequences and rebuild the
+ * row list.
+ *
+ * Defined by commit_block (JetEngine developer notes, "Sequence": a denoised
+ * block is moved into the sequence's token stream) and the state machine
+ * ("Scheduler": ... -> DENOISING -> SAVING -> FINISHED; "Chain Mechanism":
+ * chains run across SAVING into the next block).  Call it after the SAVING
+ * forward (dbd_attn_paged_save).  For each s with seq_state[s] == SAVING:
+ *   token_stream[s][prefix_len[s] + j] = block_tokens[s][j]  for j < B and
+ *       prefix_len[s] + j < stream_cap (token_stream may be NULL);
+ *   prefix_len[s] += B;
+ *   if end_len != NULL and prefix_len[s] >= end_len[s]:
+ *       seq_state[s] = DBD_FINISHED (block_tokens[s] kept);
+ *   else: block_tokens[s][:] = mask_token_id, seq_state[s] = DBD_DENOISING.
+ * Other sequences are untouched.  Then, as dbd_remask_commit with
+ * DBD_COMPACT_ONLY, row_index_out / *num_rows_out list every masked
+ * position of every DENOISING sequence (the new blocks included).
+ * Layouts: block_tokens int32 [S][B], seq_state uint8 [S], prefix_len int32
+ * [S] (all in/out); token_stream int32 [S][stream_cap]; end_len int32 [S];
+ * row_index_out int32 [S*B].
+ * Requirements: as dbd_remask_commit; stream_cap >= 1 when token_stream is
+ * given.
+ * ---------------------------------------------------------------------- */
+dbd_status dbd_commit_block(int S, int B, int mask_token_id,
+                            int32_t* block_tokens, uint8_t* seq_state,
+                            int32_t* prefix_len, int32_t* token_stream,
+                            int stream_cap, const int32_t* end_len,
+                            int32_t* row_index_out, int32_t* num_rows_out,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
  * dbd_round -- one whole denoise round: dbd_attn_paged, then
  * dbd_lmhead_conf on the row list (row_index, *num_rows), then
  * dbd_remask_commit, which overwrites (row_index, *num_rows) with the next
@@ -254,6 +321,21 @@ typedef struct dbd_round_args {
   int tokens_per_step;
   float eb_threshold;
   float* entropy; /* float [S*B]; required for DBD_RULE_ENTROPY_BOUNDED */
+  /* SAVING step.  With save_kv != 0 the round is a whole scheduler step for
+   * a batch that mixes DENOISING and SAVING sequences: the attention is
+   * dbd_attn_paged_save (SAVING sequences' block K/V go into their pages),
+   * the LM head projects the listed rows, and the remask kernel commits
+   * the rule for sequences DENOISING on entry and, for those SAVING on
+   * entry, the block commit of dbd_commit_block (token_stream, stream_cap,
+   * end_len as there).  A sequence that the rule fills stays SAVING until
+   * the next step's SAVING forward.  k_cache, v_cache and prefix_len are
+   * then written and must be writable; num_pages bounds the page ids
+   * written.  save_kv == 0: none of these fields is read. */
+  int save_kv;
+  int num_pages;
+  int32_t* token_stream; /* may be NULL */
+  int stream_cap;
+  const int32_t* end_len; /* may be NULL */
 } dbd_round_args;
 
 dbd_status dbd_round(const dbd_round_args* a, void* stream);

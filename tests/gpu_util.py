@@ -152,6 +152,7 @@ class RoundState:
                           page_table=dev_i32(fx.page_table), prefix_len=dev_i32(fx.prefix_len),
                           w_vocab=dev_bf16(fx.w_vocab))
         self.w = w
+        self.maxp = int(fx.page_table.shape[1])
 
     def init_rows(self):
         b = self.bufs
@@ -162,14 +163,14 @@ class RoundState:
         w = self.w
         a = api.make_round_args(
             S=w.S, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, page_size=w.P,
-            max_pages_per_seq=w.max_pages, Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
+            max_pages_per_seq=self.maxp, Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
             dynamic_threshold=w.tau, attn_out=attn_out, bufs=self.bufs, **rin_dev, **self.fixed)
         need = api.dbd_round_workspace_size(a)
         if self.bufs.workspace.numel() < need:
             self.bufs.workspace = torch.empty(need, dtype=torch.uint8, device="cuda")
             a = api.make_round_args(
                 S=w.S, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, page_size=w.P,
-                max_pages_per_seq=w.max_pages, Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
+                max_pages_per_seq=self.maxp, Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
                 dynamic_threshold=w.tau, attn_out=attn_out, bufs=self.bufs, **rin_dev,
                 **self.fixed)
         return a

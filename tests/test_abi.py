@@ -26,6 +26,7 @@ def test_header_declares_the_round_calls():
     names = declared_functions()
     for n in ("dbd_attn_paged", "dbd_lmhead_conf", "dbd_remask_commit", "dbd_round",
               "dbd_lmhead_conf_entropy", "dbd_remask_commit_rule",
+              "dbd_attn_paged_save", "dbd_commit_block",
               "dbd_graph_create", "dbd_graph_launch", "dbd_graph_destroy",
               "dbd_attn_workspace_size", "dbd_lmhead_workspace_size",
               "dbd_round_workspace_size", "dbd_validate_inputs", "dbd_last_error",
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(lib, n)
-    assert api.dbd_abi_version() == 2
+    assert api.dbd_abi_version() == 3
 
 
 def _attn(**kw):
@@ -98,6 +99,36 @@ def test_lmhead_rejects(args, status):
     assert L.dbd_lmhead_conf(*args, 16, None, 16, 16, 16, 16, 256, 1 << 20, None) == status
 
 
+def _save(**kw):
+    a = dict(S=2, B=4, Hq=4, Hkv=2, D=64, P=16, maxp=3, npages=6, state=16, kc=16)
+    a.update(kw)
+    return api.lib().dbd_attn_paged_save(a["S"], a["B"], a["Hq"], a["Hkv"], a["D"], a["P"],
+                                         a["maxp"], a["npages"], 16, 16, 16, a["kc"], 16, 16, 16,
+                                         a["state"], 0.0, 16, None, 0, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), api.DBD_ERR_INVALID_ARG), (dict(D=96), api.DBD_ERR_UNSUPPORTED),
+    (dict(npages=0), api.DBD_ERR_INVALID_ARG), (dict(state=None), api.DBD_ERR_INVALID_ARG),
+    (dict(kc=None), api.DBD_ERR_INVALID_ARG), (dict(state=17), api.DBD_ERR_INVALID_ARG),
+    (dict(), api.DBD_ERR_WORKSPACE)])
+def test_attn_save_rejects(kw, status):
+    assert _save(**kw) == status
+
+
+@pytest.mark.parametrize("S,B,prefix,stream,cap,end,status", [
+    (0, 4, 16, None, 0, None, api.DBD_ERR_INVALID_ARG),
+    (2, 65, 16, None, 0, None, api.DBD_ERR_INVALID_ARG),
+    (2, 4, None, None, 0, None, api.DBD_ERR_INVALID_ARG),     # prefix_len is written
+    (2, 4, 16, 16, 0, None, api.DBD_ERR_INVALID_ARG),         # a stream needs a capacity
+    (2, 4, 16, 18, 8, None, api.DBD_ERR_INVALID_ARG),         # misaligned stream
+    (2, 4, 16, None, 0, 20, api.DBD_ERR_INVALID_ARG)])        # misaligned end lengths
+def test_commit_block_rejects(S, B, prefix, stream, cap, end, status):
+    L = api.lib()
+    st = L.dbd_commit_block(S, B, 5, 16, 16, prefix, stream, cap, end, 16, 16, None)
+    assert st == status and L.dbd_last_error()
+
+
 def test_lmhead_workspace_required():
     L = api.lib()
     assert L.dbd_lmhead_conf(16, 128, 1024, 5, 16, None, 16, 16, 16, 16, None, 0, None) == api.DBD_ERR_WORKSPACE
@@ -146,6 +177,20 @@ def test_round_rejects():
     with pytest.raises(api.DbdError) as e:
         api.dbd_round(a, stream=0)
     assert e.value.status == api.DBD_ERR_INVALID_ARG
+    # a SAVING step needs the page count it may write to
+    a.rule = 0
+    for n in ("q", "k_blk", "v_blk", "k_cache", "v_cache", "page_table", "prefix_len",
+              "attn_out", "hidden", "w_vocab", "row_index", "num_rows", "argmax_tok", "conf",
+              "block_tokens", "seq_state"):
+        setattr(a, n, 256)
+    a.save_kv, a.num_pages = 1, 0
+    with pytest.raises(api.DbdError) as e:
+        api.dbd_round(a, stream=0)
+    assert b"num_pages" in api.lib().dbd_last_error()
+    a.num_pages, a.token_stream, a.stream_cap = 4, 256, 0
+    with pytest.raises(api.DbdError) as e:
+        api.dbd_round(a, stream=0)
+    assert b"stream_cap" in api.lib().dbd_last_error()
 
 
 def test_validate_inputs():
