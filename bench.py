@@ -107,7 +107,8 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     t0 = time.time()
-    fx = synth.make_fixed(w)
+    # room for one more block per sequence, which the SAVING step writes
+    fx = synth.make_fixed(w, reserve_tokens=w.B)
     rins = [synth.make_round(w, r, fx.w_vocab) for r in range(1, w.rounds + 1)]
     log(f"inputs generated in {time.time() - t0:.1f}s")
 
@@ -129,7 +130,7 @@ def main():
         workspace=torch.empty(1, dtype=torch.uint8, device=dev))
     attn_out = torch.empty((w.S, w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
     shape = dict(S=w.S, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, page_size=w.P,
-                 max_pages_per_seq=w.max_pages, Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
+                 max_pages_per_seq=int(fx.page_table.shape[1]), Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
                  dynamic_threshold=w.tau)
 
     def round_args():
@@ -217,6 +218,43 @@ def main():
     log(f"attention {t_attn:.1f} us, LM head {', '.join(f'M={m}: {t:.1f} us' for m, t in lm_times.items())}, "
         f"remask {t_remask:.1f} us")
 
+    # ---- a whole block on the device: B gated rounds, then the SAVING step
+    # (attention with the K/V write, the block commit), one graph per block
+    L0 = fixed["prefix_len"].clone()
+    loop_args = []
+    for i in range(w.B):
+        a = api.make_round_args(**shape, **per_round[i % len(per_round)], **fixed,
+                                attn_out=attn_out, bufs=bufs)
+        a.gate_on_rows = 1
+        loop_args.append(a)
+    loop_args.append(api.make_round_args(**shape, **per_round[0], **fixed, attn_out=attn_out,
+                                         bufs=bufs, save_kv=True))
+    loop_graph = api.dbd_graph_create(loop_args)
+
+    def loop_step():
+        fixed["prefix_len"].copy_(L0)
+        reset()
+        loop_graph.launch()
+
+    for _ in range(args.warmup):
+        loop_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        loop_step()
+    torch.cuda.synchronize()
+    t_block = (time.perf_counter() - t0) * 1e6 / args.steps
+    fixed["prefix_len"].copy_(L0)
+    loop_graph.close()
+    ss_all = torch.full_like(st0, 3)
+    t_save = ev_time(lambda: api.dbd_attn_paged_save(r1["q"], r1["k_blk"], r1["v_blk"],
+                                                     fixed["k_cache"], fixed["v_cache"],
+                                                     fixed["page_table"], fixed["prefix_len"],
+                                                     ss_all, attn_out, ws=bufs.workspace))
+    log(f"block on the device ({w.B} gated rounds + SAVING step): {t_block:.1f} us, "
+        f"{w.S * w.B / t_block * 1e6:.0f} committed tokens/s; attention with the K/V write "
+        f"(every sequence SAVING): {t_save:.1f} us")
+
     # algorithmic work
     L = fx.prefix_len.astype(np.int64)
     npages = -(-L // w.P)
@@ -255,6 +293,10 @@ def main():
         "breakdown_us": {"attention": round(t_attn, 2),
                          "lmhead": {str(m): round(t, 2) for m, t in lm_times.items()},
                          "remask": round(t_remask, 2),
+                         "attention_kv_save": round(t_save, 2),
+                         "block_loop": {"rounds": w.B, "saving_step": True,
+                                        "us_per_block": round(t_block, 2),
+                                        "committed_tokens_per_s": round(w.S * w.B / t_block * 1e6, 1)},
                          "attention_roofline": {k: (round(v, 4) if isinstance(v, float) else v)
                                                 for k, v in attn_roof.items()},
                          "lmhead_roofline_M%d" % M1: {k: (round(v, 4) if isinstance(v, float) else v)

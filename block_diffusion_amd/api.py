@@ -37,7 +37,8 @@ class dbd_round_args(C.Structure):
         ("num_committed", _vp), ("workspace", _vp), ("workspace_bytes", C.c_size_t),
         ("rule", C.c_int), ("tokens_per_step", C.c_int), ("eb_threshold", C.c_float),
         ("entropy", _vp), ("save_kv", C.c_int), ("num_pages", C.c_int),
-        ("token_stream", _vp), ("stream_cap", C.c_int), ("end_len", _vp)]
+        ("token_stream", _vp), ("stream_cap", C.c_int), ("end_len", _vp),
+        ("gate_on_rows", C.c_int), ("round_counter", _vp)]
 
 
 class DbdError(RuntimeError):

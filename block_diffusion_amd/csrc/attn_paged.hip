@@ -35,6 +35,10 @@
 // Keys past the end of a prefix or block are masked to -inf; their loads
 // re-read a valid key, so nothing past a page or buffer is touched.
 //
+// Gate: with AttnArgs::gate set, all three kernels return at once when the
+// device count it points to is 0 -- a round of a device-side block loop
+// that has nothing left to denoise.
+//
 // SAVING forward (the SAVE instances): the forward over a finished block
 // also stores the block's keys and values into the sequence's pages at
 // positions prefix_len + j (JetEngine developer notes, "Important
@@ -156,6 +160,7 @@ struct Dec {      // a position in the tile stream
 // Tile prefix sums: plan[s] = sum over s' < s of (ceil(L_s'/16) + ceil(B/16)).
 __global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
   __shared__ int s_wsum[16];
+  if (a.gate != nullptr && *a.gate <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = a.S, nB = (a.B + kKT - 1) / kKT;
   const int per = (S + 1023) / 1024;
@@ -193,6 +198,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t ring_[NR * Gm::SLOT];
   lds_u16* const ring = (lds_u16*)ring_;
 
+  if (a.gate != nullptr && ldc(a.gate, 0) <= 0) return;
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int S = a.S, NHG = a.Hkv * a.n_rg, nB = (a.B + kKT - 1) / kKT;
   const int R = a.G * a.B;
@@ -503,6 +509,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
 template <int D, int RT>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   constexpr int ROWS = 16 * RT;
+  if (a.gate != nullptr && *a.gate <= 0) return;
   const int NHG = a.Hkv * a.n_rg, nB = (a.B + kKT - 1) / kKT;
   const int seg = blockIdx.x;
   const int s = seg / NHG, hg = seg % NHG;

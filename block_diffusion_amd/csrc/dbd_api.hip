@@ -82,7 +82,7 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
                         float scale, dbd_bf16* out, void* ws, size_t ws_bytes,
                         hipStream_t st, const uint8_t* save_state = nullptr,
                         dbd_bf16* kc_out = nullptr, dbd_bf16* vc_out = nullptr,
-                        int num_pages = 0) {
+                        int num_pages = 0, const int32_t* gate = nullptr) {
   dbd::AttnPlan plan = dbd::attn_plan(S, B, Hq, Hkv, D, P, max_pages);
   if (ws == nullptr || ws_bytes < plan.ws_bytes)
     return fail(DBD_ERR_WORKSPACE, "attention workspace needs %zu bytes (got %zu)", plan.ws_bytes, ws_bytes);
@@ -100,6 +100,7 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
   a.scale_log2 = sc * 1.4426950408889634f;
   a.save_state = save_state; a.k_cache_out = kc_out; a.v_cache_out = vc_out;
   a.num_pages = num_pages;
+  a.gate = gate;
   hipError_t e = dbd::attn_launch(plan, a, st);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return DBD_OK;
@@ -136,7 +137,8 @@ dbd_status enqueue_remask(int S, int B, int mask, float tau, uint32_t flags, int
                           int32_t* row_index_out, int32_t* num_rows_out,
                           int32_t* num_committed, hipStream_t st,
                           int32_t* prefix_len = nullptr, int32_t* token_stream = nullptr,
-                          int stream_cap = 0, const int32_t* end_len = nullptr) {
+                          int stream_cap = 0, const int32_t* end_len = nullptr,
+                          int32_t* round_counter = nullptr, const int32_t* rows_in = nullptr) {
   dbd::RemaskArgs a{};
   a.S = S; a.B = B; a.mask_id = mask; a.tau = tau; a.flags = flags;
   a.rule = rule; a.k = k < 1 ? 1 : k; a.eb = eb; a.entropy = entropy;
@@ -146,6 +148,7 @@ dbd_status enqueue_remask(int S, int B, int mask, float tau, uint32_t flags, int
   a.num_committed = num_committed;
   a.prefix_len = prefix_len; a.token_stream = token_stream; a.stream_cap = stream_cap;
   a.end_len = end_len;
+  a.round_counter = round_counter; a.rows_in = rows_in;
   hipError_t e = dbd::remask_launch(a, st);
   if (e != hipSuccess) return hip_fail(e, "remask launch");
   return DBD_OK;
@@ -183,6 +186,8 @@ dbd_status check_round(const dbd_round_args* a) {
     }
     if (a->end_len != nullptr) REQUIRE_PTR(a->end_len);
   }
+  REQUIRE(!(a->save_kv && a->gate_on_rows), "gate_on_rows cannot be set on a save_kv step");
+  if (a->round_counter != nullptr) REQUIRE(aligned(a->round_counter, 4), "round_counter is not 4-byte aligned");
   const size_t need = dbd_round_workspace_size(a);
   if (a->workspace == nullptr || a->workspace_bytes < need)
     return fail(DBD_ERR_WORKSPACE, "round workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
@@ -201,7 +206,8 @@ dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
                               a->prefix_len, a->softmax_scale, a->attn_out, ws, plan.ws_bytes, st,
                               save ? a->seq_state : nullptr,
                               save ? const_cast<dbd_bf16*>(a->k_cache) : nullptr,
-                              save ? const_cast<dbd_bf16*>(a->v_cache) : nullptr, a->num_pages);
+                              save ? const_cast<dbd_bf16*>(a->v_cache) : nullptr, a->num_pages,
+                              a->gate_on_rows ? a->num_rows : nullptr);
   if (s != DBD_OK) return s;
   const int max_rows = a->S * a->B;
   float* ent = a->rule == DBD_RULE_ENTROPY_BOUNDED ? a->entropy : nullptr;
@@ -215,7 +221,7 @@ dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
                         a->num_rows, a->num_committed, st,
                         save ? const_cast<int32_t*>(a->prefix_len) : nullptr,
                         save ? a->token_stream : nullptr, a->stream_cap,
-                        save ? a->end_len : nullptr);
+                        save ? a->end_len : nullptr, a->round_counter, a->num_rows);
 }
 
 }  // namespace

@@ -32,6 +32,9 @@ struct AttnArgs {
   uint16_t* k_cache_out;   // the same buffers as k_cache, v_cache
   uint16_t* v_cache_out;
   int num_pages;
+  // may be NULL; otherwise every attention kernel returns at once when
+  // *gate <= 0 (a round with no row left to denoise)
+  const int32_t* gate;
 };
 
 struct AttnPlan {
@@ -88,6 +91,9 @@ struct RemaskArgs {
   int32_t* token_stream;      // [S][stream_cap], may be NULL
   int stream_cap;
   const int32_t* end_len;     // [S], may be NULL
+  // may be NULL: incremented when *rows_in > 0 on entry (an active round)
+  int32_t* round_counter;
+  const int32_t* rows_in;
 };
 
 constexpr int kRemaskMaxSeqs = 8192;

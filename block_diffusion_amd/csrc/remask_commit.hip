@@ -48,6 +48,8 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int S = a.S, B = a.B;
+  // rows_in may alias num_rows_out: read it before pass 2 writes the count
+  if (a.round_counter != nullptr && tid == 0 && *a.rows_in > 0) *a.round_counter += 1;
 
   // pass 1: commit, state, still-masked set
   for (int s = wave; s < S; s += 16) {

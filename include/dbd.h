@@ -336,6 +336,14 @@ typedef struct dbd_round_args {
   int32_t* token_stream; /* may be NULL */
   int stream_cap;
   const int32_t* end_len; /* may be NULL */
+  /* Device-side loop control.  gate_on_rows != 0: the round's attention
+   * returns at once when *num_rows is 0 on entry (no DENOISING sequence
+   * has a masked position left), and the LM head and the remask then have
+   * nothing to do, so the round changes nothing.  Not allowed together with
+   * save_kv.  round_counter (int32 device scalar, may be NULL) is
+   * incremented by every round that starts with *num_rows > 0. */
+  int gate_on_rows;
+  int32_t* round_counter;
 } dbd_round_args;
 
 dbd_status dbd_round(const dbd_round_args* a, void* stream);
@@ -345,7 +353,17 @@ size_t dbd_round_workspace_size(const dbd_round_args* a);
  * its own per-round inputs), captured once and replayed with one launch and
  * no host work in between (dlmrt README, "Highlights": denoising loop on the
  * device; JetEngine developer notes: CUDA-graph replay of the denoise
- * batch).  The captured pointers and scalars are fixed at creation. */
+ * batch).  The captured pointers and scalars are fixed at creation.
+ *
+ * A whole block as one graph, "begin -> while (not done) round -> commit"
+ * (dlmrt README, "Highlights": the loop condition decided on the GPU;
+ * developer notes, "Chain Mechanism": the denoise steps and the SAVING step
+ * of a block in one chain, with no host synchronisation between them):
+ * B rounds with gate_on_rows set, then one step with save_kv set.  Every
+ * commit rule commits at least one position of every DENOISING sequence
+ * with a mask left, so a block needs at most B rounds; the rounds after
+ * the block is done return at once on the device.  Several such blocks may
+ * follow one another in one graph. */
 typedef struct dbd_graph dbd_graph;
 dbd_status dbd_graph_create(const dbd_round_args* args, int n_rounds,
                             dbd_graph** out);

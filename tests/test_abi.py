@@ -191,6 +191,10 @@ def test_round_rejects():
     with pytest.raises(api.DbdError) as e:
         api.dbd_round(a, stream=0)
     assert b"stream_cap" in api.lib().dbd_last_error()
+    a.token_stream, a.gate_on_rows = None, 1    # a SAVING step is never gated off
+    with pytest.raises(api.DbdError) as e:
+        api.dbd_round(a, stream=0)
+    assert b"gate_on_rows" in api.lib().dbd_last_error()
 
 
 def test_validate_inputs():
