@@ -848,3 +848,102 @@ def check_multiblock_stream(impl):
 
 SAVE_CHECKS = [check_kvsave_attention, check_kvsave_untouched, check_commit_block_worked,
                check_step_commit_order, check_multiblock_stream]
+
+
+# ------------------------------------------------------------------ sampling
+
+def check_philox_known_answers(impl):
+    """Philox4x32-10 against the known-answer vectors published with the
+    Random123 library (zero counter and key; all-ones; the digits of pi)."""
+    cases = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+             ((0xFFFFFFFF,) * 4, (0xFFFFFFFF,) * 2, (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+             ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+              (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+    for ctr, key, out in cases:
+        got = impl.philox4x32_10(*[np.array([x]) for x in ctr], *[np.array([x]) for x in key])
+        assert [int(g[0]) for g in got] == list(out), [hex(int(g[0])) for g in got]
+
+
+def check_uniform01(impl):
+    u = impl.uniform01(np.array([0, 511, 512, 0xFFFFFFFF], dtype=np.uint64))
+    assert u[0] == 2.0 ** -24 and u[1] == 2.0 ** -24 and u[2] == 3 * 2.0 ** -24
+    assert u[3] == 1 - 2.0 ** -24
+    assert np.all(u.astype(np.float32).astype(np.float64) == u)      # exact in float32
+
+
+def _chi2_sf(x, k):
+    from scipy.stats import chi2
+    return chi2.sf(x, k)
+
+
+def check_sampler_distribution(impl):
+    """Many draws (steps 0..N-1) of one row follow softmax(l / T): a
+    chi-square test over the tokens with expected count >= 5 (fixed seeds,
+    so the outcome is fixed too).  Catches a dropped block normaliser, a
+    Gumbel of the wrong sign, u and e sharing a word, the wrong temperature
+    in either stage."""
+    g = np.random.default_rng(31)
+    V, N = 77, 4000
+    for T, spread in ((1.0, 1.5), (0.6, 1.0), (2.0, 3.0)):
+        l = g.normal(0, spread, V)
+        l[5] = -np.inf                                  # the mask token
+        p = np.exp((l - l[np.isfinite(l)].max()) / T)
+        p /= p.sum()
+        cnt = np.zeros(V)
+        for step in range(N):
+            t, _, _ = impl.sample_row(l, T, 0x1234_5678_9ABC, 3, step)
+            cnt[t] += 1
+        assert cnt[5] == 0
+        keep = p * N >= 5
+        x = np.sum((cnt[keep] - N * p[keep]) ** 2 / (N * p[keep])) + \
+            (cnt[~keep].sum() - N * p[~keep].sum()) ** 2 / max(N * p[~keep].sum(), 1e-9)
+        pv = _chi2_sf(x, keep.sum())
+        assert pv > 1e-4, (T, x, pv)
+
+
+def check_sampler_block_choice(impl):
+    """Which block wins follows the blocks' shares of the mass, and inside a
+    block the candidate follows the members' shares: a row whose mass sits
+    in two tokens of different blocks, and one whose mass sits in two tokens
+    of one block, each drawn N times."""
+    V, N = 64, 3000
+    for a, b in ((3, 36), (3, 6)):          # 3 and 36: chunks 0 and 1; 3 and 6: one block
+        l = np.full(V, -40.0)
+        l[a], l[b] = 0.0, np.log(3.0)       # p = 1/4, 3/4
+        hits = sum(impl.sample_row(l, 1.0, 99, 1, s)[0] == b for s in range(N))
+        assert abs(hits / N - 0.75) < 4 * np.sqrt(0.75 * 0.25 / N), (a, b, hits)
+
+
+def check_sampler_greedy_limit(impl):
+    """At T -> 0 the draw is the greedy token, and the confidence is the
+    greedy max_p (at temperature 1) for every temperature."""
+    g = np.random.default_rng(32)
+    for _ in range(20):
+        l = g.normal(0, 2, 300)
+        l[7] = -np.inf
+        top = np.argsort(-l)
+        if l[top[0]] - l[top[1]] < 0.05:
+            continue
+        t, c, _ = impl.sample_row(l, 1e-3, int(g.integers(1 << 40)), 5, 0)
+        p = np.exp(l - l[top[0]])
+        assert t == top[0] and abs(c - 1.0 / p.sum()) < 1e-12
+        t2, c2, _ = impl.sample_row(l, 1.7, 11, 5, 2)
+        assert abs(c2 - np.exp(l[t2] - l[top[0]]) / p.sum()) < 1e-12
+
+
+def check_sampler_seeds(impl):
+    """The same (seed, row, step) gives the same token; rows, steps and
+    seeds each give independent draws (a near-uniform row: about 1/V
+    agreement between two streams)."""
+    l = np.zeros(512)
+    same = [impl.sample_row(l, 1.0, 5, 9, s)[0] for s in range(50)]
+    again = [impl.sample_row(l, 1.0, 5, 9, s)[0] for s in range(50)]
+    assert same == again
+    for kw in (dict(seed=6, row=9), dict(seed=5, row=10), dict(seed=5 + (1 << 32), row=9)):
+        other = [impl.sample_row(l, 1.0, kw["seed"], kw["row"], s)[0] for s in range(50)]
+        assert sum(x == y for x, y in zip(same, other)) <= 3
+    assert len(set(same)) >= 40
+
+
+SAMPLE_CHECKS = [check_philox_known_answers, check_uniform01, check_sampler_distribution,
+                 check_sampler_block_choice, check_sampler_greedy_limit, check_sampler_seeds]

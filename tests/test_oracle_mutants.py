@@ -8,7 +8,7 @@ import types
 
 import pytest
 
-from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS, SAVE_CHECKS
+from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS, SAMPLE_CHECKS, SAVE_CHECKS
 
 ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 
@@ -63,6 +63,20 @@ MUTANTS = [
      "if end_len is not None and L[s] > end_len[s]:", "save"),
     ("block_commit.py", "ts[s, L[s] + j] = toks[s, j]", "ts[s, L[s] + j] = toks[s, B - 1 - j]", "save"),
     ("block_commit.py", "only = np.where(saving0, SAVING, 0).astype(state.dtype)", "only = state", "save"),
+    ("sampling.py", "m + np.log(np.where(live, S, 1.0)) - np.log(-np.log(eu))", "m - np.log(-np.log(eu))",
+     "sample"),
+    ("sampling.py", "m + np.log(np.where(live, S, 1.0)) - np.log(-np.log(eu))",
+     "m + np.log(np.where(live, S, 1.0)) + np.log(-np.log(eu))", "sample"),
+    ("sampling.py", "eu = np.stack([uniform01(w[1]), uniform01(w[3])], axis=1)", "eu = u", "sample"),
+    ("sampling.py", "target = u * S\n", "target = u * S * 0.5\n", "sample"),
+    ("sampling.py", "z[:V] = logits / temperature", "z[:V] = logits", "sample"),
+    ("sampling.py", "lse = np.max(logits) + np.log(np.sum(np.exp(logits - np.max(logits))))",
+     "lse = np.max(logits)", "sample"),
+    ("sampling.py", "    for _ in range(10):", "    for _ in range(9):", "sample"),
+    ("sampling.py", "c = [hi1 ^ c[1] ^ k[0], lo1, hi0 ^ c[3] ^ k[1], lo0]",
+     "c = [lo1 ^ c[1] ^ k[0], hi1, hi0 ^ c[3] ^ k[1], lo0]", "sample"),
+    ("sampling.py", "return ((w >> np.uint64(9)).astype(np.float64) + 0.5) / float(1 << 23)",
+     "return ((w >> np.uint64(8)).astype(np.float64) + 0.5) / float(1 << 24)", "sample"),
 ]
 
 
@@ -70,7 +84,7 @@ def load_mutant(fname, old, new):
     pkg = types.ModuleType("oracle_mut")
     pkg.__path__ = []
     sys.modules["oracle_mut"] = pkg
-    for dep in ("bf16.py", "remask.py"):
+    for dep in ("bf16.py", "remask.py", "lmhead.py"):
         if dep == fname:
             continue
         spec = importlib.util.spec_from_file_location("oracle_mut." + dep[:-3], os.path.join(ORACLE, dep))
@@ -93,7 +107,7 @@ def test_mutant_is_caught(mut):
     fname, old, new, fam = mut
     mod = load_mutant(fname, old, new)
     checks = {"attn": ATTN_CHECKS, "lm": LM_CHECKS, "remask": REMASK_CHECKS, "rule": RULE_CHECKS,
-              "save": SAVE_CHECKS}[fam]
+              "save": SAVE_CHECKS, "sample": SAMPLE_CHECKS}[fam]
     caught = []
     for chk in checks:
         try:
