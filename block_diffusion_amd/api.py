@@ -38,7 +38,8 @@ class dbd_round_args(C.Structure):
         ("rule", C.c_int), ("tokens_per_step", C.c_int), ("eb_threshold", C.c_float),
         ("entropy", _vp), ("save_kv", C.c_int), ("num_pages", C.c_int),
         ("token_stream", _vp), ("stream_cap", C.c_int), ("end_len", _vp),
-        ("gate_on_rows", C.c_int), ("round_counter", _vp)]
+        ("gate_on_rows", C.c_int), ("round_counter", _vp),
+        ("sample", C.c_int), ("temperature", C.c_float), ("seed", C.c_uint64), ("step", C.c_uint32)]
 
 
 class DbdError(RuntimeError):
@@ -79,6 +80,9 @@ def lib() -> C.CDLL:
     L.dbd_attn_paged_save.restype = i
     L.dbd_commit_block.argtypes = [i, i, i] + [_vp] * 4 + [i] + [_vp] * 3 + [_vp]
     L.dbd_commit_block.restype = i
+    L.dbd_lmhead_sample.argtypes = [i] * 4 + [_vp] * 4 + [f, C.c_uint64, C.c_uint32] + \
+        [_vp] * 4 + [sz, _vp]
+    L.dbd_lmhead_sample.restype = i
     L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
     L.dbd_round.restype = i
     L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
@@ -248,6 +252,27 @@ def dbd_lmhead_conf(hidden, w_vocab, num_rows, argmax_tok, conf, mask_token_id,
                                              _ptr(row_index), _ptr(num_rows), _ptr(w_vocab),
                                              _ptr(argmax_tok), _ptr(conf), _ptr(entropy),
                                              _ptr(ws), nb, _stream(stream)))
+
+
+def dbd_lmhead_sample(hidden, w_vocab, num_rows, token, conf, mask_token_id, temperature, seed,
+                      step, row_index=None, max_rows=None, ws=None, stream=None, entropy=None):
+    """Temperature sampling in the fused LM head: token[row] drawn from
+    softmax(l / temperature), conf[row] its probability at temperature 1."""
+    V, Hd = w_vocab.shape
+    if max_rows is None:
+        max_rows = row_index.shape[0] if row_index is not None else hidden.shape[0]
+    _need(hidden, torch.bfloat16, (hidden.shape[0], Hd), "hidden")
+    _need(w_vocab, torch.bfloat16, (V, Hd), "w_vocab")
+    _need(num_rows, torch.int32, (1,), "num_rows")
+    need = dbd_lmhead_workspace_size(max_rows, V)
+    if ws is None and need:
+        ws = workspace(need, hidden.device)
+    nb = ws.numel() if ws is not None else 0
+    _check(lib().dbd_lmhead_sample(max_rows, Hd, V, int(mask_token_id), _ptr(hidden),
+                                   _ptr(row_index), _ptr(num_rows), _ptr(w_vocab),
+                                   float(temperature), int(seed) & ((1 << 64) - 1), int(step),
+                                   _ptr(token), _ptr(conf), _ptr(entropy), _ptr(ws), nb,
+                                   _stream(stream)))
 
 
 def dbd_remask_commit(block_tokens, seq_state, argmax_tok, conf, row_index_out, num_rows_out,

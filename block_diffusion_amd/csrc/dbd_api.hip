@@ -109,7 +109,8 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
 dbd_status enqueue_lm(int max_rows, int Hd, int V, int mask, const dbd_bf16* hidden,
                       const int32_t* row_index, const int32_t* num_rows,
                       const dbd_bf16* w, int32_t* argmax_tok, float* conf, float* entropy,
-                      void* ws, size_t ws_bytes, hipStream_t st) {
+                      void* ws, size_t ws_bytes, hipStream_t st, bool sample = false,
+                      float temperature = 1.f, uint64_t seed = 0, uint32_t step = 0) {
   if (max_rows == 0) return DBD_OK;
   const size_t need = dbd::lmhead_ws_bytes(max_rows, V);
   if (ws == nullptr || ws_bytes < need)
@@ -118,13 +119,18 @@ dbd_status enqueue_lm(int max_rows, int Hd, int V, int mask, const dbd_bf16* hid
   dbd::LmArgs a{};
   a.hidden = hidden; a.row_index = row_index; a.num_rows = num_rows; a.w = w;
   a.Hd = Hd; a.V = V; a.mask_id = mask; a.max_rows = max_rows;
-  const size_t one = need / 4;
+  const size_t one = need / dbd::kLmPartArrays;
   char* base = static_cast<char*>(ws);
   a.pm = reinterpret_cast<float*>(base);
   a.pa = reinterpret_cast<int32_t*>(base + one);
   a.ps = reinterpret_cast<float*>(base + 2 * one);
   a.pt = reinterpret_cast<float*>(base + 3 * one);
+  a.pg = reinterpret_cast<float*>(base + 4 * one);
+  a.pl = reinterpret_cast<float*>(base + 5 * one);
   a.argmax_tok = argmax_tok; a.conf = conf; a.entropy = entropy;
+  a.sample = sample ? 1 : 0;
+  a.inv_temp = 1.f / temperature;
+  a.key0 = (uint32_t)seed; a.key1 = (uint32_t)(seed >> 32); a.step = step;
   hipError_t e = dbd::lmhead_launch(a, st);
   if (e != hipSuccess) return hip_fail(e, "LM-head launch");
   return DBD_OK;
@@ -172,6 +178,8 @@ dbd_status check_round(const dbd_round_args* a) {
   if (s != DBD_OK) return s;
   s = check_rule(a->rule, a->eb_threshold, a->entropy, true);
   if (s != DBD_OK) return s;
+  if (a->sample) REQUIRE(isfinite(a->temperature) && a->temperature > 0.f,
+                         "temperature must be finite and > 0 (got %g)", (double)a->temperature);
   REQUIRE_PTR(a->q); REQUIRE_PTR(a->k_blk); REQUIRE_PTR(a->v_blk);
   REQUIRE_PTR(a->k_cache); REQUIRE_PTR(a->v_cache);
   REQUIRE_PTR(a->page_table); REQUIRE_PTR(a->prefix_len); REQUIRE_PTR(a->attn_out);
@@ -212,7 +220,8 @@ dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
   const int max_rows = a->S * a->B;
   float* ent = a->rule == DBD_RULE_ENTROPY_BOUNDED ? a->entropy : nullptr;
   s = enqueue_lm(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index, a->num_rows,
-                 a->w_vocab, a->argmax_tok, a->conf, ent, ws + attn_ws, a->workspace_bytes - attn_ws, st);
+                 a->w_vocab, a->argmax_tok, a->conf, ent, ws + attn_ws, a->workspace_bytes - attn_ws, st,
+                 a->sample != 0, a->temperature, a->seed, a->step);
   if (s != DBD_OK) return s;
   const uint32_t fl = (a->flags & ~DBD_COMPACT_ONLY) | (save ? dbd::kCommitSaving : 0u);
   return enqueue_remask(a->S, a->B, a->mask_token_id, a->dynamic_threshold, fl,
@@ -340,6 +349,25 @@ dbd_status dbd_lmhead_conf_entropy(int max_rows, int Hd, int V, int mask_token_i
   return enqueue_lm(max_rows, Hd, V, mask_token_id, hidden, row_index, num_rows, w_vocab,
                     argmax_tok, conf, entropy, workspace, workspace_bytes,
                     static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_lmhead_sample(int max_rows, int Hd, int V, int mask_token_id,
+                             const dbd_bf16* hidden, const int32_t* row_index,
+                             const int32_t* num_rows, const dbd_bf16* w_vocab, float temperature,
+                             uint64_t seed, uint32_t step, int32_t* token, float* conf,
+                             float* entropy, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  dbd_status s = check_lm(max_rows, Hd, V, mask_token_id);
+  if (s != DBD_OK) return s;
+  REQUIRE(isfinite(temperature) && temperature > 0.f, "temperature must be finite and > 0 (got %g)",
+          (double)temperature);
+  REQUIRE_PTR(hidden); REQUIRE_PTR(num_rows); REQUIRE_PTR(w_vocab);
+  REQUIRE_PTR(token); REQUIRE_PTR(conf);
+  if (row_index != nullptr) REQUIRE_PTR(row_index);
+  if (entropy != nullptr) REQUIRE_PTR(entropy);
+  return enqueue_lm(max_rows, Hd, V, mask_token_id, hidden, row_index, num_rows, w_vocab, token,
+                    conf, entropy, workspace, workspace_bytes, static_cast<hipStream_t>(stream), true,
+                    temperature, seed, step);
 }
 
 dbd_status dbd_remask_commit(int S, int B, int mask_token_id, float dynamic_threshold,

@@ -65,7 +65,16 @@ struct LmArgs {
   int32_t* argmax_tok;
   float* conf;
   float* entropy;  // may be NULL: softmax entropy per listed row (nats)
+  // temperature sampling (sample != 0): argmax_tok receives the drawn token
+  int sample;
+  float inv_temp;  // 1 / temperature
+  uint32_t key0, key1, step;
+  float* pg;       // [max_rows][kLmGrid] partial largest Gumbel value (log2 units)
+  float* pl;       // [max_rows][kLmGrid] partial logit of its candidate
 };
+
+// partial arrays of the LM-head workspace: pm, pa, ps, pt, pg, pl
+constexpr int kLmPartArrays = 6;
 
 size_t lmhead_ws_bytes(int max_rows, int V);
 hipError_t lmhead_launch(const LmArgs& a, hipStream_t stream);

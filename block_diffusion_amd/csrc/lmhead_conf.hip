@@ -32,6 +32,18 @@
 // at the end the two waves sharing rows fold through LDS and the workgroup
 // writes one partial per (row, team).
 //
+// Sampling (SMP instances): the token is drawn from softmax(l / T) instead
+// of taken as the argmax, exactly and without any extra pass.  Each block of
+// 16 vocabulary columns that a lane holds for a row (chunk c = 32 aligned
+// columns, half h: columns 32c + 8q + 4h + r) draws two uniforms from
+// Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy as 1, 2,
+// 3"; counter (c, row id, step, 0), key = the 64-bit seed): one picks a
+// column inside the block by inverse CDF of exp(l/T), the other a Gumbel
+// variable located at the block's log-sum-exp.  The block with the largest
+// Gumbel value wins (the Gumbel-max trick over blocks), so the token has
+// probability exp(l_v/T) / sum exp(l/T).  The confidence stays the model's
+// probability of that token at temperature 1.
+//
 // lmhead_merge_kernel: one wave per row folds the partials of all teams,
 // (m,a,s) + (m',a',s') = (max, id of the larger max or the lower id on equal
 // maxima, s*e^(m-max) + s'*e^(m'-max)), in a fixed order, and writes the
@@ -87,6 +99,42 @@ __device__ __forceinline__ void fold(Part& x, float m2, int a2, float s2, float 
   x.a = a;
 }
 
+// Sampling draw of one block or of a set of blocks: the largest Gumbel value
+// so far (log2 units), the candidate column of that block, and its logit at
+// temperature 1 (natural units).  Lower candidate on equal values.
+struct Pick {
+  float g;
+  int c;
+  float l;
+};
+
+__device__ __forceinline__ void pick_fold(Pick& x, float g2, int c2, float l2) {
+  if (g2 > x.g || (g2 == x.g && c2 < x.c)) {
+    x.g = g2; x.c = c2; x.l = l2;
+  }
+}
+
+// Philox4x32-10: ten rounds of two 32x32->64 products of words 0 and 2,
+// their halves mixed with words 1 and 3 and the key, the key bumped by the
+// Weyl constants between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t& c0, uint32_t& c1, uint32_t& c2, uint32_t& c3,
+                                              uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c0), lo0 = 0xD2511F53u * c0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c2), lo1 = 0xCD9E8D57u * c2;
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+}
+
+// ((w >> 9) + 0.5) / 2^23 in (0, 1), exact in float32
+__device__ __forceinline__ float uniform01(uint32_t w) {
+  return (float)(((w >> 9) << 1) | 1u) * (1.0f / 16777216.0f);
+}
+
 // One 1 KB direct-to-LDS load: lane l copies the 16 bytes at base + off to
 // lds + 16*l.  Inline assembly, so that the compiler neither adds its own
 // vmcnt waits for the LDS it writes nor moves LDS accesses across it; the
@@ -115,11 +163,13 @@ __device__ __forceinline__ int team_size(int M) { return M <= 256 ? 1 : (M <= 51
 // One pass of one workgroup: rows [m_base, m_end) of the compact row list
 // (R = 64*MB row slots, two waves of 32*MB rows) against vocabulary columns
 // [v_lo, v_hi), as seen by one wave; WL: this wave streams W (else hidden
-// rows); ENT: also accumulate sum e^(l-m)(l-m) for the entropy.  Writes one
-// partial per valid row into slot `team`.
-template <int MB, bool WL, bool ENT>
+// rows); MODE bit 0 (ENT): also accumulate sum e^(l-m)(l-m) for the
+// entropy; bit 1 (SMP): draw a sampled token instead of the argmax.  Writes
+// one partial per valid row into slot `team`.
+template <int MB, bool WL, int MODE>
 __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
                                         int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
+  constexpr bool ENT = (MODE & 1) != 0, SMP = (MODE & 2) != 0;
   constexpr int R = 64 * MB, RH = 32 * MB;
   constexpr int HPW = R / 16;                  // 1 KB hidden loads per hidden wave per stage
   constexpr int NLD = WL ? WPW : HPW;          // this wave's loads per stage
@@ -243,6 +293,19 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   Part run[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) run[mb] = Part{-INFINITY, 0x7fffffff, 0.f, 0.f};
+  // sampling: running draw and the row id (s*B + position) of each row the
+  // lane holds; rows past the list use a listed row (never written)
+  Pick pick[MB];
+  uint32_t rid[MB];
+  if constexpr (SMP) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      pick[mb] = Pick{-INFINITY, 0x7fffffff, 0.f};
+      const int m = m_base + wm * RH + mb * 32 + (lane & 31);
+      const int mm = m < m_end ? m : m_base;
+      rid[mb] = (uint32_t)(a.row_index ? a.row_index[mm] : mm);
+    }
+  }
 
   // Accumulators start at 0, or at -inf on columns that are not candidates
   // (the mask id, columns past the range): MFMA accumulation keeps them at
@@ -271,6 +334,47 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
         for (int mb = 0; mb < MB; ++mb) acc[nb][mb] = b;
       }
     }
+  };
+
+  // Sampling draw of one block: the lane's 16 values x (log2 units, -inf
+  // for non-candidates) of row block mb in 32-column chunk nb, columns
+  // vb0 + 8*(i/4) + (i%4), block maximum bm.
+  auto sample_block = [&](const float* x, float bm, int vb0, int nb, int mb) {
+    // the lanes of this block and of the other half of the chunk draw the
+    // same four words; half h uses words 2h and 2h+1
+    uint32_t w0 = (uint32_t)((vb0 - 4 * (lane >> 5)) >> 5), w1 = rid[mb], w2 = a.step, w3 = 0u;
+    philox4x32_10(w0, w1, w2, w3, a.key0, a.key1);
+    const bool h = (lane >> 5) != 0;
+    const float u = uniform01(h ? w2 : w0);
+    const float eg = uniform01(h ? w3 : w1);
+    if (bm == -INFINITY) return;                      // no candidate in this block
+    const float bmT = bm * a.inv_temp;
+    float e[16], S = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      e[i] = fast_exp2(fmaf(x[i], a.inv_temp, -bmT));
+      S += e[i];
+    }
+    // inverse CDF: the first member whose running sum reaches u*S (the last
+    // member with weight if rounding leaves none)
+    const float target = u * S;
+    float cum = 0.f;
+    int ci = -1, last = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      cum += e[i];
+      last = e[i] > 0.f ? i : last;
+      ci = (ci < 0 && e[i] > 0.f && cum >= target) ? i : ci;
+    }
+    ci = ci < 0 ? last : ci;
+    float xc = x[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) xc = (i == ci) ? x[i] : xc;
+    // Gumbel at the block's log-sum-exp, log2 units (a constant shift of
+    // m + ln S - ln(-ln e) in natural units)
+    const float G = bmT + __log2f(S) - __log2f(-__log2f(eg));
+    pick_fold(pick[mb], G, vb0 + 8 * (ci >> 2) + (ci & 3), xc * (1.0f / kLog2e));
+    (void)nb;
   };
 
   // reduce a finished tile: lane holds row (lane & 31) of each row block mb
@@ -305,6 +409,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
 #pragma unroll
         for (int i = 15; i >= 0; --i) bi = (x[i] == bm) ? 8 * (i >> 2) + (i & 3) : bi;
         bi += vb0;
+        if constexpr (SMP) sample_block(x, bm, vb0, nb, mb);
         const float mn = fmaxf(m, bm);
         float sb = 0.f, tb = 0.f;
         if (ENT) {
@@ -344,6 +449,13 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       idx = (pm > m || (pm == m && pi < idx)) ? pi : idx;
       // to natural units: t = tt * ln 2
       fold(run[mb], mx * (1.0f / kLog2e), idx, sum, tt * (1.0f / kLog2e));
+      if constexpr (SMP) {
+        // the other half of each chunk
+        const float g2 = shfl_xor_f(pick[mb].g, 32);
+        const int c2 = shfl_xor_i(pick[mb].c, 32);
+        const float l2 = shfl_xor_f(pick[mb].l, 32);
+        pick_fold(pick[mb], g2, c2, l2);
+      }
     }
   };
 
@@ -420,6 +532,9 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   lds_i32* const s_a = (lds_i32*)(Hr + 2 * 256);
   lds_f32* const s_s = (lds_f32*)(Hr + 4 * 256);
   lds_f32* const s_t = (lds_f32*)(Hr + 6 * 256);
+  lds_f32* const s_g = (lds_f32*)(Hr + 8 * 256);
+  lds_i32* const s_c = (lds_i32*)(Hr + 10 * 256);
+  lds_f32* const s_l = (lds_f32*)(Hr + 12 * 256);
   if (wn == 1 && lane < 32) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -428,6 +543,11 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       s_a[k] = run[mb].a;
       s_s[k] = run[mb].s;
       s_t[k] = run[mb].t;
+      if constexpr (SMP) {
+        s_g[k] = pick[mb].g;
+        s_c[k] = pick[mb].c;
+        s_l[k] = pick[mb].l;
+      }
     }
   }
   __syncthreads();
@@ -436,20 +556,25 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
     for (int mb = 0; mb < MB; ++mb) {
       const int k = (wm * MB + mb) * 32 + lane;
       fold(run[mb], s_m[k], s_a[k], s_s[k], s_t[k]);
+      if constexpr (SMP) pick_fold(pick[mb], s_g[k], s_c[k], s_l[k]);
       const int m = m_base + wm * RH + mb * 32 + lane;
       if (m < m_end) {
         const size_t o = (size_t)m * nteam + team;
         a.pm[o] = run[mb].m;
-        a.pa[o] = run[mb].a;
+        a.pa[o] = SMP ? pick[mb].c : run[mb].a;
         a.ps[o] = run[mb].s;
         if (ENT) a.pt[o] = run[mb].t;
+        if constexpr (SMP) {
+          a.pg[o] = pick[mb].g;
+          a.pl[o] = pick[mb].l;
+        }
       }
     }
   }
   __syncthreads();   // the partial scratch is read before the next pass loads
 }
 
-template <int MB, bool ENT>
+template <int MB, int MODE>
 __device__ __forceinline__ void lm_pass_any(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
                                             int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
   if (v_hi <= v_lo) {
@@ -460,17 +585,21 @@ __device__ __forceinline__ void lm_pass_any(const LmArgs& a, int m_base, int m_e
       a.pa[o] = 0x7fffffff;
       a.ps[o] = 0.f;
       a.pt[o] = 0.f;
+      if (MODE & 2) {
+        a.pg[o] = -INFINITY;
+        a.pl[o] = 0.f;
+      }
     }
     return;
   }
   if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 2)
-    lm_pass<MB, true, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
+    lm_pass<MB, true, MODE>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
   else
-    lm_pass<MB, false, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
+    lm_pass<MB, false, MODE>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr);
 }
 }  // namespace
 
-template <bool ENT>
+template <int MODE>
 __global__ __launch_bounds__(256, 1) void lmhead_tile_kernel(LmArgs a) {
   __shared__ __align__(16) uint16_t Wr_[NWS * WSLOT];
   __shared__ __align__(16) uint16_t Hr_[NHS * HSLOT];
@@ -492,10 +621,10 @@ __global__ __launch_bounds__(256, 1) void lmhead_tile_kernel(LmArgs a) {
     const int m_end = min(m_base + R, p0 + Mp);
     if (m_base >= m_end) continue;
     switch (R / 64) {
-      case 1: lm_pass_any<1, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
-      case 2: lm_pass_any<2, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
-      case 3: lm_pass_any<3, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
-      default: lm_pass_any<4, ENT>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      case 1: lm_pass_any<1, MODE>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      case 2: lm_pass_any<2, MODE>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      case 3: lm_pass_any<3, MODE>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
+      default: lm_pass_any<4, MODE>(a, m_base, m_end, v_lo, v_hi, team, nteam, Wr, Hr); break;
     }
   }
 }
@@ -508,9 +637,12 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(LmArgs a) {
   const int nteam = kLmGrid / team_size(M);
   const size_t base = (size_t)r * nteam;
   Part x{-INFINITY, 0x7fffffff, 0.f, 0.f};
-  const bool ent = a.entropy != nullptr;
-  for (int t = lane; t < nteam; t += 64)
+  Pick pk{-INFINITY, 0x7fffffff, 0.f};
+  const bool ent = a.entropy != nullptr, smp = a.sample != 0;
+  for (int t = lane; t < nteam; t += 64) {
     fold(x, a.pm[base + t], a.pa[base + t], a.ps[base + t], ent ? a.pt[base + t] : 0.f);
+    if (smp) pick_fold(pk, a.pg[base + t], a.pa[base + t], a.pl[base + t]);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float m2 = shfl_xor_f(x.m, off);
@@ -518,11 +650,21 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(LmArgs a) {
     const float s2 = shfl_xor_f(x.s, off);
     const float t2 = shfl_xor_f(x.t, off);
     fold(x, m2, a2, s2, t2);
+    const float g2 = shfl_xor_f(pk.g, off);
+    const int c2 = shfl_xor_i(pk.c, off);
+    const float l2 = shfl_xor_f(pk.l, off);
+    pick_fold(pk, g2, c2, l2);
   }
   if (lane == 0) {
     const int row = a.row_index ? a.row_index[r] : r;
-    a.argmax_tok[row] = x.a;
-    a.conf[row] = 1.f / x.s;
+    if (smp) {
+      // the drawn token and its probability at temperature 1
+      a.argmax_tok[row] = pk.c;
+      a.conf[row] = __expf(pk.l - x.m) / x.s;
+    } else {
+      a.argmax_tok[row] = x.a;
+      a.conf[row] = 1.f / x.s;
+    }
     if (a.entropy) a.entropy[row] = __logf(x.s) - x.t / x.s;
   }
 }
@@ -530,13 +672,17 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(LmArgs a) {
 size_t lmhead_ws_bytes(int max_rows, int V) {
   (void)V;
   const size_t one = ((size_t)max_rows * kLmGrid * 4 + 255) & ~(size_t)255;
-  return 4 * one;
+  return kLmPartArrays * one;
 }
 
 hipError_t lmhead_launch(const LmArgs& a, hipStream_t st) {
-  // the entropy sums only when a caller wants the entropy
-  if (a.entropy) lmhead_tile_kernel<true><<<kLmGrid, 256, 0, st>>>(a);
-  else lmhead_tile_kernel<false><<<kLmGrid, 256, 0, st>>>(a);
+  // the entropy sums only when a caller wants the entropy, the draw only
+  // when sampling
+  const int mode = (a.entropy ? 1 : 0) | (a.sample ? 2 : 0);
+  if (mode == 0) lmhead_tile_kernel<0><<<kLmGrid, 256, 0, st>>>(a);
+  else if (mode == 1) lmhead_tile_kernel<1><<<kLmGrid, 256, 0, st>>>(a);
+  else if (mode == 2) lmhead_tile_kernel<2><<<kLmGrid, 256, 0, st>>>(a);
+  else lmhead_tile_kernel<3><<<kLmGrid, 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   lmhead_merge_kernel<<<(a.max_rows + 3) / 4, 256, 0, st>>>(a);

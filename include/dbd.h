@@ -189,6 +189,36 @@ dbd_status dbd_lmhead_conf_entropy(int max_rows, int Hd, int V,
                                    float* entropy, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
+/* dbd_lmhead_conf with the token drawn from softmax(l / temperature)
+ * instead of taken as the argmax (SamplingParams temperature, JetEngine
+ * README usage examples; the scheduler's postprocess samples before the
+ * remasking strategy selects, developer notes, "Scheduler").  Exact draw,
+ * fused in the same pass, no logit stored:
+ *   blocks: for chunk c (columns 32c..32c+31) and half h in {0,1}, the 16
+ *     columns 32c + 8q + 4h + r (q, r in 0..3) other than the mask token;
+ *   words: Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy
+ *     as 1, 2, 3") of counter (c, row, step, 0) and key (seed low word,
+ *     seed high word), row = row_index[r]; half h uses word 2h for u and
+ *     word 2h+1 for e, each as ((w >> 9) + 0.5) / 2^23;
+ *   per block, with z = l / temperature: m_b = max z, S_b = sum exp(z-m_b),
+ *     candidate = first column (increasing id) whose running sum of
+ *     exp(z - m_b) reaches u*S_b, G_b = m_b + ln S_b - ln(-ln e);
+ *   token[row] = the candidate of the block with the largest G_b (lower id
+ *     on ties), which has probability exp(z_v) / sum exp(z);
+ *   conf[row] = that token's probability at temperature 1 (softmax of l
+ *     without the mask token), the value the commit rules compare.
+ * entropy may be NULL (else as dbd_lmhead_conf_entropy).  step lets every
+ * round draw fresh numbers from the same seed.  Requirements: as
+ * dbd_lmhead_conf; temperature finite and > 0.  Top-k / top-p filtering is
+ * not provided. */
+dbd_status dbd_lmhead_sample(int max_rows, int Hd, int V, int mask_token_id,
+                             const dbd_bf16* hidden, const int32_t* row_index,
+                             const int32_t* num_rows, const dbd_bf16* w_vocab,
+                             float temperature, uint64_t seed, uint32_t step,
+                             int32_t* token, float* conf, float* entropy,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* ------------------------------------------------------------------------
  * dbd_remask_commit -- threshold remask (low_confidence_dynamic) and the
  * next round's row list.
@@ -344,6 +374,13 @@ typedef struct dbd_round_args {
    * incremented by every round that starts with *num_rows > 0. */
   int gate_on_rows;
   int32_t* round_counter;
+  /* Temperature sampling (dbd_lmhead_sample) instead of the greedy token
+   * when sample != 0: argmax_tok receives the drawn token, conf its
+   * probability at temperature 1.  Give each round its own step. */
+  int sample;
+  float temperature;
+  uint64_t seed;
+  uint32_t step;
 } dbd_round_args;
 
 dbd_status dbd_round(const dbd_round_args* a, void* stream);

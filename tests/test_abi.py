@@ -26,7 +26,7 @@ def test_header_declares_the_round_calls():
     names = declared_functions()
     for n in ("dbd_attn_paged", "dbd_lmhead_conf", "dbd_remask_commit", "dbd_round",
               "dbd_lmhead_conf_entropy", "dbd_remask_commit_rule",
-              "dbd_attn_paged_save", "dbd_commit_block",
+              "dbd_attn_paged_save", "dbd_commit_block", "dbd_lmhead_sample",
               "dbd_graph_create", "dbd_graph_launch", "dbd_graph_destroy",
               "dbd_attn_workspace_size", "dbd_lmhead_workspace_size",
               "dbd_round_workspace_size", "dbd_validate_inputs", "dbd_last_error",
@@ -155,6 +155,14 @@ def test_remask_rule_rejects(rule, eb, entropy, flags, status):
     st = L.dbd_remask_commit_rule(2, 4, 5, rule, 0.9, 1, eb, flags, 16, 16, 16, 16, entropy,
                                   16, 16, None, None)
     assert st == status and L.dbd_last_error()
+
+
+@pytest.mark.parametrize("T", [0.0, -1.0, float("inf"), float("nan")])
+def test_lmhead_sample_rejects_temperature(T):
+    L = api.lib()
+    st = L.dbd_lmhead_sample(16, 128, 1024, 5, 16, None, 16, 16, T, 1, 0, 16, 16, None, 256,
+                             1 << 20, None)
+    assert st == api.DBD_ERR_INVALID_ARG and b"temperature" in L.dbd_last_error()
 
 
 def test_lmhead_entropy_requires_output():
