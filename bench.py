@@ -209,6 +209,10 @@ def main():
         lm_times[M] = ev_time(lambda: api.dbd_lmhead_conf(
             r1["hidden"], fixed["w_vocab"], nr, bufs.argmax_tok, bufs.conf, w.mask_id,
             row_index=lm_rows, max_rows=n, ws=bufs.workspace))
+    nr1 = torch.tensor([rows_per_round[0]], dtype=torch.int32, device=dev)
+    t_lm_sample = ev_time(lambda: api.dbd_lmhead_sample(
+        r1["hidden"], fixed["w_vocab"], nr1, bufs.argmax_tok, bufs.conf, w.mask_id, 1.0, 1234, 1,
+        row_index=lm_rows, max_rows=n, ws=bufs.workspace))
     conf_r = torch.rand(n, device=dev)
     arg_r = torch.zeros(n, dtype=torch.int32, device=dev)
     tk, ss = tok0.clone(), st0.clone()
@@ -216,7 +220,8 @@ def main():
     t_remask = ev_time(lambda: api.dbd_remask_commit(tk, ss, arg_r, conf_r, ri, nr2, w.mask_id,
                                                      2.0))   # tau > 1: one commit each, no state change until full
     log(f"attention {t_attn:.1f} us, LM head {', '.join(f'M={m}: {t:.1f} us' for m, t in lm_times.items())}, "
-        f"remask {t_remask:.1f} us")
+        f"remask {t_remask:.1f} us, LM head with temperature sampling M={rows_per_round[0]}: "
+        f"{t_lm_sample:.1f} us")
 
     # ---- a whole block on the device: B gated rounds, then the SAVING step
     # (attention with the K/V write, the block commit), one graph per block
@@ -294,6 +299,7 @@ def main():
                          "lmhead": {str(m): round(t, 2) for m, t in lm_times.items()},
                          "remask": round(t_remask, 2),
                          "attention_kv_save": round(t_save, 2),
+                         "lmhead_sample_T1_M%d" % rows_per_round[0]: round(t_lm_sample, 2),
                          "block_loop": {"rounds": w.B, "saving_step": True,
                                         "us_per_block": round(t_block, 2),
                                         "committed_tokens_per_s": round(w.S * w.B / t_block * 1e6, 1)},
