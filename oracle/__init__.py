@@ -24,10 +24,12 @@ from .remask import (remask, remask_rule, compact_rows, DENOISING, SAVING,
 from .round import denoise_round
 from .block_commit import kv_save, commit_block, step_commit, FINISHED
 from .sampling import philox4x32_10, uniform01, sample_row, lmhead_sample
+from .prefill import prefill_attention, prefill_store
 
 __all__ = ["widen", "attention", "attention_group", "lmhead_rows",
            "lmhead_logits", "lmhead_entropy", "remask", "remask_rule",
            "compact_rows", "denoise_round", "DENOISING", "SAVING",
            "RULE_DYNAMIC", "RULE_STATIC", "RULE_SEQUENTIAL", "RULE_ENTROPY",
            "kv_save", "commit_block", "step_commit", "FINISHED",
-           "philox4x32_10", "uniform01", "sample_row", "lmhead_sample"]
+           "philox4x32_10", "uniform01", "sample_row", "lmhead_sample",
+           "prefill_attention", "prefill_store"]

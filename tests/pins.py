@@ -947,3 +947,123 @@ def check_sampler_seeds(impl):
 
 SAMPLE_CHECKS = [check_philox_known_answers, check_uniform01, check_sampler_distribution,
                  check_sampler_block_choice, check_sampler_greedy_limit, check_sampler_seeds]
+
+
+# ------------------------------------------------- block-causal prefill
+
+def _prefill_case(seed, lens=(7, 0, 12, 5), Hq=4, Hkv=2, D=8):
+    g = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = bf(g.standard_normal((T, Hq, D)))
+    k = bf(g.standard_normal((T, Hkv, D)))
+    v = bf(g.standard_normal((T, Hkv, D)))
+    return q, k, v, cu
+
+
+def check_prefill_bruteforce(impl):
+    """Scalar loops over the mask's definition."""
+    for seed, B in ((0, 3), (1, 1), (2, 5), (3, 16)):
+        q, k, v, cu = _prefill_case(seed)
+        got = impl.prefill_attention(q, k, v, cu, B)
+        T, Hq, D = q.shape
+        G = Hq // k.shape[1]
+        sc = 1.0 / math.sqrt(D)
+        for s in range(len(cu) - 1):
+            a, b = int(cu[s]), int(cu[s + 1])
+            for i in range(b - a):
+                for h in range(Hq):
+                    keys = [j for j in range(b - a) if j // B <= i // B]
+                    qi = [float(x) for x in wid(q[a + i, h])]
+                    z = [math.fsum(x * y for x, y in zip(qi, wid(k[a + j, h // G]))) * sc for j in keys]
+                    mz = max(z)
+                    e = [math.exp(t - mz) for t in z]
+                    den = math.fsum(e)
+                    for d in range(D):
+                        ref = math.fsum(e[n] * float(wid(v[a + j, h // G])[d]) for n, j in enumerate(keys)) / den
+                        assert abs(got[a + i, h, d] - ref) < 1e-12, (seed, B, s, i, h)
+
+
+def _sdpa(q, k, v, causal):
+    import torch
+    qt = torch.from_numpy(wid(q)).permute(1, 0, 2)       # [H][L][D]
+    G = q.shape[1] // k.shape[1]
+    kt = torch.from_numpy(wid(k)).permute(1, 0, 2).repeat_interleave(G, 0)
+    vt = torch.from_numpy(wid(v)).permute(1, 0, 2).repeat_interleave(G, 0)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=causal)
+    return o.permute(1, 0, 2).numpy()
+
+
+def check_prefill_special_cases(impl):
+    """A block at least as long as the prompt is full attention; a block of
+    one token is causal attention (PyTorch's float64 SDPA, per prompt)."""
+    q, k, v, cu = _prefill_case(4, lens=(9, 13, 1))
+    full = impl.prefill_attention(q, k, v, cu, 64)
+    causal = impl.prefill_attention(q, k, v, cu, 1)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        assert np.max(np.abs(full[a:b] - _sdpa(q[a:b], k[a:b], v[a:b], False))) < 1e-12
+        assert np.max(np.abs(causal[a:b] - _sdpa(q[a:b], k[a:b], v[a:b], True))) < 1e-12
+
+
+def check_prefill_matches_denoise(impl):
+    """Each full block of a prompt sees exactly what a denoise step of that
+    block sees once the earlier blocks are in the cache: the prefill rows of
+    block b equal the (separately pinned) denoise attention with prefix
+    length b*B over a cache filled by the store."""
+    import oracle as real
+    B, P, Hq, Hkv, D = 3, 4, 4, 2, 8
+    lens = (9, 6, 12)
+    q, k, v, cu = _prefill_case(5, lens=lens, Hq=Hq, Hkv=Hkv, D=D)
+    got = impl.prefill_attention(q, k, v, cu, B)
+    S = len(lens)
+    npg = [-(-L // P) for L in lens]
+    pt = np.full((S, max(npg)), -1, dtype=np.int32)
+    perm = np.random.default_rng(6).permutation(sum(npg))
+    o = 0
+    for s, n in enumerate(npg):
+        pt[s, :n] = perm[o:o + n]
+        o += n
+    kc = np.zeros((sum(npg), Hkv, P, D), dtype=np.uint16)
+    vc = np.zeros_like(kc)
+    kc, vc = impl.prefill_store(kc, vc, pt, k, v, cu)
+    for s, L in enumerate(lens):
+        a = int(cu[s])
+        for b0 in range(0, L, B):
+            blk = slice(a + b0, a + b0 + B)
+            ref = real.attention(q[None, blk], k[None, blk], v[None, blk], kc, vc, pt[s:s + 1],
+                                 np.array([b0], np.int32))
+            assert np.max(np.abs(got[blk] - ref[0])) < 1e-12, (s, b0)
+
+
+def check_prefill_store(impl):
+    q, k, v, cu = _prefill_case(7, lens=(5, 0, 9), Hq=4, Hkv=2, D=8)
+    P = 4
+    pt = np.array([[3, 0, -1], [-1, -1, -1], [1, 4, 2]], dtype=np.int32)
+    kc0 = bf(np.random.default_rng(8).standard_normal((6, 2, P, 8)))
+    vc0 = bf(np.random.default_rng(9).standard_normal((6, 2, P, 8)))
+    kc, vc = impl.prefill_store(kc0, vc0, pt, k, v, cu)
+    touched = np.zeros((6, P), dtype=bool)
+    for s in range(3):
+        a = int(cu[s])
+        for j in range(int(cu[s + 1]) - a):
+            pg = pt[s, j // P]
+            assert np.array_equal(kc[pg, :, j % P], k[a + j]) and np.array_equal(vc[pg, :, j % P], v[a + j])
+            touched[pg, j % P] = True
+    keep = ~touched
+    assert np.array_equal(kc.transpose(0, 2, 1, 3)[keep], kc0.transpose(0, 2, 1, 3)[keep])
+    assert np.array_equal(vc.transpose(0, 2, 1, 3)[keep], vc0.transpose(0, 2, 1, 3)[keep])
+
+
+def check_prefill_packing(impl):
+    """Prompts do not see each other: packed results equal per-prompt ones."""
+    q, k, v, cu = _prefill_case(10, lens=(4, 7, 0, 3))
+    got = impl.prefill_attention(q, k, v, cu, 2)
+    for s in range(len(cu) - 1):
+        a, b = int(cu[s]), int(cu[s + 1])
+        one = impl.prefill_attention(q[a:b], k[a:b], v[a:b], np.array([0, b - a]), 2)
+        assert np.array_equal(got[a:b], one)
+
+
+PREFILL_CHECKS = [check_prefill_bruteforce, check_prefill_special_cases, check_prefill_matches_denoise,
+                  check_prefill_store, check_prefill_packing]

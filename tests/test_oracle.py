@@ -3,7 +3,7 @@ special cases, invariants, hand-worked fixtures)."""
 import pytest
 
 import oracle
-from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS, SAVE_CHECKS, SAMPLE_CHECKS
+from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS, SAVE_CHECKS, SAMPLE_CHECKS, PREFILL_CHECKS
 
 
 @pytest.mark.parametrize("check", ATTN_CHECKS, ids=lambda f: f.__name__)
@@ -33,6 +33,11 @@ def test_saving_step_pins(check):
 
 @pytest.mark.parametrize("check", SAMPLE_CHECKS, ids=lambda f: f.__name__)
 def test_sampling_pins(check):
+    check(oracle)
+
+
+@pytest.mark.parametrize("check", PREFILL_CHECKS, ids=lambda f: f.__name__)
+def test_prefill_pins(check):
     check(oracle)
 
 

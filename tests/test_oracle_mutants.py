@@ -8,7 +8,7 @@ import types
 
 import pytest
 
-from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS, SAMPLE_CHECKS, SAVE_CHECKS
+from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, PREFILL_CHECKS, RULE_CHECKS, SAMPLE_CHECKS, SAVE_CHECKS
 
 ORACLE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle")
 
@@ -77,6 +77,15 @@ MUTANTS = [
      "c = [lo1 ^ c[1] ^ k[0], hi1, hi0 ^ c[3] ^ k[1], lo0]", "sample"),
     ("sampling.py", "return ((w >> np.uint64(9)).astype(np.float64) + 0.5) / float(1 << 23)",
      "return ((w >> np.uint64(8)).astype(np.float64) + 0.5) / float(1 << 24)", "sample"),
+    ("prefill.py", "allowed = blk[None, :] <= blk[:, None]", "allowed = blk[None, :] < blk[:, None]",
+     "prefill"),
+    ("prefill.py", "allowed = blk[None, :] <= blk[:, None]",
+     "allowed = np.arange(L)[None, :] <= np.arange(L)[:, None]", "prefill"),
+    ("prefill.py", "blk = np.arange(L) // block_len", "blk = (np.arange(L) + 1) // block_len", "prefill"),
+    ("prefill.py", "scale = 1.0 / np.sqrt(D)", "scale = 1.0 / D", "prefill"),
+    ("prefill.py", "h = g * G + gi", "h = gi * Hkv + g", "prefill"),
+    ("prefill.py", "kc[page, :, j % P, :] = k[a + j]", "kc[page, :, (j + 1) % P, :] = k[a + j]", "prefill"),
+    ("prefill.py", "vc[page, :, j % P, :] = v[a + j]", "vc[page, :, j % P, :] = k[a + j]", "prefill"),
 ]
 
 
@@ -107,7 +116,7 @@ def test_mutant_is_caught(mut):
     fname, old, new, fam = mut
     mod = load_mutant(fname, old, new)
     checks = {"attn": ATTN_CHECKS, "lm": LM_CHECKS, "remask": REMASK_CHECKS, "rule": RULE_CHECKS,
-              "save": SAVE_CHECKS, "sample": SAMPLE_CHECKS}[fam]
+              "save": SAVE_CHECKS, "sample": SAMPLE_CHECKS, "prefill": PREFILL_CHECKS}[fam]
     caught = []
     for chk in checks:
         try:
