@@ -260,6 +260,34 @@ def main():
         f"{w.S * w.B / t_block * 1e6:.0f} committed tokens/s; attention with the K/V write "
         f"(every sequence SAVING): {t_save:.1f} us")
 
+    # ---- block-causal prefill of the same batch: every sequence's prefix as
+    # one prompt (packed), the same heads and block length; inputs drawn on
+    # the device (seeded), the prompt K/V stored into the paged cache
+    Lp = fx.prefix_len.astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(Lp)]).astype(np.int32)
+    Tp = int(cu[-1])
+    gen = torch.Generator(device=dev).manual_seed(4321)
+    qp = torch.randn((Tp, w.Hq, w.D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    kp = torch.randn((Tp, w.Hkv, w.D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    vp = torch.randn((Tp, w.Hkv, w.D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    op = torch.empty_like(qp)
+    cu_d = torch.from_numpy(cu).to(dev)
+    kc_p, vc_p = torch.empty_like(fixed["k_cache"]), torch.empty_like(fixed["v_cache"])
+    pf_ws = api.workspace(api.lib().dbd_prefill_workspace_size(w.S), dev)
+    t_prefill = ev_time(lambda: api.dbd_prefill_attn(qp, kp, vp, cu_d, op, w.B,
+                                                     page_table=fixed["page_table"], k_cache=kc_p,
+                                                     v_cache=vc_p, ws=pf_ws))
+    # 2*D flops each for q.k and p.v per (row, visible key)
+    vis = 0
+    for Ls in Lp:
+        i = np.arange(Ls)
+        vis += int(np.minimum(Ls, (i // w.B + 1) * w.B).sum())
+    pf_flops = 4.0 * w.D * w.Hq * vis
+    pf_tflops = pf_flops / (t_prefill * 1e-6) / 1e12
+    del qp, kp, vp, op, kc_p, vc_p
+    log(f"block-causal prefill of the batch's prefixes ({Tp} tokens, block {w.B}): {t_prefill:.1f} us, "
+        f"{pf_tflops:.0f} TFLOP/s ({pf_tflops / PEAK_BF16_TFLOPS:.1%} of bf16 peak)")
+
     # algorithmic work
     L = fx.prefix_len.astype(np.int64)
     npages = -(-L // w.P)
@@ -300,6 +328,10 @@ def main():
                          "remask": round(t_remask, 2),
                          "attention_kv_save": round(t_save, 2),
                          "lmhead_sample_T1_M%d" % rows_per_round[0]: round(t_lm_sample, 2),
+                         "prefill": {"tokens": Tp, "block_length": w.B, "us": round(t_prefill, 2),
+                                     "tflops": round(pf_tflops, 1),
+                                     "frac_bf16_peak": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
+                                     "kv_store": True},
                          "block_loop": {"rounds": w.B, "saving_step": True,
                                         "us_per_block": round(t_block, 2),
                                         "committed_tokens_per_s": round(w.S * w.B / t_block * 1e6, 1)},

@@ -83,6 +83,10 @@ def lib() -> C.CDLL:
     L.dbd_lmhead_sample.argtypes = [i] * 4 + [_vp] * 4 + [f, C.c_uint64, C.c_uint32] + \
         [_vp] * 4 + [sz, _vp]
     L.dbd_lmhead_sample.restype = i
+    L.dbd_prefill_attn.argtypes = [i] * 6 + [_vp] * 4 + [f, _vp] + [i] * 3 + [_vp] * 4 + [sz, _vp]
+    L.dbd_prefill_attn.restype = i
+    L.dbd_prefill_workspace_size.argtypes = [i]
+    L.dbd_prefill_workspace_size.restype = sz
     L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
     L.dbd_round.restype = i
     L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
@@ -273,6 +277,34 @@ def dbd_lmhead_sample(hidden, w_vocab, num_rows, token, conf, mask_token_id, tem
                                    float(temperature), int(seed) & ((1 << 64) - 1), int(step),
                                    _ptr(token), _ptr(conf), _ptr(entropy), _ptr(ws), nb,
                                    _stream(stream)))
+
+
+def dbd_prefill_attn(q, k, v, cu_seqlens, out, block_length, softmax_scale=0.0, page_table=None,
+                     k_cache=None, v_cache=None, ws=None, stream=None):
+    """Block-causal prefill attention over packed prompts; with k_cache /
+    v_cache / page_table also the prompts' K/V stored into the pages."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    S = cu_seqlens.shape[0] - 1
+    _need(q, torch.bfloat16, (T, Hq, D), "q")
+    _need(k, torch.bfloat16, (T, Hkv, D), "k")
+    _need(v, torch.bfloat16, (T, Hkv, D), "v")
+    _need(out, torch.bfloat16, (T, Hq, D), "out")
+    _need(cu_seqlens, torch.int32, (S + 1,), "cu_seqlens")
+    P = maxp = npages = 0
+    if k_cache is not None:
+        npages, _, P, _ = k_cache.shape
+        maxp = page_table.shape[1]
+        _need(v_cache, torch.bfloat16, tuple(k_cache.shape), "v_cache")
+        _need(page_table, torch.int32, (S, maxp), "page_table")
+    need = lib().dbd_prefill_workspace_size(S)
+    if ws is None:
+        ws = workspace(need, q.device)
+    _check(lib().dbd_prefill_attn(S, T, Hq, Hkv, D, int(block_length), _ptr(q), _ptr(k), _ptr(v),
+                                  _ptr(cu_seqlens), float(softmax_scale), _ptr(out), P, maxp,
+                                  npages, _ptr(page_table), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(ws), ws.numel(), _stream(stream)))
+    return out
 
 
 def dbd_remask_commit(block_tokens, seq_state, argmax_tok, conf, row_index_out, num_rows_out,

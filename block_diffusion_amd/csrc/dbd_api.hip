@@ -416,6 +416,52 @@ dbd_status dbd_remask_commit_rule(int S, int B, int mask_token_id, int rule,
                         static_cast<hipStream_t>(stream));
 }
 
+size_t dbd_prefill_workspace_size(int S) {
+  if (S < 1) return 0;
+  return dbd::prefill_ws_bytes(S);
+}
+
+dbd_status dbd_prefill_attn(int S, int T, int Hq, int Hkv, int D, int block_length,
+                            const dbd_bf16* q, const dbd_bf16* k, const dbd_bf16* v,
+                            const int32_t* cu_seqlens, float softmax_scale, dbd_bf16* out,
+                            int page_size, int max_pages_per_seq, int num_pages,
+                            const int32_t* page_table, dbd_bf16* k_cache, dbd_bf16* v_cache,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  REQUIRE(S >= 1 && S <= 65535, "S must be in [1,65535] (got %d)", S);
+  REQUIRE(T >= 0, "T must be >= 0 (got %d)", T);
+  REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  REQUIRE(256 % (Hq / Hkv) == 0, "Hq/Hkv must divide 256 (got %d)", Hq / Hkv);
+  REQUIRE(block_length >= 1, "block_length must be >= 1 (got %d)", block_length);
+  if (D != 64 && D != 128) return fail(DBD_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
+  REQUIRE((long)T * Hkv * D * 2 < (1L << 32), "T*Hkv*D*2 must be below 2^32");
+  REQUIRE((long)T * (Hq / Hkv) < (1L << 31), "T*Hq/Hkv too large");
+  REQUIRE(!isnan(softmax_scale), "softmax_scale is NaN");
+  REQUIRE_PTR(cu_seqlens);
+  if (T > 0) {
+    REQUIRE_PTR(q); REQUIRE_PTR(k); REQUIRE_PTR(v); REQUIRE_PTR(out);
+  }
+  if (k_cache != nullptr) {
+    REQUIRE_PTR(k_cache); REQUIRE_PTR(v_cache); REQUIRE_PTR(page_table);
+    REQUIRE(page_size >= 1 && max_pages_per_seq >= 1 && num_pages >= 1,
+            "page_size, max_pages_per_seq and num_pages must be >= 1 with a cache");
+  }
+  const size_t need = dbd::prefill_ws_bytes(S);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DBD_ERR_WORKSPACE, "prefill workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  REQUIRE(aligned(workspace, 256), "workspace is not 256-byte aligned");
+  dbd::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.cu_seqlens = cu_seqlens; a.out = out;
+  a.plan = static_cast<int32_t*>(workspace);
+  a.S = S; a.T_total = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.B = block_length;
+  const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.page_table = page_table; a.k_cache_out = k_cache; a.v_cache_out = k_cache ? v_cache : nullptr;
+  a.P = page_size; a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
+  hipError_t e = dbd::prefill_launch(a, D, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return DBD_OK;
+}
+
 dbd_status dbd_round(const dbd_round_args* a, void* stream) {
   dbd_status s = check_round(a);
   if (s != DBD_OK) return s;

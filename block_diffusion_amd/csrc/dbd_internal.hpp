@@ -111,4 +111,25 @@ constexpr int kRemaskMaxSeqs = 8192;
 constexpr uint32_t kCommitSaving = 4u;
 hipError_t remask_launch(const RemaskArgs& a, hipStream_t stream);
 
+// ----------------------------------------------------------- prefill
+struct PrefillArgs {
+  const uint16_t* q;           // [T][Hq][D] packed prompts
+  const uint16_t* k;           // [T][Hkv][D]
+  const uint16_t* v;
+  const int32_t* cu_seqlens;   // [S+1]
+  uint16_t* out;               // [T][Hq][D]
+  int32_t* plan;               // [S+1] tile prefix sums (workspace)
+  int S, T_total, Hq, Hkv, G, B;
+  float scale_log2;
+  // optional store of the prompts' K/V into the paged cache
+  const int32_t* page_table;   // [S][max_pages]
+  uint16_t* k_cache_out;       // NULL: no store
+  uint16_t* v_cache_out;
+  int P, max_pages, num_pages;
+};
+
+size_t prefill_ws_bytes(int S);
+int prefill_grid(int S, int T_total, int Hkv, int G);
+hipError_t prefill_launch(const PrefillArgs& a, int D, hipStream_t stream);
+
 }  // namespace dbd

@@ -318,6 +318,43 @@ dbd_status dbd_commit_block(int S, int B, int mask_token_id,
                             void* stream);
 
 /* ------------------------------------------------------------------------
+ * dbd_prefill_attn -- block-causal attention of a prefill over packed
+ * prompts, with the prompts' K/V optionally stored into the paged cache.
+ *
+ * Defined by the prefill pattern of a block-diffusion model (JetEngine
+ * developer notes, "ModelRunner": prefill and denoise use different
+ * attention patterns; "Layers": block-sparse varlen attention for the
+ * prefill, a store kernel for the cache; README, "Block Diffusion
+ * Decoding": earlier blocks fully visible, bidirectional in the block):
+ *   prompt s = rows cu_seqlens[s] .. cu_seqlens[s+1]-1 (L_s tokens);
+ *   token i of prompt s, q head h (kv head g = h / (Hq/Hkv)) attends to the
+ *   tokens j of prompt s with floor(j / block_length) <= floor(i /
+ *   block_length);
+ *   out = softmax(q . k^T * scale) . v over those keys.
+ * block_length = 1 is causal attention; block_length >= L_s is full
+ * attention.  With k_cache != NULL, token j of prompt s (every kv head) is
+ * also written to page page_table[s][j / page_size], slot j % page_size
+ * (positions past the table or page ids outside [0, num_pages) are not
+ * written).
+ * Layouts: q, out [T][Hq][D]; k, v [T][Hkv][D] (bf16, packed prompts);
+ * cu_seqlens int32 [S+1], non-decreasing, cu_seqlens[0] = 0,
+ * cu_seqlens[S] <= T; caches and page_table as dbd_attn_paged.
+ * Requirements: D in {64, 128}, Hq % Hkv == 0, 256 % (Hq/Hkv) == 0,
+ * block_length >= 1, T*Hkv*D*2 < 2^32, pointers 16-byte aligned.
+ * workspace: dbd_prefill_workspace_size(S) bytes, 256-B aligned.
+ * ---------------------------------------------------------------------- */
+dbd_status dbd_prefill_attn(int S, int T, int Hq, int Hkv, int D,
+                            int block_length, const dbd_bf16* q,
+                            const dbd_bf16* k, const dbd_bf16* v,
+                            const int32_t* cu_seqlens, float softmax_scale,
+                            dbd_bf16* out, int page_size,
+                            int max_pages_per_seq, int num_pages,
+                            const int32_t* page_table, dbd_bf16* k_cache,
+                            dbd_bf16* v_cache, void* workspace,
+                            size_t workspace_bytes, void* stream);
+size_t dbd_prefill_workspace_size(int S);
+
+/* ------------------------------------------------------------------------
  * dbd_round -- one whole denoise round: dbd_attn_paged, then
  * dbd_lmhead_conf on the row list (row_index, *num_rows), then
  * dbd_remask_commit, which overwrites (row_index, *num_rows) with the next

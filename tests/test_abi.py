@@ -27,6 +27,7 @@ def test_header_declares_the_round_calls():
     for n in ("dbd_attn_paged", "dbd_lmhead_conf", "dbd_remask_commit", "dbd_round",
               "dbd_lmhead_conf_entropy", "dbd_remask_commit_rule",
               "dbd_attn_paged_save", "dbd_commit_block", "dbd_lmhead_sample",
+              "dbd_prefill_attn", "dbd_prefill_workspace_size",
               "dbd_graph_create", "dbd_graph_launch", "dbd_graph_destroy",
               "dbd_attn_workspace_size", "dbd_lmhead_workspace_size",
               "dbd_round_workspace_size", "dbd_validate_inputs", "dbd_last_error",
@@ -127,6 +128,25 @@ def test_commit_block_rejects(S, B, prefix, stream, cap, end, status):
     L = api.lib()
     st = L.dbd_commit_block(S, B, 5, 16, 16, prefix, stream, cap, end, 16, 16, None)
     assert st == status and L.dbd_last_error()
+
+
+def _prefill(**kw):
+    a = dict(S=2, T=40, Hq=8, Hkv=2, D=128, B=4, cu=16, ws=256, wsb=1 << 12, kc=None)
+    a.update(kw)
+    return api.lib().dbd_prefill_attn(a["S"], a["T"], a["Hq"], a["Hkv"], a["D"], a["B"], 16, 16, 16,
+                                      a["cu"], 0.0, 16, 16, 4, 8, 16, a["kc"], 16, a["ws"],
+                                      a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=0), api.DBD_ERR_INVALID_ARG), (dict(B=0), api.DBD_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), api.DBD_ERR_INVALID_ARG), (dict(Hq=24, Hkv=2), api.DBD_ERR_INVALID_ARG),
+    (dict(D=96), api.DBD_ERR_UNSUPPORTED), (dict(cu=None), api.DBD_ERR_INVALID_ARG),
+    (dict(T=1 << 22, Hkv=8, Hq=8), api.DBD_ERR_INVALID_ARG),
+    (dict(ws=None), api.DBD_ERR_WORKSPACE), (dict(wsb=8), api.DBD_ERR_WORKSPACE),
+    (dict(ws=272), api.DBD_ERR_INVALID_ARG), (dict(kc=18), api.DBD_ERR_INVALID_ARG)])
+def test_prefill_rejects(kw, status):
+    assert _prefill(**kw) == status
 
 
 def test_lmhead_workspace_required():
