@@ -430,7 +430,8 @@ dbd_status dbd_prefill_attn(int S, int T, int Hq, int Hkv, int D, int block_leng
   REQUIRE(S >= 1 && S <= 65535, "S must be in [1,65535] (got %d)", S);
   REQUIRE(T >= 0, "T must be >= 0 (got %d)", T);
   REQUIRE(Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
-  REQUIRE(256 % (Hq / Hkv) == 0, "Hq/Hkv must divide 256 (got %d)", Hq / Hkv);
+  REQUIRE(dbd::prefill_rows_per_wg() % (Hq / Hkv) == 0, "Hq/Hkv must divide %d (got %d)",
+          dbd::prefill_rows_per_wg(), Hq / Hkv);
   REQUIRE(block_length >= 1, "block_length must be >= 1 (got %d)", block_length);
   if (D != 64 && D != 128) return fail(DBD_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", D);
   REQUIRE((long)T * Hkv * D * 2 < (1L << 32), "T*Hkv*D*2 must be below 2^32");

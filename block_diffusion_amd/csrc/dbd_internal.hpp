@@ -129,6 +129,7 @@ struct PrefillArgs {
 };
 
 size_t prefill_ws_bytes(int S);
+int prefill_rows_per_wg();   // query rows per workgroup (G must divide it)
 int prefill_grid(int S, int T_total, int Hkv, int G);
 hipError_t prefill_launch(const PrefillArgs& a, int D, hipStream_t stream);
 

@@ -9,16 +9,19 @@
 //
 // Unlike the denoise step, this is a dense contraction: every key tile is
 // used by many query rows, so the kernel is MFMA-bound.  Work item = (prompt
-// s, kv head g, tile of 256 query rows); a row is (token t, head gi) with
+// s, kv head g, tile of 64*PF_RT query rows); a row is (token t, head gi) with
 // row = t*G + gi, so the G query heads of a kv head share every key tile.
-// Four waves of 64 rows (four 16-row MFMA tiles) share a 3-stage LDS ring of
+// Four waves of 16*PF_RT rows share a 3-stage LDS ring of
 // 32-key K/V tiles that the waves fill with direct-to-LDS loads
 // (global_load_lds_dwordx4, 16-byte chunks XOR-permuted by row).  Per run of
-// 16 keys a wave computes S^T = K Q^T (v_mfma_f32_16x16x32_bf16), an online
-// softmax in fp32 (base 2), and O^T += V^T P^T (v_mfma_f32_16x16x16bf16_1k)
-// with V^T read by ds_read_b64_tr_b16.  The block-causal mask is a per-row
+// 32 keys a wave computes S^T = K Q^T in two 16-key halves, an online
+// softmax in fp32 (base 2), and O^T += V^T P^T, all with
+// v_mfma_f32_16x16x32_bf16 (the K = 32 form runs at twice the rate of the
+// K = 16 one on gfx950), V^T read by ds_read_b64_tr_b16.  The block-causal mask is a per-row
 // key bound, min(L, (floor(t/B)+1)*B); runs past a wave's largest bound are
-// skipped and runs below its smallest bound need no mask.  The running
+// skipped and runs below its smallest bound need no mask.  Row sums add
+// the fp32 probabilities (the P V product takes them rounded to bf16).  The
+// running
 // maximum is only moved when some row's new maximum exceeds it by more than
 // 2^8 (probabilities up to 2^8 are exact in the fp32 sums), which leaves
 // most runs without the rescale of the accumulators.
@@ -36,11 +39,26 @@ namespace {
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kPfKT = 32;                  // keys per stage
-constexpr int kPfNS = 3;                   // ring stages
-constexpr int kPfRT = 4;                   // 16-row MFMA tiles per wave
+#ifndef PF_KT
+#define PF_KT 32
+#endif
+#ifndef PF_NS
+#define PF_NS 2
+#endif
+#ifndef PF_RT
+#define PF_RT 2
+#endif
+#ifndef PF_OCC
+#define PF_OCC 2
+#endif
+#ifndef PF_SUM_ROUNDED
+#define PF_SUM_ROUNDED 0   // row sums over the fp32 probabilities
+#endif
+constexpr int kPfKT = PF_KT;               // keys per stage
+constexpr int kPfNS = PF_NS;               // ring stages
+constexpr int kPfRT = PF_RT;               // 16-row MFMA tiles per wave
 constexpr int kPfWaveRows = 16 * kPfRT;    // 64
-constexpr int kPfRows = 4 * kPfWaveRows;   // 256 query rows per workgroup
+constexpr int kPfRows = 4 * kPfWaveRows;   // query rows per workgroup
 
 template <int D>
 __device__ __forceinline__ int pswz(int r) {
@@ -72,7 +90,7 @@ __device__ __forceinline__ int pf_ldc(const int32_t* p, size_t i) {
 
 }  // namespace
 
-// plan[s] = sum over s' < s of ceil(L_s' * G / 256); plan[S] = the total
+// plan[s] = sum over s' < s of ceil(L_s' * G / kPfRows); plan[S] = the total
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
   __shared__ int s_wsum[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -110,7 +128,7 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(PrefillArgs a) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int RT = kPfRT, KT = kPfKT, NS = kPfNS;
   constexpr int KS = D / 32, DT = D / 16;
   constexpr int KVE = KT * D;              // elements of one K (or V) stage
@@ -118,6 +136,7 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int RPI = 64 / LPR;            // rows per 1 KB load
   constexpr int NLD = 2 * KT / RPI / 4;    // 1 KB loads per wave per stage (K and V)
   static_assert(NLD >= 1 && (2 * KT / RPI) % 4 == 0, "stage split over four waves");
+  static_assert(KT % 32 == 0, "runs of 32 keys");
   __shared__ __align__(16) uint16_t ring_[NS * 2 * KVE];
   lds_u16* const ring = (lds_u16*)ring_;
 
@@ -217,30 +236,39 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
   }
 
   // one run of 16 keys starting at key j0 from LDS rows kt16 / vt16
-  auto run16 = [&](const lds_u16* kt16, const lds_u16* vt16, int j0, bool masked) {
-    bf16x8 kf[KS];
+  // one run of 32 keys starting at key j0 from LDS rows kt32 / vt32: two
+  // 16-key halves for S^T, one softmax step, and P V with K = 32 MFMAs whose
+  // k slots 8*lg .. 8*lg+7 hold keys 4*lg .. 4*lg+3 of the first half, then
+  // of the second (the same order in both operands)
+  auto run32 = [&](const lds_u16* kt32, const lds_u16* vt32, int j0, bool masked) {
+    f32x4 sc[2][RT];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      kf[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kt16 + poff<D>(lr, lg + 4 * ks)));
-    f32x4 sc[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      sc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < 2; ++hh) {
+      bf16x8 kf[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], sc[rt], 0, 0, 0);
+        kf[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kt32 + hh * 16 * D + poff<D>(lr, lg + 4 * ks)));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        sc[hh][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          sc[hh][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], sc[hh][rt], 0, 0, 0);
+      }
     }
-    float xs[RT][4], tmax[RT];
+    float xs[RT][8], tmax[RT];
     bool grow = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       tmax[rt] = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = j0 + 4 * lg + i;
-        xs[rt][i] = (!masked || j < klim[rt]) ? sc[rt][i] * a.scale_log2 : -INFINITY;
+      for (int i = 0; i < 8; ++i) {
+        const int j = j0 + 16 * (i >> 2) + 4 * lg + (i & 3);
+        const float sv = sc[i >> 2][rt][i & 3];
+        xs[rt][i] = (!masked || j < klim[rt]) ? sv : -INFINITY;   // raw scores
         tmax[rt] = fmaxf(tmax[rt], xs[rt][i]);
       }
+      tmax[rt] *= a.scale_log2;
       tmax[rt] = fmaxf(tmax[rt], shfl_xor_f(tmax[rt], 16));
       tmax[rt] = fmaxf(tmax[rt], shfl_xor_f(tmax[rt], 32));
       grow |= tmax[rt] > m_run[rt] + 8.f;
@@ -258,30 +286,42 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
       }
     }
-    i16x4 pb[RT];
+    bf16x8 pb[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       float psum = 0.f;
-      short pbits[4];
+      uint32_t pw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t b = f2bf(fast_exp2(xs[rt][i] - m_run[rt]));
-        pbits[i] = (short)b;
-        psum += bf2f(b);
+      for (int i = 0; i < 8; i += 2) {
+        const float e0 = fast_exp2(fmaf(xs[rt][i], a.scale_log2, -m_run[rt]));
+        const float e1 = fast_exp2(fmaf(xs[rt][i + 1], a.scale_log2, -m_run[rt]));
+        const uint16_t b0 = f2bf(e0), b1 = f2bf(e1);
+#if PF_SUM_ROUNDED
+        psum += bf2f(b0) + bf2f(b1);
+#else
+        psum += e0 + e1;
+#endif
+        pw[i >> 1] = (uint32_t)b0 | ((uint32_t)b1 << 16);
       }
-      pb[rt] = i16x4{pbits[0], pbits[1], pbits[2], pbits[3]};
+      pb[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
       l_run[rt] += psum;
     }
-    // O^T[d][row] += V^T[d][key] P^T[key][row]; lane w of 16-lane group lg
-    // reads V[4*lg + w/4][16*dt + 4*(w%4) .. +3] by transpose reads
+    // O^T[d][row] += V^T[d][key] P^T[key][row]; in each half, lane w of
+    // 16-lane group lg reads V[4*lg + w/4][16*dt + 4*(w%4) .. +3] by
+    // transpose reads and receives V[4*lg .. 4*lg+3][16*dt + w]
     const int vrow = 4 * lg + (lr >> 2), vsub = 4 * (lr & 1), vch = (lr & 3) >> 1;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) i16x4*)(vt16 + poff<D>(vrow, 2 * dt + vch) + vsub));
+      const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vt32 + poff<D>(vrow, 2 * dt + vch) + vsub));
+      const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4*)(vt32 + 16 * D + poff<D>(vrow, 2 * dt + vch) + vsub));
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 v8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
-        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
+        acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt], acc[rt][dt], 0, 0, 0);
     }
   };
 
@@ -298,9 +338,9 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     issue(st + NS - 1);
     const lds_u16* slot = ring + (st % NS) * 2 * KVE;
 #pragma unroll
-    for (int hh = 0; hh < KT / 16; ++hh) {
-      const int j0 = st * KT + 16 * hh;
-      if (j0 < kend_w) run16(slot + hh * 16 * D, slot + KVE + hh * 16 * D, j0, j0 + 16 > kfree_w);
+    for (int hh = 0; hh < KT / 32; ++hh) {
+      const int j0 = st * KT + 32 * hh;
+      if (j0 < kend_w) run32(slot + hh * 32 * D, slot + KVE + hh * 32 * D, j0, j0 + 32 > kfree_w);
     }
   }
   pf_wait_vm<0>();   // no load may land in LDS after the workgroup is gone
@@ -326,6 +366,8 @@ __global__ __launch_bounds__(256, 1) void prefill_attn_kernel(PrefillArgs a) {
     }
   }
 }
+
+int prefill_rows_per_wg() { return kPfRows; }
 
 size_t prefill_ws_bytes(int S) { return ((size_t)(S + 1) * sizeof(int32_t) + 255) & ~(size_t)255; }
 

@@ -339,7 +339,7 @@ dbd_status dbd_commit_block(int S, int B, int mask_token_id,
  * Layouts: q, out [T][Hq][D]; k, v [T][Hkv][D] (bf16, packed prompts);
  * cu_seqlens int32 [S+1], non-decreasing, cu_seqlens[0] = 0,
  * cu_seqlens[S] <= T; caches and page_table as dbd_attn_paged.
- * Requirements: D in {64, 128}, Hq % Hkv == 0, 256 % (Hq/Hkv) == 0,
+ * Requirements: D in {64, 128}, Hq % Hkv == 0, 128 % (Hq/Hkv) == 0,
  * block_length >= 1, T*Hkv*D*2 < 2^32, pointers 16-byte aligned.
  * workspace: dbd_prefill_workspace_size(S) bytes, 256-B aligned.
  * ---------------------------------------------------------------------- */

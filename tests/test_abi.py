@@ -141,6 +141,7 @@ def _prefill(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(S=0), api.DBD_ERR_INVALID_ARG), (dict(B=0), api.DBD_ERR_INVALID_ARG),
     (dict(Hq=6, Hkv=4), api.DBD_ERR_INVALID_ARG), (dict(Hq=24, Hkv=2), api.DBD_ERR_INVALID_ARG),
+    (dict(Hq=512, Hkv=2), api.DBD_ERR_INVALID_ARG),
     (dict(D=96), api.DBD_ERR_UNSUPPORTED), (dict(cu=None), api.DBD_ERR_INVALID_ARG),
     (dict(T=1 << 22, Hkv=8, Hq=8), api.DBD_ERR_INVALID_ARG),
     (dict(ws=None), api.DBD_ERR_WORKSPACE), (dict(wsb=8), api.DBD_ERR_WORKSPACE),
