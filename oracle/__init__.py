@@ -23,7 +23,8 @@ from .remask import (remask, remask_rule, compact_rows, DENOISING, SAVING,
                      RULE_DYNAMIC, RULE_STATIC, RULE_SEQUENTIAL, RULE_ENTROPY)
 from .round import denoise_round
 from .block_commit import kv_save, commit_block, step_commit, FINISHED
-from .sampling import philox4x32_10, uniform01, sample_row, lmhead_sample
+from .sampling import (philox4x32_10, uniform01, sample_row, lmhead_sample, topk_topp_keep,
+                       sample_filtered)
 from .prefill import prefill_attention, prefill_store
 
 __all__ = ["widen", "attention", "attention_group", "lmhead_rows",
@@ -32,4 +33,5 @@ __all__ = ["widen", "attention", "attention_group", "lmhead_rows",
            "RULE_DYNAMIC", "RULE_STATIC", "RULE_SEQUENTIAL", "RULE_ENTROPY",
            "kv_save", "commit_block", "step_commit", "FINISHED",
            "philox4x32_10", "uniform01", "sample_row", "lmhead_sample",
+           "topk_topp_keep", "sample_filtered",
            "prefill_attention", "prefill_store"]

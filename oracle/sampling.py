@@ -34,8 +34,19 @@ plus token selection).  The pages give no formula.  Readings taken:
     to its sum of exp(z), independently of its value, so the token has
     probability exp(z_v) / sum exp(z) -- the Gumbel-max trick applied to
     blocks instead of single tokens (16 times fewer random numbers).
-Top-k and top-p filtering are not part of this reading (they need order
-statistics over the whole vocabulary before the draw).
+
+Top-k / top-p filtering (README usage examples: topk, topp; developer
+notes, "Benchmarking": top_p 0.95; "Ruled-Out Optimizations": a separate
+sampler after the logits was faster than a fused one).  Readings:
+  * tokens other than the mask token are ranked by logit, higher first, the
+    lower id first among equal logits;
+  * top_k > 0 keeps the first top_k of that ranking (all if fewer);
+  * top_p < 1 then keeps the shortest leading run of the kept tokens whose
+    running sum of exp((l - m) / T) reaches top_p times their total (at
+    least one token), i.e. top-p applies to the top-k distribution;
+  * the draw is the block draw above with every token outside the kept set
+    given zero weight; the confidence is unchanged (the model's
+    probability of the drawn token at temperature 1).
 """
 import numpy as np
 
@@ -70,17 +81,20 @@ def uniform01(words):
     return ((w >> np.uint64(9)).astype(np.float64) + 0.5) / float(1 << 23)
 
 
-def sample_row(logits, temperature, seed, row_id, step):
+def sample_row(logits, temperature, seed, row_id, step, keep=None):
     """One row: logits [V] float64 (mask token at -inf).  Returns
     (token, conf, info) where info holds what the tests need to recognise
     draws that float32 rounding could decide otherwise: the gap between the
     two largest G_b, the runner-up block's candidate, and the winning
     block's distance from its inverse-CDF boundaries (relative to S_b) with
-    the neighbouring candidates."""
+    the neighbouring candidates.  keep (bool [V], optional): only these
+    tokens can be drawn."""
     V = logits.shape[0]
     nc = -(-V // 32)
     z = np.full(nc * 32, -np.inf)
     z[:V] = logits / temperature
+    if keep is not None:
+        z[:V][~np.asarray(keep, dtype=bool)] = -np.inf
     ids = np.arange(nc * 32)
     # [chunk][q][h][r] -> [chunk][h][16 members in (q, r) order]
     zb = z.reshape(nc, 4, 2, 4).transpose(0, 2, 1, 3).reshape(nc, 2, 16)
@@ -136,3 +150,41 @@ def lmhead_sample(h_rows, w_vocab_bits, mask_id, row_ids, temperature, seed, ste
             toks[i0 + j], conf[i0 + j] = t, c
             infos.append(inf)
     return toks, conf, infos
+
+
+def topk_topp_keep(logits, temperature, top_k, top_p):
+    """The kept set of the filtering readings above: bool [V], and info on
+    the top-p boundary (its margin relative to the kept total, and the kept
+    sets one token shorter and one longer) for the tests."""
+    V = logits.shape[0]
+    cand = np.nonzero(np.isfinite(logits))[0]
+    order = cand[np.lexsort((cand, -logits[cand]))]      # higher logit, then lower id
+    n = order.size
+    k = n if (top_k <= 0 or top_k >= n) else int(top_k)
+    kept = order[:k]
+    info = dict(margin=np.inf, shorter=None, longer=None)
+    if top_p < 1.0:
+        m = logits[order[0]]
+        w = np.exp((logits[kept] - m) / temperature)
+        cum = np.cumsum(w)
+        target = top_p * cum[-1]
+        j = min(int(np.searchsorted(cum, target, side="left")), k - 1)
+        lo = cum[j - 1] if j > 0 else 0.0
+        info["margin"] = float(min(abs(target - lo), abs(cum[j] - target)) / cum[-1])
+        mk = lambda jj: np.isin(np.arange(V), kept[:jj + 1])
+        info["shorter"] = mk(max(j - 1, 0))
+        info["longer"] = mk(min(j + 1, k - 1))
+        kept = kept[:j + 1]
+    keep = np.zeros(V, dtype=bool)
+    keep[kept] = True
+    return keep, info
+
+
+def sample_filtered(logits, temperature, top_k, top_p, seed, row_id, step):
+    """One row drawn after top-k / top-p filtering.  Returns (token, conf,
+    info) like sample_row, info also holding the filter's boundary info."""
+    keep, finfo = topk_topp_keep(logits, temperature, top_k, top_p)
+    tok, conf, info = sample_row(logits, temperature, seed, row_id, step, keep)
+    info["filter"] = finfo
+    info["keep"] = keep
+    return tok, conf, info

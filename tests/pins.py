@@ -945,8 +945,79 @@ def check_sampler_seeds(impl):
     assert len(set(same)) >= 40
 
 
+def check_filter_bruteforce(impl):
+    """The kept set against a direct reading: rank by (higher logit, lower
+    id), keep the first top_k, then the shortest run reaching top_p of the
+    kept mass; ties at the boundary included."""
+    g = np.random.default_rng(41)
+    # equal logits: the running mass hits top_p times the total exactly
+    for top_p, n in ((0.25, 1), (0.5, 2), (0.75, 3)):
+        keep, _ = impl.topk_topp_keep(np.zeros(4), 1.0, 0, top_p)
+        assert np.array_equal(np.nonzero(keep)[0], np.arange(n)), (top_p, keep)
+    for trial in range(300):
+        V = int(g.integers(2, 14))
+        l = np.round(g.normal(0, 1.5, V), 1)            # rounding makes ties common
+        l[int(g.integers(0, V))] = -np.inf              # the mask token
+        T = float(g.choice([0.5, 1.0, 2.0]))
+        top_k = int(g.integers(0, V + 2))
+        top_p = float(g.choice([0.0, 0.3, 0.6, 0.9, 0.95, 1.0]))
+        keep, _ = impl.topk_topp_keep(l, T, top_k, top_p)
+        ranked = sorted([v for v in range(V) if np.isfinite(l[v])], key=lambda v: (-l[v], v))
+        if 0 < top_k < len(ranked):
+            ranked = ranked[:top_k]
+        if top_p < 1.0:
+            m = max(l[v] for v in ranked)
+            w = [math.exp((l[v] - m) / T) for v in ranked]
+            tot = math.fsum(w)
+            run, out = 0.0, []
+            for v, x in zip(ranked, w):
+                out.append(v)
+                run += x
+                if run >= top_p * tot:
+                    break
+            ranked = out
+        assert set(np.nonzero(keep)[0].tolist()) == set(ranked), (trial, l, T, top_k, top_p)
+
+
+def check_filtered_distribution(impl):
+    """Draws after filtering follow softmax(l/T) restricted to the kept set
+    (chi-square), and never leave it."""
+    from scipy.stats import chi2
+    g = np.random.default_rng(42)
+    V, N = 60, 3000
+    for T, top_k, top_p in ((1.0, 6, 1.0), (0.7, 0, 0.8), (1.3, 20, 0.9)):
+        l = g.normal(0, 1.2, V)
+        l[3] = -np.inf
+        keep, _ = impl.topk_topp_keep(l, T, top_k, top_p)
+        p = np.where(keep, np.exp((l - l[np.isfinite(l)].max()) / T), 0.0)
+        p /= p.sum()
+        cnt = np.zeros(V)
+        for step in range(N):
+            cnt[impl.sample_filtered(l, T, top_k, top_p, 77, 2, step)[0]] += 1
+        assert np.all(cnt[~keep] == 0)
+        x = np.sum((cnt[keep] - N * p[keep]) ** 2 / (N * p[keep]))
+        assert chi2.sf(x, keep.sum() - 1) > 1e-4, (T, top_k, top_p, x)
+
+
+def check_filter_special_cases(impl):
+    """No filtering draws exactly what the plain sampler draws; top_p = 0 or
+    top_k = 1 leaves the greedy token; top_k beyond the vocabulary is no
+    filter."""
+    g = np.random.default_rng(43)
+    for step in range(40):
+        l = g.normal(0, 2, 200)
+        l[9] = -np.inf
+        a = impl.sample_filtered(l, 0.9, 0, 1.0, 5, 1, step)[0]
+        assert a == impl.sample_row(l, 0.9, 5, 1, step)[0]
+        assert impl.sample_filtered(l, 0.9, 1000, 1.0, 5, 1, step)[0] == a
+        top = int(np.argmax(l))
+        assert impl.sample_filtered(l, 0.9, 0, 0.0, 5, 1, step)[0] == top
+        assert impl.sample_filtered(l, 0.9, 1, 1.0, 5, 1, step)[0] == top
+
+
 SAMPLE_CHECKS = [check_philox_known_answers, check_uniform01, check_sampler_distribution,
-                 check_sampler_block_choice, check_sampler_greedy_limit, check_sampler_seeds]
+                 check_sampler_block_choice, check_sampler_greedy_limit, check_sampler_seeds,
+                 check_filter_bruteforce, check_filtered_distribution, check_filter_special_cases]
 
 
 # ------------------------------------------------- block-causal prefill

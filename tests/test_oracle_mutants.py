@@ -77,6 +77,15 @@ MUTANTS = [
      "c = [lo1 ^ c[1] ^ k[0], hi1, hi0 ^ c[3] ^ k[1], lo0]", "sample"),
     ("sampling.py", "return ((w >> np.uint64(9)).astype(np.float64) + 0.5) / float(1 << 23)",
      "return ((w >> np.uint64(8)).astype(np.float64) + 0.5) / float(1 << 24)", "sample"),
+    ("sampling.py", "order = cand[np.lexsort((cand, -logits[cand]))]",
+     "order = cand[np.lexsort((cand, logits[cand]))]", "sample"),
+    ("sampling.py", "order = cand[np.lexsort((cand, -logits[cand]))]",
+     "order = cand[np.lexsort((-cand, -logits[cand]))]", "sample"),
+    ("sampling.py", "j = min(int(np.searchsorted(cum, target, side=\"left\")), k - 1)",
+     "j = min(int(np.searchsorted(cum, target, side=\"right\")), k - 1)", "sample"),
+    ("sampling.py", "w = np.exp((logits[kept] - m) / temperature)",
+     "w = np.exp((logits[order] - m) / temperature)", "sample"),
+    ("sampling.py", "z[:V][~np.asarray(keep, dtype=bool)] = -np.inf", "pass", "sample"),
     ("prefill.py", "allowed = blk[None, :] <= blk[:, None]", "allowed = blk[None, :] < blk[:, None]",
      "prefill"),
     ("prefill.py", "allowed = blk[None, :] <= blk[:, None]",
