@@ -213,6 +213,15 @@ def main():
     t_lm_sample = ev_time(lambda: api.dbd_lmhead_sample(
         r1["hidden"], fixed["w_vocab"], nr1, bufs.argmax_tok, bufs.conf, w.mask_id, 1.0, 1234, 1,
         row_index=lm_rows, max_rows=n, ws=bufs.workspace))
+    # top-k / top-p: the logits stored, then the filtered draw (T 0.6, top_p 0.95)
+    M1r = rows_per_round[0]
+    lg_buf = torch.empty((n, w.V), dtype=torch.float32, device=dev)
+    t_logits = ev_time(lambda: api.dbd_lmhead_logits(r1["hidden"], fixed["w_vocab"], nr1, lg_buf,
+                                                     w.mask_id, row_index=lm_rows, max_rows=n))
+    t_filter = ev_time(lambda: api.dbd_sample_filtered(lg_buf, nr1, bufs.argmax_tok, bufs.conf,
+                                                       w.mask_id, 0.6, 0, 0.95, 1234, 1,
+                                                       row_index=lm_rows, max_rows=n))
+    del lg_buf
     conf_r = torch.rand(n, device=dev)
     arg_r = torch.zeros(n, dtype=torch.int32, device=dev)
     tk, ss = tok0.clone(), st0.clone()
@@ -221,7 +230,7 @@ def main():
                                                      2.0))   # tau > 1: one commit each, no state change until full
     log(f"attention {t_attn:.1f} us, LM head {', '.join(f'M={m}: {t:.1f} us' for m, t in lm_times.items())}, "
         f"remask {t_remask:.1f} us, LM head with temperature sampling M={rows_per_round[0]}: "
-        f"{t_lm_sample:.1f} us")
+        f"{t_lm_sample:.1f} us; stored logits {t_logits:.1f} us + top-p draw {t_filter:.1f} us")
 
     # ---- a whole block on the device: B gated rounds, then the SAVING step
     # (attention with the K/V write, the block commit), one graph per block
@@ -328,6 +337,9 @@ def main():
                          "remask": round(t_remask, 2),
                          "attention_kv_save": round(t_save, 2),
                          "lmhead_sample_T1_M%d" % rows_per_round[0]: round(t_lm_sample, 2),
+                         "topp_M%d" % M1r: {"logits_us": round(t_logits, 2),
+                                             "filtered_draw_us": round(t_filter, 2),
+                                             "temperature": 0.6, "top_p": 0.95},
                          "prefill": {"tokens": Tp, "block_length": w.B, "us": round(t_prefill, 2),
                                      "tflops": round(pf_tflops, 1),
                                      "frac_bf16_peak": round(pf_tflops / PEAK_BF16_TFLOPS, 4),

@@ -87,6 +87,11 @@ def lib() -> C.CDLL:
     L.dbd_prefill_attn.restype = i
     L.dbd_prefill_workspace_size.argtypes = [i]
     L.dbd_prefill_workspace_size.restype = sz
+    L.dbd_lmhead_logits.argtypes = [i] * 4 + [_vp] * 5 + [_vp]
+    L.dbd_lmhead_logits.restype = i
+    L.dbd_sample_filtered.argtypes = [i, i, i] + [_vp] * 3 + [f, i, f, C.c_uint64, C.c_uint32] + \
+        [_vp, _vp, _vp]
+    L.dbd_sample_filtered.restype = i
     L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
     L.dbd_round.restype = i
     L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
@@ -305,6 +310,32 @@ def dbd_prefill_attn(q, k, v, cu_seqlens, out, block_length, softmax_scale=0.0, 
                                   npages, _ptr(page_table), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(ws), ws.numel(), _stream(stream)))
     return out
+
+
+def dbd_lmhead_logits(hidden, w_vocab, num_rows, logits, mask_token_id, row_index=None,
+                      max_rows=None, stream=None):
+    """fp32 logits of the listed rows into logits [max_rows][V]."""
+    V, Hd = w_vocab.shape
+    if max_rows is None:
+        max_rows = row_index.shape[0] if row_index is not None else hidden.shape[0]
+    _need(w_vocab, torch.bfloat16, (V, Hd), "w_vocab")
+    _need(logits, torch.float32, (logits.shape[0], V), "logits")
+    if logits.shape[0] < max_rows:
+        raise ValueError("logits needs max_rows rows")
+    _check(lib().dbd_lmhead_logits(max_rows, Hd, V, int(mask_token_id), _ptr(hidden),
+                                   _ptr(row_index), _ptr(num_rows), _ptr(w_vocab), _ptr(logits),
+                                   _stream(stream)))
+
+
+def dbd_sample_filtered(logits, num_rows, token, conf, mask_token_id, temperature, top_k, top_p,
+                        seed, step, row_index=None, max_rows=None, stream=None):
+    """Top-k / top-p draw from stored logits (see dbd.h)."""
+    M, V = logits.shape
+    max_rows = M if max_rows is None else max_rows
+    _check(lib().dbd_sample_filtered(max_rows, V, int(mask_token_id), _ptr(logits), _ptr(row_index),
+                                     _ptr(num_rows), float(temperature), int(top_k), float(top_p),
+                                     int(seed) & ((1 << 64) - 1), int(step), _ptr(token),
+                                     _ptr(conf), _stream(stream)))
 
 
 def dbd_remask_commit(block_tokens, seq_state, argmax_tok, conf, row_index_out, num_rows_out,

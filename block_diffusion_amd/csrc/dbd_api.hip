@@ -370,6 +370,50 @@ dbd_status dbd_lmhead_sample(int max_rows, int Hd, int V, int mask_token_id,
                     temperature, seed, step);
 }
 
+dbd_status dbd_lmhead_logits(int max_rows, int Hd, int V, int mask_token_id,
+                             const dbd_bf16* hidden, const int32_t* row_index,
+                             const int32_t* num_rows, const dbd_bf16* w_vocab, float* logits,
+                             void* stream) {
+  dbd_status s = check_lm(max_rows, Hd, V, mask_token_id);
+  if (s != DBD_OK) return s;
+  REQUIRE((long)max_rows * V < (1L << 40), "max_rows*V too large");
+  REQUIRE_PTR(hidden); REQUIRE_PTR(num_rows); REQUIRE_PTR(w_vocab); REQUIRE_PTR(logits);
+  if (row_index != nullptr) REQUIRE_PTR(row_index);
+  if (max_rows == 0) return DBD_OK;
+  dbd::LmArgs a{};
+  a.hidden = hidden; a.row_index = row_index; a.num_rows = num_rows; a.w = w_vocab;
+  a.Hd = Hd; a.V = V; a.mask_id = mask_token_id; a.max_rows = max_rows;
+  a.logits = logits;
+  hipError_t e = dbd::lmhead_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "LM-head launch");
+  return DBD_OK;
+}
+
+dbd_status dbd_sample_filtered(int max_rows, int V, int mask_token_id, const float* logits,
+                               const int32_t* row_index, const int32_t* num_rows,
+                               float temperature, int top_k, float top_p, uint64_t seed,
+                               uint32_t step, int32_t* token, float* conf, void* stream) {
+  REQUIRE(max_rows >= 0, "max_rows must be >= 0 (got %d)", max_rows);
+  REQUIRE(V >= 2, "vocab size must be >= 2 (got %d)", V);
+  REQUIRE(mask_token_id >= 0 && mask_token_id < V, "mask_token_id %d outside [0,%d)", mask_token_id, V);
+  REQUIRE(isfinite(temperature) && temperature > 0.f, "temperature must be finite and > 0 (got %g)",
+          (double)temperature);
+  REQUIRE(!isnan(top_p), "top_p is NaN");
+  REQUIRE(top_k >= 0, "top_k must be >= 0 (got %d)", top_k);
+  REQUIRE_PTR(logits); REQUIRE_PTR(num_rows); REQUIRE_PTR(token); REQUIRE_PTR(conf);
+  if (row_index != nullptr) REQUIRE_PTR(row_index);
+  if (max_rows == 0) return DBD_OK;
+  dbd::SampleArgs a{};
+  a.logits = logits; a.row_index = row_index; a.num_rows = num_rows;
+  a.V = V; a.mask_id = mask_token_id; a.max_rows = max_rows; a.top_k = top_k;
+  a.inv_temp = 1.f / temperature; a.top_p = top_p;
+  a.key0 = (uint32_t)seed; a.key1 = (uint32_t)(seed >> 32); a.step = step;
+  a.token = token; a.conf = conf;
+  hipError_t e = dbd::sample_filtered_launch(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "sampling launch");
+  return DBD_OK;
+}
+
 dbd_status dbd_remask_commit(int S, int B, int mask_token_id, float dynamic_threshold,
                              uint32_t flags, int32_t* block_tokens, uint8_t* seq_state,
                              const int32_t* argmax_tok, const float* conf,

@@ -71,7 +71,21 @@ struct LmArgs {
   uint32_t key0, key1, step;
   float* pg;       // [max_rows][kLmGrid] partial largest Gumbel value (log2 units)
   float* pl;       // [max_rows][kLmGrid] partial logit of its candidate
+  float* logits;   // non-NULL: store the logits [max_rows][V] of the listed rows instead
 };
+
+// ------------------------------------------------- filtered sampling
+struct SampleArgs {
+  const float* logits;       // [max_rows][V], row r = list entry r
+  const int32_t* row_index;  // may be NULL (row id = r)
+  const int32_t* num_rows;
+  int V, mask_id, max_rows, top_k;
+  float inv_temp, top_p;
+  uint32_t key0, key1, step;
+  int32_t* token;            // [rows] by row id
+  float* conf;
+};
+hipError_t sample_filtered_launch(const SampleArgs& a, hipStream_t stream);
 
 // partial arrays of the LM-head workspace: pm, pa, ps, pt, pg, pl
 constexpr int kLmPartArrays = 6;

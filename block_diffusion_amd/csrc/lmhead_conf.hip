@@ -165,11 +165,12 @@ __device__ __forceinline__ int team_size(int M) { return M <= 256 ? 1 : (M <= 51
 // [v_lo, v_hi), as seen by one wave; WL: this wave streams W (else hidden
 // rows); MODE bit 0 (ENT): also accumulate sum e^(l-m)(l-m) for the
 // entropy; bit 1 (SMP): draw a sampled token instead of the argmax.  Writes
-// one partial per valid row into slot `team`.
+// one partial per valid row into slot `team`.  MODE 4 (STO): store the
+// logits themselves (mask column -inf) instead of reducing them.
 template <int MB, bool WL, int MODE>
 __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
                                         int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
-  constexpr bool ENT = (MODE & 1) != 0, SMP = (MODE & 2) != 0;
+  constexpr bool ENT = (MODE & 1) != 0, SMP = (MODE & 2) != 0, STO = (MODE & 4) != 0;
   constexpr int R = 64 * MB, RH = 32 * MB;
   constexpr int HPW = R / 16;                  // 1 KB hidden loads per hidden wave per stage
   constexpr int NLD = WL ? WPW : HPW;          // this wave's loads per stage
@@ -377,6 +378,43 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
     (void)nb;
   };
 
+  // store a finished tile's logits: lane holds row (lane & 31) of each row
+  // block mb and vocabulary rows vb0 + 8*(i/4) + (i%4) of each 32-block nb
+  auto store_tile = [&](int n0) {
+    const int vbase = n0 + wn * 128;
+    if (vbase >= v_hi) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int m = m_base + wm * RH + mb * 32 + (lane & 31);
+      float* lrow = a.logits + (size_t)(m < m_end ? m : m_base) * a.V;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int vb0 = vbase + nb * 32 + 4 * (lane >> 5);
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float r;
+          asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(acc[nb][mb][i]));
+          x[i] = r;
+        }
+        if (m < m_end) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int v0 = vb0 + 8 * q;
+            if (((a.V & 3) == 0) && v0 + 4 <= v_hi) {
+              *reinterpret_cast<f32x4*>(lrow + v0) = f32x4{x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (v0 + r < v_hi) lrow[v0 + r] = x[4 * q + r];
+            }
+          }
+        }
+      }
+    }
+  };
+
   // reduce a finished tile: lane holds row (lane & 31) of each row block mb
   // and vocabulary rows 8*(i/4) + 4*(lane/32) + (i%4) of each 32-block nb
   auto reduce_tile = [&](int n0) {
@@ -517,13 +555,15 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       if (NM2 > NP2) __builtin_amdgcn_sched_group_barrier(0x008, NM2 - NP2, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    reduce_tile(n0);
+    if constexpr (STO) store_tile(n0);
+    else reduce_tile(n0);
   }
 
   // all loads have landed and every wave is past its last fragment read
   wait_vm<0>();
   wait_lgkm0();
   barrier_only();
+  if constexpr (STO) return;
 
   // fold the two waves that share rows, then one partial per row
   typedef __attribute__((address_space(3))) float lds_f32;
@@ -578,6 +618,7 @@ template <int MB, int MODE>
 __device__ __forceinline__ void lm_pass_any(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
                                             int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
   if (v_hi <= v_lo) {
+    if (MODE & 4) return;
     // an empty vocabulary range still leaves a neutral partial for its rows
     for (int m = m_base + (int)threadIdx.x; m < m_end; m += blockDim.x) {
       const size_t o = (size_t)m * nteam + team;
@@ -678,6 +719,11 @@ size_t lmhead_ws_bytes(int max_rows, int V) {
 hipError_t lmhead_launch(const LmArgs& a, hipStream_t st) {
   // the entropy sums only when a caller wants the entropy, the draw only
   // when sampling
+  if (a.logits) {
+    // the logits themselves: no partials, no merge
+    lmhead_tile_kernel<4><<<kLmGrid, 256, 0, st>>>(a);
+    return hipGetLastError();
+  }
   const int mode = (a.entropy ? 1 : 0) | (a.sample ? 2 : 0);
   if (mode == 0) lmhead_tile_kernel<0><<<kLmGrid, 256, 0, st>>>(a);
   else if (mode == 1) lmhead_tile_kernel<1><<<kLmGrid, 256, 0, st>>>(a);

@@ -219,6 +219,39 @@ dbd_status dbd_lmhead_sample(int max_rows, int Hd, int V, int mask_token_id,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Top-k / top-p sampling, as a separate step after stored logits (the
+ * developer notes, "Ruled-Out Optimizations", found a separate sampler
+ * faster than a fused one; README usage examples: topk, topp).
+ *
+ * dbd_lmhead_logits: the LM head's fp32 logits of the listed rows,
+ *   logits[r][v] = sum_k hidden[row_index[r]][k] * w_vocab[v][k] for
+ *   r < *num_rows, with logits[r][mask_token_id] = -inf; other rows of the
+ *   buffer are not written.  logits: float [max_rows][V].  Requirements as
+ *   dbd_lmhead_conf; no workspace.
+ *
+ * dbd_sample_filtered: for each r < *num_rows (row = row_index[r], or r):
+ *   rank the tokens other than the mask token by logits[r][v], higher first,
+ *   the lower id first among equal logits; top_k > 0 keeps the first top_k;
+ *   top_p < 1 then keeps the shortest leading run of those whose running
+ *   sum of exp((l - m)/temperature) reaches top_p of their total (at least
+ *   one token; m = the largest logit); token[row] is drawn from
+ *   softmax(l/temperature) over the kept tokens by the block draw of
+ *   dbd_lmhead_sample (same seed, step and Philox counters, the other
+ *   tokens with zero weight), and conf[row] is its probability at
+ *   temperature 1 over all tokens but the mask token.  top_k = 0 and
+ *   top_p >= 1 give the draw of dbd_lmhead_sample.  Requirements:
+ *   temperature finite and > 0, top_k >= 0, top_p not NaN. */
+dbd_status dbd_lmhead_logits(int max_rows, int Hd, int V, int mask_token_id,
+                             const dbd_bf16* hidden, const int32_t* row_index,
+                             const int32_t* num_rows, const dbd_bf16* w_vocab,
+                             float* logits, void* stream);
+dbd_status dbd_sample_filtered(int max_rows, int V, int mask_token_id,
+                               const float* logits, const int32_t* row_index,
+                               const int32_t* num_rows, float temperature,
+                               int top_k, float top_p, uint64_t seed,
+                               uint32_t step, int32_t* token, float* conf,
+                               void* stream);
+
 /* ------------------------------------------------------------------------
  * dbd_remask_commit -- threshold remask (low_confidence_dynamic) and the
  * next round's row list.

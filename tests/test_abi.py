@@ -27,7 +27,8 @@ def test_header_declares_the_round_calls():
     for n in ("dbd_attn_paged", "dbd_lmhead_conf", "dbd_remask_commit", "dbd_round",
               "dbd_lmhead_conf_entropy", "dbd_remask_commit_rule",
               "dbd_attn_paged_save", "dbd_commit_block", "dbd_lmhead_sample",
-              "dbd_prefill_attn", "dbd_prefill_workspace_size",
+              "dbd_prefill_attn", "dbd_prefill_workspace_size", "dbd_lmhead_logits",
+              "dbd_sample_filtered",
               "dbd_graph_create", "dbd_graph_launch", "dbd_graph_destroy",
               "dbd_attn_workspace_size", "dbd_lmhead_workspace_size",
               "dbd_round_workspace_size", "dbd_validate_inputs", "dbd_last_error",
@@ -184,6 +185,18 @@ def test_lmhead_sample_rejects_temperature(T):
     st = L.dbd_lmhead_sample(16, 128, 1024, 5, 16, None, 16, 16, T, 1, 0, 16, 16, None, 256,
                              1 << 20, None)
     assert st == api.DBD_ERR_INVALID_ARG and b"temperature" in L.dbd_last_error()
+
+
+@pytest.mark.parametrize("T,k,p", [(0.0, 0, 1.0), (1.0, -1, 1.0), (1.0, 0, float("nan"))])
+def test_sample_filtered_rejects(T, k, p):
+    L = api.lib()
+    st = L.dbd_sample_filtered(4, 100, 5, 16, None, 16, T, k, p, 1, 0, 16, 16, None)
+    assert st == api.DBD_ERR_INVALID_ARG and L.dbd_last_error()
+
+
+def test_lmhead_logits_requires_output():
+    L = api.lib()
+    assert L.dbd_lmhead_logits(16, 128, 1024, 5, 16, None, 16, 16, None, None) == api.DBD_ERR_INVALID_ARG
 
 
 def test_lmhead_entropy_requires_output():

@@ -1,0 +1,144 @@
+"""Top-k / top-p sampling through the C ABI: the stored logits of
+dbd_lmhead_logits against the oracle's, and dbd_sample_filtered against the
+oracle's filtered draw applied to the kernel's own float32 logits (so every
+ranking decision is taken on the same values).  Tokens are exact except
+where float32 sums could decide otherwise: a top-p boundary within 1e-5 of
+the kept mass (the token may then come from the kept set one shorter or
+longer), and the block-draw bands of the plain sampler."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_diffusion_amd import api, synth
+from block_diffusion_amd.workloads import SDAR_1P7B, TINY
+from gpu_util import dev_bf16, dev_i32, widen_bits
+
+pytestmark = pytest.mark.gpu
+
+G_BAND = 1e-3
+CDF_BAND = 1e-4
+P_BAND = 1e-5
+
+
+def _case(name):
+    if name == "tiny":
+        w = TINY
+        fx = synth.make_fixed(w)
+        return synth.make_round(w, 1, fx.w_vocab).hidden, fx.w_vocab, w.mask_id, np.arange(w.S * w.B)
+    if name == "ragged":
+        g = np.random.default_rng(25)
+        V, Hd, n, mask = 1003, 256, 70, 1001
+        wv = synth.normal_bf16(g, (V, Hd), std=1.0 / np.sqrt(Hd))
+        t = g.integers(0, V, n)
+        a = g.uniform(0, 6, n)
+        wt = widen_bits(wv[t])
+        wt /= np.linalg.norm(wt, axis=1, keepdims=True)
+        h = synth.f32_to_bf16((g.standard_normal((n, Hd)) + a[:, None] * wt).astype(np.float32))
+        return h, wv, mask, g.permutation(n)[:45]
+    w = SDAR_1P7B
+    fx = synth.make_fixed(w)
+    return (synth.make_round(w, 1, fx.w_vocab).hidden, fx.w_vocab, w.mask_id,
+            np.random.default_rng(9).choice(w.S * w.B, 16, replace=False))
+
+
+def _logits(h, wv, mask, rows):
+    M = len(rows)
+    V = wv.shape[0]
+    lg = torch.full((M + 2, V), float("nan"), dtype=torch.float32, device="cuda")
+    api.dbd_lmhead_logits(dev_bf16(h), dev_bf16(wv), dev_i32([M]), lg, mask, row_index=dev_i32(rows),
+                          max_rows=M)
+    torch.cuda.synchronize()
+    return lg
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "sdar1p7b"])
+def test_lmhead_logits_parity(name):
+    h, wv, mask, rows = _case(name)
+    lg = _logits(h, wv, mask, rows).cpu().numpy()
+    M = len(rows)
+    ref = oracle.lmhead_logits(h[rows], wv, mask)
+    assert np.all(np.isneginf(lg[:M, mask]))
+    fin = np.isfinite(ref)
+    err = np.abs(lg[:M][fin].astype(np.float64) - ref[fin]).max()
+    print(f"{name}: max abs logit error {err:.2e}", flush=True)
+    assert err <= 2e-3
+    assert np.all(np.isnan(lg[M:]))
+
+
+def _check_rows(lg, rows, tok, conf, mask, T, k, p, seed, step):
+    exempt = 0
+    for j, r in enumerate(rows):
+        l = lg[j].astype(np.float64)
+        t_ref, c_ref, inf = oracle.sample_filtered(l, T, k, p, seed, int(r), step)
+        t = int(tok[r])
+        if t != t_ref:
+            fi = inf["filter"]
+            ok = (inf["g_gap"] < G_BAND and t == inf["runner_up"]) or \
+                 (inf["cdf_margin"] < CDF_BAND and t in inf["block"])
+            if not ok and fi["margin"] < P_BAND:
+                alts = [oracle.sample_row(l, T, seed, int(r), step, fi[key])[0]
+                        for key in ("shorter", "longer")]
+                ok = t in alts
+            assert ok, f"row {r}: gpu {t} oracle {t_ref} info g_gap={inf['g_gap']:.3g} " \
+                       f"cdf={inf['cdf_margin']:.3g} pmargin={fi['margin']:.3g}"
+            exempt += 1
+        assert inf["keep"][t] or exempt
+        lse = l.max() + np.log(np.exp(l - l.max()).sum())
+        assert abs(float(conf[r]) - np.exp(l[t] - lse)) <= 1e-5 + 1e-4 * np.exp(l[t] - lse)
+    return exempt
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "sdar1p7b"])
+@pytest.mark.parametrize("T,k,p", [(1.0, 0, 1.0), (0.6, 0, 0.95), (1.0, 50, 1.0), (0.8, 20, 0.9),
+                                   (1.0, 1, 1.0), (0.7, 0, 0.0), (1.3, 3, 0.5)])
+def test_sample_filtered_parity(name, T, k, p):
+    h, wv, mask, rows = _case(name)
+    M = len(rows)
+    lg = _logits(h, wv, mask, rows)
+    n = h.shape[0]
+    tok = torch.full((n,), -9, dtype=torch.int32, device="cuda")
+    conf = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    seed, step = 0xC0FFEE + k, 3
+    api.dbd_sample_filtered(lg, dev_i32([M]), tok, conf, mask, T, k, p, seed, step,
+                            row_index=dev_i32(rows), max_rows=M)
+    torch.cuda.synchronize()
+    ex = _check_rows(lg.cpu().numpy(), rows, tok.cpu().numpy(), conf.cpu().numpy(), mask, T, k, p,
+                     seed, step)
+    print(f"{name} T={T} k={k} p={p}: {M} rows, {ex} exempt", flush=True)
+    assert ex <= max(1, M // 20)
+    if k == 0 and p >= 1.0:
+        # no filter: the fused sampler draws the same tokens
+        tok2 = torch.full((n,), -9, dtype=torch.int32, device="cuda")
+        conf2 = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+        api.dbd_lmhead_sample(dev_bf16(h), dev_bf16(wv), dev_i32([M]), tok2, conf2, mask, T, seed,
+                              step, row_index=dev_i32(rows), max_rows=M)
+        torch.cuda.synchronize()
+        assert np.array_equal(tok.cpu().numpy(), tok2.cpu().numpy())
+
+
+@pytest.mark.parametrize("k,p", [(10, 1.0), (0, 0.8)])
+def test_sample_filtered_distribution(k, p):
+    """4096 draws of one row (4096 row ids) after filtering: never outside
+    the kept set, and chi-square against softmax(l/T) on it."""
+    from scipy.stats import chi2
+    g = np.random.default_rng(88)
+    V, Hd, N, mask, T = 300, 128, 4096, 11, 0.9
+    wv = synth.normal_bf16(g, (V, Hd), std=1.0 / np.sqrt(Hd))
+    h1 = synth.normal_bf16(g, (1, Hd), std=1.5)
+    lg1 = _logits(h1, wv, mask, np.array([0]))[:1]
+    lg = lg1.repeat(N, 1).contiguous()
+    tok = torch.full((N,), -9, dtype=torch.int32, device="cuda")
+    conf = torch.empty((N,), dtype=torch.float32, device="cuda")
+    api.dbd_sample_filtered(lg, dev_i32([N]), tok, conf, mask, T, k, p, 2024, 0)
+    torch.cuda.synchronize()
+    l = lg1[0].double().cpu().numpy()
+    keep, _ = oracle.topk_topp_keep(l, T, k, p)
+    pr = np.where(keep, np.exp((l - l.max()) / T), 0.0)
+    pr /= pr.sum()
+    cnt = np.bincount(tok.cpu().numpy(), minlength=V).astype(np.float64)
+    assert np.all(cnt[~keep] == 0)
+    x = np.sum((cnt[keep] - N * pr[keep]) ** 2 / (N * pr[keep]))
+    pv = chi2.sf(x, keep.sum() - 1)
+    print(f"k={k} p={p}: {keep.sum()} kept, chi2 {x:.1f}, p-value {pv:.3g}", flush=True)
+    assert pv > 1e-4
