@@ -25,9 +25,11 @@
 // block) once prefix_len reaches end_len[s].  A sequence that the rule
 // fills in this launch stays SAVING until its own SAVING forward.
 //
-// One workgroup of 16 waves.  Pass 1: a wave per sequence, lane = block
-// position (B <= 64): ballots of the masked set; the rule's choice is built
-// one wave-wide selection at a time (max or min, then the lowest lane).
+// One workgroup of 16 waves.  Pass 1: a wave holds 64/SEGW sequences at
+// once (SEGW = the power of two >= B), one per segment of lanes, lane =
+// block position within it: ballots of the masked set; the rule's choice is
+// built one segment-wide selection at a time (max or min, then the lowest
+// position).
 // The still-masked set of each sequence is kept as a 64-bit mask in LDS.
 // Pass 2: exclusive scan of the per-sequence counts.  Pass 3: each
 // still-masked position writes s*B+i at its rank, so the list is
@@ -51,43 +53,62 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
   // rows_in may alias num_rows_out: read it before pass 2 writes the count
   if (a.round_counter != nullptr && tid == 0 && *a.rows_in > 0) *a.round_counter += 1;
 
+  // A wave holds NSEG sequences at once, one per segment of SEGW lanes
+  // (SEGW = the power of two >= B); lane = segment * SEGW + position.
+  // Ballots are cut to the segment's bits, and reductions shuffle with
+  // offsets below SEGW, so they stay inside the segment; every branch on a
+  // sequence's data is taken by all lanes of its segment together.
+  const int SEGW = B <= 1 ? 1 : 1 << (32 - __clz(B - 1));
+  const int NSEG = 64 / SEGW;
+  const int seg = lane / SEGW, pos = lane % SEGW;
+  const unsigned long long segmask = SEGW == 64 ? ~0ull : ((1ull << SEGW) - 1ull);
+  auto sball = [&](bool p) { return (__ballot(p) >> (seg * SEGW)) & segmask; };
+  auto seg_max = [&](float x) {
+    for (int off = SEGW >> 1; off >= 1; off >>= 1) x = fmaxf(x, shfl_xor_f(x, off));
+    return x;
+  };
+  auto seg_min = [&](float x) {
+    for (int off = SEGW >> 1; off >= 1; off >>= 1) x = fminf(x, shfl_xor_f(x, off));
+    return x;
+  };
+
   // pass 1: commit, state, still-masked set
-  for (int s = wave; s < S; s += 16) {
-    const uint8_t st = a.seq_state[s];  // same for every lane of the wave
-    const bool in = lane < B;
-    if (st == kSaving && (a.flags & kCommitSaving)) {
+  for (int base = wave * NSEG; base < S; base += 16 * NSEG) {
+    const int s = base + seg;
+    const bool live = s < S;
+    const uint8_t st = live ? a.seq_state[s] : (uint8_t)0;   // same on the segment's lanes
+    const bool in = live && pos < B;
+    if (live && st == kSaving && (a.flags & kCommitSaving)) {
       const int L = a.prefix_len[s];
-      if (a.token_stream != nullptr && in && L + lane >= 0 && L + lane < a.stream_cap)
-        a.token_stream[(size_t)s * a.stream_cap + L + lane] = a.block_tokens[s * B + lane];
+      if (a.token_stream != nullptr && in && L + pos >= 0 && L + pos < a.stream_cap)
+        a.token_stream[(size_t)s * a.stream_cap + L + pos] = a.block_tokens[s * B + pos];
       const int L2 = L + B;
       const bool fin = a.end_len != nullptr && L2 >= a.end_len[s];
-      if (in && !fin) a.block_tokens[s * B + lane] = a.mask_id;
-      if (lane == 0) {
+      if (in && !fin) a.block_tokens[s * B + pos] = a.mask_id;
+      if (pos == 0) {
         a.prefix_len[s] = L2;
         a.seq_state[s] = fin ? kFinished : kDenoising;
         if (a.num_committed && !(a.flags & kCompactOnly)) a.num_committed[s] = 0;
       }
-      const unsigned long long fresh = __ballot(in && !fin);
-      if (lane == 0) s_left[s] = fresh;
+      const unsigned long long fresh = sball(in && !fin);
+      if (pos == 0) s_left[s] = fresh;
       continue;
     }
     const bool den = st == kDenoising;
-    const bool masked = in && den && a.block_tokens[s * B + lane] == a.mask_id;
-    const unsigned long long mball = __ballot(masked);
+    const bool masked = in && den && a.block_tokens[s * B + pos] == a.mask_id;
+    const unsigned long long mball = sball(masked);
     bool still = masked;
-    if (den && !(a.flags & kCompactOnly)) {
+    if (live && den && !(a.flags & kCompactOnly)) {
       unsigned long long cball = 0ull;
       if (a.rule == 0) {
-        const float c = masked ? a.conf[s * B + lane] : -INFINITY;
-        cball = __ballot(masked && c >= a.tau);
+        const float c = masked ? a.conf[s * B + pos] : -INFINITY;
+        cball = sball(masked && c >= a.tau);
         if (cball == 0ull && mball != 0ull) {
           if (a.flags & kFallbackLeftmost) {
             cball = mball & (~mball + 1ull);  // lowest set bit
           } else {
-            float best = c;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) best = fmaxf(best, shfl_xor_f(best, off));
-            const unsigned long long tie = __ballot(masked && c == best);
+            const float best = seg_max(c);
+            const unsigned long long tie = sball(masked && c == best);
             cball = tie & (~tie + 1ull);
           }
         }
@@ -100,15 +121,13 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
           rest ^= low;
         }
       } else if (a.rule == 1) {
-        // k times: the most confident remaining position, lowest lane on ties
-        const float c = masked ? a.conf[s * B + lane] : -INFINITY;
+        // k times: the most confident remaining position, lowest on ties
+        const float c = masked ? a.conf[s * B + pos] : -INFINITY;
         unsigned long long rest = mball;
         for (int r = 0; r < a.k && rest != 0ull; ++r) {
-          const bool cand = (rest >> lane) & 1ull;
-          float best = cand ? c : -INFINITY;
-#pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) best = fmaxf(best, shfl_xor_f(best, off));
-          unsigned long long tie = __ballot(cand && c == best);
+          const bool cand = (rest >> pos) & 1ull;
+          const float best = seg_max(cand ? c : -INFINITY);
+          unsigned long long tie = sball(cand && c == best);
           if (tie == 0ull) tie = rest;   // every remaining value is -inf or NaN
           const unsigned long long pick = tie & (~tie + 1ull);
           cball |= pick;
@@ -116,15 +135,13 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
         }
       } else {
         // ascending entropy; stop before the running sum passes the budget
-        const float e = masked ? a.entropy[s * B + lane] : INFINITY;
+        const float e = masked ? a.entropy[s * B + pos] : INFINITY;
         unsigned long long rest = mball;
         float run = 0.f;
         while (rest != 0ull) {
-          const bool cand = (rest >> lane) & 1ull;
-          float lo = cand ? e : INFINITY;
-#pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) lo = fminf(lo, shfl_xor_f(lo, off));
-          unsigned long long tie = __ballot(cand && e == lo);
+          const bool cand = (rest >> pos) & 1ull;
+          const float lo = seg_min(cand ? e : INFINITY);
+          unsigned long long tie = sball(cand && e == lo);
           if (tie == 0ull) tie = rest;   // every remaining value is +inf or NaN
           const unsigned long long pick = tie & (~tie + 1ull);
           const float nxt = run + lo;
@@ -134,19 +151,19 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
           run = nxt;
         }
       }
-      const bool commit = (cball >> lane) & 1ull;
-      if (commit) a.block_tokens[s * B + lane] = a.argmax_tok[s * B + lane];
+      const bool commit = (cball >> pos) & 1ull;
+      if (commit) a.block_tokens[s * B + pos] = a.argmax_tok[s * B + pos];
       still = masked && !commit;
-      const unsigned long long sball = __ballot(still);
-      if (lane == 0) {
-        if (sball == 0ull) a.seq_state[s] = kSaving;
+      const unsigned long long left = sball(still);
+      if (pos == 0) {
+        if (left == 0ull) a.seq_state[s] = kSaving;
         if (a.num_committed) a.num_committed[s] = __popcll(cball);
       }
-    } else if (!(a.flags & kCompactOnly) && a.num_committed && lane == 0) {
+    } else if (live && !(a.flags & kCompactOnly) && a.num_committed && pos == 0) {
       a.num_committed[s] = 0;
     }
-    const unsigned long long left = __ballot(still);
-    if (lane == 0) s_left[s] = left;
+    const unsigned long long left = sball(still);
+    if (live && pos == 0) s_left[s] = left;
   }
   __syncthreads();
 
@@ -175,12 +192,14 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
   if (tid == 1023) *a.num_rows_out = wpre + incl;
   __syncthreads();
 
-  // pass 3: scatter row ids
-  for (int s = wave; s < S; s += 16) {
+  // pass 3: scatter row ids, NSEG sequences per wave as in pass 1
+  for (int base = wave * NSEG; base < S; base += 16 * NSEG) {
+    const int s = base + seg;
+    if (s >= S || pos >= B) continue;
     const unsigned long long left = s_left[s];
-    if (lane < B && ((left >> lane) & 1ull)) {
-      const unsigned long long below = lane ? (left & ((1ull << lane) - 1ull)) : 0ull;
-      a.row_index_out[s_off[s] + __popcll(below)] = s * B + lane;
+    if ((left >> pos) & 1ull) {
+      const unsigned long long below = pos ? (left & ((1ull << pos) - 1ull)) : 0ull;
+      a.row_index_out[s_off[s] + __popcll(below)] = s * B + pos;
     }
   }
 }
