@@ -180,8 +180,40 @@ def main():
     log(f"{args.steps} steps in {elapsed * 1e3:.2f} ms: {ms_per_step:.3f} ms/step, "
         f"{value:.0f} block-tokens/s")
 
-    # ---- per entry point, HIP events on the launch stream
+    # ---- per round (eager rounds, HIP events between them, median over
+    # repetitions) and the same step with the 256 MB MALL flushed before it
+    # (a 512 MB scratch write, untimed): the cold figure
     stream = torch.cuda.current_stream()
+    ra = round_args()
+    round_times = [[] for _ in ra]
+    for _ in range(max(args.steps // 2, 5)):
+        reset()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(ra) + 1)]
+        evs[0].record(stream)
+        for i, a in enumerate(ra):
+            api.dbd_round(a)
+            evs[i + 1].record(stream)
+        evs[-1].synchronize()
+        for i in range(len(ra)):
+            round_times[i].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
+    round_us = [float(np.median(x)) for x in round_times]
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(max(args.steps // 2, 5)):
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    cold_ms = float(np.median(cold))
+    log("per round (eager, median): " + ", ".join(f"r{i + 1} {t:.1f} us ({w.S * w.B / t * 1e6:.0f} "
+                                                  f"block-tokens/s)" for i, t in enumerate(round_us))
+        + f"; cold step (MALL flushed) {cold_ms:.3f} ms")
+
+    # ---- per entry point, HIP events on the launch stream
     it = args.kernel_iters
 
     def ev_time(fn):
@@ -297,6 +329,21 @@ def main():
     log(f"block-causal prefill of the batch's prefixes ({Tp} tokens, block {w.B}): {t_prefill:.1f} us, "
         f"{pf_tflops:.0f} TFLOP/s ({pf_tflops / PEAK_BF16_TFLOPS:.1%} of bf16 peak)")
 
+    # ---- practical ceilings on this machine: a streaming read of 4 GiB (the
+    # library's measurement kernel) and a large bf16 GEMM (hipBLASLt through
+    # torch.matmul)
+    big = torch.ones((1 << 31,), dtype=torch.bfloat16, device=dev)
+    sink = torch.empty(api.lib().dbd_stream_read_sink_words(), dtype=torch.int32, device=dev)
+    t_read = ev_time(lambda: api.dbd_stream_read(big, sink))
+    read_tbs = big.numel() * 2 / (t_read * 1e-6) / 1e12
+    del big, sink
+    ga = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    gb = torch.randn((8192, 8192), device=dev, dtype=torch.float32).to(torch.bfloat16)
+    t_gemm = ev_time(lambda: torch.matmul(ga, gb))
+    gemm_tf = 2.0 * 8192 ** 3 / (t_gemm * 1e-6) / 1e12
+    del ga, gb
+    log(f"practical ceilings: streaming read {read_tbs:.2f} TB/s, bf16 GEMM 8192^3 {gemm_tf:.0f} TFLOP/s")
+
     # algorithmic work
     L = fx.prefix_len.astype(np.int64)
     npages = -(-L // w.P)
@@ -336,6 +383,14 @@ def main():
                          "lmhead": {str(m): round(t, 2) for m, t in lm_times.items()},
                          "remask": round(t_remask, 2),
                          "attention_kv_save": round(t_save, 2),
+                         "per_round_eager_us": [round(t, 1) for t in round_us],
+                         "per_round_block_tokens_per_s": [round(w.S * w.B / t * 1e6, 1) for t in round_us],
+                         "cold_ms_per_step": round(cold_ms, 4),
+                         "cold_block_tokens_per_s": round(w.S * w.B * w.rounds / (cold_ms * 1e-3), 1),
+                         "practical_ceilings": {"stream_read_TBps": round(read_tbs, 3),
+                                                "bf16_gemm_8192_TFLOPs": round(gemm_tf, 1),
+                                                "attention_frac_of_read": round(attn_roof["achieved"] / 1e3 / read_tbs, 4),
+                                                "lmhead_frac_of_gemm": round(lm_roof["achieved"] / gemm_tf, 4)},
                          "lmhead_sample_T1_M%d" % rows_per_round[0]: round(t_lm_sample, 2),
                          "topp_M%d" % M1r: {"logits_us": round(t_logits, 2),
                                              "filtered_draw_us": round(t_filter, 2),

@@ -92,6 +92,10 @@ def lib() -> C.CDLL:
     L.dbd_sample_filtered.argtypes = [i, i, i] + [_vp] * 3 + [f, i, f, C.c_uint64, C.c_uint32] + \
         [_vp, _vp, _vp]
     L.dbd_sample_filtered.restype = i
+    L.dbd_stream_read.argtypes = [_vp, sz, _vp, _vp]
+    L.dbd_stream_read.restype = i
+    L.dbd_stream_read_sink_words.argtypes = []
+    L.dbd_stream_read_sink_words.restype = i
     L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
     L.dbd_round.restype = i
     L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
@@ -336,6 +340,12 @@ def dbd_sample_filtered(logits, num_rows, token, conf, mask_token_id, temperatur
                                      _ptr(num_rows), float(temperature), int(top_k), float(top_p),
                                      int(seed) & ((1 << 64) - 1), int(step), _ptr(token),
                                      _ptr(conf), _stream(stream)))
+
+
+def dbd_stream_read(data, sink, stream=None):
+    """Streaming read of a device buffer (measurement helper)."""
+    nbytes = data.numel() * data.element_size()
+    _check(lib().dbd_stream_read(_ptr(data), nbytes - nbytes % 16, _ptr(sink), _stream(stream)))
 
 
 def dbd_remask_commit(block_tokens, seq_state, argmax_tok, conf, row_index_out, num_rows_out,

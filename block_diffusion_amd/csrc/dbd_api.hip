@@ -507,6 +507,17 @@ dbd_status dbd_prefill_attn(int S, int T, int Hq, int Hkv, int D, int block_leng
   return DBD_OK;
 }
 
+dbd_status dbd_stream_read(const void* data, size_t bytes, uint32_t* sink, void* stream) {
+  REQUIRE_PTR(data); REQUIRE_PTR(sink);
+  REQUIRE(bytes % 16 == 0, "bytes must be a multiple of 16 (got %zu)", bytes);
+  hipError_t e = dbd::stream_read_launch(data, bytes, sink, dbd::kStreamReadGrid,
+                                         static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream read launch");
+  return DBD_OK;
+}
+
+int dbd_stream_read_sink_words(void) { return dbd::kStreamReadGrid; }
+
 dbd_status dbd_round(const dbd_round_args* a, void* stream) {
   dbd_status s = check_round(a);
   if (s != DBD_OK) return s;

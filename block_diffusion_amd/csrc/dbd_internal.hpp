@@ -87,6 +87,11 @@ struct SampleArgs {
 };
 hipError_t sample_filtered_launch(const SampleArgs& a, hipStream_t stream);
 
+// ------------------------------------------------------- calibration
+constexpr int kStreamReadGrid = 2048;   // workgroups of the read ceiling kernel
+hipError_t stream_read_launch(const void* data, size_t bytes, uint32_t* sink, int grid,
+                              hipStream_t stream);
+
 // partial arrays of the LM-head workspace: pm, pa, ps, pt, pg, pl
 constexpr int kLmPartArrays = 6;
 

@@ -487,6 +487,15 @@ dbd_status dbd_validate_inputs(int S, int B, int page_size,
                                const int32_t* block_tokens,
                                const uint8_t* seq_state);
 
+/* Measurement helper: reads `bytes` (a multiple of 16) of device memory
+ * once, as a plain streaming read, and writes a digest word per workgroup
+ * to sink (dbd_stream_read_sink_words() words), so that the memory-bound
+ * kernels can be compared with the device's practical read bandwidth as
+ * well as with the nominal HBM peak. */
+dbd_status dbd_stream_read(const void* data, size_t bytes, uint32_t* sink,
+                           void* stream);
+int dbd_stream_read_sink_words(void);
+
 const char* dbd_last_error(void);
 int dbd_abi_version(void);
 

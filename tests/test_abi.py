@@ -28,7 +28,7 @@ def test_header_declares_the_round_calls():
               "dbd_lmhead_conf_entropy", "dbd_remask_commit_rule",
               "dbd_attn_paged_save", "dbd_commit_block", "dbd_lmhead_sample",
               "dbd_prefill_attn", "dbd_prefill_workspace_size", "dbd_lmhead_logits",
-              "dbd_sample_filtered",
+              "dbd_sample_filtered", "dbd_stream_read", "dbd_stream_read_sink_words",
               "dbd_graph_create", "dbd_graph_launch", "dbd_graph_destroy",
               "dbd_attn_workspace_size", "dbd_lmhead_workspace_size",
               "dbd_round_workspace_size", "dbd_validate_inputs", "dbd_last_error",
