@@ -142,3 +142,22 @@ def test_sample_filtered_distribution(k, p):
     pv = chi2.sf(x, keep.sum() - 1)
     print(f"k={k} p={p}: {keep.sum()} kept, chi2 {x:.1f}, p-value {pv:.3g}", flush=True)
     assert pv > 1e-4
+
+
+def test_lmhead_logits_many_rows():
+    """1500 listed rows (two passes of the tile kernel at four-member teams)
+    of a ragged vocabulary: sampled rows against the oracle's logits, every
+    mask column -inf, rows past the list untouched."""
+    g = np.random.default_rng(61)
+    V, Hd, n, mask = 2003, 256, 1600, 77
+    wv = synth.normal_bf16(g, (V, Hd), std=1.0 / np.sqrt(Hd))
+    h = synth.normal_bf16(g, (n, Hd))
+    rows = g.permutation(n)[:1500]
+    lg = _logits(h, wv, mask, rows).cpu().numpy()
+    M = len(rows)
+    samp = np.sort(g.choice(M, 40, replace=False))
+    ref = oracle.lmhead_logits(h[rows[samp]], wv, mask)
+    fin = np.isfinite(ref)
+    assert np.abs(lg[samp][fin].astype(np.float64) - ref[fin]).max() <= 2e-3
+    assert np.all(np.isneginf(lg[:M, mask]))
+    assert np.all(np.isnan(lg[M:]))

@@ -35,8 +35,8 @@ LOOP_MIX = Workload(name="loop_mix_b16", seed_id=51, S=12, B=16, Hq=16, Hkv=4, D
 class Loop:
     """Device buffers of a multi-block run and its schedule of steps."""
 
-    def __init__(self, w, nb):
-        self.w, self.nb = w, nb
+    def __init__(self, w, nb, rule=0, k=1):
+        self.w, self.nb, self.rule, self.k = w, nb, rule, k
         self.fx = fx = synth.make_fixed(w, reserve_tokens=nb * w.B)
         self.L0 = fx.prefix_len.copy()
         self.end = (self.L0 + nb * w.B).astype(np.int32)
@@ -83,6 +83,7 @@ class Loop:
             a = api.make_round_args(**kw)
         a.gate_on_rows = 0 if save else 1
         a.round_counter = api._ptr(self.counter)
+        a.rule, a.tokens_per_step = self.rule, self.k
         return a
 
     def reset(self):
@@ -155,10 +156,12 @@ def _run_eager_checked(lp):
             check_lm_rows(samp, now["arg"], conf, rin.hidden, fx.w_vocab, w.mask_id)
         if save:
             et, es, eL, ets, _, erows = oracle.step_commit(toks, state, L, conf, now["arg"],
-                                                           w.mask_id, 0, tau=np.float32(w.tau),
-                                                           token_stream=ts, end_len=lp.end)
+                                                           w.mask_id, lp.rule, tau=np.float32(w.tau),
+                                                           tokens_per_step=lp.k, token_stream=ts,
+                                                           end_len=lp.end)
         else:
-            et, es, _ = oracle.remask(toks, state, conf, now["arg"], w.mask_id, np.float32(w.tau))
+            et, es, _ = oracle.remask_rule(toks, state, conf, now["arg"], w.mask_id, lp.rule,
+                                           tau=np.float32(w.tau), tokens_per_step=lp.k)
             eL, ets, erows = L, ts, oracle.compact_rows(et, es, w.mask_id)
         assert np.array_equal(now["tokens"], et) and np.array_equal(now["state"], es), f"step {k}"
         assert np.array_equal(now["L"], eL) and np.array_equal(now["ts"], ets), f"step {k}"
@@ -189,5 +192,26 @@ def test_block_loop_graph(w, nb):
             got = lp.snapshot()
             for key, v in eager.items():
                 assert np.array_equal(np.asarray(got[key]), np.asarray(v)), f"replay {rep}: {key}"
+    finally:
+        graph.close()
+
+
+def test_block_loop_static_rule():
+    """The static rule commits exactly k = 3 positions per round, so a block
+    of 8 needs ceil(8/3) = 3 rounds and the other 5 gated rounds of each
+    block change nothing; graph replays equal the eager run."""
+    w = LOOP_FAST.with_(name="loop_static_b8")
+    lp = Loop(w, 2, rule=1, k=3)
+    lp.reset()
+    eager, active = _run_eager_checked(lp)
+    assert active == 2 * 3
+    graph = api.dbd_graph_create(lp.args)
+    try:
+        lp.reset()
+        graph.launch()
+        torch.cuda.synchronize()
+        got = lp.snapshot()
+        for key, v in eager.items():
+            assert np.array_equal(np.asarray(got[key]), np.asarray(v)), key
     finally:
         graph.close()

@@ -130,3 +130,18 @@ def test_prefill_deterministic_and_empty():
     ref = oracle.prefill_attention(q, k, v, cu, 4)
     mx, rl = attn_errors(widen_bits(a), ref)
     assert mx <= ATTN_MAX_ABS and rl <= ATTN_REL_L2
+
+
+def test_prefill_many_short_prompts():
+    """300 prompts of 0..40 tokens (most workgroups hold one partial tile),
+    D = 64, G = 2, block 8, with the store."""
+    g = np.random.default_rng(31)
+    lens = tuple(int(x) for x in g.integers(0, 41, 300))
+    q, k, v, cu = _prompts(32, lens, 4, 2, 64)
+    store = _paged(33, lens, 2, 64, 16)
+    out, (kc, vc) = _run(q, k, v, cu, 8, store)
+    ref = oracle.prefill_attention(q, k, v, cu, 8)
+    mx, rl = attn_errors(widen_bits(out), ref)
+    assert mx <= ATTN_MAX_ABS and rl <= ATTN_REL_L2, (mx, rl)
+    ek, ev = oracle.prefill_store(store[1], store[2], store[0], k, v, cu)
+    assert np.array_equal(kc, ek) and np.array_equal(vc, ev)

@@ -37,6 +37,11 @@ def _save_case(name):
         w = Workload(name="save_ragged", seed_id=40, S=7, B=5, Hq=8, Hkv=2, D=128, P=16,
                      Hd=256, V=1024, mask_id=7, prefix_lo=0, prefix_hi=64, tau=0.9, rounds=5,
                      a_max=12.0, prefix_fixed=(14, 16, 0, 31, 47, 3, 64))
+    elif name == "llada_b64":
+        # LLaDA heads (MHA, 32 x 128) and 64-token blocks that span pages
+        w = Workload(name="save_llada", seed_id=42, S=3, B=64, Hq=32, Hkv=32, D=128, P=256,
+                     Hd=256, V=1024, mask_id=7, prefix_lo=0, prefix_hi=600, tau=0.9, rounds=64,
+                     a_max=12.0, prefix_fixed=(230, 0, 511))
     elif name == "rt4_d64":
         # G*B = 80 query rows per kv head: two row groups, only the first writes
         w = Workload(name="save_rt4", seed_id=41, S=5, B=5, Hq=32, Hkv=2, D=64, P=32,
@@ -49,7 +54,7 @@ def _save_case(name):
     return w, fx, rin
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged_d128", "rt4_d64", "sdar1p7b"])
+@pytest.mark.parametrize("name", ["tiny", "ragged_d128", "rt4_d64", "llada_b64", "sdar1p7b"])
 def test_attn_save_parity(name):
     w, fx, rin = _save_case(name)
     g = np.random.default_rng(w.seed_id + 77)
