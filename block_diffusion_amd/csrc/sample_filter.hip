@@ -92,15 +92,38 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   const uint32_t rid = (uint32_t)(a.row_index ? a.row_index[r] : r);
   const float invT = a.inv_temp;
 
-  // ---- max logit and sum exp(l - m) at temperature 1
-  float mloc = -INFINITY;
-  for (int v = tid; v < V; v += kSfThreads)
-    if (v != mask) mloc = fmaxf(mloc, l[v]);
-  const float m = block_reduce(mloc, [](float x, float y) { return fmaxf(x, y); }, s_f);
-  float s1 = 0.f;
-  for (int v = tid; v < V; v += kSfThreads)
-    if (v != mask) s1 += __expf(l[v] - m);
-  const float S1 = block_reduce(s1, [](float x, float y) { return x + y; }, s_f);
+  // every logit of the row once, 16 bytes per load when rows are 16-byte
+  // aligned (V % 4 == 0), else one at a time
+  auto each = [&](auto fn) {
+    if ((V & 3) == 0) {
+      const f32x4* l4 = reinterpret_cast<const f32x4*>(l);
+      for (int q = tid; q < (V >> 2); q += kSfThreads) {
+        const f32x4 x = l4[q];
+        fn(4 * q, x.x); fn(4 * q + 1, x.y); fn(4 * q + 2, x.z); fn(4 * q + 3, x.w);
+      }
+    } else {
+      for (int v = tid; v < V; v += kSfThreads) fn(v, l[v]);
+    }
+  };
+
+  // ---- one pass: max logit m, sum exp(l - m) (temperature 1) and
+  // sum exp((l - m)/T), online per thread, then merged over the workgroup
+  float mt = -INFINITY, s1t = 0.f, sTt = 0.f;
+  each([&](int v, float x) {
+    if (v == mask) return;
+    if (x > mt) {
+      const float d = mt - x;                 // -inf on the first value
+      s1t = s1t * __expf(d);
+      sTt = sTt * __expf(d * invT);
+      mt = x;
+    }
+    s1t += __expf(x - mt);
+    sTt += __expf((x - mt) * invT);
+  });
+  const float m = block_reduce(mt, [](float x, float y) { return fmaxf(x, y); }, s_f);
+  const float wt = mt == -INFINITY ? 0.f : 1.f;
+  const float S1 = block_reduce(wt * s1t * __expf(mt - m), [](float x, float y) { return x + y; }, s_f);
+  const float ST = block_reduce(wt * sTt * __expf((mt - m) * invT), [](float x, float y) { return x + y; }, s_f);
 
   // kept-set test: key above the boundary key, or equal to it with id at
   // most the boundary id; bk = 0 with bid = V keeps everything
@@ -123,14 +146,13 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
         s_mass[i] = 0.f;
       }
       __syncthreads();
-      for (int v = tid; v < V; v += kSfThreads) {
-        const float x = l[v];
+      each([&](int v, float x) {
         const uint32_t key = okey(x);
-        if (!in(v, key) || (key & pmask) != prefix) continue;
+        if (!in(v, key) || (key & pmask) != prefix) return;
         const int d = (key >> shift) & 255;
         if (use_mass) atomicAdd(&s_mass[d], __expf((x - m) * invT));
         else atomicAdd(&s_hist[d], 1u);
-      }
+      });
       __syncthreads();
       if (tid == 0) {
         // from the largest digit down: the digit where the running total
@@ -239,13 +261,15 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   uint32_t pk = 0u;
   int pid = V;
   if (a.top_p < 1.f) {
-    // total mass of the top-k set at temperature T
-    float z = 0.f;
-    for (int v = tid; v < V; v += kSfThreads) {
-      const float x = l[v];
-      if (keep_k(v, okey(x))) z += __expf((x - m) * invT);
+    // total mass of the top-k set at temperature T (all tokens: ST)
+    float Z = ST;
+    if (use_k) {
+      float z = 0.f;
+      each([&](int v, float x) {
+        if (keep_k(v, okey(x))) z += __expf((x - m) * invT);
+      });
+      Z = block_reduce(z, [](float x, float y) { return x + y; }, s_f);
     }
-    const float Z = block_reduce(z, [](float x, float y) { return x + y; }, s_f);
     radix([&](int v, uint32_t key) { return keep_k(v, key); }, true, a.top_p * Z, 0, pk, pid);
   }
   auto keep = [&](int v, uint32_t key) {
@@ -264,15 +288,23 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
       float x[16];
       float bm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = 32 * c + 8 * (i >> 2) + 4 * h + (i & 3);
-        float xv = -INFINITY;
-        if (v < V) {
-          const float lv = l[v];
-          if (keep(v, okey(lv))) xv = lv * kLog2e;
+      for (int q = 0; q < 4; ++q) {
+        const int v0 = 32 * c + 8 * q + 4 * h;
+        float lv[4];
+        if ((V & 3) == 0 && v0 + 4 <= V) {
+          const f32x4 x4 = *reinterpret_cast<const f32x4*>(l + v0);
+          lv[0] = x4.x; lv[1] = x4.y; lv[2] = x4.z; lv[3] = x4.w;
+        } else {
+#pragma unroll
+          for (int r2 = 0; r2 < 4; ++r2) lv[r2] = v0 + r2 < V ? l[v0 + r2] : -INFINITY;
         }
-        x[i] = xv;
-        bm = fmaxf(bm, xv);
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) {
+          const int v = v0 + r2;
+          const float xv = (v < V && keep(v, okey(lv[r2]))) ? lv[r2] * kLog2e : -INFINITY;
+          x[4 * q + r2] = xv;
+          bm = fmaxf(bm, xv);
+        }
       }
       if (bm == -INFINITY) continue;
       const float u = sf_uniform(h ? w2 : w0);
