@@ -20,18 +20,22 @@
 //
 // Per wave, tiles go straight from global memory into a ring of kRing LDS
 // slots (global_load_lds_dwordx4: kKT keys of K and of V in runs of 16 that
-// never cross a page, plus the segment's query rows when the tile starts
-// one), kRing-1 tiles in flight while one is computed.  Rows are stored with
+// never cross a page), kRing-1 tiles in flight while one is computed.  A
+// segment's query rows go from global memory straight into the MFMA operand
+// registers at its first tile, so a slot holds K and V only and the waves
+// per CU do not shrink with the rows per segment.  Rows are stored with
 // their 16-byte chunks XOR-permuted by row so fragment reads hit distinct
-// banks.  Per run of 16 keys:
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (lane: query row, 4 keys);
+// banks.  Per run of 32 keys:
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 for each 16-key half
+//     (lane: query row, 4 keys of each half);
 //   * online softmax in fp32, base 2 (scores pre-scaled by scale*log2 e),
 //     probabilities rounded to bf16 for the MFMA, the row sum taken over the
-//     rounded values;
-//   * the score accumulator layout is exactly the B operand of
-//     O^T += V^T P^T (v_mfma_f32_16x16x16bf16_1k); the V^T operand comes
-//     straight from the row-major V rows with the LDS transpose read
-//     ds_read_b64_tr_b16.
+//     rounded values; the running maximum moves only when it grows by more
+//     than 2^8, so most runs skip the accumulator rescale;
+//   * the two halves' score accumulators together are the B operand of
+//     O^T += V^T P^T with the K = 32 MFMA (v_mfma_f32_16x16x32_bf16, twice
+//     the rate of the K = 16 form); the V^T operand comes straight from the
+//     row-major V rows with the LDS transpose read ds_read_b64_tr_b16.
 // Keys past the end of a prefix or block are masked to -inf; their loads
 // re-read a valid key, so nothing past a page or buffer is touched.
 //
@@ -69,7 +73,8 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #ifndef ATTN_KT
 #define ATTN_KT 32
 #endif
-constexpr int kKT = ATTN_KT;   // keys per tile (a multiple of 16)
+constexpr int kKT = ATTN_KT;   // keys per tile (a multiple of 32)
+static_assert(kKT % 32 == 0, "runs of 32 keys");
 constexpr int kRing = ATTN_RING;       // ring slots per wave
 constexpr int kMaxWavesPerCU = ATTN_WAVES;
 constexpr int kCUs = 256;      // MI355X compute units
@@ -93,7 +98,7 @@ struct Geo {
   static constexpr int KS = D / 32;
   static constexpr int DT = D / 16;
   static constexpr int KV = kKT * D;                // elements of one K (or V) tile
-  static constexpr int SLOT = 2 * KV + ROWS * D;    // K, V, Q
+  static constexpr int SLOT = 2 * KV;               // K, V
   static constexpr int LPR = D / 8;                 // lanes per row in a 1 KB load
   static constexpr int RPI = 64 / LPR;              // rows per 1 KB load
 };
@@ -245,8 +250,8 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
     }
   };
 
-  // load tile `d` (and the segment's query rows if with_q) into `slot`
-  auto dma_tile = [&](lds_u16* slot, const Dec& d, bool with_q) INL {
+  // load tile `d` into `slot`
+  auto dma_tile = [&](lds_u16* slot, const Dec& d) INL {
     wait_lgkm0();   // the slot's previous tile has been read out
     const int g = d.hg / a.n_rg, rg = d.hg % a.n_rg;
     // kKT/16 runs of 16 keys; a run never crosses a page (the page size is a
@@ -277,19 +282,6 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       }
       dma_rows16<D, RT>(slot + hh * 16 * D, sk, stride, nvalid, lane);
       dma_rows16<D, RT>(slot + KV + hh * 16 * D, sv, stride, nvalid, lane);
-    }
-    if (with_q) {
-      // query row r = rg*ROWS + i -> (pos, gi) = (r / G, r % G); rows past
-      // G*B re-read the last real row (their outputs are never written)
-#pragma unroll
-      for (int r0 = 0; r0 < ROWS; r0 += Gm::RPI) {
-        const int row = r0 + lane / Gm::LPR;
-        const int lc = (lane % Gm::LPR) ^ rswz<D>(row);
-        const int rr = min(rg * ROWS + row, R - 1);
-        const int pos = rr / a.G, gi = rr % a.G;
-        const uint16_t* src = a.q + ((size_t)(d.s * a.B + pos) * a.Hq + g * a.G + gi) * D + lc * 8;
-        dma16(src, slot + 2 * KV + r0 * D);
-      }
     }
   };
 
@@ -381,12 +373,17 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       finalize(prev);
     }
     if (k == 0 || dc.j == 0) {
+      // the segment's query rows, straight from global memory into the MFMA
+      // operand registers: row r = rg*ROWS + i -> (pos, gi) = (r / G, r % G);
+      // rows past G*B re-read the last real row (never written out)
+      const int g = dc.hg / a.n_rg, rg = dc.hg % a.n_rg;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
+        const int rr = min(rg * ROWS + rt * 16 + lr, R - 1);
+        const int pos = rr / a.G, gi = rr % a.G;
+        const uint16_t* qp = a.q + ((size_t)(dc.s * a.B + pos) * a.Hq + g * a.G + gi) * D;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          qf[rt][ks] = __builtin_bit_cast(
-              bf16x8, *(const lds_u32x4*)(slot + 2 * KV + eoff<D>(rt * 16 + lr, lg + 4 * ks)));
+        for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = ld_bf16x8(qp + (lg + 4 * ks) * 8);
         m_run[rt] = -INFINITY;
         l_run[rt] = 0.f;
 #pragma unroll
@@ -394,66 +391,93 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       }
     }
     const int nvalid_t = dc.j < dc.nP ? dc.L - kKT * dc.j : a.B - kKT * (dc.j - dc.nP);
+    // runs of 32 keys: S^T for two 16-key halves, one softmax step, and
+    // O^T += V^T P^T with K = 32 MFMAs whose k slots 8*lg .. 8*lg+7 hold keys
+    // 4*lg .. 4*lg+3 of the first half, then of the second (the same order
+    // in both operands).  Keys past the valid count are -inf.
 #pragma unroll
-    for (int hh = 0; hh < kKT / 16; ++hh) {
-      const int nvalid = nvalid_t - 16 * hh;   // valid keys of this run (may be <= 0)
-      const lds_u16* kt16 = slot + hh * 16 * D;
-      bf16x8 kf[KS];
+    for (int h2 = 0; h2 < kKT / 32; ++h2) {
+      f32x4 sc[2][RT];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kt16 + eoff<D>(lr, lg + 4 * ks)));
-      f32x4 sc[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        sc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int hh = 0; hh < 2; ++hh) {
+        const lds_u16* kt16 = slot + (2 * h2 + hh) * 16 * D;
+        bf16x8 kf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], sc[rt], 0, 0, 0);
+          kf[ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(kt16 + eoff<D>(lr, lg + 4 * ks)));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          sc[hh][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            sc[hh][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], sc[hh][rt], 0, 0, 0);
+        }
       }
-      i16x4 pb[RT];
+      const int nv0 = nvalid_t - 32 * h2;        // valid keys from this run's first (may be <= 0)
+      float xs[RT][8], tmax[RT];
+      bool grow = false;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        float x[4];
-        float tmax = -INFINITY;
+        tmax[rt] = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = (4 * lg + i < nvalid) ? sc[rt][i] * a.scale_log2 : -INFINITY;
-          tmax = fmaxf(tmax, x[i]);
+        for (int i = 0; i < 8; ++i) {
+          const int key = 16 * (i >> 2) + 4 * lg + (i & 3);
+          xs[rt][i] = key < nv0 ? sc[i >> 2][rt][i & 3] * a.scale_log2 : -INFINITY;
+          tmax[rt] = fmaxf(tmax[rt], xs[rt][i]);
         }
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-        // a run with no valid key leaves the state as it is (m_run is finite
-        // once the segment's first key has been seen)
-        const float m_new = fmaxf(m_run[rt], tmax);
-        const float alpha = fast_exp2(m_run[rt] - m_new);
-        m_run[rt] = m_new;
-        float psum = 0.f;
-        short pbits[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint16_t b = f2bf(fast_exp2(x[i] - m_new));
-          pbits[i] = (short)b;
-          psum += bf2f(b);
-        }
-        pb[rt] = i16x4{pbits[0], pbits[1], pbits[2], pbits[3]};
-        l_run[rt] = l_run[rt] * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+        tmax[rt] = fmaxf(tmax[rt], shfl_xor_f(tmax[rt], 16));
+        tmax[rt] = fmaxf(tmax[rt], shfl_xor_f(tmax[rt], 32));
+        grow |= tmax[rt] > m_run[rt] + 8.f;
       }
-      // O^T[d][row] += V^T[d][key] P^T[key][row]: lane 16*lg + lr needs
-      // V[keys 4*lg .. 4*lg+3][d = 16*dt + lr].  ds_read_b64_tr_b16 hands
-      // lane i of each 16-lane group element i%4 of the 8-byte words read by
-      // lanes i/4 + 4k (k = 0..3) of its group, so lane w of group lg reads
-      // V[4*lg + w/4][16*dt + 4*(w%4) .. +3].
-      const lds_u16* vt = slot + KV + hh * 16 * D;
+      // the running maxima (and the rescale) move only when some row's
+      // maximum grows by more than 2^8; below that, probabilities up to 2^8
+      // against the old maxima are exact in the fp32 sums.  A run with no
+      // valid key leaves everything as it is.
+      if (__ballot(grow) != 0ull) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const float m_new = fmaxf(m_run[rt], tmax[rt]);
+          const float alpha = m_run[rt] == -INFINITY ? 0.f : fast_exp2(m_run[rt] - m_new);
+          m_run[rt] = m_new;
+          l_run[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+        }
+      }
+      bf16x8 pb[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float psum = 0.f;
+        uint32_t pw[4];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const uint16_t b0 = f2bf(fast_exp2(xs[rt][i] - m_run[rt]));
+          const uint16_t b1 = f2bf(fast_exp2(xs[rt][i + 1] - m_run[rt]));
+          psum += bf2f(b0) + bf2f(b1);
+          pw[i >> 1] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+        }
+        pb[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        l_run[rt] += psum;
+      }
+      // O^T[d][row] += V^T[d][key] P^T[key][row]: in each half, lane w of
+      // 16-lane group lg needs V[keys 4*lg .. 4*lg+3][d = 16*dt + w].
+      // ds_read_b64_tr_b16 hands lane i of each 16-lane group element i%4 of
+      // the 8-byte words read by lanes i/4 + 4k (k = 0..3) of its group, so
+      // lane w of group lg reads V[4*lg + w/4][16*dt + 4*(w%4) .. +3].
+      const lds_u16* vt = slot + KV + 2 * h2 * 16 * D;
       const int vrow = 4 * lg + (lr >> 2), vsub = 4 * (lr & 1), vch = (lr & 3) >> 1;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (__attribute__((address_space(3))) i16x4*)(vt + eoff<D>(vrow, 2 * dt + vch) + vsub));
+        const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(vt + 16 * D + eoff<D>(vrow, 2 * dt + vch) + vsub));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 v8 = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
-          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[rt], acc[rt][dt], 0, 0, 0);
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt], acc[rt][dt], 0, 0, 0);
       }
     }
     if constexpr (SAVE) {
@@ -463,15 +487,9 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
 
   // the stream: tiles 0..n-1; loads run NR-1 tiles ahead (past the end
   // they repeat the last tile into the idle slot)
-  bool first_dma = true;
   auto next_dma = [&](lds_u16* slot, int kt) INL {
-    if (kt < n) {
-      dma_tile(slot, dd, first_dma || dd.j == 0);
-      first_dma = false;
-      if (kt + 1 < n) advance(dd);
-    } else {
-      dma_tile(slot, dd, false);
-    }
+    dma_tile(slot, dd);
+    if (kt + 1 < n) advance(dd);
   };
 #pragma unroll
   for (int u = 0; u + 1 < NR; ++u) next_dma(ring + u * Gm::SLOT, u);
@@ -564,7 +582,7 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
   p.n_rg = (R + 16 * p.RT - 1) / (16 * p.RT);
   const long max_seg_tiles = ((long)max_pages * page_size + kKT - 1) / kKT + (B + kKT - 1) / kKT;
   p.maxp = (int)((max_seg_tiles + 63) / 64 + 1);
-  const int slot_bytes = (2 * kKT * D + 16 * p.RT * D) * 2;
+  const int slot_bytes = 2 * kKT * D * 2;
   const int waves_per_cu = std::max(1, std::min(kMaxWavesPerCU, kLdsPerCU / (kRing * slot_bytes)));
   p.grid = kCUs * waves_per_cu;
   p.plan_bytes = ((size_t)(S + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
