@@ -342,7 +342,15 @@ def main():
     t_gemm = ev_time(lambda: torch.matmul(ga, gb))
     gemm_tf = 2.0 * 8192 ** 3 / (t_gemm * 1e-6) / 1e12
     del ga, gb
-    log(f"practical ceilings: streaming read {read_tbs:.2f} TB/s, bf16 GEMM 8192^3 {gemm_tf:.0f} TFLOP/s")
+    # the LM head's own product as a plain library GEMM: bf16 logits of the
+    # first round's rows (no argmax, no softmax), hipBLASLt through linear()
+    M1g = rows_per_round[0]
+    hg = r1["hidden"].view(-1, w.Hd)[:M1g]
+    t_lmgemm = ev_time(lambda: torch.nn.functional.linear(hg, fixed["w_vocab"]))
+    lmgemm_tf = 2.0 * M1g * w.Hd * w.V / (t_lmgemm * 1e-6) / 1e12
+    log(f"practical ceilings: streaming read {read_tbs:.2f} TB/s, bf16 GEMM 8192^3 {gemm_tf:.0f} TFLOP/s, "
+        f"LM-head-shaped GEMM ({M1g} x {w.Hd} x {w.V}, bf16 logits out) {t_lmgemm:.1f} us = "
+        f"{lmgemm_tf:.0f} TFLOP/s")
 
     # algorithmic work
     L = fx.prefix_len.astype(np.int64)
@@ -390,7 +398,9 @@ def main():
                          "practical_ceilings": {"stream_read_TBps": round(read_tbs, 3),
                                                 "bf16_gemm_8192_TFLOPs": round(gemm_tf, 1),
                                                 "attention_frac_of_read": round(attn_roof["achieved"] / 1e3 / read_tbs, 4),
-                                                "lmhead_frac_of_gemm": round(lm_roof["achieved"] / gemm_tf, 4)},
+                                                "lmhead_frac_of_gemm": round(lm_roof["achieved"] / gemm_tf, 4),
+                                                "lmhead_shape_gemm_us": round(t_lmgemm, 2),
+                                                "lmhead_shape_gemm_TFLOPs": round(lmgemm_tf, 1)},
                          "lmhead_sample_T1_M%d" % rows_per_round[0]: round(t_lm_sample, 2),
                          "topp_M%d" % M1r: {"logits_us": round(t_logits, 2),
                                              "filtered_draw_us": round(t_filter, 2),

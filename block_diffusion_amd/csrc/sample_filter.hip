@@ -5,8 +5,8 @@
 // separate sampler after the logits faster than a fused one ("Ruled-Out
 // Optimizations").  Here the LM head stores the listed rows' logits
 // (lmhead_tile_kernel, store mode) and this kernel draws each row's token:
-//   * tokens other than the mask token are ranked by logit, higher first,
-//     the lower id first among equal logits;
+//   * candidates are the finite logits other than the mask token's, ranked
+//     by logit, higher first, the lower id first among equal logits;
 //   * top_k > 0 keeps the first top_k; top_p < 1 then keeps the shortest
 //     leading run of those whose running sum of exp((l - m)/T) reaches
 //     top_p of their total (at least one token);
@@ -15,13 +15,34 @@
 //     step, 0); per 16-column block an inverse-CDF candidate and a Gumbel
 //     value at the block's log-sum-exp; the largest Gumbel wins), the other
 //     tokens having zero weight; the confidence is the drawn token's
-//     probability at temperature 1.
-// One workgroup of 1024 threads per listed row.  The ranking is never
-// sorted: a radix select over the order-preserving 32-bit image of the
-// logits finds the top-k boundary (counts per 8-bit digit, four passes over
-// the row) and the top-p boundary (sums of exp((l - m)/T) per digit), and a
-// pass in id order settles ties at a boundary value.  Each pass re-reads the
-// row (L2 / HBM); passes that a filter does not need are skipped.
+//     probability at temperature 1.  A row without a candidate gets the
+//     mask token with confidence 0.
+//
+// One workgroup of 1024 threads per listed row; the ranking is never
+// sorted as a whole.  Passes over the row (16-byte loads, several in flight
+// per thread):
+//   1. the row maximum m;
+//   2. (filters only) a histogram over 4096 value bins below m, bin =
+//      floor((m - l) log2(e) / T * 32) (the last bin takes everything
+//      further down), with per bin the candidate count (top-k) and the sum
+//      of exp((l - m)/T) in 2^-40 fixed point (top-p: integer sums, so the
+//      boundary does not depend on the order of the atomic adds).  The bin
+//      is a monotone function of the logit, so every bin holds a run of
+//      the ranking;
+//   3. a scan over the bins finds the bin holding a boundary (the top_k-th
+//      candidate, or the first candidate whose running mass reaches top_p
+//      of the kept total); one more pass gathers that bin's candidates
+//      into LDS as (key, ~id), a bitonic sort puts them in ranking order
+//      and a scan over them gives the boundary candidate.  A bin of more
+//      than 2048 candidates (long runs of equal logits, extreme
+//      temperatures) is resolved instead by a radix select over the
+//      order-preserving 32-bit image of its logits (8-bit digits, four
+//      passes, then a pass in id order for ties);
+//   4. the block draw over the kept set, which also sums exp(l - m) for
+//      the confidence.
+// Without a filter only passes 1 and 4 run.
+#include <climits>
+
 #include "dbd_device.hpp"
 #include "dbd_internal.hpp"
 
@@ -30,10 +51,18 @@ namespace dbd {
 namespace {
 
 constexpr int kSfThreads = 1024;
+constexpr int kSfWaves = kSfThreads / 64;
+constexpr int kSfBins = 4096;             // value bins below the row maximum
+constexpr float kSfBinsPerLog2 = 32.f;    // bins per unit of (m - l) log2(e) / T
+constexpr int kSfCap = 2048;              // candidates of one bin sorted in LDS
+constexpr float kSfFix = 1099511627776.f; // 2^40: fixed-point scale of the masses
 
 __device__ __forceinline__ uint32_t okey(float f) {
   const uint32_t b = __float_as_uint(f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);   // larger float -> larger key
+}
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // the same Philox4x32-10 and uniforms as the fused sampler
@@ -53,259 +82,381 @@ __device__ __forceinline__ float sf_uniform(uint32_t w) {
   return (float)(((w >> 9) << 1) | 1u) * (1.0f / 16777216.0f);
 }
 
-// block-wide reductions over 1024 threads (16 waves) through LDS
-template <typename T, typename F>
-__device__ T block_reduce(T v, F op, T* s_tmp) {
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src_lane) {
+  const uint32_t lo = __shfl((uint32_t)v, src_lane, 64), hi = __shfl((uint32_t)(v >> 32), src_lane, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// block-wide reduction over 1024 threads (16 waves) through LDS
+template <typename F>
+__device__ float block_reduce(float v, F op, float* s_tmp) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    v = op(v, __shfl_xor(v, off, 64));
-  }
+  for (int off = 32; off >= 1; off >>= 1) v = op(v, __shfl_xor(v, off, 64));
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
   if (lane == 0) s_tmp[wave] = v;
   __syncthreads();
-  T r = s_tmp[0];
-  for (int w = 1; w < kSfThreads / 64; ++w) r = op(r, s_tmp[w]);
+  float r = s_tmp[0];
+  for (int w = 1; w < kSfWaves; ++w) r = op(r, s_tmp[w]);
   return r;
 }
 
 }  // namespace
 
 __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
-  __shared__ float s_f[16];
-  __shared__ int s_i[16];
-  __shared__ uint32_t s_hist[256];
-  __shared__ float s_mass[256];
-  __shared__ int s_sel[2];
-  __shared__ float s_rem;
-  __shared__ float s_gbest[16];
-  __shared__ int s_cbest[16];
-  __shared__ float s_lbest[16];
-  __shared__ int s_cnt[kSfThreads];     // per-thread tie counts / masses in id order
-  __shared__ float s_ms[kSfThreads];
+  __shared__ uint32_t s_bc[kSfBins];     // candidates per bin
+  __shared__ uint64_t s_bm[kSfBins];     // fixed-point mass per bin
+  __shared__ uint64_t s_g[kSfCap];       // one bin's candidates, (key << 32) | ~id
+  __shared__ uint64_t s_w[kSfWaves];
+  __shared__ float s_f[kSfWaves];
+  __shared__ int s_n, s_first;
+  __shared__ uint64_t s_before;
+  __shared__ int s_sel;
+  __shared__ float s_gbest[kSfWaves];
+  __shared__ int s_cbest[kSfWaves];
+  __shared__ float s_lbest[kSfWaves];
+  // radix-select scratch on top of s_g: it runs only when a bin did not fit
+  uint64_t* const s_h64 = s_g;                                        // [256]
+  int* const s_cnt = reinterpret_cast<int*>(s_g + 256);               // [1024]
+  static_assert(256 * 8 + kSfThreads * 4 <= kSfCap * 8, "radix scratch must fit in the gather buffer");
 
   const int r = blockIdx.x;
   if (r >= *a.num_rows) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int V = a.V, mask = a.mask_id;
   const float* l = a.logits + (size_t)r * V;
   const uint32_t rid = (uint32_t)(a.row_index ? a.row_index[r] : r);
   const float invT = a.inv_temp;
 
-  // every logit of the row once, 16 bytes per load when rows are 16-byte
-  // aligned (V % 4 == 0), else one at a time
+  auto cand = [&](int v, float x) { return v != mask && fabsf(x) <= 3.402823466e38f; };
+
+  // every logit of the row once; with 16-byte aligned rows (V % 4 == 0)
+  // each thread keeps four 16-byte loads in flight
   auto each = [&](auto fn) {
     if ((V & 3) == 0) {
       const f32x4* l4 = reinterpret_cast<const f32x4*>(l);
-      for (int q = tid; q < (V >> 2); q += kSfThreads) {
-        const f32x4 x = l4[q];
+      const int n4 = V >> 2;
+      auto fn4 = [&](int q, const f32x4& x) {
         fn(4 * q, x.x); fn(4 * q + 1, x.y); fn(4 * q + 2, x.z); fn(4 * q + 3, x.w);
+      };
+      int q = tid;
+      for (; q + 3 * kSfThreads < n4; q += 4 * kSfThreads) {
+        const f32x4 x0 = l4[q], x1 = l4[q + kSfThreads], x2 = l4[q + 2 * kSfThreads],
+                    x3 = l4[q + 3 * kSfThreads];
+        fn4(q, x0); fn4(q + kSfThreads, x1); fn4(q + 2 * kSfThreads, x2); fn4(q + 3 * kSfThreads, x3);
       }
+      for (; q < n4; q += kSfThreads) fn4(q, l4[q]);
     } else {
       for (int v = tid; v < V; v += kSfThreads) fn(v, l[v]);
     }
   };
 
-  // ---- one pass: max logit m, sum exp(l - m) (temperature 1) and
-  // sum exp((l - m)/T), online per thread, then merged over the workgroup
-  float mt = -INFINITY, s1t = 0.f, sTt = 0.f;
+  // ---- pass 1: the maximum candidate logit
+  float mt = -INFINITY;
   each([&](int v, float x) {
-    if (v == mask) return;
-    if (x > mt) {
-      const float d = mt - x;                 // -inf on the first value
-      s1t = s1t * __expf(d);
-      sTt = sTt * __expf(d * invT);
-      mt = x;
-    }
-    s1t += __expf(x - mt);
-    sTt += __expf((x - mt) * invT);
+    if (cand(v, x)) mt = fmaxf(mt, x);
   });
   const float m = block_reduce(mt, [](float x, float y) { return fmaxf(x, y); }, s_f);
-  const float wt = mt == -INFINITY ? 0.f : 1.f;
-  const float S1 = block_reduce(wt * s1t * __expf(mt - m), [](float x, float y) { return x + y; }, s_f);
-  const float ST = block_reduce(wt * sTt * __expf((mt - m) * invT), [](float x, float y) { return x + y; }, s_f);
+  if (m == -INFINITY) {
+    if (tid == 0) {
+      a.token[rid] = mask;
+      a.conf[rid] = 0.f;
+    }
+    return;
+  }
 
-  // kept-set test: key above the boundary key, or equal to it with id at
-  // most the boundary id; bk = 0 with bid = V keeps everything
-  uint32_t kk = 0u;     // top-k boundary key
-  int kid = V;          // top-k boundary id among keys == kk
-  const int nval = V - 1;
-  const bool use_k = a.top_k > 0 && a.top_k < nval;
-  auto keep_k = [&](int v, uint32_t key) { return v != mask && (key > kk || (key == kk && v <= kid)); };
+  const float c2 = invT * kLog2e;               // exp((l - m)/T) = 2^((l - m) c2)
+  const float c3 = c2 * kSfBinsPerLog2;
+  auto bin_of = [&](float x) -> int {
+    const float d = (m - x) * c3;               // >= 0, monotone in x
+    return d < (float)(kSfBins - 1) ? (int)d : kSfBins - 1;
+  };
+  auto mass_of = [&](float x) -> uint64_t {
+    return (uint64_t)(fast_exp2((x - m) * c2) * kSfFix);
+  };
 
-  // radix select of the rank-`need` element (1-based, from the top) among
-  // the elements `in` admits; counts (MASS false) or mass (MASS true)
-  auto radix = [&](auto in, bool use_mass, float need_f, int need_i, uint32_t& key_out,
-                   int& id_out) {
-    uint32_t prefix = 0u, pmask = 0u;
-    float rem_f = need_f;
-    int rem_i = need_i;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kSfThreads) {
-        s_hist[i] = 0u;
-        s_mass[i] = 0.f;
+  // exclusive prefix over the workgroup (thread order) of a 64-bit value;
+  // `total` = the sum over all threads
+  auto block_scan = [&](uint64_t v, uint64_t& total) -> uint64_t {
+    uint64_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint64_t y = shfl_u64(x, lane >= off ? lane - off : lane);
+      x += lane >= off ? y : 0ull;
+    }
+    __syncthreads();
+    if (lane == 63) s_w[wave] = x;
+    __syncthreads();
+    uint64_t run = 0ull, tot = 0ull;
+    for (int w = 0; w < kSfWaves; ++w) {
+      const uint64_t t = s_w[w];
+      run += w < wave ? t : 0ull;
+      tot += t;
+    }
+    total = tot;
+    return run + x - v;
+  };
+
+  // first slot s of [0, n) (four per thread, thread-major) with val(s) > 0
+  // whose inclusive running sum reaches tgt, or -1; `before` = the running
+  // sum ahead of it, `total` = the sum of all slots
+  auto find_first = [&](auto val, int n, uint64_t tgt, uint64_t& before, uint64_t& total) -> int {
+    uint64_t v[4], sum = 0ull;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 4 * tid + j;
+      v[j] = s < n ? val(s) : 0ull;
+      sum += v[j];
+    }
+    if (tid == 0) s_first = INT_MAX;
+    uint64_t run = block_scan(sum, total);
+    int mine = -1;
+    uint64_t mb = 0ull;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (mine < 0 && v[j] > 0ull && run + v[j] >= tgt) {
+        mine = 4 * tid + j;
+        mb = run;
       }
+      run += v[j];
+    }
+    if (mine >= 0) atomicMin(&s_first, mine);
+    __syncthreads();
+    const int f = s_first;
+    if (mine >= 0 && mine == f) s_before = mb;
+    __syncthreads();
+    before = s_before;
+    __syncthreads();
+    return f == INT_MAX ? -1 : f;
+  };
+
+  // the candidates of bin b that pred admits, into s_g in ranking order
+  // (descending (key, ~id)); returns their number, > kSfCap if they did not
+  // fit (s_g then holds no list)
+  auto gather_sort = [&](int b, auto pred) -> int {
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    each([&](int v, float x) {
+      if (!cand(v, x) || bin_of(x) != b || !pred(v, x)) return;
+      const int i = atomicAdd(&s_n, 1);
+      if (i < kSfCap) s_g[i] = ((uint64_t)okey(x) << 32) | (uint32_t)~(uint32_t)v;
+    });
+    __syncthreads();
+    const int n = s_n;
+    if (n > kSfCap) return n;
+    int n2 = 1;
+    while (n2 < n) n2 <<= 1;
+    for (int i = n + tid; i < n2; i += kSfThreads) s_g[i] = 0ull;   // below every candidate
+    __syncthreads();
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += kSfThreads) {
+          const int p = i ^ j;
+          if (p > i) {
+            const uint64_t x = s_g[i], y = s_g[p];
+            if ((i & k) == 0 ? x < y : x > y) {
+              s_g[i] = y;
+              s_g[p] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    return n;
+  };
+  auto entry_key = [&](int i) { return (uint32_t)(s_g[i] >> 32); };
+  auto entry_id = [&](int i) { return (int)~(uint32_t)s_g[i]; };
+
+  // radix select among the candidates `in` admits: the first, in ranking
+  // order, whose running count (use_mass false) or fixed-point mass reaches
+  // `need`.  Four passes of 8-bit digits of the order-preserving key, then
+  // the tied candidates (key == the selected key) share one value, so the
+  // boundary is the c-th of them in id order, c = need left / their mass
+  // (rounded up); a pass counts them per thread over contiguous id ranges.
+  auto radix = [&](auto in, bool use_mass, uint64_t need, uint32_t& key_out, int& id_out) {
+    uint32_t prefix = 0u, pmask = 0u;
+    uint64_t rem = need;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kSfThreads) s_h64[i] = 0ull;
       __syncthreads();
       each([&](int v, float x) {
         const uint32_t key = okey(x);
-        if (!in(v, key) || (key & pmask) != prefix) return;
-        const int d = (key >> shift) & 255;
-        if (use_mass) atomicAdd(&s_mass[d], __expf((x - m) * invT));
-        else atomicAdd(&s_hist[d], 1u);
+        if (!in(v, x) || (key & pmask) != prefix) return;
+        atomicAdd(reinterpret_cast<unsigned long long*>(&s_h64[(key >> shift) & 255]),
+                  (unsigned long long)(use_mass ? mass_of(x) : 1ull));
       });
       __syncthreads();
-      if (tid == 0) {
-        // from the largest digit down: the digit where the running total
-        // first reaches the remaining need (the last non-empty digit if
-        // rounding leaves it short)
-        float cf = 0.f;
-        int ci = 0, pick = -1, last = -1;
-        for (int d = 255; d >= 0; --d) {
-          const bool ne = use_mass ? s_mass[d] > 0.f : s_hist[d] > 0u;
-          if (!ne) continue;
-          last = d;
-          if (use_mass) {
-            if (cf + s_mass[d] >= rem_f) { pick = d; break; }
-            cf += s_mass[d];
-          } else {
-            if (ci + (int)s_hist[d] >= rem_i) { pick = d; break; }
-            ci += (int)s_hist[d];
-          }
-        }
-        if (pick < 0) {
-          pick = last < 0 ? 0 : last;
-          // remove the digits above the last one from the need
-          cf = 0.f; ci = 0;
-          for (int d = 255; d > last; --d) { cf += s_mass[d]; ci += (int)s_hist[d]; }
-        }
-        s_sel[0] = pick;
-        s_sel[1] = rem_i - ci;
-        s_rem = rem_f - cf;
+      uint64_t before, total;
+      // slot i = digit 255 - i: from the largest digit down
+      int sl = find_first([&](int i) { return s_h64[255 - i]; }, 256, rem, before, total);
+      if (sl < 0) {      // not reachable: the need is within the admitted total
+        sl = 0;
+        before = 0ull;
       }
-      __syncthreads();
-      const int pick = s_sel[0];
-      rem_i = s_sel[1];
-      rem_f = s_rem;
-      prefix |= (uint32_t)pick << shift;
+      rem -= before;
+      prefix |= (uint32_t)(255 - sl) << shift;
       pmask |= 255u << shift;
-      __syncthreads();
     }
-    // ties at the boundary key, in id order: the id where the running count
-    // (mass) of tied elements reaches the remaining need
+    const uint64_t w = use_mass ? mass_of(key_float(prefix)) : 1ull;
+    uint64_t c = w == 0ull ? 1ull : (rem + w - 1ull) / w;
+    c = c < 1ull ? 1ull : c;
     const int per = (V + kSfThreads - 1) / kSfThreads;
     const int v0 = tid * per, v1 = min(V, v0 + per);
     int cnt = 0;
-    float ms = 0.f;
     for (int v = v0; v < v1; ++v) {
       const float x = l[v];
-      const uint32_t key = okey(x);
-      if (in(v, key) && key == prefix) {
-        ++cnt;
-        if (use_mass) ms += __expf((x - m) * invT);
-      }
+      cnt += (in(v, x) && okey(x) == prefix) ? 1 : 0;
     }
-    // the thread (in id order) where the running count (mass) reaches it
     s_cnt[tid] = cnt;
-    s_ms[tid] = ms;
     __syncthreads();
-    if (tid == 0) {
-      int c = 0, t = 0;
-      float f = 0.f;
-      for (t = 0; t < kSfThreads; ++t) {
-        const bool reach = use_mass ? (f + s_ms[t] >= rem_f) : (c + s_cnt[t] >= rem_i);
-        if (reach && s_cnt[t] > 0) break;
-        c += s_cnt[t];
-        f += s_ms[t];
-      }
-      if (t == kSfThreads) {        // rounding left it short: the last tie
-        for (t = kSfThreads - 1; t > 0 && s_cnt[t] == 0; --t) {}
-        c = 0; f = 0.f;
-        for (int u = 0; u < t; ++u) { c += s_cnt[u]; f += s_ms[u]; }
-      }
-      s_sel[0] = t;
-      s_sel[1] = rem_i - c;
-      s_rem = rem_f - f;
+    uint64_t before, total;
+    int t = find_first([&](int i) { return (uint64_t)s_cnt[i]; }, kSfThreads, c, before, total);
+    if (t < 0) {       // fewer ties than c (not reachable): the last tie
+      t = find_first([&](int i) { return (uint64_t)s_cnt[i]; }, kSfThreads, total, before, total);
+      c = total;
     }
-    __syncthreads();
-    int idc = V;
-    if (tid == s_sel[0]) {
-      int need2 = s_sel[1];
-      float rf = s_rem;
-      int lastv = v0;
+    if (tid == t) {
+      uint64_t k = c - before;
+      int idc = v0;
       for (int v = v0; v < v1; ++v) {
         const float x = l[v];
-        const uint32_t key = okey(x);
-        if (!(in(v, key) && key == prefix)) continue;
-        lastv = v;
-        if (use_mass) {
-          const float w = __expf((x - m) * invT);
-          if (w >= rf) { idc = v; break; }
-          rf -= w;
-        } else {
-          if (need2 <= 1) { idc = v; break; }
-          --need2;
-        }
+        if (!(in(v, x) && okey(x) == prefix)) continue;
+        idc = v;
+        if (--k == 0ull) break;
       }
-      if (idc == V) idc = lastv;
-      s_sel[0] = idc;
+      s_sel = idc;
     }
     __syncthreads();
     key_out = prefix;
-    id_out = s_sel[0];
+    id_out = s_sel;
     __syncthreads();
   };
 
-  if (use_k) {
-    radix([&](int v, uint32_t) { return v != mask; }, false, 0.f, a.top_k, kk, kid);
-  }
-  uint32_t pk = 0u;
-  int pid = V;
-  if (a.top_p < 1.f) {
-    // total mass of the top-k set at temperature T (all tokens: ST)
-    float Z = ST;
-    if (use_k) {
-      float z = 0.f;
-      each([&](int v, float x) {
-        if (keep_k(v, okey(x))) z += __expf((x - m) * invT);
-      });
-      Z = block_reduce(z, [](float x, float y) { return x + y; }, s_f);
+  // kept-set tests: key above the boundary key, or equal to it with id at
+  // most the boundary id; key 0 with id V keeps everything
+  uint32_t kk = 0u, pk = 0u;
+  int kid = V, pid = V;
+  auto keep_k = [&](int v, uint32_t key) { return v != mask && (key > kk || (key == kk && v <= kid)); };
+  const bool use_k = a.top_k > 0 && a.top_k < V - 1;
+  const bool use_p = a.top_p < 1.f;
+
+  if (use_k || use_p) {
+    // ---- pass 2: the value-bin histogram
+    for (int i = tid; i < kSfBins; i += kSfThreads) {
+      s_bc[i] = 0u;
+      s_bm[i] = 0ull;
     }
-    radix([&](int v, uint32_t key) { return keep_k(v, key); }, true, a.top_p * Z, 0, pk, pid);
+    __syncthreads();
+    each([&](int v, float x) {
+      if (!cand(v, x)) return;
+      const int b = bin_of(x);
+      if (use_k) atomicAdd(&s_bc[b], 1u);
+      if (use_p) atomicAdd(reinterpret_cast<unsigned long long*>(&s_bm[b]),
+                           (unsigned long long)mass_of(x));
+    });
+    __syncthreads();
+
+    int bk = kSfBins, rk = 0, listed = -1;     // top-k boundary bin, rank in it, sorted bin
+    if (use_k) {
+      uint64_t before, total;
+      const int b = find_first([&](int s) { return (uint64_t)s_bc[s]; }, kSfBins, (uint64_t)a.top_k,
+                               before, total);
+      if (b >= 0) {                            // else fewer candidates than top_k: keep all
+        bk = b;
+        rk = a.top_k - (int)before;
+        const int n = gather_sort(bk, [](int, float) { return true; });
+        if (n <= kSfCap) {
+          kk = entry_key(rk - 1);
+          kid = entry_id(rk - 1);
+          listed = bk;
+        } else {
+          radix([&](int v, float x) { return cand(v, x) && bin_of(x) == bk; }, false, (uint64_t)rk, kk,
+                kid);
+        }
+      }
+    }
+    if (use_p) {
+      // mass of the kept part of the top-k boundary bin
+      uint64_t massk = 0ull;
+      if (bk < kSfBins) {
+        uint64_t part = 0ull;
+        if (listed == bk) {
+          for (int i = tid; i < rk; i += kSfThreads) part += mass_of(key_float(entry_key(i)));
+        } else {
+          each([&](int v, float x) {
+            if (cand(v, x) && bin_of(x) == bk && keep_k(v, okey(x))) part += mass_of(x);
+          });
+        }
+        block_scan(part, massk);
+      }
+      auto pval = [&](int s) -> uint64_t { return s < bk ? s_bm[s] : (s == bk ? massk : 0ull); };
+      uint64_t before, Z;
+      find_first(pval, kSfBins, ~0ull, before, Z);          // the kept total
+      uint64_t tgt = 0ull;
+      if (a.top_p > 0.f) {
+        const double t = ceil((double)a.top_p * (double)Z);
+        tgt = t >= (double)Z ? Z : (uint64_t)t;
+      }
+      // >= 0: the maximum is kept and has mass 2^40
+      const int bp = find_first(pval, kSfBins, tgt, before, Z);
+      const uint64_t rem = tgt - before;
+      int n = kSfCap + 1;
+      if (bp == bk && listed == bk) n = rk;                  // the sorted top-k part
+      else if (bp != bk) n = gather_sort(bp, [](int, float) { return true; });
+      if (n <= kSfCap) {
+        uint64_t b2, t2;
+        int e = find_first([&](int i) { return mass_of(key_float(entry_key(i))); }, n, rem, b2, t2);
+        e = e < 0 ? n - 1 : e;
+        pk = entry_key(e);
+        pid = entry_id(e);
+      } else {
+        radix([&](int v, float x) { return cand(v, x) && bin_of(x) == bp && keep_k(v, okey(x)); },
+              true, rem, pk, pid);
+      }
+    }
   }
-  auto keep = [&](int v, uint32_t key) {
-    return keep_k(v, key) && (key > pk || (key == pk && v <= pid));
+  auto keep = [&](int v, float x) {
+    const uint32_t key = okey(x);
+    return cand(v, x) && keep_k(v, key) && (key > pk || (key == pk && v <= pid));
   };
 
-  // ---- the block draw over the kept set (log2 units as the fused sampler)
-  float gbest = -INFINITY, lbest = 0.f;
+  // ---- pass 4: the block draw over the kept set (log2 units as the fused
+  // sampler), and sum exp(l - m) over the candidates for the confidence
+  float gbest = -INFINITY, lbest = 0.f, s1 = 0.f;
   int cbest = 0x7fffffff;
   const int nchunk = (V + 31) / 32;
   for (int c = tid; c < nchunk; c += kSfThreads) {
+    float lv[32];
+    if ((V & 3) == 0 && 32 * c + 32 <= V) {
+      const f32x4* p4 = reinterpret_cast<const f32x4*>(l + 32 * c);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const f32x4 x4 = p4[i];
+        lv[4 * i] = x4.x; lv[4 * i + 1] = x4.y; lv[4 * i + 2] = x4.z; lv[4 * i + 3] = x4.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) lv[i] = 32 * c + i < V ? l[32 * c + i] : -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) s1 += cand(32 * c + i, lv[i]) ? fast_exp2((lv[i] - m) * kLog2e) : 0.f;
     uint32_t w0 = (uint32_t)c, w1 = rid, w2 = a.step, w3 = 0u;
     sf_philox(w0, w1, w2, w3, a.key0, a.key1);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      // half h: columns 32c + 8q + 4h + r'
       float x[16];
       float bm = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int v0 = 32 * c + 8 * q + 4 * h;
-        float lv[4];
-        if ((V & 3) == 0 && v0 + 4 <= V) {
-          const f32x4 x4 = *reinterpret_cast<const f32x4*>(l + v0);
-          lv[0] = x4.x; lv[1] = x4.y; lv[2] = x4.z; lv[3] = x4.w;
-        } else {
-#pragma unroll
-          for (int r2 = 0; r2 < 4; ++r2) lv[r2] = v0 + r2 < V ? l[v0 + r2] : -INFINITY;
-        }
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int r2 = 0; r2 < 4; ++r2) {
-          const int v = v0 + r2;
-          const float xv = (v < V && keep(v, okey(lv[r2]))) ? lv[r2] * kLog2e : -INFINITY;
+          const int i = 8 * q + 4 * h + r2, v = 32 * c + i;
+          const float xv = keep(v, lv[i]) ? lv[i] * kLog2e : -INFINITY;
           x[4 * q + r2] = xv;
           bm = fmaxf(bm, xv);
         }
-      }
       if (bm == -INFINITY) continue;
       const float u = sf_uniform(h ? w2 : w0);
       const float eg = sf_uniform(h ? w3 : w1);
@@ -330,21 +481,21 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
 #pragma unroll
       for (int i = 1; i < 16; ++i) xc = (i == ci) ? x[i] : xc;
       const float G = bmT + __log2f(S) - __log2f(-__log2f(eg));
-      const int cand = 32 * c + 8 * (ci >> 2) + 4 * h + (ci & 3);
-      if (G > gbest || (G == gbest && cand < cbest)) {
-        gbest = G; cbest = cand; lbest = xc * (1.0f / kLog2e);
+      const int cnd = 32 * c + 8 * (ci >> 2) + 4 * h + (ci & 3);
+      if (G > gbest || (G == gbest && cnd < cbest)) {
+        gbest = G; cbest = cnd; lbest = xc * (1.0f / kLog2e);
       }
     }
   }
+  const float S1 = block_reduce(s1, [](float x, float y) { return x + y; }, s_f);
   // argmax of (G, lower candidate) over the workgroup
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float g2 = __shfl_xor(gbest, off, 64);
-    const int c2 = __shfl_xor(cbest, off, 64);
+    const int c2i = __shfl_xor(cbest, off, 64);
     const float l2 = __shfl_xor(lbest, off, 64);
-    if (g2 > gbest || (g2 == gbest && c2 < cbest)) { gbest = g2; cbest = c2; lbest = l2; }
+    if (g2 > gbest || (g2 == gbest && c2i < cbest)) { gbest = g2; cbest = c2i; lbest = l2; }
   }
-  const int wave = tid >> 6, lane = tid & 63;
   if (lane == 0) {
     s_gbest[wave] = gbest;
     s_cbest[wave] = cbest;
@@ -352,7 +503,7 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   }
   __syncthreads();
   if (tid == 0) {
-    for (int w = 1; w < kSfThreads / 64; ++w)
+    for (int w = 1; w < kSfWaves; ++w)
       if (s_gbest[w] > gbest || (s_gbest[w] == gbest && s_cbest[w] < cbest)) {
         gbest = s_gbest[w]; cbest = s_cbest[w]; lbest = s_lbest[w];
       }

@@ -161,3 +161,71 @@ def test_lmhead_logits_many_rows():
     assert np.abs(lg[samp][fin].astype(np.float64) - ref[fin]).max() <= 2e-3
     assert np.all(np.isneginf(lg[:M, mask]))
     assert np.all(np.isnan(lg[M:]))
+
+
+def _direct_rows(V, mask, seed):
+    """Logit rows that stress the boundary search: long runs of equal logits
+    (6000 and 1500 tokens at one value), a plain spread, -inf tokens, an
+    all-equal row and a row with five tokens far above the rest; the mask
+    column is -inf as the LM head stores it."""
+    g = np.random.default_rng(seed)
+    rows = []
+    for n_tie in (6000, 1500):
+        x = (g.standard_normal(V) * 2).astype(np.float32)
+        x[g.choice(V, n_tie, replace=False)] = 3.0
+        rows.append(x)
+    rows.append((g.standard_normal(V) * 3).astype(np.float32))
+    x = (g.standard_normal(V) * 2).astype(np.float32)
+    x[g.choice(V, 100, replace=False)] = -np.inf
+    rows.append(x)
+    rows.append(np.zeros(V, np.float32))
+    x = g.standard_normal(V).astype(np.float32)
+    x[:5] = 12.0
+    rows.append(x)
+    lg = np.stack(rows)
+    lg[:, mask] = -np.inf
+    return lg
+
+
+@pytest.mark.parametrize("V", [20000, 20003])
+@pytest.mark.parametrize("T,k,p", [(1.0, 0, 0.9), (1.0, 3000, 1.0), (1.0, 3000, 0.9), (0.7, 1500, 0.95),
+                                   (50.0, 0, 0.5), (0.05, 0, 0.99), (1.0, 19990, 0.999), (0.6, 0, 0.95),
+                                   (1.0, 0, 0.0), (1.3, 3, 0.5)])
+def test_sample_filtered_boundary_rows(V, T, k, p):
+    """Stored-logit rows whose filter boundary falls inside a run of equal
+    logits too long for the in-LDS sort (the radix path), inside a shorter
+    run (the sorted path), at extreme temperatures (everything in one value
+    bin, or almost nothing near the top), and with top_k above the number
+    of finite logits (keep them all)."""
+    mask = 7
+    lg_h = _direct_rows(V, mask, 400 + V % 7)
+    M = lg_h.shape[0]
+    lg = torch.from_numpy(lg_h).to("cuda")
+    tok = torch.full((M,), -9, dtype=torch.int32, device="cuda")
+    conf = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    seed, step = 77 + k, 5
+    api.dbd_sample_filtered(lg, dev_i32([M]), tok, conf, mask, T, k, p, seed, step)
+    torch.cuda.synchronize()
+    ex = _check_rows(lg_h, np.arange(M), tok.cpu().numpy(), conf.cpu().numpy(), mask, T, k, p, seed,
+                     step)
+    print(f"V={V} T={T} k={k} p={p}: {M} rows, {ex} exempt", flush=True)
+    assert ex <= 1
+
+
+def test_sample_filtered_no_candidate():
+    """A row whose only finite logit is the mask token's draws the mask
+    token with confidence 0; the other rows are unaffected."""
+    V, mask = 4096, 3
+    lg_h = np.full((2, V), -np.inf, np.float32)
+    lg_h[0, mask] = 5.0
+    lg_h[1] = np.random.default_rng(2).standard_normal(V).astype(np.float32)
+    lg_h[1, mask] = -np.inf
+    lg = torch.from_numpy(lg_h).to("cuda")
+    tok = torch.full((2,), -9, dtype=torch.int32, device="cuda")
+    conf = torch.full((2,), float("nan"), dtype=torch.float32, device="cuda")
+    api.dbd_sample_filtered(lg, dev_i32([2]), tok, conf, mask, 1.0, 10, 0.9, 5, 0)
+    torch.cuda.synchronize()
+    t, c = tok.cpu().numpy(), conf.cpu().numpy()
+    assert t[0] == mask and c[0] == 0.0
+    ex = _check_rows(lg_h[1:], np.array([1]), t, c, mask, 1.0, 10, 0.9, 5, 0)
+    assert ex <= 1
