@@ -342,13 +342,23 @@ def main():
     t_gemm = ev_time(lambda: torch.matmul(ga, gb))
     gemm_tf = 2.0 * 8192 ** 3 / (t_gemm * 1e-6) / 1e12
     del ga, gb
+    # register-resident bf16 MFMA loop on random operands (the library's
+    # measurement kernel): the matrix cores' practical rate, power limit included
+    mf_ops = torch.randn((api.lib().dbd_mfma_peak_operand_bytes() // 2,), generator=gen, device=dev,
+                         dtype=torch.float32).to(torch.bfloat16)
+    mf_sink = torch.empty((api.lib().dbd_mfma_peak_sink_floats(),), dtype=torch.float32, device=dev)
+    mf_iters = 1024
+    t_mfma = ev_time(lambda: api.dbd_mfma_peak(mf_ops, mf_iters, mf_sink))
+    mfma_tf = api.lib().dbd_mfma_peak_flops(mf_iters) / (t_mfma * 1e-6) / 1e12
+    del mf_ops, mf_sink
     # the LM head's own product as a plain library GEMM: bf16 logits of the
     # first round's rows (no argmax, no softmax), hipBLASLt through linear()
     M1g = rows_per_round[0]
     hg = r1["hidden"].view(-1, w.Hd)[:M1g]
     t_lmgemm = ev_time(lambda: torch.nn.functional.linear(hg, fixed["w_vocab"]))
     lmgemm_tf = 2.0 * M1g * w.Hd * w.V / (t_lmgemm * 1e-6) / 1e12
-    log(f"practical ceilings: streaming read {read_tbs:.2f} TB/s, bf16 GEMM 8192^3 {gemm_tf:.0f} TFLOP/s, "
+    log(f"practical ceilings: streaming read {read_tbs:.2f} TB/s, MFMA loop {mfma_tf:.0f} TFLOP/s, "
+        f"bf16 GEMM 8192^3 {gemm_tf:.0f} TFLOP/s, "
         f"LM-head-shaped GEMM ({M1g} x {w.Hd} x {w.V}, bf16 logits out) {t_lmgemm:.1f} us = "
         f"{lmgemm_tf:.0f} TFLOP/s")
 
@@ -396,9 +406,11 @@ def main():
                          "cold_ms_per_step": round(cold_ms, 4),
                          "cold_block_tokens_per_s": round(w.S * w.B * w.rounds / (cold_ms * 1e-3), 1),
                          "practical_ceilings": {"stream_read_TBps": round(read_tbs, 3),
+                                                "mfma_loop_TFLOPs": round(mfma_tf, 1),
                                                 "bf16_gemm_8192_TFLOPs": round(gemm_tf, 1),
                                                 "attention_frac_of_read": round(attn_roof["achieved"] / 1e3 / read_tbs, 4),
                                                 "lmhead_frac_of_gemm": round(lm_roof["achieved"] / gemm_tf, 4),
+                                                "lmhead_frac_of_mfma_loop": round(lm_roof["achieved"] / mfma_tf, 4),
                                                 "lmhead_shape_gemm_us": round(t_lmgemm, 2),
                                                 "lmhead_shape_gemm_TFLOPs": round(lmgemm_tf, 1)},
                          "lmhead_sample_T1_M%d" % rows_per_round[0]: round(t_lm_sample, 2),

@@ -96,6 +96,14 @@ def lib() -> C.CDLL:
     L.dbd_stream_read.restype = i
     L.dbd_stream_read_sink_words.argtypes = []
     L.dbd_stream_read_sink_words.restype = i
+    L.dbd_mfma_peak.argtypes = [_vp, i, _vp, _vp]
+    L.dbd_mfma_peak.restype = i
+    L.dbd_mfma_peak_operand_bytes.argtypes = []
+    L.dbd_mfma_peak_operand_bytes.restype = sz
+    L.dbd_mfma_peak_sink_floats.argtypes = []
+    L.dbd_mfma_peak_sink_floats.restype = i
+    L.dbd_mfma_peak_flops.argtypes = [i]
+    L.dbd_mfma_peak_flops.restype = C.c_double
     L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
     L.dbd_round.restype = i
     L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
@@ -346,6 +354,17 @@ def dbd_stream_read(data, sink, stream=None):
     """Streaming read of a device buffer (measurement helper)."""
     nbytes = data.numel() * data.element_size()
     _check(lib().dbd_stream_read(_ptr(data), nbytes - nbytes % 16, _ptr(sink), _stream(stream)))
+
+
+def dbd_mfma_peak(operands, iters, sink, stream=None):
+    """Register-resident bf16 MFMA loop (measurement helper); returns the
+    launch's floating-point operation count."""
+    if operands.numel() * operands.element_size() < lib().dbd_mfma_peak_operand_bytes():
+        raise ValueError("operand buffer smaller than dbd_mfma_peak_operand_bytes()")
+    if sink.numel() * sink.element_size() < 4 * lib().dbd_mfma_peak_sink_floats():
+        raise ValueError("sink smaller than dbd_mfma_peak_sink_floats() floats")
+    _check(lib().dbd_mfma_peak(_ptr(operands), int(iters), _ptr(sink), _stream(stream)))
+    return lib().dbd_mfma_peak_flops(int(iters))
 
 
 def dbd_remask_commit(block_tokens, seq_state, argmax_tok, conf, row_index_out, num_rows_out,

@@ -1,8 +1,17 @@
-// Practical streaming-read ceiling of the device, for the measurement of the
-// memory-bound kernels against both the nominal and a measured peak.
-// Every thread reads 16-byte chunks, four at a time, grid-stride over the
-// buffer; the XOR of everything read goes to one word per workgroup so
-// that no load can be dropped.
+// Practical ceilings of the device, for the measurement of the kernels
+// against both the nominal and a measured peak.
+//
+// stream_read_kernel: every thread reads 16-byte chunks, four at a time,
+// grid-stride over the buffer; the XOR of everything read goes to one word
+// per workgroup so that no load can be dropped.
+//
+// mfma_peak_kernel: a register-resident loop of v_mfma_f32_32x32x16_bf16.
+// Each wave loads eight A and eight B operand fragments of one of 64
+// operand sets once, then runs eight independent accumulator chains (more
+// than the instruction's latency in issue slots), the operand pair of each
+// chain rotating every step so that the multipliers see changing data as
+// in a real GEMM (the chip's power limit depends on it).  Each thread
+// writes the sum of its accumulators so that no product can be dropped.
 #include "dbd_device.hpp"
 #include "dbd_internal.hpp"
 
@@ -34,6 +43,40 @@ __global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restric
 hipError_t stream_read_launch(const void* data, size_t bytes, uint32_t* sink, int grid,
                               hipStream_t st) {
   stream_read_kernel<<<grid, 512, 0, st>>>(static_cast<const u32x4*>(data), bytes / 16, sink);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void mfma_peak_kernel(const bf16x8* __restrict__ src, int iters,
+                                                       float* sink) {
+  const int lane = threadIdx.x & 63;
+  const int set = (blockIdx.x * 4 + (threadIdx.x >> 6)) % kMfmaPeakSets;
+  const bf16x8* p = src + (size_t)set * 16 * 64 + lane;
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = p[i * 64];
+    b[i] = p[(8 + i) * 64];
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) acc[c] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(c + r) & 7], b[(3 * c + r) & 7], acc[c], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  sink[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+hipError_t mfma_peak_launch(const void* operands, int iters, float* sink, hipStream_t st) {
+  mfma_peak_kernel<<<kMfmaPeakGrid, 256, 0, st>>>(static_cast<const bf16x8*>(operands), iters, sink);
   return hipGetLastError();
 }
 

@@ -518,6 +518,23 @@ dbd_status dbd_stream_read(const void* data, size_t bytes, uint32_t* sink, void*
 
 int dbd_stream_read_sink_words(void) { return dbd::kStreamReadGrid; }
 
+size_t dbd_mfma_peak_operand_bytes(void) { return (size_t)dbd::kMfmaPeakSets * 16 * 64 * 16; }
+int dbd_mfma_peak_sink_floats(void) { return dbd::kMfmaPeakGrid * 256; }
+double dbd_mfma_peak_flops(int iters) {
+  // 2 * 32 * 32 * 16 per instruction
+  return iters <= 0 ? 0.0
+                    : (double)dbd::kMfmaPeakGrid * 4 * iters * dbd::kMfmaPeakPerIter * 32768.0;
+}
+
+dbd_status dbd_mfma_peak(const void* operands, int iters, float* sink, void* stream) {
+  REQUIRE(iters >= 1 && iters <= 4096, "iters must be in [1, 4096] (got %d)", iters);
+  REQUIRE_PTR(operands);
+  REQUIRE_PTR(sink);
+  hipError_t e = dbd::mfma_peak_launch(operands, iters, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "MFMA ceiling launch");
+  return DBD_OK;
+}
+
 dbd_status dbd_round(const dbd_round_args* a, void* stream) {
   dbd_status s = check_round(a);
   if (s != DBD_OK) return s;

@@ -91,6 +91,10 @@ hipError_t sample_filtered_launch(const SampleArgs& a, hipStream_t stream);
 constexpr int kStreamReadGrid = 2048;   // workgroups of the read ceiling kernel
 hipError_t stream_read_launch(const void* data, size_t bytes, uint32_t* sink, int grid,
                               hipStream_t stream);
+constexpr int kMfmaPeakGrid = 1024;     // workgroups of four waves
+constexpr int kMfmaPeakSets = 64;       // operand sets of 16 fragments x 64 lanes x 16 bytes
+constexpr int kMfmaPeakPerIter = 64;    // MFMAs per wave per iteration
+hipError_t mfma_peak_launch(const void* operands, int iters, float* sink, hipStream_t stream);
 
 // partial arrays of the LM-head workspace: pm, pa, ps, pt, pg, pl
 constexpr int kLmPartArrays = 6;

@@ -496,6 +496,21 @@ dbd_status dbd_stream_read(const void* data, size_t bytes, uint32_t* sink,
                            void* stream);
 int dbd_stream_read_sink_words(void);
 
+/* Measurement helper: a register-resident loop of bf16 matrix-core
+ * multiply-adds (v_mfma_f32_32x32x16_bf16).  `operands` (device,
+ * dbd_mfma_peak_operand_bytes() bytes of bf16 values, e.g. random
+ * normals, 16-byte aligned) is read once; then every wave issues
+ * iters * 64 of the instruction over eight independent accumulator chains
+ * whose operands rotate every step, and every thread writes the sum of its
+ * accumulators to sink (device, dbd_mfma_peak_sink_floats() floats).  One
+ * launch performs dbd_mfma_peak_flops(iters) floating-point operations;
+ * their rate is the device's practical bf16 matrix-core rate on changing
+ * data, the power limit included.  iters must be in [1, 4096]. */
+dbd_status dbd_mfma_peak(const void* operands, int iters, float* sink, void* stream);
+size_t dbd_mfma_peak_operand_bytes(void);
+int dbd_mfma_peak_sink_floats(void);
+double dbd_mfma_peak_flops(int iters);
+
 const char* dbd_last_error(void);
 int dbd_abi_version(void);
 

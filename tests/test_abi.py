@@ -29,6 +29,8 @@ def test_header_declares_the_round_calls():
               "dbd_attn_paged_save", "dbd_commit_block", "dbd_lmhead_sample",
               "dbd_prefill_attn", "dbd_prefill_workspace_size", "dbd_lmhead_logits",
               "dbd_sample_filtered", "dbd_stream_read", "dbd_stream_read_sink_words",
+              "dbd_mfma_peak", "dbd_mfma_peak_operand_bytes", "dbd_mfma_peak_sink_floats",
+              "dbd_mfma_peak_flops",
               "dbd_graph_create", "dbd_graph_launch", "dbd_graph_destroy",
               "dbd_attn_workspace_size", "dbd_lmhead_workspace_size",
               "dbd_round_workspace_size", "dbd_validate_inputs", "dbd_last_error",
@@ -255,3 +257,18 @@ def test_validate_inputs():
     bad = dict(ok, mask_token_id=1024)
     with pytest.raises(api.DbdError):
         api.dbd_validate_inputs(**bad)
+
+
+def test_mfma_ceiling_host_checks():
+    """The MFMA ceiling helper validates its arguments on the host and
+    reports its work: 1024 workgroups x 4 waves x 64 instructions of
+    2*32*32*16 flops per iteration."""
+    L = api.lib()
+    assert L.dbd_mfma_peak_operand_bytes() == 64 * 16 * 64 * 16
+    assert L.dbd_mfma_peak_sink_floats() == 1024 * 256
+    assert L.dbd_mfma_peak_flops(3) == 1024 * 4 * 3 * 64 * 2 * 32 * 32 * 16
+    assert L.dbd_mfma_peak_flops(0) == 0.0
+    assert L.dbd_mfma_peak(16, 0, 16, None) == api.DBD_ERR_INVALID_ARG
+    assert L.dbd_mfma_peak(16, 4097, 16, None) == api.DBD_ERR_INVALID_ARG
+    assert L.dbd_mfma_peak(None, 4, 16, None) == api.DBD_ERR_INVALID_ARG
+    assert L.dbd_mfma_peak(16, 4, 8, None) == api.DBD_ERR_INVALID_ARG     # misaligned sink
