@@ -17,7 +17,12 @@
 // XCD and from L2 for the other members.
 //
 // A tile is 256 vocabulary columns x R <= 256 rows, four waves of 128 x R/2
-// computing C^T[v][m] = W[v].h[m] with v_mfma_f32_32x32x16_bf16.  K streams
+// computing C^T[v][m] = W[v].h[m] with v_mfma_f32_32x32x16_bf16.  A team's
+// range rarely ends on a tile boundary: in its partial last tile of nbl
+// 32-column blocks the two waves that share rows take ceil(nbl/2) blocks
+// each instead of 4 and 0..4, so the tile costs what its columns need
+// (12% off the LM head at 256 rows, whose ranges of 2.3 tiles used to take
+// three full tiles).  K streams
 // in stages of 64 (one 128-byte line per row) straight from global memory
 // into LDS (global_load_lds_dwordx4; 16-byte chunks XOR-permuted by row so
 // fragment reads are bank-conflict free):
@@ -254,7 +259,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   int chk[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) chk[j] = ((2 * j + (lane >> 5)) ^ rswz(fr)) << 3;
-  const lds_u16* const wfr = Wr + (wn * 128 + fr) * TK;
+  const lds_u16* wfr = Wr + (wn * 128 + fr) * TK;    // this wave's first W row; set per tile
   const lds_u16* const hfr = Hr + (wm * RH + fr) * TK;
   auto read_frags = [&](int ws, int hs, int j, bf16x8* af, bf16x8* bfr) {
     const lds_u16* w = wfr + ws * WSLOT + chk[j];
@@ -268,25 +273,29 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   };
 
   f32x16 acc[4][MB];
-  auto mfma_rows = [&](const bf16x8* af, const bf16x8* bfr, int mb) {
+  // NBW: the 32-column blocks this wave computes in the current tile
+  auto mfma_rows = [&](auto nbw_c, const bf16x8* af, const bf16x8* bfr, int mb) {
+    constexpr int NBW = decltype(nbw_c)::value;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NBW; ++nb)
       acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[nb], bfr[mb], acc[nb][mb], 0, 0, 0);
   };
   // one k-step's MFMAs with the next step's fragment reads interleaved,
   // fenced so that nothing else is scheduled into it
-  auto step = [&](const bf16x8* af, const bf16x8* bfr, int ws, int hs, int jn, bf16x8* an, bf16x8* bn) {
+  auto step = [&](auto nbw_c, const bf16x8* af, const bf16x8* bfr, int ws, int hs, int jn, bf16x8* an,
+                  bf16x8* bn) {
+    constexpr int NBW = decltype(nbw_c)::value;
     __builtin_amdgcn_sched_barrier(0);
     read_frags(ws, hs, jn, an, bn);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) mfma_rows(af, bfr, mb);
-    constexpr int NPAIR = 4 * MB < 4 + MB ? 4 * MB : 4 + MB;
+    for (int mb = 0; mb < MB; ++mb) mfma_rows(nbw_c, af, bfr, mb);
+    constexpr int NPAIR = NBW * MB < 4 + MB ? NBW * MB : 4 + MB;
 #pragma unroll
     for (int r = 0; r < NPAIR; ++r) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
-    if (4 * MB > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, 4 * MB - NPAIR, 0);
+    if (NBW * MB > NPAIR) __builtin_amdgcn_sched_group_barrier(0x008, NBW * MB - NPAIR, 0);
     if (4 + MB > NPAIR) __builtin_amdgcn_sched_group_barrier(0x100, 4 + MB - NPAIR, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -311,8 +320,8 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   // Accumulators start at 0, or at -inf on columns that are not candidates
   // (the mask id, columns past the range): MFMA accumulation keeps them at
   // -inf, so the reduction needs no per-value test.
-  auto init_acc = [&](int n0) {
-    const int vbase = n0 + wn * 128;
+  auto init_acc = [&](int n0, int wofs) {
+    const int vbase = n0 + wofs;
     const bool plain = (vbase + 128 <= v_hi) && (a.mask_id < vbase || a.mask_id >= vbase + 128);
     if (plain) {
 #pragma unroll
@@ -380,15 +389,16 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
 
   // store a finished tile's logits: lane holds row (lane & 31) of each row
   // block mb and vocabulary rows vb0 + 8*(i/4) + (i%4) of each 32-block nb
-  auto store_tile = [&](int n0) {
-    const int vbase = n0 + wn * 128;
+  auto store_tile = [&](auto nbw_c, int n0, int wofs) {
+    constexpr int NBW = decltype(nbw_c)::value;
+    const int vbase = n0 + wofs;
     if (vbase >= v_hi) return;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = m_base + wm * RH + mb * 32 + (lane & 31);
       float* lrow = a.logits + (size_t)(m < m_end ? m : m_base) * a.V;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NBW; ++nb) {
         __builtin_amdgcn_sched_barrier(0);
         const int vb0 = vbase + nb * 32 + 4 * (lane >> 5);
         float x[16];
@@ -417,18 +427,19 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
 
   // reduce a finished tile: lane holds row (lane & 31) of each row block mb
   // and vocabulary rows 8*(i/4) + 4*(lane/32) + (i%4) of each 32-block nb
-  auto reduce_tile = [&](int n0) {
-    const int vbase = n0 + wn * 128;
+  auto reduce_tile = [&](auto nbw_c, int n0, int wofs) {
+    constexpr int NBW = decltype(nbw_c)::value;
+    const int vbase = n0 + wofs;
     if (vbase >= v_hi) return;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      // block-online reduction of the lane's 64 values of this row, 16 at a
-      // time: block max, lowest id reaching it, sum(2^(x - m)) rescaled once
-      // per block.  Values are in log2 units; non-candidates are -inf.
+      // block-online reduction of the lane's 16*NBW values of this row, 16
+      // at a time: block max, lowest id reaching it, sum(2^(x - m)) rescaled
+      // once per block.  Values are in log2 units; non-candidates are -inf.
       float m = -INFINITY, sum = 0.f, tt = 0.f;   // tt: sum 2^(x-m) (x-m)
       int idx = 0x7fffffff;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int nb = 0; nb < NBW; ++nb) {
         __builtin_amdgcn_sched_barrier(0);
         const int vb0 = vbase + nb * 32 + 4 * (lane >> 5);
         float x[16];
@@ -513,50 +524,82 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   if (!WL) issue(Hr + HSLOT);
   int ws = 0, hs = 0;      // ring slots of the stage being computed
   bf16x8 fa0[4], fb0[MB], fa1[4], fb1[MB];
+  // Tile geometry of this wave: a full tile gives each of the two waves
+  // sharing rows 128 columns (four 32-column blocks); a partial last tile of
+  // nbl blocks gives each ceil(nbl/2) of them, so that both waves' MFMA
+  // work shrinks with the tile (the sampling modes keep full-width tiles,
+  // whose register budget has no room for more variants).  wofs: the
+  // wave's first W row in the slot.
+  auto tile_geom = [&](int t, int& wofs, int& nbw) {
+    const int wt = min(NT, v_hi - (v_lo + t * NT));
+    const int h = (SMP || wt >= NT) ? 4 : ((wt + 31) / 32 + 1) / 2;
+    wofs = wn * 32 * h;
+    nbw = h;
+  };
+  int wofs_n, nbw_n;       // geometry of the tile whose fragments are read next
+  tile_geom(0, wofs_n, nbw_n);
+  wfr = Wr + (wofs_n + fr) * TK;
   read_frags(ws, hs, 0, fa0, fb0);
 
   for (int tile = 0; tile < ntile; ++tile) {
     const int n0 = v_lo + tile * NT;
-    init_acc(n0);
-    for (int kt = 0; kt < nk; ++kt) {
-      lds_u16* const wt = Wr + (ws == 0 ? NWS - 1 : ws - 1) * WSLOT;
-      constexpr int Q = WPW / 4;
-      if (WL) issue_part(wt, I{}, std::integral_constant<int, Q>{});
-      step(fa0, fb0, ws, hs, 1, fa1, fb1);
-      if (WL) issue_part(wt, std::integral_constant<int, Q>{}, std::integral_constant<int, 2 * Q>{});
-      step(fa1, fb1, ws, hs, 2, fa0, fb0);
-      if (WL) issue_part(wt, std::integral_constant<int, 2 * Q>{}, std::integral_constant<int, 3 * Q>{});
-      step(fa0, fb0, ws, hs, 3, fa1, fb1);
-      if (WL) {
-        issue_part(wt, std::integral_constant<int, 3 * Q>{}, std::integral_constant<int, 4 * Q>{});
-        advance();
+    const int wofs = wofs_n, nbw = nbw_n;
+    if (tile + 1 < ntile) tile_geom(tile + 1, wofs_n, nbw_n);
+    auto run_tile = [&](auto nbw_c) {
+      constexpr int NBW = decltype(nbw_c)::value;
+      init_acc(n0, wofs);
+      for (int kt = 0; kt < nk; ++kt) {
+        lds_u16* const wt = Wr + (ws == 0 ? NWS - 1 : ws - 1) * WSLOT;
+        constexpr int Q = WPW / 4;
+        if (WL) issue_part(wt, I{}, std::integral_constant<int, Q>{});
+        step(nbw_c, fa0, fb0, ws, hs, 1, fa1, fb1);
+        if (WL) issue_part(wt, std::integral_constant<int, Q>{}, std::integral_constant<int, 2 * Q>{});
+        step(nbw_c, fa1, fb1, ws, hs, 2, fa0, fb0);
+        if (WL) issue_part(wt, std::integral_constant<int, 2 * Q>{}, std::integral_constant<int, 3 * Q>{});
+        step(nbw_c, fa0, fb0, ws, hs, 3, fa1, fb1);
+        if (WL) {
+          issue_part(wt, std::integral_constant<int, 3 * Q>{}, std::integral_constant<int, 4 * Q>{});
+          advance();
+        }
+        // k-step 3: half its MFMAs, the sync for the next stage, the hidden
+        // loads, and the other half under the next stage's first fragments
+        // (of the next tile after the last stage)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mb = 0; mb < MB / 2; ++mb) mfma_rows(nbw_c, fa1, fb1, mb);
+        __builtin_amdgcn_sched_barrier(0);
+        sync();
+        if (!WL) issue(Hr + hs * HSLOT);
+        ws = ws == NWS - 1 ? 0 : ws + 1;
+        hs = hs == NHS - 1 ? 0 : hs + 1;
+        if (kt == nk - 1) wfr = Wr + (wofs_n + fr) * TK;
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(ws, hs, 0, fa0, fb0);
+#pragma unroll
+        for (int mb = MB / 2; mb < MB; ++mb) mfma_rows(nbw_c, fa1, fb1, mb);
+        constexpr int NM2 = NBW * (MB - MB / 2), NP2 = NM2 < 4 + MB ? NM2 : 4 + MB;
+#pragma unroll
+        for (int r = 0; r < NP2; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        }
+        if (4 + MB > NP2) __builtin_amdgcn_sched_group_barrier(0x100, 4 + MB - NP2, 0);
+        if (NM2 > NP2) __builtin_amdgcn_sched_group_barrier(0x008, NM2 - NP2, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // k-step 3: half its MFMAs, the sync for the next stage, the hidden
-      // loads, and the other half under the next stage's first fragments
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int mb = 0; mb < MB / 2; ++mb) mfma_rows(fa1, fb1, mb);
-      __builtin_amdgcn_sched_barrier(0);
-      sync();
-      if (!WL) issue(Hr + hs * HSLOT);
-      ws = ws == NWS - 1 ? 0 : ws + 1;
-      hs = hs == NHS - 1 ? 0 : hs + 1;
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(ws, hs, 0, fa0, fb0);
-#pragma unroll
-      for (int mb = MB / 2; mb < MB; ++mb) mfma_rows(fa1, fb1, mb);
-      constexpr int NM2 = 4 * (MB - MB / 2), NP2 = NM2 < 4 + MB ? NM2 : 4 + MB;
-#pragma unroll
-      for (int r = 0; r < NP2; ++r) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      if constexpr (STO) store_tile(nbw_c, n0, wofs);
+      else reduce_tile(nbw_c, n0, wofs);
+    };
+    if constexpr (SMP) {
+      run_tile(std::integral_constant<int, 4>{});
+    } else {
+      switch (nbw) {
+        case 1: run_tile(std::integral_constant<int, 1>{}); break;
+        case 2: run_tile(std::integral_constant<int, 2>{}); break;
+        case 3: run_tile(std::integral_constant<int, 3>{}); break;
+        default: run_tile(std::integral_constant<int, 4>{}); break;
       }
-      if (4 + MB > NP2) __builtin_amdgcn_sched_group_barrier(0x100, 4 + MB - NP2, 0);
-      if (NM2 > NP2) __builtin_amdgcn_sched_group_barrier(0x008, NM2 - NP2, 0);
-      __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (STO) store_tile(n0);
-    else reduce_tile(n0);
   }
 
   // all loads have landed and every wave is past its last fragment read
