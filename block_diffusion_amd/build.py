@@ -9,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -29,19 +30,44 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm toolchain required to build libdbd)")
 
 
+def check_isa(asm_dir: str, verbose: bool = False) -> None:
+    """Scans the kept gfx950 assembly for LDS-DMA wait-state hazards
+    (isa_check); raises if any is found."""
+    from block_diffusion_amd import isa_check
+    found, n = [], 0
+    for f in sorted(glob.glob(os.path.join(asm_dir, f"*-hip-amdgcn-amd-amdhsa-{ARCH}.s"))):
+        with open(f) as fh:
+            k, h = isa_check.scan(fh.read())
+        n += k
+        found += [(os.path.basename(f),) + x for x in h]
+    if found:
+        msg = "\n".join(f"  {f}:{line} {kern}: '{dma}' after '{w}'" for f, kern, line, dma, w in found[:20])
+        raise RuntimeError(f"{len(found)} LDS-DMA wait-state hazard(s) in the compiled kernels:\n{msg}")
+    if verbose:
+        print(f"ISA check: {n} LDS-DMA instructions, no wait-state hazard", flush=True)
+
+
 def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(HERE, "..", "include"), "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in r.stderr.splitlines()
-                    if "packed-fp32-ops" not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
+    # -save-temps keeps the device assembly that is linked, for check_isa
+    with tempfile.TemporaryDirectory(prefix="dbd_build_") as work:
+        cmd = [hipcc(), *FLAGS, "-save-temps", "-I", os.path.abspath(os.path.join(HERE, "..", "include")),
+               "-o", tmp, *srcs]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True, cwd=work)
+        err = "\n".join(l for l in r.stderr.splitlines()
+                        if "packed-fp32-ops" not in l)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
+        if err.strip() and verbose:
+            print(err, file=sys.stderr)
+        try:
+            check_isa(work, verbose)
+        except RuntimeError:
+            os.remove(tmp)
+            raise
     os.replace(tmp, LIB)
     return LIB
 

@@ -16,7 +16,9 @@
 // A wave finishes each segment it touches with (max, sum, unnormalised
 // output); a segment split over several waves leaves fp32 partials that
 // attn_combine_kernel merges, one that fits in one wave is written directly.
-// attn_plan_kernel first turns prefix lengths into tile prefix sums.
+// Each wave (and each combine workgroup) first turns the prefix lengths
+// into tile prefix sums itself: a separate planning launch would cost more
+// than the few loads it saves.
 //
 // Per wave, tiles go straight from global memory into a ring of kRing LDS
 // slots (global_load_lds_dwordx4: kKT keys of K and of V in runs of 16 that
@@ -158,43 +160,10 @@ __device__ __forceinline__ int state_of(const uint8_t* st, int s) {
 struct Dec {      // a position in the tile stream
   int s, hg, j;   // sequence, segment within the sequence, tile within the segment
   int L, nP, tiles;
+  int p;          // tiles of all sequences before s
 };
 
 }  // namespace
-
-// Tile prefix sums: plan[s] = sum over s' < s of (ceil(L_s'/16) + ceil(B/16)).
-__global__ __launch_bounds__(1024) void attn_plan_kernel(AttnArgs a) {
-  __shared__ int s_wsum[16];
-  if (a.gate != nullptr && *a.gate <= 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int S = a.S, nB = (a.B + kKT - 1) / kKT;
-  const int per = (S + 1023) / 1024;
-  const int b0 = tid * per;
-  int local = 0;
-  for (int j = 0; j < per; ++j)
-    if (b0 + j < S) local += (a.prefix_len[b0 + j] + kKT - 1) / kKT + nB;
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) s_wsum[wave] = incl;
-  __syncthreads();
-  int run = 0;
-  for (int w = 0; w < wave; ++w) run += s_wsum[w];
-  run += incl - local;
-  for (int j = 0; j < per; ++j)
-    if (b0 + j < S) {
-      a.plan[b0 + j] = run;
-      run += (a.prefix_len[b0 + j] + kKT - 1) / kKT + nB;
-    }
-  if (tid == 1023) {
-    int tot = 0;
-    for (int w = 0; w < 16; ++w) tot += s_wsum[w];
-    a.plan[S] = tot;
-  }
-}
 
 template <int D, int RT, int NR, bool SAVE>
 __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
@@ -207,7 +176,22 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
   const int S = a.S, NHG = a.Hkv * a.n_rg, nB = (a.B + kKT - 1) / kKT;
   const int R = a.G * a.B;
-  const long T = (long)NHG * ldc(a.plan, S);
+  // tile prefix sums plan(s) = tiles of the sequences before s (each has
+  // ceil(L/kKT) + nB >= 1 tiles): lane l sums sequences [l*c, l*c + c)
+  const int c = (S + 63) / 64;
+  int mine = 0;
+  for (int i = 0; i < c; ++i) {
+    const int s = lane * c + i;
+    if (s < S) mine += (a.prefix_len[s] + kKT - 1) / kKT + nB;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  const int start = incl - mine;                                    // plan(l*c)
+  const long T = (long)NHG * __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
   const long NWe = min((long)a.grid, max(1L, T / 64));
   const long w = blockIdx.x;
   if (w >= NWe) return;
@@ -215,16 +199,18 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   const int n = (int)(t1 - t0);
   if (n <= 0) return;
 
-  // locate t0: largest s with NHG*plan[s] <= t0 (64-way search)
-  int lo = 0, hi = S;
-  while (hi - lo > 1) {
-    const int step = (hi - lo + 63) / 64;
-    const int idx = min(lo + lane * step, hi);
-    const bool pred = idx < hi && (long)NHG * a.plan[idx] <= t0;
-    const unsigned long long bal = __ballot(pred);
-    const int k = 63 - __clzll(bal);
-    lo = __builtin_amdgcn_readfirstlane(lo + k * step);
-    hi = min(hi, lo + step);
+  // locate t0: the largest s with NHG*plan(s) <= t0 -- the lane whose
+  // sequences hold it (lane 0 always qualifies: plan(0) = 0), then a walk
+  // through that lane's at most c sequences
+  const unsigned long long bal = __ballot(lane * c < S && (long)NHG * start <= t0);
+  const int k = 63 - __clzll(bal);
+  int s_lo = __builtin_amdgcn_readfirstlane(k * c);
+  int p_lo = __builtin_amdgcn_readfirstlane(__shfl(start, k, 64));
+  for (int i = 1; i < c && s_lo + 1 < S; ++i) {
+    const int tl = (ldc(a.prefix_len, s_lo) + kKT - 1) / kKT + nB;
+    if ((long)NHG * (p_lo + tl) > t0) break;
+    ++s_lo;
+    p_lo += tl;
   }
   auto load_seq = [&](Dec& d) INL {
     d.L = ldc(a.prefix_len, d.s);
@@ -232,10 +218,11 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
     d.tiles = d.nP + nB;
   };
   Dec dc;
-  dc.s = lo;
+  dc.s = s_lo;
+  dc.p = p_lo;
   load_seq(dc);
   {
-    const long rem = t0 - (long)NHG * ldc(a.plan, lo);
+    const long rem = t0 - (long)NHG * p_lo;
     dc.hg = (int)(rem / dc.tiles);
     dc.j = (int)(rem % dc.tiles);
   }
@@ -245,6 +232,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       d.j = 0;
       if (++d.hg == NHG) {
         d.hg = 0;
+        d.p += d.tiles;
         if (++d.s < S) load_seq(d);
       }
     }
@@ -297,7 +285,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       l_run[rt] += shfl_xor_f(l_run[rt], 32);
     }
     const int g = d.hg / a.n_rg, rg = d.hg % a.n_rg;
-    const long ts = (long)NHG * ldc(a.plan, d.s) + (long)d.hg * d.tiles;
+    const long ts = (long)NHG * d.p + (long)d.hg * d.tiles;
     const long w0 = ((ts + 1) * NWe - 1) / T;
     const long w1 = ((ts + d.tiles) * NWe - 1) / T;
     if (w0 == w1) {
@@ -366,6 +354,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       if (prev.hg == 0) {
         --prev.s;
         load_seq(prev);
+        prev.p -= prev.tiles;
         prev.hg = NHG - 1;
       } else {
         --prev.hg;
@@ -510,6 +499,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       if (prev.hg == 0) {
         --prev.s;
         load_seq(prev);
+        prev.p -= prev.tiles;
         prev.hg = NHG - 1;
       } else {
         --prev.hg;
@@ -532,10 +522,30 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int seg = blockIdx.x;
   const int s = seg / NHG, hg = seg % NHG;
   const int g = hg / a.n_rg, rg = hg % a.n_rg;
-  const long T = (long)NHG * a.plan[a.S];
+  // the tiles of all sequences, and of those before s
+  __shared__ int s_red[2][4];
+  int all = 0, before = 0;
+  for (int i = threadIdx.x; i < a.S; i += 256) {
+    const int t = (a.prefix_len[i] + kKT - 1) / kKT + nB;
+    all += t;
+    before += i < s ? t : 0;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    all += __shfl_xor(all, off, 64);
+    before += __shfl_xor(before, off, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    s_red[0][threadIdx.x >> 6] = all;
+    s_red[1][threadIdx.x >> 6] = before;
+  }
+  __syncthreads();
+  all = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+  before = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+  const long T = (long)NHG * all;
   const long NW = min((long)a.grid, max(1L, T / 64));
   const int tiles = (a.prefix_len[s] + kKT - 1) / kKT + nB;
-  const long ts = (long)NHG * a.plan[s] + (long)hg * tiles;
+  const long ts = (long)NHG * before + (long)hg * tiles;
   const long w0 = ((ts + 1) * NW - 1) / T;
   const long w1 = ((ts + tiles) * NW - 1) / T;
   const int pieces = (int)(w1 - w0 + 1);
@@ -585,16 +595,14 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
   const int slot_bytes = 2 * kKT * D * 2;
   const int waves_per_cu = std::max(1, std::min(kMaxWavesPerCU, kLdsPerCU / (kRing * slot_bytes)));
   p.grid = kCUs * waves_per_cu;
-  p.plan_bytes = ((size_t)(S + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   const size_t slots = (size_t)S * Hkv * p.n_rg * p.maxp * 16 * p.RT;
   p.o_bytes = (slots * D * sizeof(float) + 255) & ~(size_t)255;
-  p.ws_bytes = p.plan_bytes + p.o_bytes + slots * sizeof(float2);
+  p.ws_bytes = p.o_bytes + slots * sizeof(float2);
   return p;
 }
 
 template <int D, int RT>
 static hipError_t launch_dr(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
-  attn_plan_kernel<<<1, 1024, 0, st>>>(a);
   if (a.save_state != nullptr)
     attn_stream_kernel<D, RT, kRing, true><<<p.grid, 64, 0, st>>>(a);
   else

@@ -91,9 +91,8 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
   a.q = q; a.k_blk = k_blk; a.v_blk = v_blk; a.k_cache = k_cache; a.v_cache = v_cache;
   a.page_table = page_table; a.prefix_len = prefix_len; a.out = out;
   char* w = static_cast<char*>(ws);
-  a.plan = reinterpret_cast<int32_t*>(w);
-  a.part_o = reinterpret_cast<float*>(w + plan.plan_bytes);
-  a.part_ml = reinterpret_cast<float2*>(w + plan.plan_bytes + plan.o_bytes);
+  a.part_o = reinterpret_cast<float*>(w);
+  a.part_ml = reinterpret_cast<float2*>(w + plan.o_bytes);
   a.S = S; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.P = P; a.max_pages = max_pages;
   a.n_rg = plan.n_rg; a.maxp = plan.maxp; a.grid = plan.grid;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);

@@ -17,7 +17,6 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* prefix_len;
   uint16_t* out;
-  int32_t* plan;   // [S+1] exclusive prefix sums of tiles per sequence
   float* part_o;   // [S*NHG*maxp][rows][D] unnormalised sums of split segments
   float2* part_ml; // [S*NHG*maxp][rows] (max, sum), log2 units
   int S, B, Hq, Hkv, G, P, max_pages;
@@ -39,7 +38,7 @@ struct AttnArgs {
 
 struct AttnPlan {
   int D, RT, n_rg, maxp, grid;
-  size_t plan_bytes, o_bytes, ws_bytes;  // workspace: plan | part_o | part_ml
+  size_t o_bytes, ws_bytes;  // workspace: part_o | part_ml
 };
 
 AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size,

@@ -143,10 +143,15 @@ __device__ __forceinline__ float uniform01(uint32_t w) {
 // One 1 KB direct-to-LDS load: lane l copies the 16 bytes at base + off to
 // lds + 16*l.  Inline assembly, so that the compiler neither adds its own
 // vmcnt waits for the LDS it writes nor moves LDS accesses across it; the
-// rings are paced by explicit waits.  M0 carries the LDS address (the s_nop
-// is the wait state a freshly written M0 needs before an LDS DMA).
+// rings are paced by explicit waits.  M0 carries the LDS address.  The
+// s_nop 4 gives the five wait states that a VMEM instruction needs after a
+// VALU instruction wrote an SGPR it reads: the compiler may materialise the
+// base pair with v_readlane (an SGPR spill reload) right before the
+// assembly, and it does not insert those wait states for an operand of
+// inline assembly (a stale base register sends the load anywhere).  They
+// also cover the one wait state a freshly written M0 needs.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, const lds_u16* lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
 }
 

@@ -69,8 +69,13 @@ __device__ __forceinline__ int poff(int r, int c) {
   return r * D + ((c ^ pswz<D>(r)) << 3);
 }
 
+// One 1 KB direct-to-LDS load (lane l: 16 bytes at base + off to lds +
+// 16*l).  s_nop 4: the five wait states a VMEM instruction needs after a
+// VALU write of an SGPR it reads (the base pair may come from v_readlane;
+// the compiler adds no wait states for inline-assembly operands), which
+// also cover the one a fresh M0 needs.
 __device__ __forceinline__ void pf_dma16(const void* base, uint32_t off, const lds_u16* lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
 }
 template <int N>
