@@ -143,15 +143,16 @@ __device__ __forceinline__ float uniform01(uint32_t w) {
 // One 1 KB direct-to-LDS load: lane l copies the 16 bytes at base + off to
 // lds + 16*l.  Inline assembly, so that the compiler neither adds its own
 // vmcnt waits for the LDS it writes nor moves LDS accesses across it; the
-// rings are paced by explicit waits.  M0 carries the LDS address.  The
-// s_nop 4 gives the five wait states that a VMEM instruction needs after a
-// VALU instruction wrote an SGPR it reads: the compiler may materialise the
-// base pair with v_readlane (an SGPR spill reload) right before the
-// assembly, and it does not insert those wait states for an operand of
-// inline assembly (a stale base register sends the load anywhere).  They
-// also cover the one wait state a freshly written M0 needs.
+// rings are paced by explicit waits.  M0 carries the LDS address; the s_nop
+// is the one wait state a freshly written M0 needs.  A VMEM instruction also
+// needs five wait states after a VALU instruction wrote an SGPR it reads,
+// and the compiler inserts none for an operand of inline assembly: if it
+// ever materialised the base pair with v_readlane (an SGPR spill reload)
+// right before this, the load would use a stale base.  The build scans the
+// linked assembly for that pattern and refuses the library (isa_check.py);
+// five wait states here instead would cost 1-2% of the kernel.
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, const lds_u16* lds) {
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
 }
 
@@ -537,19 +538,23 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   // wave's first W row in the slot.
   auto tile_geom = [&](int t, int& wofs, int& nbw) {
     const int wt = min(NT, v_hi - (v_lo + t * NT));
-    const int h = (SMP || wt >= NT) ? 4 : ((wt + 31) / 32 + 1) / 2;
+    const int h = wt >= NT ? 4 : ((wt + 31) / 32 + 1) / 2;
     wofs = wn * 32 * h;
     nbw = h;
   };
-  int wofs_n, nbw_n;       // geometry of the tile whose fragments are read next
-  tile_geom(0, wofs_n, nbw_n);
-  wfr = Wr + (wofs_n + fr) * TK;
+  int wofs_n = wn * 128, nbw_n = 4;   // geometry of the tile whose fragments are read next
+  if constexpr (!SMP) {
+    tile_geom(0, wofs_n, nbw_n);
+    wfr = Wr + (wofs_n + fr) * TK;
+  }
   read_frags(ws, hs, 0, fa0, fb0);
 
   for (int tile = 0; tile < ntile; ++tile) {
     const int n0 = v_lo + tile * NT;
     const int wofs = wofs_n, nbw = nbw_n;
-    if (tile + 1 < ntile) tile_geom(tile + 1, wofs_n, nbw_n);
+    if constexpr (!SMP) {
+      if (tile + 1 < ntile) tile_geom(tile + 1, wofs_n, nbw_n);
+    }
     auto run_tile = [&](auto nbw_c) {
       constexpr int NBW = decltype(nbw_c)::value;
       init_acc(n0, wofs);
@@ -577,7 +582,9 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
         if (!WL) issue(Hr + hs * HSLOT);
         ws = ws == NWS - 1 ? 0 : ws + 1;
         hs = hs == NHS - 1 ? 0 : hs + 1;
-        if (kt == nk - 1) wfr = Wr + (wofs_n + fr) * TK;
+        if constexpr (!SMP) {
+          if (kt == nk - 1) wfr = Wr + (wofs_n + fr) * TK;
+        }
         __builtin_amdgcn_sched_barrier(0);
         read_frags(ws, hs, 0, fa0, fb0);
 #pragma unroll

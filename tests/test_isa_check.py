@@ -2,8 +2,8 @@
 (block_diffusion_amd.isa_check) on small hand-written listings: a VALU
 write of the DMA's SGPR base or of M0 within five wait states is reported,
 five wait states (s_nop 4) in between are not; the walk follows the
-fall-through path across block labels unless an unconditional branch ends
-the previous block."""
+fall-through path across block labels (unless an unconditional branch ends
+the previous block) and every branch to a label."""
 from block_diffusion_amd import isa_check
 
 HDR = "_ZN3dbd6kernelEv:\n"
@@ -40,4 +40,13 @@ def test_fall_through_across_a_label_is_followed():
     body = "\tv_readlane_b32 s5, v255, 5\n.LBB0_3:\n\tglobal_load_lds_dwordx4 v2, s[4:5]\n"
     assert len(_scan(body)[1]) == 1
     body = "\tv_readlane_b32 s5, v255, 5\n\ts_branch .LBB0_9\n.LBB0_3:\n\tglobal_load_lds_dwordx4 v2, s[4:5]\n"
+    assert _scan(body)[1] == []
+
+
+def test_branch_sources_are_followed():
+    body = ("\tv_readlane_b32 s5, v255, 5\n\ts_cbranch_scc1 .LBB0_3\n\ts_mov_b32 s7, 0\n"
+            "\ts_nop 7\n\ts_branch .LBB0_9\n.LBB0_3:\n\tglobal_load_lds_dwordx4 v2, s[4:5]\n")
+    assert len(_scan(body)[1]) == 1
+    body = ("\tv_readlane_b32 s5, v255, 5\n\ts_nop 4\n\ts_cbranch_scc1 .LBB0_3\n\ts_branch .LBB0_9\n"
+            ".LBB0_3:\n\tglobal_load_lds_dwordx4 v2, s[4:5]\n")
     assert _scan(body)[1] == []
