@@ -239,7 +239,9 @@ dbd_status dbd_lmhead_sample(int max_rows, int Hd, int V, int mask_token_id,
  *   dbd_lmhead_sample (same seed, step and Philox counters, the other
  *   tokens with zero weight), and conf[row] is its probability at
  *   temperature 1 over all tokens but the mask token.  top_k = 0 and
- *   top_p >= 1 give the draw of dbd_lmhead_sample.  Requirements:
+ *   top_p >= 1 give the draw of dbd_lmhead_sample.  Only finite logits
+ *   are candidates (-inf ones are never ranked or drawn); a row with no
+ *   candidate gets token = mask_token_id and conf = 0.  Requirements:
  *   temperature finite and > 0, top_k >= 0, top_p not NaN. */
 dbd_status dbd_lmhead_logits(int max_rows, int Hd, int V, int mask_token_id,
                              const dbd_bf16* hidden, const int32_t* row_index,

@@ -39,7 +39,8 @@ Top-k / top-p filtering (README usage examples: topk, topp; developer
 notes, "Benchmarking": top_p 0.95; "Ruled-Out Optimizations": a separate
 sampler after the logits was faster than a fused one).  Readings:
   * tokens other than the mask token are ranked by logit, higher first, the
-    lower id first among equal logits;
+    lower id first among equal logits; only finite logits take part (the
+    mask column arrives as -inf from the LM head, so it never does);
   * top_k > 0 keeps the first top_k of that ranking (all if fewer);
   * top_p < 1 then keeps the shortest leading run of the kept tokens whose
     running sum of exp((l - m) / T) reaches top_p times their total (at
