@@ -39,7 +39,8 @@ class dbd_round_args(C.Structure):
         ("entropy", _vp), ("save_kv", C.c_int), ("num_pages", C.c_int),
         ("token_stream", _vp), ("stream_cap", C.c_int), ("end_len", _vp),
         ("gate_on_rows", C.c_int), ("round_counter", _vp),
-        ("sample", C.c_int), ("temperature", C.c_float), ("seed", C.c_uint64), ("step", C.c_uint32)]
+        ("sample", C.c_int), ("temperature", C.c_float), ("seed", C.c_uint64), ("step", C.c_uint32),
+        ("filter", C.c_int), ("top_k", C.c_int), ("top_p", C.c_float), ("logits", C.c_void_p)]
 
 
 class DbdError(RuntimeError):
@@ -49,6 +50,9 @@ class DbdError(RuntimeError):
 
 
 _lib = None
+
+
+ABI_VERSION = 4          # DBD_ABI_VERSION of include/dbd.h that this binding follows
 
 
 def lib() -> C.CDLL:
@@ -120,6 +124,12 @@ def lib() -> C.CDLL:
     L.dbd_last_error.restype = C.c_char_p
     L.dbd_abi_version.argtypes = []
     L.dbd_abi_version.restype = i
+    L.dbd_round_args_size.argtypes = []
+    L.dbd_round_args_size.restype = sz
+    if L.dbd_abi_version() != ABI_VERSION or L.dbd_round_args_size() != C.sizeof(dbd_round_args):
+        raise ImportError(f"{LIB_PATH}: ABI {L.dbd_abi_version()} with a {L.dbd_round_args_size()}-byte "
+                          f"dbd_round_args, this binding expects ABI {ABI_VERSION} and "
+                          f"{C.sizeof(dbd_round_args)} bytes: rebuild the library")
     _lib = L
     return L
 

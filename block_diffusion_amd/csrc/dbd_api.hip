@@ -135,6 +135,36 @@ dbd_status enqueue_lm(int max_rows, int Hd, int V, int mask, const dbd_bf16* hid
   return DBD_OK;
 }
 
+// the listed rows' logits (store mode of the LM-head tile kernel)
+dbd_status enqueue_logits(int max_rows, int Hd, int V, int mask, const dbd_bf16* hidden,
+                          const int32_t* row_index, const int32_t* num_rows, const dbd_bf16* w,
+                          float* logits, hipStream_t st) {
+  if (max_rows == 0) return DBD_OK;
+  dbd::LmArgs a{};
+  a.hidden = hidden; a.row_index = row_index; a.num_rows = num_rows; a.w = w;
+  a.Hd = Hd; a.V = V; a.mask_id = mask; a.max_rows = max_rows;
+  a.logits = logits;
+  hipError_t e = dbd::lmhead_launch(a, st);
+  if (e != hipSuccess) return hip_fail(e, "LM-head launch");
+  return DBD_OK;
+}
+
+dbd_status enqueue_filtered(int max_rows, int V, int mask, const float* logits,
+                            const int32_t* row_index, const int32_t* num_rows, float temperature,
+                            int top_k, float top_p, uint64_t seed, uint32_t step, int32_t* token,
+                            float* conf, hipStream_t st) {
+  if (max_rows == 0) return DBD_OK;
+  dbd::SampleArgs a{};
+  a.logits = logits; a.row_index = row_index; a.num_rows = num_rows;
+  a.V = V; a.mask_id = mask; a.max_rows = max_rows; a.top_k = top_k;
+  a.inv_temp = 1.f / temperature; a.top_p = top_p;
+  a.key0 = (uint32_t)seed; a.key1 = (uint32_t)(seed >> 32); a.step = step;
+  a.token = token; a.conf = conf;
+  hipError_t e = dbd::sample_filtered_launch(a, st);
+  if (e != hipSuccess) return hip_fail(e, "sampling launch");
+  return DBD_OK;
+}
+
 dbd_status enqueue_remask(int S, int B, int mask, float tau, uint32_t flags, int rule, int k,
                           float eb, const float* entropy,
                           int32_t* block_tokens, uint8_t* seq_state,
@@ -179,6 +209,14 @@ dbd_status check_round(const dbd_round_args* a) {
   if (s != DBD_OK) return s;
   if (a->sample) REQUIRE(isfinite(a->temperature) && a->temperature > 0.f,
                          "temperature must be finite and > 0 (got %g)", (double)a->temperature);
+  if (a->filter) {
+    REQUIRE(a->sample, "filter needs sample");
+    REQUIRE(a->top_k >= 0, "top_k must be >= 0 (got %d)", a->top_k);
+    REQUIRE(!isnan(a->top_p), "top_p is NaN");
+    REQUIRE(a->rule != DBD_RULE_ENTROPY_BOUNDED, "filter does not compute the entropy the rule needs");
+    REQUIRE((long)a->S * a->B * a->V < (1L << 40), "S*B*V too large");
+    REQUIRE_PTR(a->logits);
+  }
   REQUIRE_PTR(a->q); REQUIRE_PTR(a->k_blk); REQUIRE_PTR(a->v_blk);
   REQUIRE_PTR(a->k_cache); REQUIRE_PTR(a->v_cache);
   REQUIRE_PTR(a->page_table); REQUIRE_PTR(a->prefix_len); REQUIRE_PTR(a->attn_out);
@@ -218,9 +256,18 @@ dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
   if (s != DBD_OK) return s;
   const int max_rows = a->S * a->B;
   float* ent = a->rule == DBD_RULE_ENTROPY_BOUNDED ? a->entropy : nullptr;
-  s = enqueue_lm(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index, a->num_rows,
-                 a->w_vocab, a->argmax_tok, a->conf, ent, ws + attn_ws, a->workspace_bytes - attn_ws, st,
-                 a->sample != 0, a->temperature, a->seed, a->step);
+  if (a->sample && a->filter) {
+    s = enqueue_logits(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index,
+                       a->num_rows, a->w_vocab, a->logits, st);
+    if (s != DBD_OK) return s;
+    s = enqueue_filtered(max_rows, a->V, a->mask_token_id, a->logits, a->row_index, a->num_rows,
+                         a->temperature, a->top_k, a->top_p, a->seed, a->step, a->argmax_tok,
+                         a->conf, st);
+  } else {
+    s = enqueue_lm(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index, a->num_rows,
+                   a->w_vocab, a->argmax_tok, a->conf, ent, ws + attn_ws, a->workspace_bytes - attn_ws,
+                   st, a->sample != 0, a->temperature, a->seed, a->step);
+  }
   if (s != DBD_OK) return s;
   const uint32_t fl = (a->flags & ~DBD_COMPACT_ONLY) | (save ? dbd::kCommitSaving : 0u);
   return enqueue_remask(a->S, a->B, a->mask_token_id, a->dynamic_threshold, fl,
@@ -243,6 +290,8 @@ struct dbd_graph {
 extern "C" {
 
 int dbd_abi_version(void) { return DBD_ABI_VERSION; }
+
+size_t dbd_round_args_size(void) { return sizeof(dbd_round_args); }
 
 const char* dbd_last_error(void) { return g_err.c_str(); }
 
@@ -378,14 +427,8 @@ dbd_status dbd_lmhead_logits(int max_rows, int Hd, int V, int mask_token_id,
   REQUIRE((long)max_rows * V < (1L << 40), "max_rows*V too large");
   REQUIRE_PTR(hidden); REQUIRE_PTR(num_rows); REQUIRE_PTR(w_vocab); REQUIRE_PTR(logits);
   if (row_index != nullptr) REQUIRE_PTR(row_index);
-  if (max_rows == 0) return DBD_OK;
-  dbd::LmArgs a{};
-  a.hidden = hidden; a.row_index = row_index; a.num_rows = num_rows; a.w = w_vocab;
-  a.Hd = Hd; a.V = V; a.mask_id = mask_token_id; a.max_rows = max_rows;
-  a.logits = logits;
-  hipError_t e = dbd::lmhead_launch(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "LM-head launch");
-  return DBD_OK;
+  return enqueue_logits(max_rows, Hd, V, mask_token_id, hidden, row_index, num_rows, w_vocab, logits,
+                        static_cast<hipStream_t>(stream));
 }
 
 dbd_status dbd_sample_filtered(int max_rows, int V, int mask_token_id, const float* logits,
@@ -401,16 +444,8 @@ dbd_status dbd_sample_filtered(int max_rows, int V, int mask_token_id, const flo
   REQUIRE(top_k >= 0, "top_k must be >= 0 (got %d)", top_k);
   REQUIRE_PTR(logits); REQUIRE_PTR(num_rows); REQUIRE_PTR(token); REQUIRE_PTR(conf);
   if (row_index != nullptr) REQUIRE_PTR(row_index);
-  if (max_rows == 0) return DBD_OK;
-  dbd::SampleArgs a{};
-  a.logits = logits; a.row_index = row_index; a.num_rows = num_rows;
-  a.V = V; a.mask_id = mask_token_id; a.max_rows = max_rows; a.top_k = top_k;
-  a.inv_temp = 1.f / temperature; a.top_p = top_p;
-  a.key0 = (uint32_t)seed; a.key1 = (uint32_t)(seed >> 32); a.step = step;
-  a.token = token; a.conf = conf;
-  hipError_t e = dbd::sample_filtered_launch(a, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "sampling launch");
-  return DBD_OK;
+  return enqueue_filtered(max_rows, V, mask_token_id, logits, row_index, num_rows, temperature, top_k,
+                          top_p, seed, step, token, conf, static_cast<hipStream_t>(stream));
 }
 
 dbd_status dbd_remask_commit(int S, int B, int mask_token_id, float dynamic_threshold,

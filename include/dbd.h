@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define DBD_ABI_VERSION 3
+#define DBD_ABI_VERSION 4
 
 typedef uint16_t dbd_bf16;
 
@@ -453,10 +453,24 @@ typedef struct dbd_round_args {
   float temperature;
   uint64_t seed;
   uint32_t step;
+  /* Top-k / top-p filtering of the drawn token (SamplingParams topk, topp;
+   * JetEngine README usage examples), with sample != 0 and filter != 0: the
+   * LM head stores the listed rows' logits in `logits` (dbd_lmhead_logits;
+   * float [S*B][V], caller-owned, row r = list entry r) and
+   * dbd_sample_filtered draws each row's token from them with top_k and
+   * top_p (the same seed and step).  Not allowed with the entropy-bounded
+   * rule (no entropy is computed).  filter == 0: none of these is read. */
+  int filter;
+  int top_k;
+  float top_p;
+  float* logits;
 } dbd_round_args;
 
 dbd_status dbd_round(const dbd_round_args* a, void* stream);
 size_t dbd_round_workspace_size(const dbd_round_args* a);
+/* sizeof(dbd_round_args) as this library was built, so that a binding can
+ * check its copy of the struct layout. */
+size_t dbd_round_args_size(void);
 
 /* Graph of n_rounds consecutive rounds (args[i] for round i, e.g. each with
  * its own per-round inputs), captured once and replayed with one launch and

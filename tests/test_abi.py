@@ -3,6 +3,7 @@ symbol include/dbd.h declares, and rejects invalid arguments before any HIP
 call (so these run with no device)."""
 import os
 import re
+import ctypes
 import subprocess
 
 import numpy as np
@@ -46,7 +47,8 @@ def test_library_exports_every_declared_symbol():
     for n in declared_functions():
         assert n in exported, n
         assert hasattr(lib, n)
-    assert api.dbd_abi_version() == 3
+    assert api.dbd_abi_version() == api.ABI_VERSION == 4
+    assert lib.dbd_round_args_size() == ctypes.sizeof(api.dbd_round_args)
 
 
 def _attn(**kw):

@@ -12,14 +12,9 @@ import torch
 import oracle
 from block_diffusion_amd import api, synth
 from block_diffusion_amd.workloads import SDAR_1P7B, TINY
-from gpu_util import dev_bf16, dev_i32, widen_bits
+from gpu_util import check_filtered_rows, dev_bf16, dev_i32, widen_bits
 
 pytestmark = pytest.mark.gpu
-
-G_BAND = 1e-3
-CDF_BAND = 1e-4
-P_BAND = 1e-5
-
 
 def _case(name):
     if name == "tiny":
@@ -66,29 +61,6 @@ def test_lmhead_logits_parity(name):
     assert np.all(np.isnan(lg[M:]))
 
 
-def _check_rows(lg, rows, tok, conf, mask, T, k, p, seed, step):
-    exempt = 0
-    for j, r in enumerate(rows):
-        l = lg[j].astype(np.float64)
-        t_ref, c_ref, inf = oracle.sample_filtered(l, T, k, p, seed, int(r), step)
-        t = int(tok[r])
-        if t != t_ref:
-            fi = inf["filter"]
-            ok = (inf["g_gap"] < G_BAND and t == inf["runner_up"]) or \
-                 (inf["cdf_margin"] < CDF_BAND and t in inf["block"])
-            if not ok and fi["margin"] < P_BAND:
-                alts = [oracle.sample_row(l, T, seed, int(r), step, fi[key])[0]
-                        for key in ("shorter", "longer")]
-                ok = t in alts
-            assert ok, f"row {r}: gpu {t} oracle {t_ref} info g_gap={inf['g_gap']:.3g} " \
-                       f"cdf={inf['cdf_margin']:.3g} pmargin={fi['margin']:.3g}"
-            exempt += 1
-        assert inf["keep"][t] or exempt
-        lse = l.max() + np.log(np.exp(l - l.max()).sum())
-        assert abs(float(conf[r]) - np.exp(l[t] - lse)) <= 1e-5 + 1e-4 * np.exp(l[t] - lse)
-    return exempt
-
-
 @pytest.mark.parametrize("name", ["tiny", "ragged", "sdar1p7b"])
 @pytest.mark.parametrize("T,k,p", [(1.0, 0, 1.0), (0.6, 0, 0.95), (1.0, 50, 1.0), (0.8, 20, 0.9),
                                    (1.0, 1, 1.0), (0.7, 0, 0.0), (1.3, 3, 0.5)])
@@ -103,8 +75,8 @@ def test_sample_filtered_parity(name, T, k, p):
     api.dbd_sample_filtered(lg, dev_i32([M]), tok, conf, mask, T, k, p, seed, step,
                             row_index=dev_i32(rows), max_rows=M)
     torch.cuda.synchronize()
-    ex = _check_rows(lg.cpu().numpy(), rows, tok.cpu().numpy(), conf.cpu().numpy(), mask, T, k, p,
-                     seed, step)
+    ex = check_filtered_rows(lg.cpu().numpy(), rows, tok.cpu().numpy(), conf.cpu().numpy(), mask,
+                             T, k, p, seed, step)
     print(f"{name} T={T} k={k} p={p}: {M} rows, {ex} exempt", flush=True)
     assert ex <= max(1, M // 20)
     if k == 0 and p >= 1.0:
@@ -206,8 +178,8 @@ def test_sample_filtered_boundary_rows(V, T, k, p):
     seed, step = 77 + k, 5
     api.dbd_sample_filtered(lg, dev_i32([M]), tok, conf, mask, T, k, p, seed, step)
     torch.cuda.synchronize()
-    ex = _check_rows(lg_h, np.arange(M), tok.cpu().numpy(), conf.cpu().numpy(), mask, T, k, p, seed,
-                     step)
+    ex = check_filtered_rows(lg_h, np.arange(M), tok.cpu().numpy(), conf.cpu().numpy(), mask,
+                             T, k, p, seed, step)
     print(f"V={V} T={T} k={k} p={p}: {M} rows, {ex} exempt", flush=True)
     assert ex <= 1
 
@@ -227,5 +199,5 @@ def test_sample_filtered_no_candidate():
     torch.cuda.synchronize()
     t, c = tok.cpu().numpy(), conf.cpu().numpy()
     assert t[0] == mask and c[0] == 0.0
-    ex = _check_rows(lg_h[1:], np.array([1]), t, c, mask, 1.0, 10, 0.9, 5, 0)
+    ex = check_filtered_rows(lg_h[1:], np.array([1]), t, c, mask, 1.0, 10, 0.9, 5, 0)
     assert ex <= 1

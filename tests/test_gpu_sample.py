@@ -18,7 +18,8 @@ import torch
 import oracle
 from block_diffusion_amd import api, synth
 from block_diffusion_amd.workloads import SDAR_1P7B, TINY
-from gpu_util import (CONF_ABS, RoundState, dev_bf16, dev_i32, round_inputs_dev, widen_bits)
+from gpu_util import (CONF_ABS, RoundState, check_filtered_rows, dev_bf16, dev_i32, round_inputs_dev,
+                      widen_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -161,3 +162,44 @@ def test_round_sampling_teacher_forced(w):
         if not np.any(state == oracle.DENOISING):
             break
     assert np.all(state == oracle.SAVING)
+
+
+@pytest.mark.parametrize("w", [TINY, SDAR_1P7B], ids=lambda w: w.name)
+@pytest.mark.parametrize("k,p", [(0, 0.95), (20, 0.9)])
+def test_round_filtered_teacher_forced(w, k, p):
+    """Whole blocks of rounds with top-k / top-p filtering inside the round
+    (the LM head stores the listed rows' logits, the filtered draw reads
+    them): every drawn token matches the oracle's filtered draw on the
+    round's own stored logits, and the commits are exactly the threshold
+    rule applied to the GPU's tokens and confidences."""
+    fx = synth.make_fixed(w)
+    st = RoundState(w, fx)
+    st.init_rows()
+    attn_out = torch.empty((w.S, w.B, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    logits = torch.full((w.S * w.B, w.V), float("nan"), dtype=torch.float32, device="cuda")
+    toks, state = fx.block_tokens0.copy(), fx.seq_state0.copy()
+    T, seed = 0.7, 0xF17 + k
+    for r in range(1, w.B + 1):
+        rin = synth.make_round(w, r, fx.w_vocab)
+        a = st.args(round_inputs_dev(rin), attn_out)
+        a.sample, a.temperature, a.seed, a.step = 1, T, seed, r
+        a.filter, a.top_k, a.top_p, a.logits = 1, k, p, logits.data_ptr()
+        rows0 = oracle.compact_rows(toks, state, w.mask_id)
+        api.dbd_round(a)
+        torch.cuda.synchronize()
+        arg, conf = st.bufs.argmax_tok.cpu().numpy(), st.bufs.conf.cpu().numpy()
+        if rows0.size:
+            step_sel = 1 if w is TINY else max(1, rows0.size // 16)
+            sel = np.arange(0, rows0.size, step_sel)
+            lg = logits[torch.from_numpy(sel).cuda()].cpu().numpy()
+            ex = check_filtered_rows(lg, rows0[sel], arg, conf, w.mask_id, T, k, p, seed, r)
+            print(f"round {r}: {sel.size} rows checked, {ex} exempt", flush=True)
+            assert ex <= max(1, sel.size // 20)
+        t1, s1 = st.bufs.block_tokens.cpu().numpy(), st.bufs.seq_state.cpu().numpy()
+        et, es, _ = oracle.remask(toks, state, conf, arg, w.mask_id, np.float32(w.tau))
+        assert np.array_equal(t1, et) and np.array_equal(s1, es), f"round {r}"
+        toks, state = t1, s1
+        if not np.any(state == oracle.DENOISING):
+            break
+    assert np.all(state == oracle.SAVING)
+
