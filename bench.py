@@ -180,6 +180,36 @@ def main():
     log(f"{args.steps} steps in {elapsed * 1e3:.2f} ms: {ms_per_step:.3f} ms/step, "
         f"{value:.0f} block-tokens/s")
 
+    # ---- the same step with sampling as the pages benchmark it (temperature
+    # 0.6, top_p 0.95): each round stores its rows' logits, draws the tokens
+    # with the filter, then remasks; one graph of the four rounds
+    lg_step = torch.empty((n, w.V), dtype=torch.float32, device=dev)
+    targs = round_args()
+    for i, a in enumerate(targs):
+        a.sample, a.temperature, a.seed, a.step = 1, 0.6, 20240, i + 1
+        a.filter, a.top_k, a.top_p, a.logits = 1, 0, 0.95, lg_step.data_ptr()
+    tgraph = api.dbd_graph_create(targs)
+    reset()
+    rows_topp = []
+    for a in targs:
+        rows_topp.append(int(bufs.num_rows.item()))
+        api.dbd_round(a)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        reset()
+        tgraph.launch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        reset()
+        tgraph.launch()
+    torch.cuda.synchronize()
+    ms_topp = (time.perf_counter() - t0) * 1e3 / args.steps
+    tgraph.close()
+    del lg_step, targs
+    log(f"step with temperature 0.6 / top_p 0.95 sampling (rows per round {rows_topp}): "
+        f"{ms_topp:.3f} ms/step, {w.S * w.B * w.rounds / (ms_topp * 1e-3):.0f} block-tokens/s")
+
     # ---- per round (eager rounds, HIP events between them, median over
     # repetitions) and the same step with the 256 MB MALL flushed before it
     # (a 512 MB scratch write, untimed): the cold figure
@@ -414,6 +444,9 @@ def main():
                                                 "lmhead_shape_gemm_us": round(t_lmgemm, 2),
                                                 "lmhead_shape_gemm_TFLOPs": round(lmgemm_tf, 1)},
                          "lmhead_sample_T1_M%d" % rows_per_round[0]: round(t_lm_sample, 2),
+                         "topp_step": {"ms_per_step": round(ms_topp, 4),
+                                       "block_tokens_per_s": round(w.S * w.B * w.rounds / (ms_topp * 1e-3), 1),
+                                       "rows_per_round": rows_topp, "temperature": 0.6, "top_p": 0.95},
                          "topp_M%d" % M1r: {"logits_us": round(t_logits, 2),
                                              "filtered_draw_us": round(t_filter, 2),
                                              "temperature": 0.6, "top_p": 0.95},
