@@ -136,23 +136,31 @@ dbd_status enqueue_lm(int max_rows, int Hd, int V, int mask, const dbd_bf16* hid
 }
 
 // the listed rows' logits (store mode of the LM-head tile kernel)
+// (pmax, pmax2 may be NULL: else each team's partial row maxima go there,
+// two arrays of [max_rows][kLmGrid] floats)
 dbd_status enqueue_logits(int max_rows, int Hd, int V, int mask, const dbd_bf16* hidden,
                           const int32_t* row_index, const int32_t* num_rows, const dbd_bf16* w,
-                          float* logits, hipStream_t st) {
+                          float* logits, hipStream_t st, float* pmax = nullptr,
+                          float* pmax2 = nullptr) {
   if (max_rows == 0) return DBD_OK;
   dbd::LmArgs a{};
   a.hidden = hidden; a.row_index = row_index; a.num_rows = num_rows; a.w = w;
   a.Hd = Hd; a.V = V; a.mask_id = mask; a.max_rows = max_rows;
   a.logits = logits;
+  a.pm = pmax;
+  a.pa = reinterpret_cast<int32_t*>(pmax2);
   hipError_t e = dbd::lmhead_launch(a, st);
   if (e != hipSuccess) return hip_fail(e, "LM-head launch");
   return DBD_OK;
 }
 
+// (pmax, pmax2: the partial row maxima enqueue_logits left for the same
+// rows, or NULL)
 dbd_status enqueue_filtered(int max_rows, int V, int mask, const float* logits,
                             const int32_t* row_index, const int32_t* num_rows, float temperature,
                             int top_k, float top_p, uint64_t seed, uint32_t step, int32_t* token,
-                            float* conf, hipStream_t st) {
+                            float* conf, hipStream_t st, const float* pmax = nullptr,
+                            const float* pmax2 = nullptr) {
   if (max_rows == 0) return DBD_OK;
   dbd::SampleArgs a{};
   a.logits = logits; a.row_index = row_index; a.num_rows = num_rows;
@@ -160,6 +168,8 @@ dbd_status enqueue_filtered(int max_rows, int V, int mask, const float* logits,
   a.inv_temp = 1.f / temperature; a.top_p = top_p;
   a.key0 = (uint32_t)seed; a.key1 = (uint32_t)(seed >> 32); a.step = step;
   a.token = token; a.conf = conf;
+  a.pmax = pmax;
+  a.pmax2 = pmax2;
   hipError_t e = dbd::sample_filtered_launch(a, st);
   if (e != hipSuccess) return hip_fail(e, "sampling launch");
   return DBD_OK;
@@ -257,12 +267,17 @@ dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
   const int max_rows = a->S * a->B;
   float* ent = a->rule == DBD_RULE_ENTROPY_BOUNDED ? a->entropy : nullptr;
   if (a->sample && a->filter) {
+    // the LM head's partial-maximum array of the round workspace carries
+    // each row's maximum to the filtered draw (one pass fewer over the row)
+    const size_t one = dbd::lmhead_ws_bytes(max_rows, a->V) / dbd::kLmPartArrays;
+    float* pmax = reinterpret_cast<float*>(ws + attn_ws);
+    float* pmax2 = reinterpret_cast<float*>(ws + attn_ws + one);
     s = enqueue_logits(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index,
-                       a->num_rows, a->w_vocab, a->logits, st);
+                       a->num_rows, a->w_vocab, a->logits, st, pmax, pmax2);
     if (s != DBD_OK) return s;
     s = enqueue_filtered(max_rows, a->V, a->mask_token_id, a->logits, a->row_index, a->num_rows,
                          a->temperature, a->top_k, a->top_p, a->seed, a->step, a->argmax_tok,
-                         a->conf, st);
+                         a->conf, st, pmax, pmax2);
   } else {
     s = enqueue_lm(max_rows, a->Hd, a->V, a->mask_token_id, a->hidden, a->row_index, a->num_rows,
                    a->w_vocab, a->argmax_tok, a->conf, ent, ws + attn_ws, a->workspace_bytes - attn_ws,

@@ -50,6 +50,9 @@ hipError_t attn_launch(const AttnPlan& plan, const AttnArgs& a,
 // workgroups of the persistent LM-head kernel (one per CU of an MI355X) and
 // the number of (max, id, sum) partials it leaves per row
 constexpr int kLmGrid = 256;
+// LM-head workgroups per team for M rows: 1, 2 or 4 for M <= 256, 512 or
+// more; kLmGrid / lm_team_size(M) teams each own a range of the vocabulary
+__host__ __device__ inline int lm_team_size(int M) { return M <= 256 ? 1 : (M <= 512 ? 2 : 4); }
 
 struct LmArgs {
   const uint16_t* hidden;
@@ -70,7 +73,9 @@ struct LmArgs {
   uint32_t key0, key1, step;
   float* pg;       // [max_rows][kLmGrid] partial largest Gumbel value (log2 units)
   float* pl;       // [max_rows][kLmGrid] partial logit of its candidate
-  float* logits;   // non-NULL: store the logits [max_rows][V] of the listed rows instead
+  float* logits;   // non-NULL: store the logits [max_rows][V] of the listed rows instead,
+                   // and with pm non-NULL each team's partial row maxima in pm (the
+                   // wave pair's first wave) and pa as floats (the second)
 };
 
 // ------------------------------------------------- filtered sampling
@@ -81,6 +86,9 @@ struct SampleArgs {
   int V, mask_id, max_rows, top_k;
   float inv_temp, top_p;
   uint32_t key0, key1, step;
+  const float* pmax;         // may be NULL: the partial row maxima of the LM head's store
+  const float* pmax2;        // mode, two arrays [max_rows][kLmGrid / lm_team_size(*num_rows)];
+                             // then no pass over the row looks for the maximum
   int32_t* token;            // [rows] by row id
   float* conf;
 };

@@ -150,10 +150,17 @@ __device__ __forceinline__ float uniform01(uint32_t w) {
 // ever materialised the base pair with v_readlane (an SGPR spill reload)
 // right before this, the load would use a stale base.  The build scans the
 // linked assembly for that pattern and refuses the library (isa_check.py);
-// five wait states here instead would cost 1-2% of the kernel.
+// five wait states in every instance would cost 1-2% of the kernel.  FIVE
+// selects them for the store-mode instance, whose partial-maximum
+// bookkeeping leaves the compiler short of SGPRs.
+template <bool FIVE>
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, const lds_u16* lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
+  if constexpr (FIVE)
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
+  else
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
 }
 
 template <int N>
@@ -168,8 +175,7 @@ __device__ __forceinline__ void barrier_only() {
   asm volatile("" ::: "memory");
 }
 
-// rows per pass member: G = 1, 2, 4 by row count
-__device__ __forceinline__ int team_size(int M) { return M <= 256 ? 1 : (M <= 512 ? 2 : 4); }
+__device__ __forceinline__ int team_size(int M) { return lm_team_size(M); }
 
 // One pass of one workgroup: rows [m_base, m_end) of the compact row list
 // (R = 64*MB row slots, two waves of 32*MB rows) against vocabulary columns
@@ -230,11 +236,11 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       for (int i = I0; i < I1; ++i) {
         const int row = 8 * (wn * NLD + i) + lr;
         const uint32_t o = row < lim ? off[i] : back + (off[i] & 0x70);
-        dma16(tb, o, slot + (wn * NLD + i) * 512);
+        dma16<STO>(tb, o, slot + (wn * NLD + i) * 512);
       }
     } else {
 #pragma unroll
-      for (int i = I0; i < I1; ++i) dma16(kb, off[i], slot + (wn * NLD + i) * 512);
+      for (int i = I0; i < I1; ++i) dma16<STO>(kb, off[i], slot + (wn * NLD + i) * 512);
     }
   };
   auto advance = [&]() {
@@ -395,14 +401,33 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
 
   // store a finished tile's logits: lane holds row (lane & 31) of each row
   // block mb and vocabulary rows vb0 + 8*(i/4) + (i%4) of each 32-block nb
-  auto store_tile = [&](auto nbw_c, int n0, int wofs) {
+  // store mode with pm given: the row maximum over the wave's columns of
+  // the pass, kept in memory rather than in a register (the tile loop has
+  // none to spare): slot (row, team) of pm for the wave with wn = 0, of pa
+  // (as floats) for wn = 1, read, raised and written back by the one lane
+  // that owns it after every tile (-inf written at the first)
+  auto tile_max = [&](int mb, float tmx, bool first) {
+    tmx = fmaxf(tmx, shfl_xor_f(tmx, 32));
+    const int m = m_base + wm * RH + mb * 32 + lane;
+    if (a.pm != nullptr && lane < 32 && m < m_end) {
+      float* slot = (wn ? reinterpret_cast<float*>(a.pa) : a.pm) + (size_t)m * nteam + team;
+      *slot = first ? tmx : fmaxf(*slot, tmx);
+    }
+  };
+  auto store_tile = [&](auto nbw_c, int n0, int wofs, bool first) {
     constexpr int NBW = decltype(nbw_c)::value;
     const int vbase = n0 + wofs;
-    if (vbase >= v_hi) return;
+    if (vbase >= v_hi) {
+      if (first)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) tile_max(mb, -INFINITY, true);
+      return;
+    }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int m = m_base + wm * RH + mb * 32 + (lane & 31);
       float* lrow = a.logits + (size_t)(m < m_end ? m : m_base) * a.V;
+      float tmx = -INFINITY;   // columns that are not candidates hold -inf
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) {
         __builtin_amdgcn_sched_barrier(0);
@@ -427,7 +452,10 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
             }
           }
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmx = fmaxf(tmx, x[i]);
       }
+      tile_max(mb, tmx, first);
     }
   };
 
@@ -599,7 +627,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
         if (NM2 > NP2) __builtin_amdgcn_sched_group_barrier(0x008, NM2 - NP2, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (STO) store_tile(nbw_c, n0, wofs);
+      if constexpr (STO) store_tile(nbw_c, n0, wofs, tile == 0);
       else reduce_tile(nbw_c, n0, wofs);
     };
     if constexpr (SMP) {
@@ -618,11 +646,11 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   wait_vm<0>();
   wait_lgkm0();
   barrier_only();
-  if constexpr (STO) return;
 
   // fold the two waves that share rows, then one partial per row
   typedef __attribute__((address_space(3))) float lds_f32;
   typedef __attribute__((address_space(3))) int lds_i32;
+  if constexpr (STO) return;
   lds_f32* const s_m = (lds_f32*)Hr;
   lds_i32* const s_a = (lds_i32*)(Hr + 2 * 256);
   lds_f32* const s_s = (lds_f32*)(Hr + 4 * 256);
@@ -673,7 +701,15 @@ template <int MB, int MODE>
 __device__ __forceinline__ void lm_pass_any(const LmArgs& a, int m_base, int m_end, int v_lo, int v_hi,
                                             int team, int nteam, lds_u16* Wr, lds_u16* Hr) {
   if (v_hi <= v_lo) {
-    if (MODE & 4) return;
+    if (MODE & 4) {
+      // store mode: nothing to store; neutral partial maxima if asked
+      if (a.pm != nullptr)
+        for (int m = m_base + (int)threadIdx.x; m < m_end; m += blockDim.x) {
+          a.pm[(size_t)m * nteam + team] = -INFINITY;
+          reinterpret_cast<float*>(a.pa)[(size_t)m * nteam + team] = -INFINITY;
+        }
+      return;
+    }
     // an empty vocabulary range still leaves a neutral partial for its rows
     for (int m = m_base + (int)threadIdx.x; m < m_end; m += blockDim.x) {
       const size_t o = (size_t)m * nteam + team;

@@ -21,7 +21,8 @@
 // One workgroup of 1024 threads per listed row; the ranking is never
 // sorted as a whole.  Passes over the row (16-byte loads, several in flight
 // per thread):
-//   1. the row maximum m;
+//   1. the row maximum m (read from the LM head's partial row maxima when
+//      the caller passes them: the round does);
 //   2. (filters only) a histogram over 4096 value bins below m, bin =
 //      floor((m - l) log2(e) / T * 32) (the last bin takes everything
 //      further down), with per bin the candidate count (top-k) and the sum
@@ -151,11 +152,18 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     }
   };
 
-  // ---- pass 1: the maximum candidate logit
+  // ---- pass 1: the maximum candidate logit, or the maximum of the LM
+  // head's partial row maxima when it left them (the same fp32 values)
   float mt = -INFINITY;
-  each([&](int v, float x) {
-    if (cand(v, x)) mt = fmaxf(mt, x);
-  });
+  if (a.pmax != nullptr) {
+    const int nteam = kLmGrid / lm_team_size(*a.num_rows);
+    for (int t = tid; t < nteam; t += kSfThreads)
+      mt = fmaxf(mt, fmaxf(a.pmax[(size_t)r * nteam + t], a.pmax2[(size_t)r * nteam + t]));
+  } else {
+    each([&](int v, float x) {
+      if (cand(v, x)) mt = fmaxf(mt, x);
+    });
+  }
   const float m = block_reduce(mt, [](float x, float y) { return fmaxf(x, y); }, s_f);
   if (m == -INFINITY) {
     if (tid == 0) {
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   const float c2 = invT * kLog2e;               // exp((l - m)/T) = 2^((l - m) c2)
   const float c3 = c2 * kSfBinsPerLog2;
   auto bin_of = [&](float x) -> int {
-    const float d = (m - x) * c3;               // >= 0, monotone in x
+    const float d = fmaxf((m - x) * c3, 0.f);   // >= 0 (m is the maximum), monotone in x
     return d < (float)(kSfBins - 1) ? (int)d : kSfBins - 1;
   };
   auto mass_of = [&](float x) -> uint64_t {
