@@ -299,8 +299,8 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
             u32x2 v;
-            v.x = (uint32_t)f2bf(acc[rt][dt].x * inv) | ((uint32_t)f2bf(acc[rt][dt].y * inv) << 16);
-            v.y = (uint32_t)f2bf(acc[rt][dt].z * inv) | ((uint32_t)f2bf(acc[rt][dt].w * inv) << 16);
+            v.x = pack_bf16x2(acc[rt][dt].x * inv, acc[rt][dt].y * inv);
+            v.y = pack_bf16x2(acc[rt][dt].z * inv, acc[rt][dt].w * inv);
             *reinterpret_cast<u32x2*>(op + 16 * dt) = v;
           }
         }
@@ -440,10 +440,10 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
         uint32_t pw[4];
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
-          const uint16_t b0 = f2bf(fast_exp2(xs[rt][i] - m_run[rt]));
-          const uint16_t b1 = f2bf(fast_exp2(xs[rt][i + 1] - m_run[rt]));
-          psum += bf2f(b0) + bf2f(b1);
-          pw[i >> 1] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+          const uint32_t w = pack_bf16x2(fast_exp2(xs[rt][i] - m_run[rt]),
+                                         fast_exp2(xs[rt][i + 1] - m_run[rt]));
+          psum += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
+          pw[i >> 1] = w;
         }
         pb[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
         l_run[rt] += psum;
@@ -575,10 +575,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int pos = rr / a.G, gi = rr % a.G;
     uint16_t* op = a.out + ((size_t)(s * a.B + pos) * a.Hq + g * a.G + gi) * D + d0;
     u32x4 packed;
-    packed.x = (uint32_t)f2bf(o[0] * inv) | ((uint32_t)f2bf(o[1] * inv) << 16);
-    packed.y = (uint32_t)f2bf(o[2] * inv) | ((uint32_t)f2bf(o[3] * inv) << 16);
-    packed.z = (uint32_t)f2bf(o[4] * inv) | ((uint32_t)f2bf(o[5] * inv) << 16);
-    packed.w = (uint32_t)f2bf(o[6] * inv) | ((uint32_t)f2bf(o[7] * inv) << 16);
+    packed.x = pack_bf16x2(o[0] * inv, o[1] * inv);
+    packed.y = pack_bf16x2(o[2] * inv, o[3] * inv);
+    packed.z = pack_bf16x2(o[4] * inv, o[5] * inv);
+    packed.w = pack_bf16x2(o[6] * inv, o[7] * inv);
     *reinterpret_cast<u32x4*>(op) = packed;
   }
 }

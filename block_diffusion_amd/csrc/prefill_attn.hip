@@ -300,13 +300,13 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
       for (int i = 0; i < 8; i += 2) {
         const float e0 = fast_exp2(fmaf(xs[rt][i], a.scale_log2, -m_run[rt]));
         const float e1 = fast_exp2(fmaf(xs[rt][i + 1], a.scale_log2, -m_run[rt]));
-        const uint16_t b0 = f2bf(e0), b1 = f2bf(e1);
+        const uint32_t w = pack_bf16x2(e0, e1);
 #if PF_SUM_ROUNDED
-        psum += bf2f(b0) + bf2f(b1);
+        psum += __uint_as_float(w << 16) + __uint_as_float(w & 0xFFFF0000u);
 #else
         psum += e0 + e1;
 #endif
-        pw[i >> 1] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+        pw[i >> 1] = w;
       }
       pb[rt] = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
       l_run[rt] += psum;
@@ -364,8 +364,8 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         u32x2 v;
-        v.x = (uint32_t)f2bf(acc[rt][dt].x * inv) | ((uint32_t)f2bf(acc[rt][dt].y * inv) << 16);
-        v.y = (uint32_t)f2bf(acc[rt][dt].z * inv) | ((uint32_t)f2bf(acc[rt][dt].w * inv) << 16);
+        v.x = pack_bf16x2(acc[rt][dt].x * inv, acc[rt][dt].y * inv);
+        v.y = pack_bf16x2(acc[rt][dt].z * inv, acc[rt][dt].w * inv);
         *reinterpret_cast<u32x2*>(op + 16 * dt) = v;
       }
     }
