@@ -414,8 +414,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
           xs[rt][i] = key < nv0 ? sc[i >> 2][rt][i & 3] * a.scale_log2 : -INFINITY;
           tmax[rt] = fmaxf(tmax[rt], xs[rt][i]);
         }
-        tmax[rt] = fmaxf(tmax[rt], shfl_xor_f(tmax[rt], 16));
-        tmax[rt] = fmaxf(tmax[rt], shfl_xor_f(tmax[rt], 32));
+        tmax[rt] = max_xor32(max_xor16(tmax[rt]));
         grow |= tmax[rt] > m_run[rt] + 8.f;
       }
       // the running maxima (and the rescale) move only when some row's

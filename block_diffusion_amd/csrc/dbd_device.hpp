@@ -56,6 +56,21 @@ __device__ __forceinline__ int shfl_xor_i(int v, int m) {
   return __shfl_xor(v, m, kWave);
 }
 
+// Reductions over the lane pairs (l, l^16) and (l, l^32) with the gfx950
+// permlane swaps (VALU; no LDS round trip as ds_bpermute takes).  Swapping
+// a register with itself, v_permlane16_swap returns, in each lane, the
+// values of its own and its xor-16 partner in its two results (16-lane
+// groups 0,1 / 2,3 exchanged), and v_permlane32_swap those of it and its
+// xor-32 partner; either order, so max and sum are exact.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Compiler-level ordering of LDS traffic among the lanes of one wave.  A
 // wave's LDS instructions execute in issue order, so a write by one lane is
 // seen by a later read of another lane of the same wave once the compiler

@@ -274,8 +274,7 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
         tmax[rt] = fmaxf(tmax[rt], xs[rt][i]);
       }
       tmax[rt] *= a.scale_log2;
-      tmax[rt] = fmaxf(tmax[rt], shfl_xor_f(tmax[rt], 16));
-      tmax[rt] = fmaxf(tmax[rt], shfl_xor_f(tmax[rt], 32));
+      tmax[rt] = max_xor32(max_xor16(tmax[rt]));
       grow |= tmax[rt] > m_run[rt] + 8.f;
     }
     // move the running maxima (and rescale) only when one has grown by more
