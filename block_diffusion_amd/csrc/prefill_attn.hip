@@ -29,6 +29,8 @@
 // Tiles of one prompt are handed out last first (the late, long rows), and
 // the workgroup of a tile also copies that tile's tokens' K/V of head g into
 // the paged cache when one is given (positions 0 .. L-1).
+#include <type_traits>
+
 #include "dbd_device.hpp"
 #include "dbd_internal.hpp"
 
@@ -49,7 +51,7 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #define PF_RT 2
 #endif
 #ifndef PF_OCC
-#define PF_OCC 2
+#define PF_OCC 3
 #endif
 #ifndef PF_SUM_ROUNDED
 #define PF_SUM_ROUNDED 0   // row sums over the fp32 probabilities
@@ -245,7 +247,10 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
   // 16-key halves for S^T, one softmax step, and P V with K = 32 MFMAs whose
   // k slots 8*lg .. 8*lg+7 hold keys 4*lg .. 4*lg+3 of the first half, then
   // of the second (the same order in both operands)
-  auto run32 = [&](const lds_u16* kt32, const lds_u16* vt32, int j0, bool masked) {
+  // (MASKED: some of the 32 keys lie past some row's bound; the other runs,
+  // most of them, skip the per-score test)
+  auto run32 = [&](auto masked_c, const lds_u16* kt32, const lds_u16* vt32, int j0) {
+    constexpr bool masked = decltype(masked_c)::value;
     f32x4 sc[2][RT];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -335,7 +340,11 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st) issue(st);
   }
-  for (int st = 0; st < nstage; ++st) {
+  // stage st: wait for it, then load stage st+NS-1; the stages below the
+  // wave's first masked key (kfree_w) run without the per-score bound test,
+  // in a loop of their own (two instances of the run in one loop body would
+  // cost registers); every wave passes the same number of barriers
+  auto stage = [&](int st, auto masked_c) {
     pf_wait_vm<NLD * (NS - 2)>();
     pf_wait_lgkm0();
     pf_barrier();
@@ -344,9 +353,12 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
 #pragma unroll
     for (int hh = 0; hh < KT / 32; ++hh) {
       const int j0 = st * KT + 32 * hh;
-      if (j0 < kend_w) run32(slot + hh * 32 * D, slot + KVE + hh * 32 * D, j0, j0 + 32 > kfree_w);
+      if (j0 < kend_w) run32(masked_c, slot + hh * 32 * D, slot + KVE + hh * 32 * D, j0);
     }
-  }
+  };
+  const int nfree = min(nstage, kfree_w / KT);
+  for (int st = 0; st < nfree; ++st) stage(st, std::false_type{});
+  for (int st = nfree; st < nstage; ++st) stage(st, std::true_type{});
   pf_wait_vm<0>();   // no load may land in LDS after the workgroup is gone
 
   // out rows: O^T columns; lane holds d = 16*dt + 4*lg .. +3 of row lr
