@@ -252,6 +252,7 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
   auto run32 = [&](auto masked_c, const lds_u16* kt32, const lds_u16* vt32, int j0) {
     constexpr bool masked = decltype(masked_c)::value;
     f32x4 sc[2][RT];
+    __builtin_amdgcn_s_setprio(1);     // the MFMA phases first, the softmax of other waves after
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       bf16x8 kf[KS];
@@ -266,6 +267,7 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
           sc[hh][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[rt][ks], sc[hh][rt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     float xs[RT][8], tmax[RT];
     bool grow = false;
 #pragma unroll
@@ -319,6 +321,7 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
     // 16-lane group lg reads V[4*lg + w/4][16*dt + 4*(w%4) .. +3] by
     // transpose reads and receives V[4*lg .. 4*lg+3][16*dt + w]
     const int vrow = 4 * lg + (lr >> 2), vsub = 4 * (lr & 1), vch = (lr & 3) >> 1;
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -332,6 +335,7 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
       for (int rt = 0; rt < RT; ++rt)
         acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[rt], acc[rt][dt], 0, 0, 0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // ring: stages 0 .. NS-2 up front; at stage st, after the barrier, load
