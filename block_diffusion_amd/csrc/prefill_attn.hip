@@ -8,20 +8,24 @@
 // every earlier block, and its own block in both directions.
 //
 // Unlike the denoise step, this is a dense contraction: every key tile is
-// used by many query rows, so the kernel is MFMA-bound.  Work item = (prompt
-// s, kv head g, tile of 64*PF_RT query rows); a row is (token t, head gi) with
-// row = t*G + gi, so the G query heads of a kv head share every key tile.
-// Four waves of 16*PF_RT rows share a 3-stage LDS ring of
-// 32-key K/V tiles that the waves fill with direct-to-LDS loads
-// (global_load_lds_dwordx4, 16-byte chunks XOR-permuted by row).  Per run of
-// 32 keys a wave computes S^T = K Q^T in two 16-key halves, an online
-// softmax in fp32 (base 2), and O^T += V^T P^T, all with
-// v_mfma_f32_16x16x32_bf16 (the K = 32 form runs at twice the rate of the
-// K = 16 one on gfx950), V^T read by ds_read_b64_tr_b16.  The block-causal mask is a per-row
-// key bound, min(L, (floor(t/B)+1)*B); runs past a wave's largest bound are
-// skipped and runs below its smallest bound need no mask.  Row sums add
-// the fp32 probabilities (the P V product takes them rounded to bf16).  The
-// running
+// used by many query rows, so its roofline is the MFMA peak; at this tiling
+// the softmax's VALU work per score is about as long as the MFMA work, so
+// both matter.  Work item = (prompt s, kv head g, tile of 64*PF_RT query
+// rows); a row is (token t, head gi) with row = t*G + gi, so the G query
+// heads of a kv head share every key tile.  Four waves of 16*PF_RT rows
+// share a PF_NS-stage LDS ring of 32-key K/V tiles that the waves fill with
+// direct-to-LDS loads (global_load_lds_dwordx4, 16-byte chunks XOR-permuted
+// by row); three workgroups fit on a CU.  Per run of 32 keys a wave
+// computes S^T = K Q^T in two 16-key halves, an online softmax in fp32
+// (base 2), and O^T += V^T P^T, all with v_mfma_f32_16x16x32_bf16 (the
+// K = 32 form runs at twice the rate of the K = 16 one on gfx950), V^T read
+// by ds_read_b64_tr_b16.  A wave raises its priority for the two MFMA
+// phases, so that among the waves of a SIMD the one with matrix work issues
+// first.  The block-causal mask is a per-row key bound,
+// min(L, (floor(t/B)+1)*B); runs past a wave's largest bound are skipped,
+// and the runs below its smallest bound (most of them) go through a loop of
+// their own without the per-score test.  Row sums add the fp32
+// probabilities (the P V product takes them rounded to bf16).  The running
 // maximum is only moved when some row's new maximum exceeds it by more than
 // 2^8 (probabilities up to 2^8 are exact in the fp32 sums), which leaves
 // most runs without the rescale of the accumulators.
