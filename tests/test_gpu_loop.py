@@ -215,3 +215,42 @@ def test_block_loop_static_rule():
             assert np.array_equal(np.asarray(got[key]), np.asarray(v)), key
     finally:
         graph.close()
+
+
+@pytest.mark.parametrize("w,nb", [(LOOP_FAST, 2), (TINY, 2)],
+                         ids=lambda x: getattr(x, "name", str(x)))
+def test_block_loop_filtered_graph(w, nb):
+    """Blocks of gated rounds with temperature sampling and top-p filtering
+    inside each round (stored logits, filtered draw), then the SAVING step:
+    every sequence finishes its blocks with valid tokens, gated rounds
+    change nothing (the round counter counts only rounds with rows), and
+    three graph replays, with eager resets between them, equal the eager
+    run bit for bit."""
+    lp = Loop(w, nb)
+    logits = torch.full((w.S * w.B, w.V), float("nan"), dtype=torch.float32, device="cuda")
+    for i, a in enumerate(lp.args):
+        a.sample, a.temperature, a.seed, a.step = 1, 0.8, 0xB10C, i + 1
+        a.filter, a.top_k, a.top_p, a.logits = 1, 0, 0.9, logits.data_ptr()
+    lp.reset()
+    for a in lp.args:
+        api.dbd_round(a)
+    torch.cuda.synchronize()
+    eager = lp.snapshot()
+    assert np.all(eager["state"] == FIN) and np.array_equal(eager["L"], lp.end)
+    ts = eager["ts"]
+    for s in range(w.S):
+        written = ts[s, int(lp.L0[s]):int(lp.end[s])]
+        assert np.all((written >= 0) & (written < w.V) & (written != w.mask_id)), s
+    assert 0 < eager["counter"] <= nb * w.B
+    print(f"{w.name}: {eager['counter']} active rounds of {nb * w.B}", flush=True)
+    graph = api.dbd_graph_create(lp.args)
+    try:
+        for rep in range(3):
+            lp.reset()
+            graph.launch()
+            torch.cuda.synchronize()
+            got = lp.snapshot()
+            for key, v in eager.items():
+                assert np.array_equal(np.asarray(got[key]), np.asarray(v)), f"replay {rep}: {key}"
+    finally:
+        graph.close()
