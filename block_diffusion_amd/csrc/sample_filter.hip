@@ -129,7 +129,7 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   const uint32_t rid = (uint32_t)(a.row_index ? a.row_index[r] : r);
   const float invT = a.inv_temp;
 
-  auto cand = [&](int v, float x) { return v != mask && fabsf(x) <= 3.402823466e38f; };
+  auto cand = [&](int v, float x) { return (v != mask) & (fabsf(x) <= 3.402823466e38f); };
 
   // every logit of the row once; with 16-byte aligned rows (V % 4 == 0)
   // each thread keeps four 16-byte loads in flight
@@ -424,9 +424,13 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
       }
     }
   }
+  // both kept-set tests compare (key, id) in ranking order (higher key,
+  // then lower id); as (key << 32 | ~id) that order is the unsigned one, so
+  // the two tests are one 64-bit comparison with the larger boundary pair
+  const uint64_t thr = max(((uint64_t)kk << 32) | (uint32_t)~(uint32_t)kid,
+                           ((uint64_t)pk << 32) | (uint32_t)~(uint32_t)pid);
   auto keep = [&](int v, float x) {
-    const uint32_t key = okey(x);
-    return cand(v, x) && keep_k(v, key) && (key > pk || (key == pk && v <= pid));
+    return cand(v, x) & ((((uint64_t)okey(x) << 32) | (uint32_t)~(uint32_t)v) >= thr);
   };
 
   // ---- pass 4: the block draw over the kept set (log2 units as the fused
