@@ -115,7 +115,6 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   __shared__ int s_sel;
   __shared__ float s_gbest[kSfWaves];
   __shared__ int s_cbest[kSfWaves];
-  __shared__ float s_lbest[kSfWaves];
   // radix-select scratch on top of s_g: it runs only when a bin did not fit
   uint64_t* const s_h64 = s_g;                                        // [256]
   int* const s_cnt = reinterpret_cast<int*>(s_g + 256);               // [1024]
@@ -435,7 +434,7 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
 
   // ---- pass 4: the block draw over the kept set (log2 units as the fused
   // sampler), and sum exp(l - m) over the candidates for the confidence
-  float gbest = -INFINITY, lbest = 0.f, s1 = 0.f;
+  float gbest = -INFINITY, s1 = 0.f;
   int cbest = 0x7fffffff;
   const int nchunk = (V + 31) / 32;
   for (int c = tid; c < nchunk; c += kSfThreads) {
@@ -479,23 +478,23 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
         e[i] = fast_exp2(fmaf(x[i], invT, -bmT));
         S += e[i];
       }
+      // the running sums never decrease and target > 0, so the members
+      // whose sum is below it are a prefix and the first member past it has
+      // weight; if rounding leaves none past it, the last member with weight
       const float target = u * S;
       float cum = 0.f;
-      int ci = -1, last = 0;
+      int below = 0, last = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         cum += e[i];
+        below += cum < target ? 1 : 0;
         last = e[i] > 0.f ? i : last;
-        ci = (ci < 0 && e[i] > 0.f && cum >= target) ? i : ci;
       }
-      ci = ci < 0 ? last : ci;
-      float xc = x[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) xc = (i == ci) ? x[i] : xc;
+      const int ci = below < 16 ? below : last;
       const float G = bmT + __log2f(S) - __log2f(-__log2f(eg));
       const int cnd = 32 * c + 8 * (ci >> 2) + 4 * h + (ci & 3);
       if (G > gbest || (G == gbest && cnd < cbest)) {
-        gbest = G; cbest = cnd; lbest = xc * (1.0f / kLog2e);
+        gbest = G; cbest = cnd;
       }
     }
   }
@@ -505,22 +504,23 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   for (int off = 32; off >= 1; off >>= 1) {
     const float g2 = __shfl_xor(gbest, off, 64);
     const int c2i = __shfl_xor(cbest, off, 64);
-    const float l2 = __shfl_xor(lbest, off, 64);
-    if (g2 > gbest || (g2 == gbest && c2i < cbest)) { gbest = g2; cbest = c2i; lbest = l2; }
+    if (g2 > gbest || (g2 == gbest && c2i < cbest)) { gbest = g2; cbest = c2i; }
   }
   if (lane == 0) {
     s_gbest[wave] = gbest;
     s_cbest[wave] = cbest;
-    s_lbest[wave] = lbest;
   }
   __syncthreads();
   if (tid == 0) {
     for (int w = 1; w < kSfWaves; ++w)
       if (s_gbest[w] > gbest || (s_gbest[w] == gbest && s_cbest[w] < cbest)) {
-        gbest = s_gbest[w]; cbest = s_cbest[w]; lbest = s_lbest[w];
+        gbest = s_gbest[w]; cbest = s_cbest[w];
       }
+    // the drawn token's own logit (a kept token always exists: the kept
+    // set holds at least the row maximum)
+    const float lb = cbest < V ? l[cbest] : -INFINITY;
     a.token[rid] = cbest;
-    a.conf[rid] = __expf(lbest - m) / S1;
+    a.conf[rid] = __expf(lb - m) / S1;
   }
 }
 
