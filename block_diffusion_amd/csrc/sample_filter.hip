@@ -110,7 +110,7 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   __shared__ uint64_t s_g[kSfCap];       // one bin's candidates, (key << 32) | ~id
   __shared__ uint64_t s_w[kSfWaves];
   __shared__ float s_f[kSfWaves];
-  __shared__ int s_n, s_first;
+  __shared__ int s_n, s_first, s_ndef;
   __shared__ uint64_t s_before;
   __shared__ int s_sel;
   __shared__ float s_gbest[kSfWaves];
@@ -237,20 +237,8 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     return f == INT_MAX ? -1 : f;
   };
 
-  // the candidates of bin b that pred admits, into s_g in ranking order
-  // (descending (key, ~id)); returns their number, > kSfCap if they did not
-  // fit (s_g then holds no list)
-  auto gather_sort = [&](int b, auto pred) -> int {
-    if (tid == 0) s_n = 0;
-    __syncthreads();
-    each([&](int v, float x) {
-      if (!cand(v, x) || bin_of(x) != b || !pred(v, x)) return;
-      const int i = atomicAdd(&s_n, 1);
-      if (i < kSfCap) s_g[i] = ((uint64_t)okey(x) << 32) | (uint32_t)~(uint32_t)v;
-    });
-    __syncthreads();
-    const int n = s_n;
-    if (n > kSfCap) return n;
+  // s_g[0, n) (n <= kSfCap) into ranking order by a bitonic sort
+  auto sort_list = [&](int n) {
     int n2 = 1;
     while (n2 < n) n2 <<= 1;
     for (int i = n + tid; i < n2; i += kSfThreads) s_g[i] = 0ull;   // below every candidate
@@ -270,6 +258,22 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
         __syncthreads();
       }
     }
+  };
+  // the candidates of bin b that pred admits, into s_g in ranking order
+  // (descending (key, ~id)); returns their number, > kSfCap if they did not
+  // fit (s_g then holds no list)
+  auto gather_sort = [&](int b, auto pred) -> int {
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    each([&](int v, float x) {
+      if (!cand(v, x) || bin_of(x) != b || !pred(v, x)) return;
+      const int i = atomicAdd(&s_n, 1);
+      if (i < kSfCap) s_g[i] = ((uint64_t)okey(x) << 32) | (uint32_t)~(uint32_t)v;
+    });
+    __syncthreads();
+    const int n = s_n;
+    if (n > kSfCap) return n;
+    sort_list(n);
     return n;
   };
   auto entry_key = [&](int i) { return (uint32_t)(s_g[i] >> 32); };
@@ -340,6 +344,16 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     __syncthreads();
   };
 
+  // the top-p boundary among the n sorted candidates of its bin: the first
+  // whose running mass reaches rem
+  auto select_sorted = [&](int n, uint64_t rem, uint32_t& key_out, int& id_out) {
+    uint64_t b2, t2;
+    int e = find_first([&](int i) { return mass_of(key_float(entry_key(i))); }, n, rem, b2, t2);
+    e = e < 0 ? max(n - 1, 0) : e;      // n >= 1: the bin has mass
+    key_out = entry_key(e);
+    id_out = entry_id(e);
+  };
+
   // kept-set tests: key above the boundary key, or equal to it with id at
   // most the boundary id; key 0 with id V keeps everything
   uint32_t kk = 0u, pk = 0u;
@@ -347,6 +361,10 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   auto keep_k = [&](int v, uint32_t key) { return v != mask && (key > kk || (key == kk && v <= kid)); };
   const bool use_k = a.top_k > 0 && a.top_k < V - 1;
   const bool use_p = a.top_p < 1.f;
+  // top-p alone: the boundary bin and the mass needed inside it, resolved
+  // during the draw pass (-1: not used)
+  int mbin = -1;
+  uint64_t mrem = 0ull;
 
   if (use_k || use_p) {
     // ---- pass 2: the value-bin histogram
@@ -409,25 +427,30 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
       const int bp = find_first(pval, kSfBins, tgt, before, Z);
       const uint64_t rem = tgt - before;
       int n = kSfCap + 1;
+      if (!use_k) {
+        mbin = bp;
+        mrem = rem;
+      } else {
       if (bp == bk && listed == bk) n = rk;                  // the sorted top-k part
       else if (bp != bk) n = gather_sort(bp, [](int, float) { return true; });
       if (n <= kSfCap) {
-        uint64_t b2, t2;
-        int e = find_first([&](int i) { return mass_of(key_float(entry_key(i))); }, n, rem, b2, t2);
-        e = e < 0 ? n - 1 : e;
-        pk = entry_key(e);
-        pid = entry_id(e);
+        select_sorted(n, rem, pk, pid);
       } else {
         radix([&](int v, float x) { return cand(v, x) && bin_of(x) == bp && keep_k(v, okey(x)); },
               true, rem, pk, pid);
+      }
       }
     }
   }
   // both kept-set tests compare (key, id) in ranking order (higher key,
   // then lower id); as (key << 32 | ~id) that order is the unsigned one, so
   // the two tests are one 64-bit comparison with the larger boundary pair
-  const uint64_t thr = max(((uint64_t)kk << 32) | (uint32_t)~(uint32_t)kid,
-                           ((uint64_t)pk << 32) | (uint32_t)~(uint32_t)pid);
+  uint64_t thr = 0ull;
+  auto set_thr = [&]() {
+    thr = max(((uint64_t)kk << 32) | (uint32_t)~(uint32_t)kid,
+              ((uint64_t)pk << 32) | (uint32_t)~(uint32_t)pid);
+  };
+  set_thr();
   auto keep = [&](int v, float x) {
     return cand(v, x) & ((((uint64_t)okey(x) << 32) | (uint32_t)~(uint32_t)v) >= thr);
   };
@@ -437,65 +460,143 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   float gbest = -INFINITY, s1 = 0.f;
   int cbest = 0x7fffffff;
   const int nchunk = (V + 31) / 32;
-  for (int c = tid; c < nchunk; c += kSfThreads) {
-    float lv[32];
-    if ((V & 3) == 0 && 32 * c + 32 <= V) {
-      const f32x4* p4 = reinterpret_cast<const f32x4*>(l + 32 * c);
+
+  // one 16-token half block of chunk c: x = its members' logits in log2
+  // units, -inf where not kept; wu, we = its two Philox words
+  auto draw_half = [&](const float (&x)[16], uint32_t wu, uint32_t we, int c, int h) {
+    float bm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const f32x4 x4 = p4[i];
-        lv[4 * i] = x4.x; lv[4 * i + 1] = x4.y; lv[4 * i + 2] = x4.z; lv[4 * i + 3] = x4.w;
+    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, x[i]);
+    if (bm == -INFINITY) return;
+    const float u = sf_uniform(wu);
+    const float eg = sf_uniform(we);
+    const float bmT = bm * invT;
+    float e[16], S = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      e[i] = fast_exp2(fmaf(x[i], invT, -bmT));
+      S += e[i];
+    }
+    // the running sums never decrease and target > 0, so the members whose
+    // sum is below it are a prefix and the first member past it has weight;
+    // if rounding leaves none past it, the last member with weight
+    const float target = u * S;
+    float cum = 0.f;
+    int below = 0, last = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      cum += e[i];
+      below += cum < target ? 1 : 0;
+      last = e[i] > 0.f ? i : last;
+    }
+    const int ci = below < 16 ? below : last;
+    const float G = bmT + __log2f(S) - __log2f(-__log2f(eg));
+    const int cnd = 32 * c + 8 * (ci >> 2) + 4 * h + (ci & 3);
+    if (G > gbest || (G == gbest && cnd < cbest)) {
+      gbest = G; cbest = cnd;
+    }
+  };
+
+  // merged (top-p alone): the boundary bin mbin is not resolved yet.  Bins
+  // are monotone in the logit, so members of lower bins are kept and members
+  // of higher bins are not, as the final test will say; members of mbin go
+  // into s_g, and a half block holding one is deferred to s_def until the
+  // boundary inside mbin is known.
+  uint32_t* const s_def = s_bc;                 // the count histogram is dead here
+  auto draw = [&](bool merged) {
+    for (int c = tid; c < nchunk; c += kSfThreads) {
+      float lv[32];
+      if ((V & 3) == 0 && 32 * c + 32 <= V) {
+        const f32x4* p4 = reinterpret_cast<const f32x4*>(l + 32 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x4 x4 = p4[i];
+          lv[4 * i] = x4.x; lv[4 * i + 1] = x4.y; lv[4 * i + 2] = x4.z; lv[4 * i + 3] = x4.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) lv[i] = 32 * c + i < V ? l[32 * c + i] : -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s1 += cand(32 * c + i, lv[i]) ? fast_exp2((lv[i] - m) * kLog2e) : 0.f;
+      uint32_t w0 = (uint32_t)c, w1 = rid, w2 = a.step, w3 = 0u;
+      sf_philox(w0, w1, w2, w3, a.key0, a.key1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // half h: columns 32c + 8q + 4h + r'
+        float x[16];
+        bool pend = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r2 = 0; r2 < 4; ++r2) {
+            const int i = 8 * q + 4 * h + r2, v = 32 * c + i;
+            bool kept;
+            if (merged) {
+              const bool cd = cand(v, lv[i]);
+              const int bn = bin_of(lv[i]);
+              kept = cd & (bn < mbin);
+              if (cd & (bn == mbin)) {
+                pend = true;
+                const int k = atomicAdd(&s_n, 1);
+                if (k < kSfCap) s_g[k] = ((uint64_t)okey(lv[i]) << 32) | (uint32_t)~(uint32_t)v;
+              }
+            } else {
+              kept = keep(v, lv[i]);
+            }
+            x[4 * q + r2] = kept ? lv[i] * kLog2e : -INFINITY;
+          }
+        if (pend) {
+          const int k = atomicAdd(&s_ndef, 1);
+          if (k < kSfBins) s_def[k] = (uint32_t)(2 * c + h);
+          continue;
+        }
+        draw_half(x, h ? w2 : w0, h ? w3 : w1, c, h);
+      }
+    }
+  };
+
+  if (mbin < 0) {
+    draw(false);
+  } else {
+    if (tid == 0) {
+      s_n = 0;
+      s_ndef = 0;
+    }
+    __syncthreads();
+    draw(true);
+    __syncthreads();
+    const int n = s_n, nd = s_ndef;
+    if (n <= kSfCap && nd <= kSfBins) {
+      sort_list(n);
+      select_sorted(n, mrem, pk, pid);
+      set_thr();
+      for (int j = tid; j < nd; j += kSfThreads) {
+        const int c = (int)(s_def[j] >> 1), h = (int)(s_def[j] & 1u);
+        uint32_t w0 = (uint32_t)c, w1 = rid, w2 = a.step, w3 = 0u;
+        sf_philox(w0, w1, w2, w3, a.key0, a.key1);
+        float x[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int r2 = 0; r2 < 4; ++r2) {
+            const int v = 32 * c + 8 * q + 4 * h + r2;
+            const float xv = v < V ? l[v] : -INFINITY;
+            x[4 * q + r2] = keep(v, xv) ? xv * kLog2e : -INFINITY;
+          }
+        draw_half(x, h ? w2 : w0, h ? w3 : w1, c, h);
       }
     } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) lv[i] = 32 * c + i < V ? l[32 * c + i] : -INFINITY;
-    }
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s1 += cand(32 * c + i, lv[i]) ? fast_exp2((lv[i] - m) * kLog2e) : 0.f;
-    uint32_t w0 = (uint32_t)c, w1 = rid, w2 = a.step, w3 = 0u;
-    sf_philox(w0, w1, w2, w3, a.key0, a.key1);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // half h: columns 32c + 8q + 4h + r'
-      float x[16];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r2 = 0; r2 < 4; ++r2) {
-          const int i = 8 * q + 4 * h + r2, v = 32 * c + i;
-          const float xv = keep(v, lv[i]) ? lv[i] * kLog2e : -INFINITY;
-          x[4 * q + r2] = xv;
-          bm = fmaxf(bm, xv);
-        }
-      if (bm == -INFINITY) continue;
-      const float u = sf_uniform(h ? w2 : w0);
-      const float eg = sf_uniform(h ? w3 : w1);
-      const float bmT = bm * invT;
-      float e[16], S = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        e[i] = fast_exp2(fmaf(x[i], invT, -bmT));
-        S += e[i];
-      }
-      // the running sums never decrease and target > 0, so the members
-      // whose sum is below it are a prefix and the first member past it has
-      // weight; if rounding leaves none past it, the last member with weight
-      const float target = u * S;
-      float cum = 0.f;
-      int below = 0, last = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        cum += e[i];
-        below += cum < target ? 1 : 0;
-        last = e[i] > 0.f ? i : last;
-      }
-      const int ci = below < 16 ? below : last;
-      const float G = bmT + __log2f(S) - __log2f(-__log2f(eg));
-      const int cnd = 32 * c + 8 * (ci >> 2) + 4 * h + (ci & 3);
-      if (G > gbest || (G == gbest && cnd < cbest)) {
-        gbest = G; cbest = cnd;
-      }
+      // the boundary bin did not fit in LDS: resolve it as with top-k and
+      // draw the row again
+      const int n2 = gather_sort(mbin, [](int, float) { return true; });
+      if (n2 <= kSfCap) select_sorted(n2, mrem, pk, pid);
+      else radix([&](int v, float x) { return cand(v, x) && bin_of(x) == mbin; }, true, mrem, pk, pid);
+      set_thr();
+      gbest = -INFINITY;
+      cbest = 0x7fffffff;
+      s1 = 0.f;
+      draw(false);
     }
   }
   const float S1 = block_reduce(s1, [](float x, float y) { return x + y; }, s_f);
