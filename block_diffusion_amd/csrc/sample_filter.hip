@@ -361,9 +361,9 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   auto keep_k = [&](int v, uint32_t key) { return v != mask && (key > kk || (key == kk && v <= kid)); };
   const bool use_k = a.top_k > 0 && a.top_k < V - 1;
   const bool use_p = a.top_p < 1.f;
-  // top-p alone: the boundary bin and the mass needed inside it, resolved
-  // during the draw pass (-1: not used)
-  int mbin = -1;
+  // one filter alone: its boundary bin and the mass (top-p) or the rank
+  // (top-k) needed inside it, resolved during the draw pass (-1: not used)
+  int mbin = -1, mrank = 0;
   uint64_t mrem = 0ull;
 
   if (use_k || use_p) {
@@ -390,6 +390,10 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
       if (b >= 0) {                            // else fewer candidates than top_k: keep all
         bk = b;
         rk = a.top_k - (int)before;
+        if (!use_p) {
+          mbin = bk;
+          mrank = rk;
+        } else {
         const int n = gather_sort(bk, [](int, float) { return true; });
         if (n <= kSfCap) {
           kk = entry_key(rk - 1);
@@ -398,6 +402,7 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
         } else {
           radix([&](int v, float x) { return cand(v, x) && bin_of(x) == bk; }, false, (uint64_t)rk, kk,
                 kid);
+        }
         }
       }
     }
@@ -497,7 +502,7 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     }
   };
 
-  // merged (top-p alone): the boundary bin mbin is not resolved yet.  Bins
+  // merged (one filter alone): the boundary bin mbin is not resolved yet.  Bins
   // are monotone in the logit, so members of lower bins are kept and members
   // of higher bins are not, as the final test will say; members of mbin go
   // into s_g, and a half block holding one is deferred to s_def until the
@@ -569,7 +574,13 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     const int n = s_n, nd = s_ndef;
     if (n <= kSfCap && nd <= kSfBins) {
       sort_list(n);
-      select_sorted(n, mrem, pk, pid);
+      if (use_k) {                              // n >= mrank: the bin holds the top_k-th
+        const int e = max(min(mrank, n) - 1, 0);
+        kk = entry_key(e);
+        kid = entry_id(e);
+      } else {
+        select_sorted(n, mrem, pk, pid);
+      }
       set_thr();
       for (int j = tid; j < nd; j += kSfThreads) {
         const int c = (int)(s_def[j] >> 1), h = (int)(s_def[j] & 1u);
@@ -590,8 +601,20 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
       // the boundary bin did not fit in LDS: resolve it as with top-k and
       // draw the row again
       const int n2 = gather_sort(mbin, [](int, float) { return true; });
-      if (n2 <= kSfCap) select_sorted(n2, mrem, pk, pid);
-      else radix([&](int v, float x) { return cand(v, x) && bin_of(x) == mbin; }, true, mrem, pk, pid);
+      if (use_k) {
+        if (n2 <= kSfCap) {
+          const int e = max(min(mrank, n2) - 1, 0);
+          kk = entry_key(e);
+          kid = entry_id(e);
+        } else {
+          radix([&](int v, float x) { return cand(v, x) && bin_of(x) == mbin; }, false, (uint64_t)mrank, kk,
+                kid);
+        }
+      } else if (n2 <= kSfCap) {
+        select_sorted(n2, mrem, pk, pid);
+      } else {
+        radix([&](int v, float x) { return cand(v, x) && bin_of(x) == mbin; }, true, mrem, pk, pid);
+      }
       set_thr();
       gbest = -INFINITY;
       cbest = 0x7fffffff;
