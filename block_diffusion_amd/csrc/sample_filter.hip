@@ -263,6 +263,9 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   // (descending (key, ~id)); returns their number, > kSfCap if they did not
   // fit (s_g then holds no list)
   auto gather_sort = [&](int b, auto pred) -> int {
+    // every thread has read any earlier value of s_n (the merged draw's
+    // count, say) before thread 0 clears it
+    __syncthreads();
     if (tid == 0) s_n = 0;
     __syncthreads();
     each([&](int v, float x) {
