@@ -789,15 +789,23 @@ __global__ __launch_bounds__(256) void lmhead_merge_kernel(LmArgs a) {
   }
   if (lane == 0) {
     const int row = a.row_index ? a.row_index[r] : r;
-    if (smp) {
-      // the drawn token and its probability at temperature 1
-      a.argmax_tok[row] = pk.c;
-      a.conf[row] = __expf(pk.l - x.m) / x.s;
+    if (x.m == -INFINITY) {
+      // no candidate (every logit but the mask's is -inf): no distribution;
+      // the mask token with confidence 0 and entropy +inf
+      a.argmax_tok[row] = a.mask_id;
+      a.conf[row] = 0.f;
+      if (a.entropy) a.entropy[row] = INFINITY;
     } else {
-      a.argmax_tok[row] = x.a;
-      a.conf[row] = 1.f / x.s;
+      if (smp) {
+        // the drawn token and its probability at temperature 1
+        a.argmax_tok[row] = pk.c;
+        a.conf[row] = __expf(pk.l - x.m) / x.s;
+      } else {
+        a.argmax_tok[row] = x.a;
+        a.conf[row] = 1.f / x.s;
+      }
+      if (a.entropy) a.entropy[row] = __logf(x.s) - x.t / x.s;
     }
-    if (a.entropy) a.entropy[row] = __logf(x.s) - x.t / x.s;
   }
 }
 

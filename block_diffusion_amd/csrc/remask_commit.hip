@@ -13,7 +13,11 @@
 //   rule 3, entropy_bounded: masked positions in ascending entropy (lower
 //     position first on ties), the longest leading run whose float32 running
 //     sum stays within the budget, at least one.
-// Confidences, entropies and the threshold are compared in float32.
+// Confidences, entropies and the threshold are compared in float32.  A NaN
+// confidence ranks below every number, a NaN entropy after every number; a
+// position stays masked while it holds the mask token, also when a commit
+// wrote the mask token itself (the LM head's answer for a row with no
+// candidate token).
 //
 // Block commit (kCommitSaving): a sequence that is SAVING on entry has had
 // its SAVING forward (the attention launch wrote its block into the KV
@@ -107,8 +111,11 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
           if (a.flags & kFallbackLeftmost) {
             cball = mball & (~mball + 1ull);  // lowest set bit
           } else {
+            // NaN ranks below every number; with every masked value NaN
+            // the tie is empty and the lowest masked position is taken
             const float best = seg_max(c);
-            const unsigned long long tie = sball(masked && c == best);
+            unsigned long long tie = sball(masked && c == best);
+            if (tie == 0ull) tie = mball;
             cball = tie & (~tie + 1ull);
           }
         }
@@ -152,8 +159,14 @@ __global__ __launch_bounds__(1024) void remask_kernel(RemaskArgs a) {
         }
       }
       const bool commit = (cball >> pos) & 1ull;
-      if (commit) a.block_tokens[s * B + pos] = a.argmax_tok[s * B + pos];
-      still = masked && !commit;
+      int tok = 0;
+      if (commit) {
+        tok = a.argmax_tok[s * B + pos];
+        a.block_tokens[s * B + pos] = tok;
+      }
+      // a commit of the mask token itself (a row with no candidate) leaves
+      // the position masked
+      still = masked && (!commit || tok == a.mask_id);
       const unsigned long long left = sball(still);
       if (pos == 0) {
         if (left == 0ull) a.seq_state[s] = kSaving;

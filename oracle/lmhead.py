@@ -15,6 +15,10 @@ Readings:
   * ties in the argmax go to the lowest token id;
   * confidence max_p = exp(m - lse), m = max logit, lse = log-sum-exp.
 
+A row with no candidate (every logit other than the mask token's is -inf)
+has no distribution; it gives the mask token itself with confidence 0 (and
+p2 = 0), so a commit of it leaves the position masked, and entropy +inf.
+
 Also returns the runner-up probability p2, which the tests use only to
 decide which rows are near-ties.
 
@@ -43,14 +47,19 @@ def lmhead_logits(h_rows, w_vocab_bits, mask_id, vchunk=512):
     return logits
 
 
-def _reduce(logits):
+def _reduce(logits, mask_id):
     m = logits.max(axis=1)
     arg = logits.argmax(axis=1)                  # first maximum = lowest id
-    e = np.exp(logits - m[:, None])
+    none = m == -np.inf                          # rows with no candidate
+    e = np.exp(logits - np.where(none, 0.0, m)[:, None])
     ssum = e.sum(axis=1)
-    p1 = 1.0 / ssum                              # exp(m - lse)
-    part = np.partition(e, -2, axis=1)[:, -2]
-    p2 = part / ssum
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p1 = 1.0 / ssum                          # exp(m - lse)
+        part = np.partition(e, -2, axis=1)[:, -2]
+        p2 = part / ssum
+    arg = np.where(none, mask_id, arg)
+    p1 = np.where(none, 0.0, p1)
+    p2 = np.where(none, 0.0, p2)
     return arg.astype(np.int64), p1, p2
 
 
@@ -65,7 +74,7 @@ def lmhead_rows(h_rows, w_vocab_bits, mask_id, chunk=256):
     p2 = np.empty(M)
     for i in range(0, M, chunk):
         logits = lmhead_logits(h_rows[i:i + chunk], w_vocab_bits, mask_id)
-        a, x1, x2 = _reduce(logits)
+        a, x1, x2 = _reduce(logits, mask_id)
         args[i:i + chunk], p1[i:i + chunk], p2[i:i + chunk] = a, x1, x2
     return args, p1, p2
 
@@ -81,9 +90,12 @@ def lmhead_entropy(h_rows, w_vocab_bits, mask_id, chunk=256):
     for i in range(0, M, chunk):
         logits = lmhead_logits(h_rows[i:i + chunk], w_vocab_bits, mask_id)
         m = logits.max(axis=1, keepdims=True)
-        z = logits - m                            # -inf at the mask column
+        none = m[:, 0] == -np.inf                 # rows with no candidate
+        z = logits - np.where(none[:, None], 0.0, m)    # -inf at the mask column
         e = np.exp(z)
         ssum = e.sum(axis=1)
         zfin = np.where(np.isfinite(z), z, 0.0)   # the mask column has p = 0
-        H[i:i + chunk] = np.log(ssum) - (e * zfin).sum(axis=1) / ssum
+        with np.errstate(divide="ignore", invalid="ignore"):
+            H[i:i + chunk] = np.log(ssum) - (e * zfin).sum(axis=1) / ssum
+        H[i:i + chunk][none] = np.inf
     return H

@@ -17,7 +17,16 @@ A DENOISING sequence with M empty on entry goes to SAVING with no commit;
 other states are untouched.
 
 conf is compared as given (the caller decides its precision; the GPU path
-passes float32 confidences and a float32 threshold).
+passes float32 confidences and a float32 threshold).  A NaN confidence is
+never >= tau and ranks below every number (-inf included) in the fallback
+and in the static rule; when every masked confidence is NaN the fallback
+takes the lowest masked position.  Likewise a NaN entropy ranks after every
+number (+inf included) and counts as +inf in the entropy budget.  The pages
+never produce NaN; this only fixes what the rule does with one.
+
+A position is masked while it holds mask_id, also after a commit that wrote
+mask_id itself (a row with no candidate token; lmhead_rows gives it the mask
+id with confidence 0): such a sequence stays DENOISING.
 
 remask_rule adds the other strategies the developer notes list under
 "Remasking Strategies" (sequential: unmask left to right;
@@ -59,17 +68,33 @@ def remask(block_tokens, seq_state, conf, argmax_tok, mask_id, tau, flags=0):
                 if flags & FALLBACK_LEFTMOST:
                     chosen = [masked[0]]
                 else:
-                    best = masked[0]
-                    for i in masked[1:]:
-                        if conf[s, i] > conf[s, best]:
-                            best = i
-                    chosen = [best]
+                    chosen = [_most_confident(masked, conf[s])]
             for i in chosen:
                 toks[s, i] = argm[s, i]
                 committed[s, i] = True
         if not np.any(toks[s] == mask_id):
             state[s] = SAVING
     return toks, state, committed
+
+
+def _most_confident(positions, conf_row):
+    """The position of the largest confidence, the lowest position among
+    equal ones; NaN ranks below every number, and when every confidence is
+    NaN the lowest position is taken."""
+    best = None
+    for i in positions:
+        if np.isnan(conf_row[i]):
+            continue
+        if best is None or conf_row[i] > conf_row[best]:
+            best = i
+    return positions[0] if best is None else best
+
+
+def _entropy_order(positions, ent_row):
+    """Positions by ascending entropy, the lower position first among equal
+    ones; NaN entropies after every number (+inf included), by position."""
+    nums = sorted((i for i in positions if not np.isnan(ent_row[i])), key=lambda i: (ent_row[i], i))
+    return nums + [i for i in positions if np.isnan(ent_row[i])]
 
 
 def compact_rows(block_tokens, seq_state, mask_id):
@@ -111,18 +136,17 @@ def remask_rule(block_tokens, seq_state, conf, argmax_tok, mask_id, rule,
                 # repeatedly take the most confident remaining position
                 rest = list(masked)
                 for _ in range(k):
-                    best = rest[0]
-                    for i in rest[1:]:
-                        if conf[s, i] > conf[s, best]:
-                            best = i
+                    best = _most_confident(rest, conf[s])
                     chosen.append(best)
                     rest.remove(best)
             elif rule == RULE_ENTROPY:
-                order = sorted(masked, key=lambda i: (ent[s, i], i))
+                order = _entropy_order(masked, ent[s])
                 cum = ent.dtype.type(0)
                 budget = ent.dtype.type(eb)
                 for i in order:
-                    nxt = ent.dtype.type(cum + ent[s, i])
+                    e_i = ent.dtype.type(np.inf) if np.isnan(ent[s, i]) else ent[s, i]
+                    with np.errstate(invalid="ignore"):        # inf + -inf stays NaN
+                        nxt = ent.dtype.type(cum + e_i)
                     if chosen and nxt > budget:
                         break
                     chosen.append(i)

@@ -18,14 +18,17 @@ plus token selection).  The pages give no formula.  Readings taken:
     where the row id is s*B + position and step is the caller's round
     number; a 32-bit word w gives the uniform ((w >> 9) + 0.5) / 2^23 in
     (0, 1), exact in float32;
-  * the draw is exact and hierarchical.  The vocabulary is cut into blocks:
-    chunk c = tokens 32c .. 32c+31, and its half h in {0, 1} holds the 16
-    tokens 32c + 8q + 4h + r (q, r in 0..3), in increasing id, without the
-    mask token and ids >= V.  Philox(c, row, step, 0) gives four words; half
-    h uses word 2h for u and word 2h+1 for e.  Per block, with z = l / T:
-      m_b = max z,  S_b = sum exp(z - m_b),
+  * the draw is exact and hierarchical (a reading: the pages name no
+    sampler).  Every token v belongs to one *block* (c, h) with
+    c = v div 32 and h = (v div 4) mod 2: each aligned run of 32 ids is cut
+    into the two interleaved sets of ids whose bit 2 is 0 or 1, 16 ids each
+    (fewer at the end of the vocabulary).  Philox(c, row, step, 0) gives
+    four words per c; block (c, h) uses word 2h for u and word 2h+1 for e.
+    Per block, with z = l / T and the mask token at weight 0:
+      m_b = max z,  S_b = sum exp(z - m_b)   (members in increasing id),
       candidate = the first member whose running sum of exp(z - m_b)
-                  reaches u * S_b (inverse CDF inside the block),
+                  reaches u * S_b (inverse CDF inside the block; if
+                  rounding leaves none, the last member with weight),
       G_b = m_b + ln S_b - ln(-ln e)   (a Gumbel draw located at the
                                         block's log-sum-exp);
     the token is the candidate of the block with the largest G_b (lower
@@ -33,7 +36,12 @@ plus token selection).  The pages give no formula.  Readings taken:
     located at log-sum-exps falls on block b with probability proportional
     to its sum of exp(z), independently of its value, so the token has
     probability exp(z_v) / sum exp(z) -- the Gumbel-max trick applied to
-    blocks instead of single tokens (16 times fewer random numbers).
+    blocks instead of single tokens (16 times fewer random numbers).  Any
+    partition of the vocabulary into blocks gives that distribution; this
+    one fixes which random words decide which token, so that a draw does
+    not depend on how the vocabulary is split among workers.
+  * a row with no candidate (every weight 0) draws the mask token with
+    confidence 0.
 
 Top-k / top-p filtering (README usage examples: topk, topp; developer
 notes, "Benchmarking": top_p 0.95; "Ruled-Out Optimizations": a separate
@@ -49,6 +57,8 @@ sampler after the logits was faster than a fused one).  Readings:
     given zero weight; the confidence is unchanged (the model's
     probability of the drawn token at temperature 1).
 """
+import math
+
 import numpy as np
 
 from .lmhead import lmhead_logits
@@ -82,59 +92,109 @@ def uniform01(words):
     return ((w >> np.uint64(9)).astype(np.float64) + 0.5) / float(1 << 23)
 
 
-def sample_row(logits, temperature, seed, row_id, step, keep=None):
+def block_of(v):
+    """The sampling block (c, h) of token id v (ints or integer arrays)."""
+    return v // 32, (v // 4) % 2
+
+
+def block_members(c, h, V):
+    """Token ids of block (c, h) in increasing order, ids >= V left out."""
+    return [v for v in range(32 * c, min(32 * c + 32, V)) if block_of(v) == (c, h)]
+
+
+def block_words(seed, row_id, step, nchunks):
+    """Philox words [nchunks][4] of counter (c, row id, step, 0), key = seed."""
+    w = philox4x32_10(np.arange(nchunks), np.full(nchunks, row_id), np.full(nchunks, step),
+                      np.zeros(nchunks), np.full(nchunks, seed & 0xFFFFFFFF),
+                      np.full(nchunks, (seed >> 32) & 0xFFFFFFFF))
+    return np.stack(w, axis=1)
+
+
+def _inverse_cdf(wt, members, u):
+    """The draw inside one block: wt [V] are the weights exp(z - m_b) (0 for
+    no weight); the first member, in id order, whose running sum reaches
+    u * S_b, or the last member with weight if rounding leaves none.
+    Returns (candidate, margin of u * S_b from the candidate's interval,
+    relative to S_b)."""
+    S_b = 0.0
+    for v in members:
+        S_b += wt[v]
+    target = u * S_b
+    cum, cand, last, lo_c, hi_c = 0.0, None, None, 0.0, 0.0
+    for v in members:
+        before = cum
+        cum += wt[v]
+        if wt[v] > 0.0:
+            last = v
+            if cand is None and cum >= target:
+                cand, lo_c, hi_c = v, before, cum
+    if cand is None:
+        cand, lo_c, hi_c = last, target, target
+    return cand, min(abs(target - lo_c), abs(hi_c - target)) / S_b
+
+
+def sample_row(logits, temperature, seed, row_id, step, keep=None, words=None, mask_id=-1):
     """One row: logits [V] float64 (mask token at -inf).  Returns
     (token, conf, info) where info holds what the tests need to recognise
     draws that float32 rounding could decide otherwise: the gap between the
-    two largest G_b, the runner-up block's candidate, and the winning
-    block's distance from its inverse-CDF boundaries (relative to S_b) with
-    the neighbouring candidates.  keep (bool [V], optional): only these
-    tokens can be drawn."""
+    two largest G_b, the runner-up block's candidate, the winning block's
+    distance from its inverse-CDF boundaries (relative to S_b), and that
+    block's members of nonzero weight.  keep (bool [V], optional): only
+    these tokens can be drawn.  words ([chunks][4] uint32, optional): the
+    random words to use instead of Philox's (hand-worked cases).  A row
+    with no candidate gives (mask_id, 0)."""
     V = logits.shape[0]
-    nc = -(-V // 32)
-    z = np.full(nc * 32, -np.inf)
-    z[:V] = logits / temperature
+    z = np.asarray(logits, dtype=np.float64) / temperature
     if keep is not None:
-        z[:V][~np.asarray(keep, dtype=bool)] = -np.inf
-    ids = np.arange(nc * 32)
-    # [chunk][q][h][r] -> [chunk][h][16 members in (q, r) order]
-    zb = z.reshape(nc, 4, 2, 4).transpose(0, 2, 1, 3).reshape(nc, 2, 16)
-    ib = ids.reshape(nc, 4, 2, 4).transpose(0, 2, 1, 3).reshape(nc, 2, 16)
-    m = zb.max(axis=2)                                   # [nc][2]
-    live = np.isfinite(m)
-    e = np.where(live[:, :, None], np.exp(zb - np.where(live, m, 0.0)[:, :, None]), 0.0)
-    S = e.sum(axis=2)
-    w = philox4x32_10(np.arange(nc), np.full(nc, row_id), np.full(nc, step), np.zeros(nc),
-                      np.full(nc, seed & 0xFFFFFFFF), np.full(nc, (seed >> 32) & 0xFFFFFFFF))
-    u = np.stack([uniform01(w[0]), uniform01(w[2])], axis=1)      # [nc][2]
-    eu = np.stack([uniform01(w[1]), uniform01(w[3])], axis=1)
-    G = np.where(live, m + np.log(np.where(live, S, 1.0)) - np.log(-np.log(eu)), -np.inf)
-    cum = np.cumsum(e, axis=2)
-    target = u * S
-    reach = cum >= target[:, :, None]
-    reach[:, :, 15] |= live                              # rounding guard: the last member
-    first = reach.argmax(axis=2)
-    # the first member reached may have zero weight only through the guard;
-    # step back to the last member with weight
-    cand = np.take_along_axis(ib, first[:, :, None], axis=2)[:, :, 0]
-    for c, h in zip(*np.nonzero(live & (np.take_along_axis(e, first[:, :, None], 2)[:, :, 0] == 0))):
-        j = int(np.nonzero(e[c, h] > 0)[0][-1])
-        cand[c, h] = ib[c, h, j]
-    Gf = G.ravel()
-    cf = cand.ravel()
-    order = np.lexsort((cf, -Gf))                        # largest G, then lower candidate
-    win = order[0]
-    tok = int(cf[win])
-    lse = np.max(logits) + np.log(np.sum(np.exp(logits - np.max(logits))))
-    conf = float(np.exp(logits[tok] - lse))
-    c, h = divmod(int(win), 2)
-    j = int(first[c, h])
-    lo = cum[c, h, j - 1] if j > 0 else 0.0
-    margin = min(abs(target[c, h] - lo), abs(cum[c, h, j] - target[c, h])) / S[c, h]
-    neighbours = set(int(x) for x in ib[c, h][e[c, h] > 0])
-    info = dict(g_gap=float(Gf[win] - Gf[order[1]]) if np.isfinite(Gf[order[1]]) else np.inf,
-                runner_up=int(cf[order[1]]), cdf_margin=float(margin), block=neighbours)
-    return tok, conf, info
+        z = np.where(np.asarray(keep, dtype=bool), z, -np.inf)
+    nc = -(-V // 32)
+    if words is None:
+        words = block_words(seed, row_id, step, nc)
+    words = np.asarray(words, dtype=np.uint64)
+    # block of every token, as one index 2c + h
+    c_of, h_of = block_of(np.arange(V))
+    b_of = 2 * c_of + h_of
+    # block maxima, then block sums of exp(z - m_b) accumulated in id order
+    # (np.add.at applies its additions in index order, unbuffered)
+    m = np.full(2 * nc, -np.inf)
+    np.maximum.at(m, b_of, z)
+    with np.errstate(invalid="ignore"):
+        wt = np.where(z > -np.inf, np.exp(z - m[b_of]), 0.0)
+    S = np.zeros(2 * nc)
+    np.add.at(S, b_of, wt)
+    live = m > -np.inf
+    info = dict(g_gap=np.inf, runner_up=-1, cdf_margin=np.inf, block=set())
+    if not live.any():
+        return int(mask_id), 0.0, info
+    # block (c, h): u from word 2h, e from word 2h + 1 of chunk c
+    blocks = np.arange(2 * nc)
+    u = uniform01(words[blocks // 2, 2 * (blocks % 2)])
+    e = uniform01(words[blocks // 2, 2 * (blocks % 2) + 1])
+    with np.errstate(divide="ignore"):
+        G = np.where(live, m + np.log(np.where(live, S, 1.0)) - np.log(-np.log(e)), -np.inf)
+    cands = {}
+
+    def cand_of(b):
+        if b not in cands:
+            cands[b] = _inverse_cdf(wt, block_members(b // 2, b % 2, V), float(u[b]))
+        return cands[b][0]
+    # largest G_b first, the lower candidate first among equal G_b
+    g1 = G.max()
+    win = min(np.nonzero(G == g1)[0].tolist(), key=cand_of)
+    tok = cand_of(win)
+    rest = np.nonzero(live & (blocks != win))[0]
+    if rest.size:
+        g2 = G[rest].max()
+        ru = min(rest[G[rest] == g2].tolist(), key=cand_of)
+        info["g_gap"] = float(g1 - g2)
+        info["runner_up"] = int(cand_of(ru))
+    info["cdf_margin"] = float(cands[win][1])
+    info["block"] = set(v for v in block_members(win // 2, win % 2, V) if wt[v] > 0.0)
+    fin = logits[np.isfinite(logits)]
+    lmax = fin.max()
+    lse = lmax + math.log(float(np.sum(np.exp(fin - lmax))))
+    conf = float(math.exp(logits[tok] - lse))
+    return int(tok), conf, info
 
 
 def lmhead_sample(h_rows, w_vocab_bits, mask_id, row_ids, temperature, seed, step, chunk=64):
@@ -147,7 +207,8 @@ def lmhead_sample(h_rows, w_vocab_bits, mask_id, row_ids, temperature, seed, ste
     for i0 in range(0, M, chunk):
         L = lmhead_logits(h_rows[i0:i0 + chunk], w_vocab_bits, mask_id)
         for j in range(L.shape[0]):
-            t, c, inf = sample_row(L[j], temperature, seed, int(row_ids[i0 + j]), step)
+            t, c, inf = sample_row(L[j], temperature, seed, int(row_ids[i0 + j]), step,
+                                   mask_id=mask_id)
             toks[i0 + j], conf[i0 + j] = t, c
             infos.append(inf)
     return toks, conf, infos
@@ -164,7 +225,7 @@ def topk_topp_keep(logits, temperature, top_k, top_p):
     k = n if (top_k <= 0 or top_k >= n) else int(top_k)
     kept = order[:k]
     info = dict(margin=np.inf, shorter=None, longer=None)
-    if top_p < 1.0:
+    if top_p < 1.0 and n > 0:
         m = logits[order[0]]
         w = np.exp((logits[kept] - m) / temperature)
         cum = np.cumsum(w)
@@ -181,11 +242,12 @@ def topk_topp_keep(logits, temperature, top_k, top_p):
     return keep, info
 
 
-def sample_filtered(logits, temperature, top_k, top_p, seed, row_id, step):
+def sample_filtered(logits, temperature, top_k, top_p, seed, row_id, step, mask_id=-1):
     """One row drawn after top-k / top-p filtering.  Returns (token, conf,
-    info) like sample_row, info also holding the filter's boundary info."""
+    info) like sample_row, info also holding the filter's boundary info.  A
+    row with no candidate gives (mask_id, 0)."""
     keep, finfo = topk_topp_keep(logits, temperature, top_k, top_p)
-    tok, conf, info = sample_row(logits, temperature, seed, row_id, step, keep)
+    tok, conf, info = sample_row(logits, temperature, seed, row_id, step, keep, mask_id=mask_id)
     info["filter"] = finfo
     info["keep"] = keep
     return tok, conf, info

@@ -385,7 +385,24 @@ def check_lm_entropy_scipy(impl):
     assert np.max(np.abs(impl.lmhead_entropy(h, w, mask) - entropy(p, axis=1))) < 1e-12
 
 
-LM_CHECKS = [check_lm_entropy_bruteforce, check_lm_entropy_closed_forms, check_lm_entropy_scipy,
+def check_lm_no_candidate(impl):
+    """A row with no candidate (every logit but the mask's is -inf: W all
+    -inf against a positive hidden row) gives the mask token, confidence 0
+    and runner-up 0, and entropy +inf; other rows are unaffected."""
+    V, Hd, mask = 10, 4, 3
+    h = bf(np.ones((2, Hd)))
+    w = bf(np.full((V, Hd), -np.inf))
+    a, p1, p2 = impl.lmhead_rows(h, w, mask)
+    assert np.all(a == mask) and np.all(p1 == 0.0) and np.all(p2 == 0.0), (a, p1, p2)
+    assert np.all(impl.lmhead_entropy(h, w, mask) == np.inf)
+    g = np.random.default_rng(12)
+    w2 = bf(g.standard_normal((V, Hd)))
+    a2, q1, _ = impl.lmhead_rows(h, w2, mask)
+    ref = lm_bruteforce(h, w2, mask)
+    assert a2[0] == ref[0][0] and abs(q1[0] - ref[0][1]) < 1e-13
+
+
+LM_CHECKS = [check_lm_no_candidate, check_lm_entropy_bruteforce, check_lm_entropy_closed_forms, check_lm_entropy_scipy,
              check_lm_golden, check_lm_bruteforce, check_lm_zero_hidden, check_lm_one_hot,
              check_lm_vocab_permutation, check_lm_mask_never_chosen,
              check_lm_ties_lowest, check_lm_scipy]
@@ -664,7 +681,35 @@ def check_rule_invariants(impl):
                 toks, state = nt, ns
 
 
-RULE_CHECKS = [check_rule_bruteforce, check_rule_special_cases, check_rule_invariants]
+def check_rule_nan_cases(impl):
+    """Hand-worked cases of the NaN readings: a NaN confidence ranks below
+    every number (the static rule takes numbers first, then NaN positions
+    from the left); a NaN entropy ranks after every number, +inf included,
+    and counts as +inf in the budget."""
+    mask, nan, inf = 9, np.nan, np.inf
+    toks = np.full((1, 4), mask, dtype=np.int64)
+    st = np.array([DEN], dtype=np.uint8)
+    argm = np.array([10, 11, 12, 13])
+    cases = [  # (rule, k, eb, conf, entropy, committed positions)
+        (1, 2, 0.0, [nan, 0.2, nan, 0.1], None, [1, 3]),
+        (1, 2, 0.0, [nan, nan, 0.3, nan], None, [0, 2]),
+        (1, 1, 0.0, [nan, -inf, nan, nan], None, [1]),
+        (3, 1, 10.0, None, [nan, 0.5, inf, 0.25], [1, 3]),
+        (3, 1, 10.0, None, [nan, nan, nan, nan], [0]),
+        (3, 1, inf, None, [nan, 1.0, nan, 2.0], [0, 1, 2, 3]),
+        (3, 1, 10.0, None, [nan, inf, nan, 2.0], [3]),
+    ]
+    for rule, k, eb, conf, ent, exp in cases:
+        c = np.zeros(4) if conf is None else np.array(conf)
+        e = None if ent is None else np.array(ent, dtype=np.float32)
+        nt, ns, com = impl.remask_rule(toks, st, c, argm, mask, rule, tokens_per_step=k, eb=eb,
+                                       entropy=e)
+        assert np.nonzero(com[0])[0].tolist() == exp, (rule, conf, ent, com[0])
+        assert all(nt[0, i] == argm[i] for i in exp)
+
+
+RULE_CHECKS = [check_rule_bruteforce, check_rule_special_cases, check_rule_invariants,
+               check_rule_nan_cases]
 
 
 # ------------------------------------------------- SAVING step, block commit
@@ -1015,9 +1060,118 @@ def check_filter_special_cases(impl):
         assert impl.sample_filtered(l, 0.9, 1, 1.0, 5, 1, step)[0] == top
 
 
-SAMPLE_CHECKS = [check_philox_known_answers, check_uniform01, check_sampler_distribution,
+def check_sampler_hand_cases(impl):
+    """Hand-worked draws with given random words (tests/golden/
+    sampling_hand_cases.json): which block wins, the inverse CDF inside it,
+    the temperature, each chunk's own words, the tie rule, no candidate."""
+    with open(os.path.join(GOLDEN, "sampling_hand_cases.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        l = np.full(c["V"], -np.inf)
+        for v, x in c["logits"]:
+            l[v] = x
+        words = np.array(c["words"], dtype=np.uint64)
+        t, conf, _ = impl.sample_row(l, c["T"], 0, 0, 0, words=words, mask_id=c["mask_id"])
+        assert t == c["expect_token"], (c["name"], t)
+        assert abs(conf - c["expect_conf"]) < 1e-12, (c["name"], conf)
+
+
+def check_sampler_counter_layout(impl):
+    """The random words of chunk c are Philox4x32-10 (pinned by its known
+    answers) at counter (c, row id, step, 0) with key (seed low word, seed
+    high word): a draw equals the draw with those words given."""
+    g = np.random.default_rng(34)
+    V = 200
+    nc = -(-V // 32)
+    for seed, row, step in ((0x1234_5678_9ABC, 7, 3), (5, 1000, 0), ((1 << 40) + 17, 3, 99)):
+        l = g.normal(0, 2, V)
+        l[11] = -np.inf
+        w = impl.philox4x32_10(np.arange(nc), np.full(nc, row), np.full(nc, step), np.zeros(nc),
+                               np.full(nc, seed & 0xFFFFFFFF), np.full(nc, seed >> 32))
+        words = np.stack([np.asarray(x, dtype=np.uint64) for x in w], axis=1)
+        for T in (0.5, 1.0, 3.0):
+            a = impl.sample_row(l, T, seed, row, step)
+            b = impl.sample_row(l, T, 0, 0, 0, words=words)
+            assert a[0] == b[0] and a[1] == b[1], (seed, row, step, T)
+
+
+def check_lmhead_sample_rows(impl):
+    """lmhead_sample is the block draw of each row's brute-force logits
+    (mask column excluded) with that row's own id: tokens and confidences
+    equal sample_row on scalar-loop logits, for rows listed out of order."""
+    g = np.random.default_rng(33)
+    V, Hd, mask = 70, 8, 12
+    h = bf(g.standard_normal((12, Hd)) * 1.5)
+    w = bf(g.standard_normal((V, Hd)))
+    row_ids = np.array([13, 2, 40, 7, 21, 5, 0, 33, 9, 18, 27, 44])
+    H, W = wid(h), wid(w)
+    for T, seed, step in ((0.8, 0xABCDEF12345, 4), (1.5, 3, 0), (0.4, 77, 9)):
+        toks, conf, _ = impl.lmhead_sample(h, w, mask, row_ids, T, seed, step)
+        for j in range(h.shape[0]):
+            l = np.array([math.fsum(float(a) * float(b) for a, b in zip(H[j], W[v])) for v in range(V)])
+            l[mask] = -np.inf
+            t, c, _ = impl.sample_row(l, T, seed, int(row_ids[j]), step)
+            assert toks[j] == t and abs(conf[j] - c) < 1e-12, (T, j, toks[j], t)
+            assert toks[j] != mask
+
+
+SAMPLE_CHECKS = [check_sampler_hand_cases, check_sampler_counter_layout, check_lmhead_sample_rows,
+                 check_philox_known_answers, check_uniform01, check_sampler_distribution,
                  check_sampler_block_choice, check_sampler_greedy_limit, check_sampler_seeds,
                  check_filter_bruteforce, check_filtered_distribution, check_filter_special_cases]
+
+
+# ------------------------------------------------------------ whole round
+
+def check_round_composition(impl):
+    """denoise_round is the composition of the separately pinned parts:
+    attention of every sequence by scalar loops, the LM head by scalar loops
+    on exactly the masked rows of DENOISING sequences (sequence-major,
+    position-minor), results scattered to those rows, the commit rule by
+    subset enumeration on those confidences, and the next row list from the
+    new state.  Sequences in every state and partly committed blocks make a
+    misaligned gather or scatter visible; three thresholds exercise both
+    branches of the rule."""
+    from types import SimpleNamespace
+    c = tiny_attn_case(seed=5, S=3, B=4, Hq=4, Hkv=2, D=8, P=4, L=(6, 0, 9))
+    V, Hd, mask = 40, 8, 39
+    g = np.random.default_rng(51)
+    w = bf(g.standard_normal((V, Hd)))
+    hid = bf(g.standard_normal((12, Hd)) * 3)
+    toks0 = np.array([[39, 7, 39, 39], [39, 39, 39, 39], [39, 1, 2, 39]], dtype=np.int64)
+    state0 = np.array([DEN, SAV, DEN], dtype=np.uint8)
+    fixed = SimpleNamespace(block_tokens0=toks0, seq_state0=state0, prefix_len=c["prefix_len"],
+                            page_table=c["page_table"], k_cache=c["k_cache"], v_cache=c["v_cache"],
+                            w_vocab=w)
+    inp = SimpleNamespace(q=c["q"], k_blk=c["k_blk"], v_blk=c["v_blk"], hidden=hid)
+    attn_ref = attn_bruteforce(c)
+    rows = [0, 2, 3, 8, 11]
+    lm = lm_bruteforce(hid[rows], w, mask)
+    conf = np.full(12, np.nan)
+    argm = np.full(12, -1, dtype=np.int64)
+    for r, (a, p1, _) in zip(rows, lm):
+        conf[r], argm[r] = p1, a
+    for tau in (0.0, 0.35, 2.0):
+        res = impl.denoise_round(inp, fixed, mask, tau)
+        assert np.max(np.abs(res["attn"] - attn_ref)) < 1e-12
+        assert res["rows"].tolist() == rows
+        for r, (a, p1, p2) in zip(rows, lm):
+            assert res["argmax"][r] == a and abs(res["p1"][r] - p1) < 1e-13 and abs(res["p2"][r] - p2) < 1e-13
+        others = [r for r in range(12) if r not in rows]
+        assert np.all(res["argmax"][others] == -1) and np.all(np.isnan(res["p1"][others]))
+        et, es = remask_bruteforce(toks0, state0, conf, argm, mask, tau)
+        assert np.array_equal(res["tokens"], et) and np.array_equal(res["state"], es), tau
+        assert np.array_equal(res["committed"], et != toks0)
+        nxt = [s * 4 + i for s in range(3) if es[s] == DEN for i in range(4) if et[s, i] == mask]
+        assert res["next_rows"].tolist() == nxt
+    # a round from a given state: the state passed in, not the initial one, decides the rows
+    t1 = np.array([[5, 7, 39, 6], [39, 39, 39, 39], [39, 1, 2, 3]], dtype=np.int64)
+    s1 = np.array([DEN, DEN, SAV], dtype=np.uint8)
+    res = impl.denoise_round(inp, fixed, mask, 0.35, block_tokens=t1, seq_state=s1)
+    assert res["rows"].tolist() == [2, 4, 5, 6, 7]
+
+
+ROUND_CHECKS = [check_round_composition]
 
 
 # ------------------------------------------------- block-causal prefill

@@ -76,6 +76,35 @@ def test_lmhead_entropy_parity(case):
     assert np.all(np.isnan(ent[others]))
 
 
+@pytest.mark.parametrize("rule", [1, 3])
+def test_remask_rule_nan(rule):
+    """NaN confidences and entropies (with -inf and +inf beside them) under
+    the static and entropy-bounded rules: exact against the oracle's reading
+    (NaN below every confidence, after every entropy, +inf in the budget)."""
+    g = np.random.default_rng(40 + rule)
+    S, B, mask = 300, 8, 151669
+    toks = np.where(g.random((S, B)) < 0.8, mask, g.integers(0, mask, (S, B))).astype(np.int32)
+    state = np.full(S, 2, np.uint8)
+    vals = np.array([np.nan, np.nan, -np.inf, np.inf, 0.5, 0.25, 0.5, 2.0], dtype=np.float32)
+    conf = g.choice(vals, S * B).astype(np.float32)
+    ent = g.choice(vals, S * B).astype(np.float32)
+    argm = g.integers(0, mask, S * B).astype(np.int32)
+    for k, eb in ((1, 10.0), (3, 1.0), (2, float("inf"))):
+        t_d, s_d = dev_i32(toks), dev_u8(state)
+        ri = torch.full((S * B,), -1, dtype=torch.int32, device="cuda")
+        nr = torch.zeros(1, dtype=torch.int32, device="cuda")
+        api.dbd_remask_commit_rule(t_d, s_d, dev_i32(argm), torch.from_numpy(conf).cuda(), ri, nr,
+                                   mask, rule, tokens_per_step=k, eb_threshold=eb,
+                                   entropy=torch.from_numpy(ent).cuda())
+        torch.cuda.synchronize()
+        et, es, _ = oracle.remask_rule(toks, state, conf, argm, mask, rule, tokens_per_step=k, eb=eb,
+                                       entropy=ent)
+        assert np.array_equal(t_d.cpu().numpy(), et), (rule, k, eb)
+        assert np.array_equal(s_d.cpu().numpy(), es)
+        rows = oracle.compact_rows(et, es, mask)
+        assert nr.item() == rows.size and np.array_equal(ri.cpu().numpy()[:rows.size], rows)
+
+
 @pytest.mark.parametrize("rule", [1, 2, 3])
 @pytest.mark.parametrize("S,B", [(1, 1), (3, 4), (128, 4), (64, 16), (8, 64), (1000, 64)])
 def test_remask_rule_parity(rule, S, B):

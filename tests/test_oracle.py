@@ -3,7 +3,8 @@ special cases, invariants, hand-worked fixtures)."""
 import pytest
 
 import oracle
-from pins import ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, RULE_CHECKS, SAVE_CHECKS, SAMPLE_CHECKS, PREFILL_CHECKS
+from pins import (ATTN_CHECKS, LM_CHECKS, REMASK_CHECKS, ROUND_CHECKS, RULE_CHECKS, SAVE_CHECKS, SAMPLE_CHECKS,
+                  PREFILL_CHECKS)
 
 
 @pytest.mark.parametrize("check", ATTN_CHECKS, ids=lambda f: f.__name__)
@@ -23,6 +24,11 @@ def test_remask_pins(check):
 
 @pytest.mark.parametrize("check", RULE_CHECKS, ids=lambda f: f.__name__)
 def test_rule_pins(check):
+    check(oracle)
+
+
+@pytest.mark.parametrize("check", ROUND_CHECKS, ids=lambda f: f.__name__)
+def test_round_pins(check):
     check(oracle)
 
 
