@@ -80,5 +80,9 @@ LLADA_LONG = Workload(
 # this variant exercises the threshold branch at full vocabulary.
 SDAR_4B_HIGHCONF = SDAR_4B.with_(name="sdar4b_b4_bs128_a16", a_max=16.0)
 
+# The same coverage variant of the SDAR-8B shapes (block 16, threshold 0.75):
+# with a <= 12 no position reaches 0.75 either.
+SDAR_8B_HIGHCONF = SDAR_8B.with_(name="sdar8b_b16_bs64_a16", a_max=16.0)
+
 ALL = (TINY, SDAR_1P7B, SDAR_4B, SDAR_8B, LLADA_LONG)
-BY_NAME = {w.name: w for w in ALL + (SDAR_4B_HIGHCONF,)}
+BY_NAME = {w.name: w for w in ALL + (SDAR_4B_HIGHCONF, SDAR_8B_HIGHCONF)}

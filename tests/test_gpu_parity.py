@@ -11,10 +11,11 @@ import torch
 import oracle
 from block_diffusion_amd import api, synth
 from block_diffusion_amd.workloads import (LLADA_LONG, SDAR_1P7B, SDAR_4B, SDAR_4B_HIGHCONF,
-                                           SDAR_8B, TINY, Workload)
+                                           SDAR_8B, SDAR_8B_HIGHCONF, TINY, Workload)
 from gpu_util import (ATTN_MAX_ABS, ATTN_REL_L2, RoundState, check_commits, check_lm_rows,
-                      compare_attn, dev_bf16, dev_i32, dev_u8, host_bits, oracle_attn_groups,
-                      round_inputs_dev, run_attn, tie_set, widen_bits)
+                      check_rows_against, compare_attn, dev_bf16, dev_i32, dev_u8, host_bits,
+                      oracle_attn_groups, oracle_rows_with_ties, round_inputs_dev, run_attn, tie_set,
+                      widen_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -70,8 +71,8 @@ def test_attention_parity_sdar1p7b_full():
 
 
 @pytest.fixture(scope="module")
-def sdar4b_fixed():
-    return synth.make_fixed(SDAR_4B)
+def sdar4b_fixed(big_fixed):
+    return big_fixed(SDAR_4B)
 
 
 def test_attention_parity_sdar4b_sampled(sdar4b_fixed):
@@ -121,10 +122,10 @@ def big_fixed():
     cache = {}
 
     def get(w):
-        if w.name not in cache:
-            cache.clear()                    # one multi-GB workload at a time
-            cache[w.name] = synth.make_fixed(w)
-        return cache[w.name]
+        key = (w.seed_id, w.S, w.B, w.prefix_lo, w.prefix_hi)   # a_max changes only the hidden rows
+        if key not in cache:
+            cache[key] = synth.make_fixed(w)
+        return cache[key]
     return get
 
 
@@ -202,6 +203,41 @@ def test_lmhead_parity_ragged(V, Hd, mask, n, M, max_rows):
     assert np.all(arg[untouched] == -7) and np.all(np.isnan(conf[untouched]))
 
 
+def test_lmhead_no_candidate_rows():
+    """Rows with no candidate token (W all -inf against positive hidden rows,
+    so every logit is -inf) give the mask token with confidence 0 and
+    entropy +inf, greedy and sampled, as the oracle does; rows of the same
+    launch with finite logits are unaffected."""
+    V, Hd, mask = 1000, 128, 7
+    g = np.random.default_rng(4)
+    wv = synth.f32_to_bf16(np.full((V, Hd), -np.inf, np.float32))
+    h = synth.f32_to_bf16(np.abs(g.standard_normal((6, Hd))).astype(np.float32) + 0.5)
+    rows = np.array([1, 4])
+    arg, conf = _lm_run(h, wv, mask, rows)
+    a, p1, _ = oracle.lmhead_rows(h[rows], wv, mask)
+    assert np.all(arg[rows] == mask) and np.all(a == mask)
+    assert np.all(conf[rows] == 0.0) and np.all(p1 == 0.0)
+    ent = torch.full((6,), float("nan"), dtype=torch.float32, device="cuda")
+    nr = dev_i32([2])
+    arg_d = torch.full((6,), -7, dtype=torch.int32, device="cuda")
+    conf_d = torch.full((6,), float("nan"), dtype=torch.float32, device="cuda")
+    api.dbd_lmhead_conf(dev_bf16(h), dev_bf16(wv), nr, arg_d, conf_d, mask, row_index=dev_i32(rows),
+                        max_rows=2, entropy=ent)
+    tok_s = torch.full((6,), -7, dtype=torch.int32, device="cuda")
+    conf_s = torch.full((6,), float("nan"), dtype=torch.float32, device="cuda")
+    api.dbd_lmhead_sample(dev_bf16(h), dev_bf16(wv), nr, tok_s, conf_s, mask, 0.7, 5, 1,
+                          row_index=dev_i32(rows), max_rows=2)
+    torch.cuda.synchronize()
+    assert np.all(ent.cpu().numpy()[rows] == np.inf)
+    assert np.all(oracle.lmhead_entropy(h[rows], wv, mask) == np.inf)
+    assert np.all(tok_s.cpu().numpy()[rows] == mask) and np.all(conf_s.cpu().numpy()[rows] == 0.0)
+    # finite rows beside them: W finite except one -inf row
+    wv2 = synth.normal_bf16(g, (V, Hd), std=1.0 / np.sqrt(Hd))
+    wv2[11] = wv[0]
+    arg2, conf2 = _lm_run(h, wv2, mask, rows)
+    check_lm_rows(rows, arg2, conf2, h, wv2, mask)
+
+
 def test_lmhead_parity_sdar1p7b_all_rows():
     w = SDAR_1P7B
     fx = synth.make_fixed(w)
@@ -273,6 +309,33 @@ def test_remask_parity(S, B, flags):
     assert np.array_equal(ri.cpu().numpy()[:rows.size], rows)
     den = state == 2
     assert np.array_equal(nc.cpu().numpy()[den], com.sum(1)[den])
+
+
+def test_remask_nan_and_mask_commit():
+    """Hand-built cases: every masked confidence NaN (the lowest masked
+    position commits), NaN below -inf, a NaN first position losing the
+    fallback to a number, and a commit of the mask token itself (the
+    position stays masked and the sequence DENOISING); exact against the
+    oracle, row list included."""
+    mask, tau = 9, 0.875
+    nan, inf = np.nan, np.inf
+    toks = np.array([[5, 9, 9, 9], [9, 9, 9, 9], [9, 9, 9, 9], [9, 1, 2, 3], [9, 9, 4, 9]], np.int32)
+    state = np.full(5, 2, np.uint8)
+    conf = np.array([0.75, nan, nan, nan, nan, -inf, nan, -inf, nan, 0.25, 0.5, 0.125,
+                     0.95, 0, 0, 0, 0.9, 0.1, 0, nan], np.float32)
+    argm = np.array([0, 121, 122, 123, 130, 131, 132, 133, 140, 141, 142, 143, 9, 0, 0, 0,
+                     150, 151, 0, 153], np.int32)
+    t_d, s_d = dev_i32(toks), dev_u8(state)
+    ri = torch.full((20,), -1, dtype=torch.int32, device="cuda")
+    nr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    api.dbd_remask_commit(t_d, s_d, dev_i32(argm), torch.from_numpy(conf).cuda(), ri, nr, mask, tau)
+    torch.cuda.synchronize()
+    et, es, _ = oracle.remask(toks, state, conf.astype(np.float64), argm, mask, float(np.float32(tau)))
+    assert et.tolist() == [[5, 121, 9, 9], [9, 131, 9, 9], [9, 9, 142, 9], [9, 1, 2, 3], [150, 9, 4, 9]]
+    assert np.array_equal(t_d.cpu().numpy(), et) and np.array_equal(s_d.cpu().numpy(), es)
+    rows = oracle.compact_rows(et, es, mask)
+    assert nr.item() == rows.size and np.array_equal(ri.cpu().numpy()[:rows.size], rows)
+    assert 12 in rows.tolist()          # the position that received the mask token
 
 
 def test_remask_compact_only():
@@ -350,26 +413,112 @@ def test_round_parity_teacher_forced(w):
     assert np.all(hist[-1][1] == oracle.SAVING)
 
 
-def test_round_sdar4b_rounds(sdar4b_fixed):
-    """Full SDAR-4B shapes: four rounds; every round's commits are exactly
-    the rule applied to the GPU's confidences; sampled confidences are checked
-    against the oracle in the LM-head test above."""
-    w, fx = SDAR_4B, sdar4b_fixed
-    st, hist = _run_rounds(w, fx, w.rounds, check_lm_full=False)
-    assert np.all(hist[-1][1] == oracle.SAVING)
-    assert (hist[0][0] != w.mask_id).sum() >= w.S
+def _sample_seqs(rows, B, min_rows, g):
+    """Sequences whose listed rows are checked against the oracle: those of
+    the first and the last listed row, then random others until at least
+    min_rows rows (or every row) are covered."""
+    seqs_all = np.unique(rows // B)
+    pick = {int(rows[0] // B), int(rows[-1] // B)}
+    for s in g.permutation(seqs_all):
+        if sum(int(np.sum(rows // B == x)) for x in pick) >= min_rows:
+            break
+        pick.add(int(s))
+    return sorted(pick)
 
 
-@pytest.mark.parametrize("w,n_rounds", [(SDAR_8B, 3), (LLADA_LONG, 2)], ids=lambda x: getattr(x, "name", str(x)))
-def test_round_large_rounds(w, n_rounds, big_fixed):
-    """First rounds of the SDAR-8B (initial commits, threshold 0.75) and
-    LLaDA shapes: every round's commits are exactly the rule applied to the
-    GPU's confidences, from the GPU's own state."""
+def _round_block(w, fx, min_rows=64, attn_rounds=2, seed=0):
+    """Rounds of one block on the GPU until every sequence is SAVING (at most
+    the workload's round cap), teacher forced: each round starts from the
+    GPU's state.  Every round: the row list is the oracle's compaction of
+    that state, and the commits are exactly the rule applied to the GPU's
+    own float32 confidences.  Sampled sequences covering at least min_rows
+    rows (those of the first and the last listed row among them) are checked
+    against the oracle: every row's confidence and token, and the commits
+    by the acceptance rule on the oracle's confidences.  The oracle's LM
+    head runs once over the sampled rows of all rounds.  Attention is
+    checked against the oracle on two (sequence, head) groups in the first
+    attn_rounds rounds and the last."""
+    g = np.random.default_rng(seed)
+    st = RoundState(w, fx)
+    st.init_rows()
+    attn_out = torch.empty((w.S, w.B, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    toks, state = fx.block_tokens0.copy(), fx.seq_state0.copy()
+    recs = []
+    last_rin = None
+    for r in range(1, w.rounds + 1):
+        rows0 = oracle.compact_rows(toks, state, w.mask_id)
+        assert st.bufs.num_rows.item() == rows0.size
+        assert np.array_equal(st.bufs.row_index.cpu().numpy()[:rows0.size], rows0)
+        if rows0.size == 0:
+            break
+        rin = synth.make_round(w, r, fx.w_vocab)
+        api.dbd_round(st.args(round_inputs_dev(rin), attn_out))
+        torch.cuda.synchronize()
+        t1 = st.bufs.block_tokens.cpu().numpy()
+        s1 = st.bufs.seq_state.cpu().numpy()
+        arg = st.bufs.argmax_tok.cpu().numpy()
+        conf = st.bufs.conf.cpu().numpy()
+        et, es, _ = oracle.remask(toks, state, conf.astype(np.float64), arg, w.mask_id,
+                                  float(np.float32(w.tau)))
+        assert np.array_equal(t1, et) and np.array_equal(s1, es), f"round {r}"
+        seqs = _sample_seqs(rows0, w.B, min_rows, g)
+        srows = np.array([x for x in rows0 if x // w.B in seqs])
+        recs.append(dict(r=r, toks=toks, state=state, t1=t1, s1=s1, seqs=seqs, rows=srows,
+                         arg=arg[srows], conf=conf[srows], hidden=rin.hidden[srows]))
+        if r <= attn_rounds:
+            groups = _sample_groups(w, fx.prefix_len, 1, 1, 100 + r)[:2]
+            mx, rl2 = compare_attn(host_bits(attn_out), oracle_attn_groups(fx, rin, groups), w.G)
+            assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, (r, mx, rl2)
+        last_rin = rin
+        toks, state = t1, s1
+    assert np.all(state == oracle.SAVING), "block not finished within the round cap"
+    if len(recs) > attn_rounds:
+        groups = _sample_groups(w, fx.prefix_len, 1, 1, 999)[:2]
+        mx, rl2 = compare_attn(host_bits(attn_out), oracle_attn_groups(fx, last_rin, groups), w.G)
+        assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2, ("last", mx, rl2)
+    # the oracle over every round's sampled rows at once
+    H = np.concatenate([x["hidden"] for x in recs])
+    a, p1, p2, ties = oracle_rows_with_ties(H, fx.w_vocab, w.mask_id)
+    o = 0
+    n_tie = n_ex = 0
+    for x in recs:
+        n = x["rows"].size
+        sl = slice(o, o + n)
+        sub_ties = {i - o: t for i, t in ties.items() if o <= i < o + n}
+        n_tie += check_rows_against(x["arg"], x["conf"], a[sl], p1[sl], p2[sl], sub_ties,
+                                    label=f"round {x['r']}")
+        p1_by_row = np.full(w.S * w.B, np.nan)
+        p1_by_row[x["rows"]] = p1[sl]
+        ok = {int(rw): (int(a[o + j]), p1[o + j] - p2[o + j], sub_ties.get(j))
+              for j, rw in enumerate(x["rows"])}
+
+        def arg_ok(row, tok, ok=ok):
+            aa, gap, ts = ok[row]
+            return tok == aa if gap >= 1e-4 else tok in ts
+        n_ex += check_commits(x["toks"], x["state"], x["t1"], x["s1"], p1_by_row, arg_ok, w.mask_id,
+                              w.tau, seqs=x["seqs"])
+        o += n
+    thr = sum(int(((x["t1"] != x["toks"]).sum(1) > 1).sum()) for x in recs)
+    print(f"{w.name}: {len(recs)} rounds, {H.shape[0]} oracle rows, tie-exempt {n_tie}, "
+          f"band-exempt sequences {n_ex}, sequence-rounds with several commits {thr}", flush=True)
+    return recs
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("w", [SDAR_4B, SDAR_4B_HIGHCONF, SDAR_8B, SDAR_8B_HIGHCONF, LLADA_LONG],
+                         ids=lambda w: w.name)
+def test_round_whole_block_sampled(w, big_fixed):
+    """Whole blocks at the SDAR-4B (literal and a <= 16), SDAR-8B (block
+    16, initial commits, threshold 0.75; literal and a <= 16) and LLaDA
+    (block 64, 16K-32K prefixes) shapes: every round until the block is
+    full, each against the oracle on at least 64 sampled rows."""
     fx = big_fixed(w)
-    st, hist = _run_rounds(w, fx, n_rounds, check_lm_full=False)
-    masked0 = (fx.block_tokens0 == w.mask_id).sum()
-    masked = [(h[0] == w.mask_id).sum() for h in hist]
-    assert masked[0] < masked0 and all(b < a for a, b in zip(masked, masked[1:]))
+    recs = _round_block(w, fx)
+    masked = [(x["toks"] == w.mask_id).sum() for x in recs] + [(recs[-1]["t1"] == w.mask_id).sum()]
+    assert all(b < a for a, b in zip(masked, masked[1:]))
+    if w.a_max >= 16.0:
+        # the threshold branch fires: some sequence commits several positions in a round
+        assert any(((x["t1"] != x["toks"]).sum(1) > 1).any() for x in recs)
 
 
 @pytest.mark.parametrize("w", [TINY, SDAR_1P7B], ids=lambda w: w.name)
