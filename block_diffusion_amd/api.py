@@ -110,6 +110,8 @@ def lib() -> C.CDLL:
     L.dbd_mfma_peak_flops.restype = C.c_double
     L.dbd_round.argtypes = [C.POINTER(dbd_round_args), _vp]
     L.dbd_round.restype = i
+    L.dbd_round_noalloc.argtypes = [C.POINTER(dbd_round_args), _vp]
+    L.dbd_round_noalloc.restype = i
     L.dbd_round_workspace_size.argtypes = [C.POINTER(dbd_round_args)]
     L.dbd_round_workspace_size.restype = sz
     L.dbd_graph_create.argtypes = [C.POINTER(dbd_round_args), i, C.POINTER(_vp)]
@@ -458,6 +460,16 @@ def dbd_round_workspace_size(args: dbd_round_args) -> int:
 
 def dbd_round(args: dbd_round_args, stream=None):
     _check(lib().dbd_round(C.byref(args), _stream(stream)))
+
+
+# the static scratch of dbd_round_noalloc (DBD_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def dbd_round_noalloc(args: dbd_round_args, stream=None):
+    """dbd_round with the library's static per-device scratch as the
+    workspace (args.workspace is not read); allocates nothing."""
+    _check(lib().dbd_round_noalloc(C.byref(args), _stream(stream)))
 
 
 class Graph:

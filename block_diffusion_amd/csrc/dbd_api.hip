@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -207,7 +208,7 @@ dbd_status check_rule(int rule, float eb, const float* entropy, bool commits) {
   return DBD_OK;
 }
 
-dbd_status check_round(const dbd_round_args* a) {
+dbd_status check_round(const dbd_round_args* a, bool check_workspace = true) {
   REQUIRE(a != nullptr, "args is NULL");
   dbd_status s = check_attn(a->S, a->B, a->Hq, a->Hkv, a->D, a->page_size, a->max_pages_per_seq);
   if (s != DBD_OK) return s;
@@ -243,6 +244,7 @@ dbd_status check_round(const dbd_round_args* a) {
   }
   REQUIRE(!(a->save_kv && a->gate_on_rows), "gate_on_rows cannot be set on a save_kv step");
   if (a->round_counter != nullptr) REQUIRE(aligned(a->round_counter, 4), "round_counter is not 4-byte aligned");
+  if (!check_workspace) return DBD_OK;
   const size_t need = dbd_round_workspace_size(a);
   if (a->workspace == nullptr || a->workspace_bytes < need)
     return fail(DBD_ERR_WORKSPACE, "round workspace needs %zu bytes (got %zu)", need, a->workspace_bytes);
@@ -292,6 +294,35 @@ dbd_status enqueue_round(const dbd_round_args* a, hipStream_t st) {
                         save ? const_cast<int32_t*>(a->prefix_len) : nullptr,
                         save ? a->token_stream : nullptr, a->stream_cap,
                         save ? a->end_len : nullptr, a->round_counter, a->num_rows);
+}
+
+// The round workspace of dbd_round_noalloc: one array per device, resident
+// for the life of the process.  In host code `scratch` names a host-side
+// stand-in, not device memory: only the address hipGetSymbolAddress returns
+// on a device may be handed to kernels.
+constexpr size_t kScratchBytes = (size_t)DBD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// scratch's device address on the current device, looked up once per device
+dbd_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DBD_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || !aligned(p, 256)) return fail(DBD_ERR_HIP, "scratch has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DBD_OK;
 }
 
 }  // namespace
@@ -588,6 +619,23 @@ dbd_status dbd_round(const dbd_round_args* a, void* stream) {
   dbd_status s = check_round(a);
   if (s != DBD_OK) return s;
   return enqueue_round(a, static_cast<hipStream_t>(stream));
+}
+
+dbd_status dbd_round_noalloc(const dbd_round_args* a, void* stream) {
+  dbd_status s = check_round(a, false);
+  if (s != DBD_OK) return s;
+  const size_t need = dbd_round_workspace_size(a);
+  if (need > kScratchBytes)
+    return fail(DBD_ERR_WORKSPACE,
+                "round workspace needs %zu bytes, beyond the %zu-byte static scratch of dbd_round_noalloc",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  s = scratch_for_current_device(&ws);
+  if (s != DBD_OK) return s;
+  dbd_round_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = kScratchBytes;
+  return enqueue_round(&b, static_cast<hipStream_t>(stream));
 }
 
 dbd_status dbd_graph_create(const dbd_round_args* args, int n_rounds, dbd_graph** out) {

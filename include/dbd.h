@@ -468,6 +468,25 @@ typedef struct dbd_round_args {
 
 dbd_status dbd_round(const dbd_round_args* a, void* stream);
 size_t dbd_round_workspace_size(const dbd_round_args* a);
+
+/* dbd_round_noalloc -- dbd_round for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation).  The same round with the same kernels, but the
+ * workspace is the library's own static device array of
+ * DBD_NOALLOC_SCRATCH_BYTES (64 MiB) on the current device, resident until
+ * the process ends; a->workspace and a->workspace_bytes are not read.
+ * The call makes no allocation of any kind (no hipMalloc, no library
+ * routine that allocates); its first call on a device looks up that
+ * device's array address once.  Returns DBD_ERR_WORKSPACE, before any HIP
+ * call, when dbd_round_workspace_size(a) exceeds the array (e.g. the
+ * SDAR-8B and LLaDA shapes of block 16 and 64 need 104 and 149 MiB); the
+ * other checks are dbd_round's.  The array's contents are not cleared and
+ * need not be: every call writes what it reads.  All calls on one device
+ * share that device's array, so calls that overlap in time on one device
+ * (different streams, or host threads without ordering) race; callers
+ * serialise them, e.g. on one stream. */
+#define DBD_NOALLOC_SCRATCH_BYTES (64u << 20)
+dbd_status dbd_round_noalloc(const dbd_round_args* a, void* stream);
 /* sizeof(dbd_round_args) as this library was built, so that a binding can
  * check its copy of the struct layout. */
 size_t dbd_round_args_size(void);

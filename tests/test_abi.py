@@ -274,3 +274,25 @@ def test_mfma_ceiling_host_checks():
     assert L.dbd_mfma_peak(16, 4097, 16, None) == api.DBD_ERR_INVALID_ARG
     assert L.dbd_mfma_peak(None, 4, 16, None) == api.DBD_ERR_INVALID_ARG
     assert L.dbd_mfma_peak(16, 4, 8, None) == api.DBD_ERR_INVALID_ARG     # misaligned sink
+
+
+def test_round_noalloc_rejects():
+    """dbd_round_noalloc checks its arguments like dbd_round, ignores the
+    workspace fields, and rejects a round whose workspace exceeds its static
+    scratch (the SDAR-8B shapes need about 104 MiB) before any HIP call."""
+    a = api.dbd_round_args()
+    a.S, a.B, a.Hq, a.Hkv, a.D, a.page_size, a.max_pages_per_seq = 64, 16, 32, 8, 128, 256, 32
+    a.Hd, a.V, a.mask_token_id, a.dynamic_threshold = 4096, 151936, 151669, 0.75
+    with pytest.raises(api.DbdError) as e:
+        api.dbd_round_noalloc(a, stream=0)
+    assert e.value.status == api.DBD_ERR_INVALID_ARG          # NULL tensors
+    for n in ("q", "k_blk", "v_blk", "k_cache", "v_cache", "page_table", "prefix_len",
+              "attn_out", "hidden", "w_vocab", "row_index", "num_rows", "argmax_tok", "conf",
+              "block_tokens", "seq_state"):
+        setattr(a, n, 256)
+    a.workspace, a.workspace_bytes = None, 0
+    assert api.lib().dbd_round_workspace_size(ctypes.byref(a)) > api.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(api.DbdError) as e:
+        api.dbd_round_noalloc(a, stream=0)
+    assert e.value.status == api.DBD_ERR_WORKSPACE
+    assert b"static scratch" in api.lib().dbd_last_error()
