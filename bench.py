@@ -44,7 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="the CPU oracle repeats whole blocks until this much time has passed")
-    ap.add_argument("--only", choices=["attention", "lmhead", "remask"],
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration entries (configs 0, 1, 3, 4)")
+    ap.add_argument("--only", choices=["attention", "lmhead", "remask", "logits", "filtered", "prefill"],
                     help="launch only this entry point (warmup + steps times, round-1 inputs) and "
                          "print its mean launch time: the run that rocprofv3 counters are taken on")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
@@ -413,6 +415,16 @@ def main():
     lm_roof["traffic"] = traffic.get(("dbd_lmhead_conf", M1))
     for r in (attn_roof, lm_roof):
         r["frac"] = r["achieved"] / r["peak"]
+    # attention + remask as one HBM figure: remask reads block tokens,
+    # confidences and tokens (12 B per position) and writes block tokens and
+    # the row list (8 B), plus the state byte read and written per sequence
+    remask_bytes = 20 * w.S * w.B + 2 * w.S
+    attn_remask = dict(bound="hbm", bytes=attn_bytes + remask_bytes,
+                       us=round(t_attn + t_remask, 2),
+                       achieved=(attn_bytes + remask_bytes) / ((t_attn + t_remask) * 1e-6) / 1e9,
+                       peak=PEAK_HBM_GBS, unit="GB/s")
+    attn_remask["frac"] = attn_remask["achieved"] / PEAK_HBM_GBS
+    log(f"attention + remask: {attn_remask['achieved']:.0f} GB/s = {attn_remask['frac']:.1%} of HBM peak")
     dominant = "attention" if step_attn >= step_lm else "lmhead"
     roof = dict(attn_roof if dominant == "attention" else lm_roof)
     roof["kernel"] = "dbd_attn_paged" if dominant == "attention" else "dbd_lmhead_conf"
@@ -459,14 +471,206 @@ def main():
                                         "committed_tokens_per_s": round(w.S * w.B / t_block * 1e6, 1)},
                          "attention_roofline": {k: (round(v, 4) if isinstance(v, float) else v)
                                                 for k, v in attn_roof.items()},
+                         "attention_remask_frac": round(attn_remask["frac"], 4),
+                         "attention_remask_roofline": {k: (round(v, 4) if isinstance(v, float) else v)
+                                                       for k, v in attn_remask.items()},
                          "lmhead_roofline_M%d" % M1: {k: (round(v, 4) if isinstance(v, float) else v)
                                                       for k, v in lm_roof.items()}},
     }
     graph.close()
 
+    if not args.no_configs:
+        # the other configurations, each as whole blocks of its own rounds
+        del fixed, per_round, bufs, attn_out
+        torch.cuda.empty_cache()
+        from block_diffusion_amd.workloads import LLADA_LONG, SDAR_1P7B, SDAR_8B, TINY
+        out["breakdown_us"]["configs"] = {}
+        for wc in (TINY, SDAR_1P7B, SDAR_8B, LLADA_LONG):
+            out["breakdown_us"]["configs"][wc.name] = config_entry(api, synth, wc, dev, max(args.steps // 4, 3))
+            torch.cuda.empty_cache()
+
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, fx, rins, args.cpu_seconds)
+        out["breakdown_us"]["cpu_oracle_1thread"] = cpu_single_thread(synth)
     print(json.dumps(out), flush=True)
+
+
+def attn_bytes_of(w, prefix_len):
+    """Algorithmic bytes of one attention launch: prefix K and V, q in and
+    out, the block's K and V, prefix lengths and page ids."""
+    import numpy as np
+    L = prefix_len.astype(np.int64)
+    npages = -(-L // w.P)
+    return int(L.sum() * w.Hkv * w.D * 2 * 2 + 2 * w.S * w.B * w.Hq * w.D * 2
+               + 2 * w.S * w.B * w.Hkv * w.D * 2 + w.S * 4 + npages.sum() * 4)
+
+
+def config_entry(api, synth, w, dev, steps):
+    """Workload w as whole blocks: the rounds from the initial state until
+    no masked row is left (each round's inputs drawn as for the parity
+    tests), captured as one graph and replayed `steps` times after a
+    warm-up; per-round eager times; attention, LM head (round-1 rows) and
+    remask per launch with their roofline fractions."""
+    import numpy as np
+    import torch
+
+    t0 = time.time()
+    fx = synth.make_fixed(w)
+
+    def dbf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    n = w.S * w.B
+    fixed = dict(k_cache=dbf(fx.k_cache), v_cache=dbf(fx.v_cache),
+                 page_table=torch.from_numpy(fx.page_table).to(dev),
+                 prefix_len=torch.from_numpy(fx.prefix_len).to(dev), w_vocab=dbf(fx.w_vocab))
+    tok0 = torch.from_numpy(fx.block_tokens0).to(dev)
+    st0 = torch.from_numpy(fx.seq_state0).to(dev)
+    bufs = api.RoundBuffers(
+        row_index=torch.zeros(n, dtype=torch.int32, device=dev),
+        num_rows=torch.zeros(1, dtype=torch.int32, device=dev),
+        argmax_tok=torch.zeros(n, dtype=torch.int32, device=dev),
+        conf=torch.zeros(n, dtype=torch.float32, device=dev),
+        block_tokens=tok0.clone(), seq_state=st0.clone(),
+        num_committed=torch.zeros(w.S, dtype=torch.int32, device=dev),
+        workspace=torch.empty(1, dtype=torch.uint8, device=dev))
+    attn_out = torch.empty((w.S, w.B, w.Hq, w.D), dtype=torch.bfloat16, device=dev)
+    shape = dict(S=w.S, B=w.B, Hq=w.Hq, Hkv=w.Hkv, D=w.D, page_size=w.P,
+                 max_pages_per_seq=int(fx.page_table.shape[1]), Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
+                 dynamic_threshold=w.tau)
+
+    def mk(pr):
+        return api.make_round_args(**shape, **pr, **fixed, attn_out=attn_out, bufs=bufs)
+
+    def reset():
+        bufs.block_tokens.copy_(tok0)
+        bufs.seq_state.copy_(st0)
+        api.dbd_remask_commit(bufs.block_tokens, bufs.seq_state, None, None, bufs.row_index,
+                              bufs.num_rows, w.mask_id, w.tau, flags=api.DBD_COMPACT_ONLY)
+
+    # the block's rounds, found by running it once (untimed)
+    reset()
+    per_round, rows = [], []
+    for r in range(1, w.rounds + 1):
+        nr = int(bufs.num_rows.item())
+        if nr == 0:
+            break
+        rin = synth.make_round(w, r, fx.w_vocab)
+        per_round.append(dict(q=dbf(rin.q), k_blk=dbf(rin.k_blk), v_blk=dbf(rin.v_blk), hidden=dbf(rin.hidden)))
+        rows.append(nr)
+        if r == 1:
+            bufs.workspace = torch.empty(api.dbd_round_workspace_size(mk(per_round[0])), dtype=torch.uint8,
+                                         device=dev)
+        api.dbd_round(mk(per_round[-1]))
+    torch.cuda.synchronize()
+    assert int(bufs.num_rows.item()) == 0, "block not finished within the round cap"
+    R = len(per_round)
+    graph = api.dbd_graph_create([mk(pr) for pr in per_round])
+    for _ in range(2):
+        reset()
+        graph.launch()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        reset()
+        graph.launch()
+    torch.cuda.synchronize()
+    ms_block = (time.perf_counter() - t1) * 1e3 / steps
+    graph.close()
+    stream = torch.cuda.current_stream()
+    ra = [mk(pr) for pr in per_round]
+    times = [[] for _ in ra]
+    for _ in range(3):
+        reset()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
+        evs[0].record(stream)
+        for i, a in enumerate(ra):
+            api.dbd_round(a)
+            evs[i + 1].record(stream)
+        evs[-1].synchronize()
+        for i in range(R):
+            times[i].append(evs[i].elapsed_time(evs[i + 1]) * 1e3)
+    round_us = [float(np.median(x)) for x in times]
+
+    def ev_time(fn, it=10):
+        for _ in range(2):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record(stream)
+        for _ in range(it):
+            fn()
+        e.record(stream)
+        e.synchronize()
+        return s.elapsed_time(e) * 1e3 / it
+
+    r1 = per_round[0]
+    t_attn = ev_time(lambda: api.dbd_attn_paged(r1["q"], r1["k_blk"], r1["v_blk"], fixed["k_cache"],
+                                                fixed["v_cache"], fixed["page_table"], fixed["prefix_len"],
+                                                attn_out, ws=bufs.workspace))
+    lm_rows = torch.arange(n, dtype=torch.int32, device=dev)
+    nr1 = torch.tensor([rows[0]], dtype=torch.int32, device=dev)
+    t_lm = ev_time(lambda: api.dbd_lmhead_conf(r1["hidden"], fixed["w_vocab"], nr1, bufs.argmax_tok, bufs.conf,
+                                               w.mask_id, row_index=lm_rows, max_rows=n, ws=bufs.workspace))
+    conf_r = torch.rand(n, device=dev)
+    arg_r = torch.zeros(n, dtype=torch.int32, device=dev)
+    tk, ss = tok0.clone(), st0.clone()
+    ri, nr2 = torch.zeros(n, dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev)
+    t_remask = ev_time(lambda: api.dbd_remask_commit(tk, ss, arg_r, conf_r, ri, nr2, w.mask_id, 2.0))
+    a_bytes = attn_bytes_of(w, fx.prefix_len)
+    r_bytes = 20 * w.S * w.B + 2 * w.S
+    lm_flops = 2.0 * rows[0] * w.Hd * w.V
+    w_bytes = 2.0 * w.V * w.Hd
+    ent = {"rounds": R, "rows_per_round": rows, "ms_per_block": round(ms_block, 4),
+           "block_tokens_per_s": round(w.S * w.B * R / (ms_block * 1e-3), 1),
+           "per_round_eager_us": [round(t, 1) for t in round_us],
+           "attention_us": round(t_attn, 2), "attention_bytes": a_bytes,
+           "attention_frac_hbm": round(a_bytes / (t_attn * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+           "attention_remask_frac_hbm": round((a_bytes + r_bytes) / ((t_attn + t_remask) * 1e-6) / 1e9
+                                              / PEAK_HBM_GBS, 4),
+           "lmhead_us_round1": round(t_lm, 2), "lmhead_rows_round1": rows[0],
+           "lmhead_frac_mfma": round(lm_flops / (t_lm * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "lmhead_w_frac_hbm": round(w_bytes / (t_lm * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+           "remask_us": round(t_remask, 2)}
+    log(f"{w.name}: {R} rounds (rows {rows[0]} -> {rows[-1]}), {ms_block:.3f} ms per block = "
+        f"{ent['block_tokens_per_s']:.0f} block-tokens/s; attention {t_attn:.1f} us "
+        f"({ent['attention_frac_hbm']:.1%} of HBM), LM head {t_lm:.1f} us at {rows[0]} rows "
+        f"({ent['lmhead_frac_mfma']:.1%} of bf16 MFMA), remask {t_remask:.1f} us "
+        f"[{time.time() - t0:.1f} s]")
+    return ent
+
+
+def cpu_single_thread(synth):
+    """The oracle with one BLAS thread on the two small configurations: the
+    tiny one as whole blocks, the SDAR-1.7B one round by round, each for a
+    bounded time (baseline only)."""
+    import numpy as np
+
+    import oracle
+    from block_diffusion_amd.workloads import SDAR_1P7B, TINY
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:
+        return None
+    res = {}
+    with threadpool_limits(1):
+        for w, budget in ((TINY, 3.0), (SDAR_1P7B, 10.0)):
+            fx = synth.make_fixed(w)
+            rins = [synth.make_round(w, r, fx.w_vocab) for r in range(1, w.rounds + 1)]
+            toks, state = fx.block_tokens0, fx.seq_state0
+            rounds, t0 = 0, time.perf_counter()
+            while True:
+                rin = rins[rounds % len(rins)]
+                if rounds % len(rins) == 0:
+                    toks, state = fx.block_tokens0, fx.seq_state0
+                r = oracle.denoise_round(rin, fx, w.mask_id, w.tau, block_tokens=toks, seq_state=state)
+                toks, state = r["tokens"], r["state"]
+                rounds += 1
+                dt = time.perf_counter() - t0
+                if dt >= budget and rounds % len(rins) == 0 or dt >= 4 * budget:
+                    break
+            res[w.name] = {"value": round(w.S * w.B * rounds / dt, 3), "unit": "block-tokens/s",
+                           "threads": 1, "rounds": rounds, "seconds": round(dt, 2)}
+    return res
 
 
 def only(args, w, api, fixed, r1, attn_out, bufs, tok0, st0):
@@ -485,6 +689,31 @@ def only(args, w, api, fixed, r1, attn_out, bufs, tok0, st0):
         fn = lambda: api.dbd_lmhead_conf(r1["hidden"], fixed["w_vocab"], nr, bufs.argmax_tok,
                                          bufs.conf, w.mask_id, row_index=rows, max_rows=n,
                                          ws=bufs.workspace)
+    elif args.only in ("logits", "filtered"):
+        rows = torch.arange(n, dtype=torch.int32, device=dev)
+        nr = torch.tensor([n], dtype=torch.int32, device=dev)
+        lg = torch.empty((n, w.V), dtype=torch.float32, device=dev)
+        api.dbd_lmhead_logits(r1["hidden"], fixed["w_vocab"], nr, lg, w.mask_id, row_index=rows, max_rows=n)
+        if args.only == "logits":
+            fn = lambda: api.dbd_lmhead_logits(r1["hidden"], fixed["w_vocab"], nr, lg, w.mask_id,
+                                               row_index=rows, max_rows=n)
+        else:
+            fn = lambda: api.dbd_sample_filtered(lg, nr, bufs.argmax_tok, bufs.conf, w.mask_id, 0.6, 0,
+                                                 0.95, 1234, 1, row_index=rows, max_rows=n)
+    elif args.only == "prefill":
+        import numpy as np
+        Lp = fixed["prefix_len"].cpu().numpy().astype(np.int64)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(Lp)]).astype(np.int32)).to(dev)
+        Tp = int(Lp.sum())
+        gen = torch.Generator(device=dev).manual_seed(4321)
+        qp = torch.randn((Tp, w.Hq, w.D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        kp = torch.randn((Tp, w.Hkv, w.D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        vp = torch.randn((Tp, w.Hkv, w.D), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        op = torch.empty_like(qp)
+        kc_p, vc_p = torch.empty_like(fixed["k_cache"]), torch.empty_like(fixed["v_cache"])
+        pf_ws = api.workspace(api.lib().dbd_prefill_workspace_size(w.S), dev)
+        fn = lambda: api.dbd_prefill_attn(qp, kp, vp, cu, op, w.B, page_table=fixed["page_table"],
+                                          k_cache=kc_p, v_cache=vc_p, ws=pf_ws)
     else:
         conf_r = torch.rand(n, device=dev)
         arg_r = torch.zeros(n, dtype=torch.int32, device=dev)
