@@ -1,9 +1,13 @@
 // Practical ceilings of the device, for the measurement of the kernels
 // against both the nominal and a measured peak.
 //
-// stream_read_kernel: every thread reads 16-byte chunks, four at a time,
-// grid-stride over the buffer; the XOR of everything read goes to one word
-// per workgroup so that no load can be dropped.
+// stream_read_kernel: the fastest plain read found on the device.  Each
+// workgroup reads whole contiguous 32 KB chunks (eight 16-byte non-temporal
+// loads in flight per thread, consecutive threads on consecutive 16 bytes),
+// chunks dealt round robin; a tail shorter than a chunk is read grid-stride.
+// The XOR of everything read goes to one word per workgroup so that no load
+// can be dropped.  Non-temporal loads stream past the caches: on MI355X they
+// read at 7.0 TB/s where plain loads of the same shape read at 6.3 TB/s.
 //
 // mfma_peak_kernel: a register-resident loop of v_mfma_f32_32x32x16_bf16.
 // Each wave loads eight A and eight B operand fragments of one of 64
@@ -17,32 +21,40 @@
 
 namespace dbd {
 
-__global__ __launch_bounds__(512) void stream_read_kernel(const u32x4* __restrict__ p, size_t n16,
-                                                          uint32_t* sink) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+constexpr int kReadThreads = 256, kReadInflight = 8;
+
+__global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* __restrict__ p, size_t n16,
+                                                                   uint32_t* sink) {
+  constexpr size_t per = (size_t)kReadThreads * kReadInflight;   // 16-byte units per chunk
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
-    acc ^= a ^ b ^ c ^ d;
+  const size_t nfull = n16 / per;
+  for (size_t c = blockIdx.x; c < nfull; c += gridDim.x) {
+    const u32x4* q = p + c * per + threadIdx.x;
+    u32x4 v[kReadInflight];
+#pragma unroll
+    for (int k = 0; k < kReadInflight; ++k) v[k] = __builtin_nontemporal_load(q + k * kReadThreads);
+#pragma unroll
+    for (int k = 0; k < kReadInflight; ++k) acc ^= v[k];
   }
-  for (; i < n16; i += stride) acc ^= p[i];
+  for (size_t i = nfull * per + (size_t)blockIdx.x * kReadThreads + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * kReadThreads)
+    acc ^= p[i];
   uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x ^= (uint32_t)__shfl_xor((int)x, off, 64);
-  __shared__ uint32_t s_x[8];
+  __shared__ uint32_t s_x[kReadThreads / 64];
   if ((threadIdx.x & 63) == 0) s_x[threadIdx.x >> 6] = x;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t y = 0u;
-    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) y ^= s_x[w];
+    for (int w = 0; w < kReadThreads / 64; ++w) y ^= s_x[w];
     sink[blockIdx.x] = y;
   }
 }
 
 hipError_t stream_read_launch(const void* data, size_t bytes, uint32_t* sink, int grid,
                               hipStream_t st) {
-  stream_read_kernel<<<grid, 512, 0, st>>>(static_cast<const u32x4*>(data), bytes / 16, sink);
+  stream_read_kernel<<<grid, kReadThreads, 0, st>>>(static_cast<const u32x4*>(data), bytes / 16, sink);
   return hipGetLastError();
 }
 

@@ -153,15 +153,24 @@ __device__ __forceinline__ float uniform01(uint32_t w) {
 // five wait states in every instance would cost 1-2% of the kernel.  FIVE
 // selects them for the store-mode instance, whose partial-maximum
 // bookkeeping leaves the compiler short of SGPRs.
-template <bool FIVE>
+template <bool FIVE, bool NT = false>
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, const lds_u16* lds) {
-  if constexpr (FIVE)
+  if constexpr (FIVE && NT)
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
+  else if constexpr (FIVE)
     asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
+  else if constexpr (NT)
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
   else
     asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(off), "s"(base), "{m0}"((uint32_t)(uintptr_t)lds) : "memory");
 }
+#ifndef LM_W_NT
+#define LM_W_NT 0
+#endif
 
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -236,7 +245,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
       for (int i = I0; i < I1; ++i) {
         const int row = 8 * (wn * NLD + i) + lr;
         const uint32_t o = row < lim ? off[i] : back + (off[i] & 0x70);
-        dma16<STO>(tb, o, slot + (wn * NLD + i) * 512);
+        dma16<STO, LM_W_NT != 0>(tb, o, slot + (wn * NLD + i) * 512);
       }
     } else {
 #pragma unroll

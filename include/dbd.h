@@ -523,7 +523,8 @@ dbd_status dbd_validate_inputs(int S, int B, int page_size,
                                const uint8_t* seq_state);
 
 /* Measurement helper: reads `bytes` (a multiple of 16) of device memory
- * once, as a plain streaming read, and writes a digest word per workgroup
+ * once (contiguous chunks per workgroup, non-temporal loads: the fastest
+ * plain read found on the device) and writes a digest word per workgroup
  * to sink (dbd_stream_read_sink_words() words), so that the memory-bound
  * kernels can be compared with the device's practical read bandwidth as
  * well as with the nominal HBM peak. */
