@@ -15,17 +15,20 @@
 // every wave streams the same number of tiles whatever the prefix lengths.
 // A wave finishes each segment it touches with (max, sum, unnormalised
 // output); a segment split over several waves leaves fp32 partials that
-// attn_combine_kernel merges, one that fits in one wave is written directly.
-// Each wave (and each combine workgroup) first turns the prefix lengths
-// into tile prefix sums itself: a separate planning launch would cost more
-// than the few loads it saves.
+// attn_combine_kernel merges, one that fits in one wave is written directly;
+// every piece records its segment's piece count for the combine launch.
+// Each wave first turns the prefix lengths into tile prefix sums itself: a
+// separate planning launch would cost more than the few loads it saves.
 //
 // Per wave, tiles go straight from global memory into a ring of kRing LDS
-// slots (global_load_lds_dwordx4: kKT keys of K and of V in runs of 16 that
-// never cross a page), kRing-1 tiles in flight while one is computed.  A
-// segment's query rows go from global memory straight into the MFMA operand
-// registers at its first tile, so a slot holds K and V only and the waves
-// per CU do not shrink with the rows per segment.  Rows are stored with
+// slots (global_load_lds_dwordx4, non-temporal: kKT keys of K and of V in
+// runs of 16 that never cross a page), kRing-1 tiles in flight while one is
+// computed.  A 16-row segment's query rows ride along in a small region of
+// its first tile's slot and go from there into the MFMA operand registers
+// (a load from global memory at that point would drain the ring: the
+// compiler's wait for it counts every load before it); larger row groups
+// load them from global memory, so their slots hold K and V only and the
+// waves per CU do not shrink with the rows per segment.  Rows are stored with
 // their 16-byte chunks XOR-permuted by row so fragment reads hit distinct
 // banks.  Per run of 32 keys:
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 for each 16-key half
@@ -97,16 +100,32 @@ __device__ __forceinline__ int eoff(int r, int c) {
   return r * D + ((c ^ rswz<D>(r)) << 3);
 }
 
+#ifndef ATTN_QLDS
+#define ATTN_QLDS 1
+#endif
+
 template <int D, int RT>
 struct Geo {
   static constexpr int ROWS = 16 * RT;
   static constexpr int KS = D / 32;
   static constexpr int DT = D / 16;
   static constexpr int KV = kKT * D;                // elements of one K (or V) tile
-  static constexpr int SLOT = 2 * KV;               // K, V
+  // 16-row segments also stage their query rows in the slot of their first
+  // tile (a 4 KB region at D = 128), so that a segment start reads them from
+  // LDS instead of global memory; larger row groups keep the slots small
+  // (four waves per CU) and load their query rows from global memory
+  static constexpr bool QLDS = ATTN_QLDS != 0 && RT == 1;
+  static constexpr int QE = QLDS ? ROWS * D : 0;    // elements of the query region
+  static constexpr int SLOT = 2 * KV + QE;          // K, V, query rows
   static constexpr int LPR = D / 8;                 // lanes per row in a 1 KB load
   static constexpr int RPI = 64 / LPR;              // rows per 1 KB load
 };
+
+// LDS bytes of one ring slot (the plan sizes the launch with it)
+inline int attn_slot_bytes(int D, int RT) {
+  const bool q = ATTN_QLDS != 0 && RT == 1;
+  return (2 * kKT * D + (q ? 16 * RT * D : 0)) * 2;
+}
 
 // One direct-to-LDS load: lane l copies 16 bytes from its own global address
 // to lds + 16*l.  Issued as inline assembly so that the compiler neither
@@ -248,10 +267,25 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
     }
   };
 
-  // load tile `d` into `slot`
-  auto dma_tile = [&](lds_u16* slot, const Dec& d) INL {
+  // load tile `d` into `slot` (with_q: also the segment's query rows)
+  auto dma_tile = [&](lds_u16* slot, const Dec& d, bool with_q) INL {
     wait_lgkm0();   // the slot's previous tile has been read out
     const int g = d.hg / a.n_rg, rg = d.hg % a.n_rg;
+    if constexpr (Gm::QLDS) {
+      if (with_q) {
+        // query row r of the row group: rr = rg*ROWS + r -> (pos, gi) =
+        // (rr / G, rr % G); rows past G*B re-read the last real row (never
+        // written out); chunks permuted by row as in the K/V tiles
+#pragma unroll
+        for (int r0 = 0; r0 < ROWS; r0 += Gm::RPI) {
+          const int row = r0 + lane / Gm::LPR;
+          const int rr = min(rg * ROWS + row, R - 1);
+          const int pos = rr / a.G, gi = rr % a.G;
+          const int lc = (lane % Gm::LPR) ^ rswz<D>(row);
+          dma16(a.q + ((size_t)(d.s * a.B + pos) * a.Hq + g * a.G + gi) * D + lc * 8, slot + 2 * KV + r0 * D);
+        }
+      }
+    }
     // kKT/16 runs of 16 keys; a run never crosses a page (the page size is a
     // multiple of 16).  A run wholly past the end re-reads the tile's first
     // key (its scores are masked).
@@ -298,6 +332,9 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
     const long ts = (long)NHG * d.p + (long)d.hg * d.tiles;
     const long w0 = ((ts + 1) * NWe - 1) / T;
     const long w1 = ((ts + d.tiles) * NWe - 1) / T;
+    // every piece of a segment records how many there are (the same value),
+    // so the combine launch reads one word instead of re-deriving the split
+    if (lane == 0) a.seg_np[d.s * NHG + d.hg] = (int)(w1 - w0 + 1);
     if (w0 == w1) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -372,17 +409,24 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
       finalize(prev);
     }
     if (k == 0 || dc.j == 0) {
-      // the segment's query rows, straight from global memory into the MFMA
-      // operand registers: row r = rg*ROWS + i -> (pos, gi) = (r / G, r % G);
-      // rows past G*B re-read the last real row (never written out)
+      // the segment's query rows into the MFMA operand registers: from the
+      // slot's query region (16-row segments), else straight from global
+      // memory: row r = rg*ROWS + i -> (pos, gi) = (r / G, r % G); rows past
+      // G*B re-read the last real row (never written out)
       const int g = dc.hg / a.n_rg, rg = dc.hg % a.n_rg;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const int rr = min(rg * ROWS + rt * 16 + lr, R - 1);
-        const int pos = rr / a.G, gi = rr % a.G;
-        const uint16_t* qp = a.q + ((size_t)(dc.s * a.B + pos) * a.Hq + g * a.G + gi) * D;
+        if constexpr (Gm::QLDS) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = ld_bf16x8(qp + (lg + 4 * ks) * 8);
+          for (int ks = 0; ks < KS; ++ks)
+            qf[rt][ks] = __builtin_bit_cast(bf16x8, *(const lds_u32x4*)(slot + 2 * KV + eoff<D>(lr, lg + 4 * ks)));
+        } else {
+          const int rr = min(rg * ROWS + rt * 16 + lr, R - 1);
+          const int pos = rr / a.G, gi = rr % a.G;
+          const uint16_t* qp = a.q + ((size_t)(dc.s * a.B + pos) * a.Hq + g * a.G + gi) * D;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) qf[rt][ks] = ld_bf16x8(qp + (lg + 4 * ks) * 8);
+        }
         m_run[rt] = -INFINITY;
         l_run[rt] = 0.f;
 #pragma unroll
@@ -485,8 +529,10 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
 
   // the stream: tiles 0..n-1; loads run NR-1 tiles ahead (past the end
   // they repeat the last tile into the idle slot)
+  // a tile carries its segment's query rows when it starts the segment or
+  // the wave's range (the first tile, kt = 0, may start mid-segment)
   auto next_dma = [&](lds_u16* slot, int kt) INL {
-    dma_tile(slot, dd);
+    dma_tile(slot, dd, kt == 0 || dd.j == 0);
     if (kt + 1 < n) advance(dd);
   };
 #pragma unroll
@@ -522,46 +568,24 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   wait_vm<0>();   // no load may land in LDS after the wave is gone
 }
 
-// Merge the partials of segments split over several waves.
+// Merge the partials of segments split over several waves.  One workgroup
+// per segment; the stream kernel recorded each segment's piece count, and
+// segments in one piece (written directly) return at once.
+constexpr int kCombineThreads = 128;
+
 template <int D, int RT>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
   constexpr int ROWS = 16 * RT;
   if (a.gate != nullptr && *a.gate <= 0) return;
-  const int NHG = a.Hkv * a.n_rg, nB = (a.B + kKT - 1) / kKT;
+  const int NHG = a.Hkv * a.n_rg;
   const int seg = blockIdx.x;
+  const int pieces = a.seg_np[seg];
+  if (pieces <= 1) return;
   const int s = seg / NHG, hg = seg % NHG;
   const int g = hg / a.n_rg, rg = hg % a.n_rg;
-  // the tiles of all sequences, and of those before s
-  __shared__ int s_red[2][4];
-  int all = 0, before = 0;
-  for (int i = threadIdx.x; i < a.S; i += 256) {
-    const int t = (a.prefix_len[i] + kKT - 1) / kKT + nB;
-    all += t;
-    before += i < s ? t : 0;
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    all += __shfl_xor(all, off, 64);
-    before += __shfl_xor(before, off, 64);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    s_red[0][threadIdx.x >> 6] = all;
-    s_red[1][threadIdx.x >> 6] = before;
-  }
-  __syncthreads();
-  all = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
-  before = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-  const long T = (long)NHG * all;
-  const long NW = min((long)a.grid, max(1L, T / 64));
-  const int tiles = (a.prefix_len[s] + kKT - 1) / kKT + nB;
-  const long ts = (long)NHG * before + (long)hg * tiles;
-  const long w0 = ((ts + 1) * NW - 1) / T;
-  const long w1 = ((ts + tiles) * NW - 1) / T;
-  const int pieces = (int)(w1 - w0 + 1);
-  if (pieces == 1) return;
   const int R = a.G * a.B;
   const size_t base = (size_t)seg * a.maxp;
-  for (int idx = threadIdx.x; idx < ROWS * (D / 8); idx += 256) {
+  for (int idx = threadIdx.x; idx < ROWS * (D / 8); idx += kCombineThreads) {
     const int row = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
     const int rr = rg * ROWS + row;
     if (rr >= R) continue;
@@ -601,12 +625,13 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
   p.n_rg = (R + 16 * p.RT - 1) / (16 * p.RT);
   const long max_seg_tiles = ((long)max_pages * page_size + kKT - 1) / kKT + (B + kKT - 1) / kKT;
   p.maxp = (int)((max_seg_tiles + 63) / 64 + 1);
-  const int slot_bytes = 2 * kKT * D * 2;
+  const int slot_bytes = attn_slot_bytes(D, p.RT);
   const int waves_per_cu = std::max(1, std::min(kMaxWavesPerCU, kLdsPerCU / (kRing * slot_bytes)));
   p.grid = kCUs * waves_per_cu;
   const size_t slots = (size_t)S * Hkv * p.n_rg * p.maxp * 16 * p.RT;
   p.o_bytes = (slots * D * sizeof(float) + 255) & ~(size_t)255;
-  p.ws_bytes = p.o_bytes + slots * sizeof(float2);
+  p.ml_bytes = (slots * sizeof(float2) + 255) & ~(size_t)255;
+  p.ws_bytes = p.o_bytes + p.ml_bytes + (size_t)S * Hkv * p.n_rg * sizeof(int32_t);
   return p;
 }
 
@@ -616,7 +641,7 @@ static hipError_t launch_dr(const AttnPlan& p, const AttnArgs& a, hipStream_t st
     attn_stream_kernel<D, RT, kRing, true><<<p.grid, 64, 0, st>>>(a);
   else
     attn_stream_kernel<D, RT, kRing, false><<<p.grid, 64, 0, st>>>(a);
-  attn_combine_kernel<D, RT><<<a.S * a.Hkv * p.n_rg, 256, 0, st>>>(a);
+  attn_combine_kernel<D, RT><<<a.S * a.Hkv * p.n_rg, kCombineThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ struct AttnArgs {
   uint16_t* out;
   float* part_o;   // [S*NHG*maxp][rows][D] unnormalised sums of split segments
   float2* part_ml; // [S*NHG*maxp][rows] (max, sum), log2 units
+  int32_t* seg_np; // [S*NHG] pieces of each segment in this launch (1: not split)
   int S, B, Hq, Hkv, G, P, max_pages;
   int n_rg;        // row groups per kv head (rows = G*B split in 16*RT)
   int maxp;        // partial slots per segment
@@ -38,7 +39,7 @@ struct AttnArgs {
 
 struct AttnPlan {
   int D, RT, n_rg, maxp, grid;
-  size_t o_bytes, ws_bytes;  // workspace: part_o | part_ml
+  size_t o_bytes, ml_bytes, ws_bytes;  // workspace: part_o | part_ml | seg_np
 };
 
 AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size,
