@@ -6,41 +6,57 @@
 // Optimizations").  Here the LM head stores the listed rows' logits
 // (lmhead_tile_kernel, store mode) and this kernel draws each row's token:
 //   * candidates are the finite logits other than the mask token's, ranked
-//     by logit, higher first, the lower id first among equal logits;
+//     by logit, higher first, the lower id first among equal logits (-0 and
+//     +0 are equal);
 //   * top_k > 0 keeps the first top_k; top_p < 1 then keeps the shortest
 //     leading run of those whose running sum of exp((l - m)/T) reaches
 //     top_p of their total (at least one token);
 //   * the token is drawn from softmax(l/T) over the kept set with the same
 //     block draw as the fused sampler (Philox4x32-10, counter (chunk, row,
 //     step, 0); per 16-column block an inverse-CDF candidate and a Gumbel
-//     value at the block's log-sum-exp; the largest Gumbel wins), the other
-//     tokens having zero weight; the confidence is the drawn token's
-//     probability at temperature 1.  A row without a candidate gets the
-//     mask token with confidence 0.
+//     value at the block's log-sum-exp; the largest Gumbel wins, the lower
+//     candidate on equal values), the other tokens having zero weight; the
+//     confidence is the drawn token's probability at temperature 1.  A row
+//     without a candidate gets the mask token with confidence 0.
 //
-// One workgroup of 1024 threads per listed row; the ranking is never
-// sorted as a whole.  Passes over the row (16-byte loads, several in flight
-// per thread):
+// One workgroup of 512 threads per listed row, two workgroups per CU, so
+// that one row's scans and barriers overlap another row's streaming.
+// Passes over the row:
 //   1. the row maximum m (read from the LM head's partial row maxima when
 //      the caller passes them: the round does);
-//   2. (filters only) a histogram over 4096 value bins below m, bin =
-//      floor((m - l) log2(e) / T * 32) (the last bin takes everything
-//      further down), with per bin the candidate count (top-k) and the sum
-//      of exp((l - m)/T) in 2^-40 fixed point (top-p: integer sums, so the
-//      boundary does not depend on the order of the atomic adds).  The bin
-//      is a monotone function of the logit, so every bin holds a run of
-//      the ranking;
+//   2. (filters only) a histogram over 4096 value bins below m: with
+//      d = (m - x) log2(e) / T * 128, bin = floor(d), the last bin
+//      taking everything further down (below 2^-32 of the maximum's mass;
+//      its members are summed in registers, so they do not all queue on
+//      one LDS address).  Per bin: the candidate count (top-k), and the sum
+//      of the members' masses exp((x - m)/T) in units of 2^-31 of the bin's
+//      upper edge, floor(2^(31 - frac(d)/128)) each (top-p).  The sums are
+//      integers, so they do not depend on the order of the atomic adds; a
+//      bin's mass relative to the maximum's is its sum times
+//      2^(-31 - bin/128), and the scans add those in float64 in a fixed
+//      order.  The pass also sums exp(x - m) for the confidence;
 //   3. a scan over the bins finds the bin holding a boundary (the top_k-th
 //      candidate, or the first candidate whose running mass reaches top_p
-//      of the kept total); one more pass gathers that bin's candidates
-//      into LDS as (key, ~id), a bitonic sort puts them in ranking order
-//      and a scan over them gives the boundary candidate.  A bin of more
-//      than 2048 candidates (long runs of equal logits, extreme
-//      temperatures) is resolved instead by a radix select over the
+//      of the kept total).  With one filter alone the boundary inside that
+//      bin is found during the draw (below); with both, one more pass
+//      gathers the bin's candidates into LDS as (key, ~id), a bitonic sort
+//      puts them in ranking order and a scan over them gives the boundary.
+//      A bin of more than 2048 candidates (long runs of equal logits,
+//      extreme temperatures) is resolved by a radix select over the
 //      order-preserving 32-bit image of its logits (8-bit digits, four
 //      passes, then a pass in id order for ties);
-//   4. the block draw over the kept set, which also sums exp(l - m) for
-//      the confidence.
+//   4. the draw, one 32-token chunk (both of its blocks) per thread at a
+//      time: per block S = the sum over its kept members of
+//      exp((x - m)/T) (the row maximum as the common reference, so no block
+//      maximum is needed) and G = log2 S + a Gumbel variable from the
+//      block's Philox word; the largest G wins (the lower block on equal
+//      values), and only the winning block's inverse CDF is evaluated, at
+//      the end.  With one filter alone a block holding a member of the
+//      boundary bin is deferred (per-wave lists, one ballot per block, the
+//      block's 16 logits staged in LDS while there is room); after the pass
+//      the bin's members are gathered from the deferred blocks into LDS,
+//      sorted, the boundary found, and the deferred blocks drawn.  Without
+//      a filter this pass also sums exp(x - m) for the confidence.
 // Without a filter only passes 1 and 4 run.
 #include <climits>
 
@@ -51,19 +67,33 @@ namespace dbd {
 
 namespace {
 
-constexpr int kSfThreads = 1024;
+constexpr int kSfThreads = 512;
 constexpr int kSfWaves = kSfThreads / 64;
-constexpr int kSfBins = 4096;             // value bins below the row maximum
-constexpr float kSfBinsPerLog2 = 32.f;    // bins per unit of (m - l) log2(e) / T
-constexpr int kSfCap = 2048;              // candidates of one bin sorted in LDS
-constexpr float kSfFix = 1099511627776.f; // 2^40: fixed-point scale of the masses
+constexpr int kSfBins = 4096;                  // value bins below the row maximum
+constexpr int kSfPer = kSfBins / kSfThreads;   // scan slots per thread
+constexpr float kSfBinsPerLog2 = 128.f;        // bins per unit of (m - l) log2(e) / T: the
+                                               // bins reach 2^-32 of the maximum's mass
+constexpr int kSfCap = 2048;                   // candidates of one bin sorted in LDS
+constexpr int kSfWaveDef = kSfBins / kSfWaves; // a wave's deferred blocks
+constexpr int kSfWaveStage = kSfBins * 2 / 16 / kSfWaves;   // of those, kept in LDS (64)
+constexpr float kSfUnitLog2 = 31.f;            // a member's mass: 2^31 at its bin's upper edge
+constexpr float kFltMax = 3.402823466e38f;
 
+template <bool B>
+struct Tag {
+  static constexpr bool value = B;
+};
+
+// order-preserving image of a float (-0 taken as +0)
 __device__ __forceinline__ uint32_t okey(float f) {
-  const uint32_t b = __float_as_uint(f);
+  const uint32_t b = __float_as_uint(f + 0.f);
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);   // larger float -> larger key
 }
 __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+__device__ __forceinline__ uint64_t rank_pair(float x, int v) {
+  return ((uint64_t)okey(x) << 32) | (uint32_t)~(uint32_t)v;
 }
 
 // the same Philox4x32-10 and uniforms as the fused sampler
@@ -87,8 +117,17 @@ __device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src_lane) {
   const uint32_t lo = __shfl((uint32_t)v, src_lane, 64), hi = __shfl((uint32_t)(v >> 32), src_lane, 64);
   return ((uint64_t)hi << 32) | lo;
 }
+__device__ __forceinline__ uint64_t to_bits(uint64_t v) { return v; }
+__device__ __forceinline__ uint64_t to_bits(double v) { return (uint64_t)__double_as_longlong(v); }
+__device__ __forceinline__ void from_bits(uint64_t b, uint64_t& v) { v = b; }
+__device__ __forceinline__ void from_bits(uint64_t b, double& v) { v = __longlong_as_double((long long)b); }
 
-// block-wide reduction over 1024 threads (16 waves) through LDS
+// lanes below this one with a set bit in `bal`
+__device__ __forceinline__ int lanes_below(uint64_t bal) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+}
+
+// block-wide reduction over the workgroup through LDS
 template <typename F>
 __device__ float block_reduce(float v, F op, float* s_tmp) {
 #pragma unroll
@@ -102,23 +141,33 @@ __device__ float block_reduce(float v, F op, float* s_tmp) {
   return r;
 }
 
+// the 16 members of block h of a chunk's 32 logits, in member order j
+// (offset 8(j/4) + 4h + j%4 in the chunk)
+__device__ __forceinline__ void half_of(const float (&lv)[32], int h, float (&x)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[4 * q + r] = lv[8 * q + 4 * h + r];
+}
+
 }  // namespace
 
-__global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
-  __shared__ uint32_t s_bc[kSfBins];     // candidates per bin
-  __shared__ uint64_t s_bm[kSfBins];     // fixed-point mass per bin
+__global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleArgs a) {
+  __shared__ uint32_t s_bc[kSfBins];     // candidates per bin; then the deferred blocks
+  __shared__ uint64_t s_bm[kSfBins];     // mass per bin in its own units
   __shared__ uint64_t s_g[kSfCap];       // one bin's candidates, (key << 32) | ~id
   __shared__ uint64_t s_w[kSfWaves];
   __shared__ float s_f[kSfWaves];
-  __shared__ int s_n, s_first, s_ndef;
+  __shared__ int s_n, s_first, s_sel, s_last;
   __shared__ uint64_t s_before;
-  __shared__ int s_sel;
   __shared__ float s_gbest[kSfWaves];
-  __shared__ int s_cbest[kSfWaves];
+  __shared__ int s_kbest[kSfWaves], s_wd[kSfWaves];
   // radix-select scratch on top of s_g: it runs only when a bin did not fit
   uint64_t* const s_h64 = s_g;                                        // [256]
-  int* const s_cnt = reinterpret_cast<int*>(s_g + 256);               // [1024]
+  int* const s_cnt = reinterpret_cast<int*>(s_g + 256);               // [kSfThreads]
   static_assert(256 * 8 + kSfThreads * 4 <= kSfCap * 8, "radix scratch must fit in the gather buffer");
+  uint32_t* const s_def = s_bc;          // the count histogram is dead by the draw
+  float* const s_stage = reinterpret_cast<float*>(s_bm);   // so are the masses: deferred blocks
 
   const int r = blockIdx.x;
   if (r >= *a.num_rows) return;
@@ -127,27 +176,54 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
   const float* l = a.logits + (size_t)r * V;
   const uint32_t rid = (uint32_t)(a.row_index ? a.row_index[r] : r);
   const float invT = a.inv_temp;
+  const bool vec = (V & 3) == 0;         // rows 16-byte aligned
+  auto fin = [](float x) { return fabsf(x) <= kFltMax; };
 
-  auto cand = [&](int v, float x) { return (v != mask) & (fabsf(x) <= 3.402823466e38f); };
-
-  // every logit of the row once; with 16-byte aligned rows (V % 4 == 0)
-  // each thread keeps four 16-byte loads in flight
+  // every logit of the row once, the mask token's as NaN (no candidate);
+  // with 16-byte aligned rows each thread keeps eight 16-byte loads in
+  // flight, the next four issued before the current four are used
   auto each = [&](auto fn) {
-    if ((V & 3) == 0) {
+    if (vec) {
       const f32x4* l4 = reinterpret_cast<const f32x4*>(l);
-      const int n4 = V >> 2;
-      auto fn4 = [&](int q, const f32x4& x) {
+      const int n4 = V >> 2, qm = mask >> 2, jm = mask & 3;
+      auto fn4 = [&](int q, f32x4 x) {
+        if (q == qm) {
+          x.x = jm == 0 ? NAN : x.x;
+          x.y = jm == 1 ? NAN : x.y;
+          x.z = jm == 2 ? NAN : x.z;
+          x.w = jm == 3 ? NAN : x.w;
+        }
         fn(4 * q, x.x); fn(4 * q + 1, x.y); fn(4 * q + 2, x.z); fn(4 * q + 3, x.w);
       };
+      constexpr int U = 4;
       int q = tid;
-      for (; q + 3 * kSfThreads < n4; q += 4 * kSfThreads) {
-        const f32x4 x0 = l4[q], x1 = l4[q + kSfThreads], x2 = l4[q + 2 * kSfThreads],
-                    x3 = l4[q + 3 * kSfThreads];
-        fn4(q, x0); fn4(q + kSfThreads, x1); fn4(q + 2 * kSfThreads, x2); fn4(q + 3 * kSfThreads, x3);
+      f32x4 cur[U];
+      bool full = q + (U - 1) * kSfThreads < n4;
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) cur[j] = l4[q + j * kSfThreads];
+      }
+      while (full) {
+        const int qn = q + U * kSfThreads;
+        const bool nfull = qn + (U - 1) * kSfThreads < n4;
+        f32x4 nx[U];
+        if (nfull) {
+#pragma unroll
+          for (int j = 0; j < U; ++j) nx[j] = l4[qn + j * kSfThreads];
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) fn4(q + j * kSfThreads, cur[j]);
+#pragma unroll
+        for (int j = 0; j < U; ++j) cur[j] = nx[j];
+        q = qn;
+        full = nfull;
       }
       for (; q < n4; q += kSfThreads) fn4(q, l4[q]);
     } else {
-      for (int v = tid; v < V; v += kSfThreads) fn(v, l[v]);
+      for (int v = tid; v < V; v += kSfThreads) {
+        const float x = l[v];
+        fn(v, v == mask ? NAN : x);
+      }
     }
   };
 
@@ -159,8 +235,8 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     for (int t = tid; t < nteam; t += kSfThreads)
       mt = fmaxf(mt, fmaxf(a.pmax[(size_t)r * nteam + t], a.pmax2[(size_t)r * nteam + t]));
   } else {
-    each([&](int v, float x) {
-      if (cand(v, x)) mt = fmaxf(mt, x);
+    each([&](int, float x) {
+      if (fin(x)) mt = fmaxf(mt, x);
     });
   }
   const float m = block_reduce(mt, [](float x, float y) { return fmaxf(x, y); }, s_f);
@@ -172,57 +248,83 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     return;
   }
 
-  const float c2 = invT * kLog2e;               // exp((l - m)/T) = 2^((l - m) c2)
+  const float c2 = invT * kLog2e;               // exp((l - m)/T) = 2^(l c2 - m c2)
   const float c3 = c2 * kSfBinsPerLog2;
-  auto bin_of = [&](float x) -> int {
-    const float d = fmaxf((m - x) * c3, 0.f);   // >= 0 (m is the maximum), monotone in x
-    return d < (float)(kSfBins - 1) ? (int)d : kSfBins - 1;
+  const float mc2 = m * c2, ml = m * kLog2e;
+  auto bin_d = [&](float x) { return fmaxf((m - x) * c3, 0.f); };        // monotone in x, +inf at -inf
+  auto bin_of = [&](float x) -> int { return (int)fminf(floorf(bin_d(x)), (float)(kSfBins - 1)); };
+  // a candidate's mass in units of 2^-31 of its bin's upper edge
+  auto mass_in_bin = [&](float x) -> uint32_t {
+    const float d = bin_d(x);
+    const float bf = fminf(floorf(d), (float)(kSfBins - 1));
+    return (uint32_t)fast_exp2(fmaf(d - bf, -1.f / kSfBinsPerLog2, kSfUnitLog2));
   };
-  auto mass_of = [&](float x) -> uint64_t {
-    return (uint64_t)(fast_exp2((x - m) * c2) * kSfFix);
+  // one unit of bin b relative to the maximum's mass
+  auto bin_scale = [](int b) -> double {
+    return exp2(-(double)b / (double)kSfBinsPerLog2 - (double)kSfUnitLog2);
+  };
+  // the largest finite float whose bin is at least b (FLT_MAX when every
+  // one is): bin_of(x) < b exactly when x is above it
+  auto bin_floor = [&](int b) -> float {
+    if (bin_of(kFltMax) >= b) return kFltMax;
+    uint32_t lo = okey(-kFltMax), hi = okey(kFltMax);
+    while (hi - lo > 1u) {                    // bin_of(key_float(lo)) >= b > bin_of(key_float(hi))
+      const uint32_t mid = lo + (hi - lo) / 2u;
+      if (bin_of(key_float(mid)) >= b) lo = mid;
+      else hi = mid;
+    }
+    return key_float(lo);
   };
 
-  // exclusive prefix over the workgroup (thread order) of a 64-bit value;
-  // `total` = the sum over all threads
-  auto block_scan = [&](uint64_t v, uint64_t& total) -> uint64_t {
-    uint64_t x = v;
+  // exclusive prefix over the workgroup (thread order) of a value held per
+  // thread, uint64_t or double; `total` = the sum over all threads.  The
+  // additions run in a fixed order, so double sums are the same on every run.
+  auto block_scan = [&](auto v, auto& total) {
+    using T = decltype(v);
+    T x = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const uint64_t y = shfl_u64(x, lane >= off ? lane - off : lane);
-      x += lane >= off ? y : 0ull;
+      T y;
+      from_bits(shfl_u64(to_bits(x), lane >= off ? lane - off : lane), y);
+      if (lane >= off) x += y;
     }
+    T excl;
+    from_bits(shfl_u64(to_bits(x), lane > 0 ? lane - 1 : 0), excl);
+    if (lane == 0) excl = T(0);
     __syncthreads();
-    if (lane == 63) s_w[wave] = x;
+    if (lane == 63) s_w[wave] = to_bits(x);
     __syncthreads();
-    uint64_t run = 0ull, tot = 0ull;
+    T run = T(0), tot = T(0);
     for (int w = 0; w < kSfWaves; ++w) {
-      const uint64_t t = s_w[w];
-      run += w < wave ? t : 0ull;
+      T t;
+      from_bits(s_w[w], t);
+      if (w < wave) run += t;
       tot += t;
     }
     total = tot;
-    return run + x - v;
+    return run + excl;
   };
 
-  // first slot s of [0, n) (four per thread, thread-major) with val(s) > 0
+  // first slot s of [0, n) (kSfPer per thread, thread-major) with val(s) > 0
   // whose inclusive running sum reaches tgt, or -1; `before` = the running
   // sum ahead of it, `total` = the sum of all slots
-  auto find_first = [&](auto val, int n, uint64_t tgt, uint64_t& before, uint64_t& total) -> int {
-    uint64_t v[4], sum = 0ull;
+  auto find_first = [&](auto val, int n, auto tgt, auto& before, auto& total) -> int {
+    using T = decltype(tgt);
+    T v[kSfPer], sum = T(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = 4 * tid + j;
-      v[j] = s < n ? val(s) : 0ull;
+    for (int j = 0; j < kSfPer; ++j) {
+      const int s = kSfPer * tid + j;
+      v[j] = s < n ? val(s) : T(0);
       sum += v[j];
     }
     if (tid == 0) s_first = INT_MAX;
-    uint64_t run = block_scan(sum, total);
+    T run = block_scan(sum, total);
     int mine = -1;
-    uint64_t mb = 0ull;
+    T mb = T(0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (mine < 0 && v[j] > 0ull && run + v[j] >= tgt) {
-        mine = 4 * tid + j;
+    for (int j = 0; j < kSfPer; ++j) {
+      if (mine < 0 && v[j] > T(0) && run + v[j] >= tgt) {
+        mine = kSfPer * tid + j;
         mb = run;
       }
       run += v[j];
@@ -230,28 +332,29 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     if (mine >= 0) atomicMin(&s_first, mine);
     __syncthreads();
     const int f = s_first;
-    if (mine >= 0 && mine == f) s_before = mb;
+    if (mine >= 0 && mine == f) s_before = to_bits(mb);
     __syncthreads();
-    before = s_before;
+    from_bits(s_before, before);
     __syncthreads();
     return f == INT_MAX ? -1 : f;
   };
 
-  // s_g[0, n) (n <= kSfCap) into ranking order by a bitonic sort
-  auto sort_list = [&](int n) {
+  // list[0, n) (n <= kSfCap) into ranking order (descending pairs) by a
+  // bitonic sort
+  auto sort_list = [&](uint64_t* list, int n) {
     int n2 = 1;
     while (n2 < n) n2 <<= 1;
-    for (int i = n + tid; i < n2; i += kSfThreads) s_g[i] = 0ull;   // below every candidate
+    for (int i = n + tid; i < n2; i += kSfThreads) list[i] = 0ull;   // below every candidate
     __syncthreads();
     for (int k = 2; k <= n2; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
         for (int i = tid; i < n2; i += kSfThreads) {
           const int p = i ^ j;
           if (p > i) {
-            const uint64_t x = s_g[i], y = s_g[p];
+            const uint64_t x = list[i], y = list[p];
             if ((i & k) == 0 ? x < y : x > y) {
-              s_g[i] = y;
-              s_g[p] = x;
+              list[i] = y;
+              list[p] = x;
             }
           }
         }
@@ -259,35 +362,36 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
       }
     }
   };
-  // the candidates of bin b that pred admits, into s_g in ranking order
-  // (descending (key, ~id)); returns their number, > kSfCap if they did not
-  // fit (s_g then holds no list)
+  // the candidates of bin b that pred admits, into s_g in ranking order;
+  // returns their number, > kSfCap if they did not fit (s_g then holds no
+  // list)
   auto gather_sort = [&](int b, auto pred) -> int {
-    // every thread has read any earlier value of s_n (the merged draw's
-    // count, say) before thread 0 clears it
+    // every thread has read any earlier value of s_n before thread 0
+    // clears it
     __syncthreads();
     if (tid == 0) s_n = 0;
     __syncthreads();
     each([&](int v, float x) {
-      if (!cand(v, x) || bin_of(x) != b || !pred(v, x)) return;
+      if (!fin(x) || bin_of(x) != b || !pred(v, x)) return;
       const int i = atomicAdd(&s_n, 1);
-      if (i < kSfCap) s_g[i] = ((uint64_t)okey(x) << 32) | (uint32_t)~(uint32_t)v;
+      if (i < kSfCap) s_g[i] = rank_pair(x, v);
     });
     __syncthreads();
     const int n = s_n;
     if (n > kSfCap) return n;
-    sort_list(n);
+    sort_list(s_g, n);
     return n;
   };
   auto entry_key = [&](int i) { return (uint32_t)(s_g[i] >> 32); };
   auto entry_id = [&](int i) { return (int)~(uint32_t)s_g[i]; };
 
-  // radix select among the candidates `in` admits: the first, in ranking
-  // order, whose running count (use_mass false) or fixed-point mass reaches
-  // `need`.  Four passes of 8-bit digits of the order-preserving key, then
-  // the tied candidates (key == the selected key) share one value, so the
-  // boundary is the c-th of them in id order, c = need left / their mass
-  // (rounded up); a pass counts them per thread over contiguous id ranges.
+  // radix select among the candidates `in` admits (all in one bin): the
+  // first, in ranking order, whose running count (use_mass false) or mass in
+  // the bin's units reaches `need`.  Four passes of 8-bit digits of the
+  // order-preserving key, then the tied candidates (key == the selected key)
+  // share one value, so the boundary is the c-th of them in id order,
+  // c = need left / their mass (rounded up); a pass counts them per thread
+  // over contiguous id ranges.
   auto radix = [&](auto in, bool use_mass, uint64_t need, uint32_t& key_out, int& id_out) {
     uint32_t prefix = 0u, pmask = 0u;
     uint64_t rem = need;
@@ -295,15 +399,16 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
       for (int i = tid; i < 256; i += kSfThreads) s_h64[i] = 0ull;
       __syncthreads();
       each([&](int v, float x) {
+        if (!fin(x)) return;
         const uint32_t key = okey(x);
         if (!in(v, x) || (key & pmask) != prefix) return;
         atomicAdd(reinterpret_cast<unsigned long long*>(&s_h64[(key >> shift) & 255]),
-                  (unsigned long long)(use_mass ? mass_of(x) : 1ull));
+                  (unsigned long long)(use_mass ? mass_in_bin(x) : 1u));
       });
       __syncthreads();
       uint64_t before, total;
       // slot i = digit 255 - i: from the largest digit down
-      int sl = find_first([&](int i) { return s_h64[255 - i]; }, 256, rem, before, total);
+      int sl = find_first([&](int i) -> uint64_t { return s_h64[255 - i]; }, 256, rem, before, total);
       if (sl < 0) {      // not reachable: the need is within the admitted total
         sl = 0;
         before = 0ull;
@@ -312,30 +417,30 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
       prefix |= (uint32_t)(255 - sl) << shift;
       pmask |= 255u << shift;
     }
-    const uint64_t w = use_mass ? mass_of(key_float(prefix)) : 1ull;
+    const uint64_t w = use_mass ? mass_in_bin(key_float(prefix)) : 1ull;
     uint64_t c = w == 0ull ? 1ull : (rem + w - 1ull) / w;
     c = c < 1ull ? 1ull : c;
     const int per = (V + kSfThreads - 1) / kSfThreads;
     const int v0 = tid * per, v1 = min(V, v0 + per);
-    int cnt = 0;
-    for (int v = v0; v < v1; ++v) {
+    auto tie = [&](int v) {
       const float x = l[v];
-      cnt += (in(v, x) && okey(x) == prefix) ? 1 : 0;
-    }
+      return v != mask && fin(x) && in(v, x) && okey(x) == prefix;
+    };
+    int cnt = 0;
+    for (int v = v0; v < v1; ++v) cnt += tie(v) ? 1 : 0;
     s_cnt[tid] = cnt;
     __syncthreads();
     uint64_t before, total;
-    int t = find_first([&](int i) { return (uint64_t)s_cnt[i]; }, kSfThreads, c, before, total);
+    int t = find_first([&](int i) -> uint64_t { return (uint64_t)s_cnt[i]; }, kSfThreads, c, before, total);
     if (t < 0) {       // fewer ties than c (not reachable): the last tie
-      t = find_first([&](int i) { return (uint64_t)s_cnt[i]; }, kSfThreads, total, before, total);
+      t = find_first([&](int i) -> uint64_t { return (uint64_t)s_cnt[i]; }, kSfThreads, total, before, total);
       c = total;
     }
     if (tid == t) {
       uint64_t k = c - before;
       int idc = v0;
       for (int v = v0; v < v1; ++v) {
-        const float x = l[v];
-        if (!(in(v, x) && okey(x) == prefix)) continue;
+        if (!tie(v)) continue;
         idc = v;
         if (--k == 0ull) break;
       }
@@ -347,49 +452,80 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
     __syncthreads();
   };
 
-  // the top-p boundary among the n sorted candidates of its bin: the first
-  // whose running mass reaches rem
-  auto select_sorted = [&](int n, uint64_t rem, uint32_t& key_out, int& id_out) {
+  // the boundary among the n sorted candidates of one bin: the first whose
+  // running mass (in the bin's units) reaches need
+  auto select_sorted = [&](int n, uint64_t need, uint32_t& key_out, int& id_out) {
     uint64_t b2, t2;
-    int e = find_first([&](int i) { return mass_of(key_float(entry_key(i))); }, n, rem, b2, t2);
+    int e = find_first([&](int i) -> uint64_t { return mass_in_bin(key_float(entry_key(i))); }, n, need, b2,
+                       t2);
     e = e < 0 ? max(n - 1, 0) : e;      // n >= 1: the bin has mass
     key_out = entry_key(e);
     id_out = entry_id(e);
   };
 
-  // kept-set tests: key above the boundary key, or equal to it with id at
-  // most the boundary id; key 0 with id V keeps everything
+  // boundary pairs (key, id) of each filter: a candidate is kept when its
+  // pair is at least the boundary's in ranking order; key 0 keeps all
   uint32_t kk = 0u, pk = 0u;
   int kid = V, pid = V;
-  auto keep_k = [&](int v, uint32_t key) { return v != mask && (key > kk || (key == kk && v <= kid)); };
+  auto keep_k = [&](int v, float x) {
+    const uint32_t key = okey(x);
+    return key > kk || (key == kk && v <= kid);
+  };
   const bool use_k = a.top_k > 0 && a.top_k < V - 1;
   const bool use_p = a.top_p < 1.f;
-  // one filter alone: its boundary bin and the mass (top-p) or the rank
-  // (top-k) needed inside it, resolved during the draw pass (-1: not used)
+  // one filter alone: its boundary bin and the rank (top-k) or the mass in
+  // the bin's units (top-p) needed inside it, resolved during the draw pass
+  // (-1: not used)
   int mbin = -1, mrank = 0;
   uint64_t mrem = 0ull;
+  float s1 = 0.f;                        // sum over the candidates of exp(l - m)
 
   if (use_k || use_p) {
-    // ---- pass 2: the value-bin histogram
+    // ---- pass 2: the value-bin histogram, and the confidence's sum
     for (int i = tid; i < kSfBins; i += kSfThreads) {
       s_bc[i] = 0u;
       s_bm[i] = 0ull;
     }
     __syncthreads();
-    each([&](int v, float x) {
-      if (!cand(v, x)) return;
-      const int b = bin_of(x);
-      if (use_k) atomicAdd(&s_bc[b], 1u);
-      if (use_p) atomicAdd(reinterpret_cast<unsigned long long*>(&s_bm[b]),
-                           (unsigned long long)mass_of(x));
-    });
+    // a non-candidate enters as -inf: no exp(x - m), no mass, no count.  The
+    // last bin (everything further down) can hold most of a row: its
+    // members are summed in registers and added once per thread, so they
+    // do not all queue on one LDS address.
+    auto hist = [&](auto with_k, auto with_p) {
+      uint32_t tail_n = 0u;
+      uint64_t tail_m = 0ull;
+      each([&](int, float x) {
+        const bool cd = fin(x);
+        const float xs = cd ? x : -INFINITY;
+        s1 += fast_exp2(fmaf(xs, kLog2e, -ml));
+        const float d = bin_d(xs);
+        const float bf = fminf(floorf(d), (float)(kSfBins - 1));
+        const int b = (int)bf;
+        const uint32_t u = (uint32_t)fast_exp2(fmaf(d - bf, -1.f / kSfBinsPerLog2, kSfUnitLog2));
+        if (b < kSfBins - 1) {
+          if constexpr (decltype(with_k)::value) atomicAdd(&s_bc[b], cd ? 1u : 0u);
+          if constexpr (decltype(with_p)::value)
+            atomicAdd(reinterpret_cast<unsigned long long*>(&s_bm[b]), (unsigned long long)u);
+        } else {
+          tail_n += cd ? 1u : 0u;
+          tail_m += u;
+        }
+      });
+      if constexpr (decltype(with_k)::value)
+        if (tail_n) atomicAdd(&s_bc[kSfBins - 1], tail_n);
+      if constexpr (decltype(with_p)::value)
+        if (tail_m) atomicAdd(reinterpret_cast<unsigned long long*>(&s_bm[kSfBins - 1]), (unsigned long long)tail_m);
+    };
+    if (use_k && use_p) hist(Tag<true>{}, Tag<true>{});
+    else if (use_k) hist(Tag<true>{}, Tag<false>{});
+    else hist(Tag<false>{}, Tag<true>{});
     __syncthreads();
 
     int bk = kSfBins, rk = 0, listed = -1;     // top-k boundary bin, rank in it, sorted bin
     if (use_k) {
       uint64_t before, total;
-      const int b = find_first([&](int s) { return (uint64_t)s_bc[s]; }, kSfBins, (uint64_t)a.top_k,
-                               before, total);
+      const int b = find_first([&](int s) -> uint64_t { return s_bc[s]; }, kSfBins, (uint64_t)a.top_k, before,
+                               total);
       if (b >= 0) {                            // else fewer candidates than top_k: keep all
         bk = b;
         rk = a.top_k - (int)before;
@@ -397,212 +533,339 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
           mbin = bk;
           mrank = rk;
         } else {
-        const int n = gather_sort(bk, [](int, float) { return true; });
-        if (n <= kSfCap) {
-          kk = entry_key(rk - 1);
-          kid = entry_id(rk - 1);
-          listed = bk;
-        } else {
-          radix([&](int v, float x) { return cand(v, x) && bin_of(x) == bk; }, false, (uint64_t)rk, kk,
-                kid);
-        }
+          const int n = gather_sort(bk, [](int, float) { return true; });
+          if (n <= kSfCap) {
+            kk = entry_key(rk - 1);
+            kid = entry_id(rk - 1);
+            listed = bk;
+          } else {
+            radix([&](int, float x) { return bin_of(x) == bk; }, false, (uint64_t)rk, kk, kid);
+          }
         }
       }
     }
     if (use_p) {
-      // mass of the kept part of the top-k boundary bin
+      // mass of the kept part of the top-k boundary bin, in its units
       uint64_t massk = 0ull;
       if (bk < kSfBins) {
         uint64_t part = 0ull;
         if (listed == bk) {
-          for (int i = tid; i < rk; i += kSfThreads) part += mass_of(key_float(entry_key(i)));
+          for (int i = tid; i < rk; i += kSfThreads) part += mass_in_bin(key_float(entry_key(i)));
         } else {
           each([&](int v, float x) {
-            if (cand(v, x) && bin_of(x) == bk && keep_k(v, okey(x))) part += mass_of(x);
+            if (fin(x) && bin_of(x) == bk && keep_k(v, x)) part += mass_in_bin(x);
           });
         }
         block_scan(part, massk);
       }
-      auto pval = [&](int s) -> uint64_t { return s < bk ? s_bm[s] : (s == bk ? massk : 0ull); };
-      uint64_t before, Z;
-      find_first(pval, kSfBins, ~0ull, before, Z);          // the kept total
-      uint64_t tgt = 0ull;
-      if (a.top_p > 0.f) {
-        const double t = ceil((double)a.top_p * (double)Z);
-        tgt = t >= (double)Z ? Z : (uint64_t)t;
+      auto units = [&](int s) -> uint64_t { return s < bk ? s_bm[s] : (s == bk ? massk : 0ull); };
+      auto pval = [&](int s) -> double { return (double)units(s) * bin_scale(s); };
+      double before, Z;
+      find_first(pval, kSfBins, (double)INFINITY, before, Z);      // the kept total
+      const double tgt = a.top_p > 0.f ? fmin((double)a.top_p * Z, Z) : 0.0;
+      int bp = find_first(pval, kSfBins, tgt, before, Z);
+      uint64_t rem;
+      if (bp >= 0) {
+        const uint64_t u = units(bp);
+        const double need = ceil((tgt - before) / bin_scale(bp));
+        rem = need < 1.0 ? 1ull : (need >= (double)u ? u : (uint64_t)need);
+      } else {
+        // the running sums fell short of a target equal to the total by
+        // rounding: the boundary is the last candidate with mass
+        if (tid == 0) s_last = -1;
+        __syncthreads();
+        int lastb = -1;
+        for (int s = tid; s < kSfBins; s += kSfThreads)
+          if (units(s) > 0ull) lastb = s;
+        if (lastb >= 0) atomicMax(&s_last, lastb);
+        __syncthreads();
+        bp = max(s_last, 0);                   // >= 0: the maximum has mass
+        rem = units(bp);
+        __syncthreads();
       }
-      // >= 0: the maximum is kept and has mass 2^40
-      const int bp = find_first(pval, kSfBins, tgt, before, Z);
-      const uint64_t rem = tgt - before;
-      int n = kSfCap + 1;
       if (!use_k) {
         mbin = bp;
         mrem = rem;
       } else {
-      if (bp == bk && listed == bk) n = rk;                  // the sorted top-k part
-      else if (bp != bk) n = gather_sort(bp, [](int, float) { return true; });
-      if (n <= kSfCap) {
-        select_sorted(n, rem, pk, pid);
-      } else {
-        radix([&](int v, float x) { return cand(v, x) && bin_of(x) == bp && keep_k(v, okey(x)); },
-              true, rem, pk, pid);
-      }
+        int n = kSfCap + 1;
+        if (bp == bk && listed == bk) n = rk;                  // the sorted top-k part
+        else if (bp != bk) n = gather_sort(bp, [](int, float) { return true; });
+        if (n <= kSfCap) {
+          select_sorted(n, rem, pk, pid);
+        } else {
+          radix([&](int v, float x) { return bin_of(x) == bp && keep_k(v, x); }, true, rem, pk, pid);
+        }
       }
     }
   }
-  // both kept-set tests compare (key, id) in ranking order (higher key,
-  // then lower id); as (key << 32 | ~id) that order is the unsigned one, so
-  // the two tests are one 64-bit comparison with the larger boundary pair
-  uint64_t thr = 0ull;
-  auto set_thr = [&]() {
-    thr = max(((uint64_t)kk << 32) | (uint32_t)~(uint32_t)kid,
-              ((uint64_t)pk << 32) | (uint32_t)~(uint32_t)pid);
-  };
-  set_thr();
-  auto keep = [&](int v, float x) {
-    return cand(v, x) & ((((uint64_t)okey(x) << 32) | (uint32_t)~(uint32_t)v) >= thr);
-  };
 
-  // ---- pass 4: the block draw over the kept set (log2 units as the fused
-  // sampler), and sum exp(l - m) over the candidates for the confidence
-  float gbest = -INFINITY, s1 = 0.f;
-  int cbest = 0x7fffffff;
-  const int nchunk = (V + 31) / 32;
-
-  // one 16-token half block of chunk c: x = its members' logits in log2
-  // units, -inf where not kept; wu, we = its two Philox words
-  auto draw_half = [&](const float (&x)[16], uint32_t wu, uint32_t we, int c, int h) {
-    float bm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, x[i]);
-    if (bm == -INFINITY) return;
-    const float u = sf_uniform(wu);
-    const float eg = sf_uniform(we);
-    const float bmT = bm * invT;
-    float e[16], S = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      e[i] = fast_exp2(fmaf(x[i], invT, -bmT));
-      S += e[i];
-    }
-    // the running sums never decrease and target > 0, so the members whose
-    // sum is below it are a prefix and the first member past it has weight;
-    // if rounding leaves none past it, the last member with weight
-    const float target = u * S;
-    float cum = 0.f;
-    int below = 0, last = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      cum += e[i];
-      below += cum < target ? 1 : 0;
-      last = e[i] > 0.f ? i : last;
-    }
-    const int ci = below < 16 ? below : last;
-    const float G = bmT + __log2f(S) - __log2f(-__log2f(eg));
-    const int cnd = 32 * c + 8 * (ci >> 2) + 4 * h + (ci & 3);
-    if (G > gbest || (G == gbest && cnd < cbest)) {
-      gbest = G; cbest = cnd;
+  // ---- pass 4: the block draw
+  const bool s1_in_draw = !(use_k || use_p);
+  float gbest = -INFINITY;
+  int kbest = INT_MAX;                   // 2c + h of the best block
+  // the final kept test: both boundaries are lower bounds in ranking order,
+  // so the larger pair decides, compared as a float with the id breaking
+  // ties
+  // Outside the chunk holding the boundary's id the test is one compare:
+  // ties at xb are all kept (ids below the boundary's) or all dropped
+  // (above), and x >= xb is x > xb_below, the float just below xb.
+  float xb = -INFINITY, xb_below = -INFINITY;
+  int idb = -1;
+  auto set_final = [&]() {
+    const uint64_t thr = max(((uint64_t)kk << 32) | (uint32_t)~(uint32_t)kid,
+                             ((uint64_t)pk << 32) | (uint32_t)~(uint32_t)pid);
+    if ((thr >> 32) == 0ull) {           // no boundary: every candidate
+      xb = -INFINITY;
+      xb_below = -INFINITY;
+      idb = -1;
+    } else {
+      xb = key_float((uint32_t)(thr >> 32));
+      const uint32_t u = __float_as_uint(xb);
+      xb_below = __uint_as_float(u == 0u ? 0x80000001u : (xb > 0.f ? u - 1u : u + 1u));
+      idb = (int)~(uint32_t)thr;
     }
   };
+  set_final();
+  // merged: members of bins below mbin are kept, those of bins above it are
+  // not, as the final test will say; bin_of(x) < mbin exactly when x > t_lo,
+  // bin_of(x) <= mbin exactly when x > t_hi
+  float t_lo = kFltMax, t_hi = -INFINITY;
+  if (mbin >= 0) {
+    t_lo = bin_floor(mbin);
+    t_hi = mbin + 1 < kSfBins ? bin_floor(mbin + 1) : -INFINITY;
+  }
 
-  // merged (one filter alone): the boundary bin mbin is not resolved yet.  Bins
-  // are monotone in the logit, so members of lower bins are kept and members
-  // of higher bins are not, as the final test will say; members of mbin go
-  // into s_g, and a half block holding one is deferred to s_def until the
-  // boundary inside mbin is known.
-  uint32_t* const s_def = s_bc;                 // the count histogram is dead here
-  auto draw = [&](bool merged) {
-    for (int c = tid; c < nchunk; c += kSfThreads) {
-      float lv[32];
-      if ((V & 3) == 0 && 32 * c + 32 <= V) {
-        const f32x4* p4 = reinterpret_cast<const f32x4*>(l + 32 * c);
+  const int nchunk = (V + 31) >> 5;
+  const int cmask = mask >> 5, imask = mask & 31;
+  auto philox_chunk = [&](int c, uint32_t (&w)[4]) {
+    w[0] = (uint32_t)c; w[1] = rid; w[2] = a.step; w[3] = 0u;
+    sf_philox(w[0], w[1], w[2], w[3], a.key0, a.key1);
+  };
+  // the final kept test for member x at offset i of its chunk, dv = idb - 32c
+  auto kept_final = [&](float x, int i, int dv) {
+    return fin(x) & ((x > xb) | ((x == xb) & (i <= dv)));
+  };
+  // S of block (c, h) under the final test, its 16 members x in member
+  // order j (token 32c + 8(j/4) + 4h + j%4), summed in that order
+  auto half_sum16 = [&](const float (&x)[16], int c, int h) {
+    const int dv = idb - 32 * c;
+    float S = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const f32x4 x4 = p4[i];
-          lv[4 * i] = x4.x; lv[4 * i + 1] = x4.y; lv[4 * i + 2] = x4.z; lv[4 * i + 3] = x4.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) lv[i] = 32 * c + i < V ? l[32 * c + i] : -INFINITY;
+    for (int j = 0; j < 16; ++j) {
+      const int i = 8 * (j >> 2) + 4 * h + (j & 3);
+      S += kept_final(x[j], i, dv) ? fast_exp2(fmaf(x[j], c2, -mc2)) : 0.f;
+    }
+    return S;
+  };
+  auto gumbel = [&](float S, uint32_t we) {
+    return __log2f(S) - __log2f(-__log2f(sf_uniform(we)));
+  };
+  auto consider = [&](float S, uint32_t we, int k) {
+    if (S > 0.f) {
+      const float G = gumbel(S, we);
+      if (G > gbest || (G == gbest && k < kbest)) {
+        gbest = G;
+        kbest = k;
       }
+    }
+  };
+  // one chunk's 32 logits from memory (NaN past the row's end: no candidate)
+  auto load_chunk = [&](int c, float (&lv)[32]) {
+    if (vec && 32 * c + 32 <= V) {
+      const f32x4* p4 = reinterpret_cast<const f32x4*>(l + 32 * c);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) s1 += cand(32 * c + i, lv[i]) ? fast_exp2((lv[i] - m) * kLog2e) : 0.f;
-      uint32_t w0 = (uint32_t)c, w1 = rid, w2 = a.step, w3 = 0u;
-      sf_philox(w0, w1, w2, w3, a.key0, a.key1);
+      for (int i = 0; i < 8; ++i) {
+        const f32x4 x4 = p4[i];
+        lv[4 * i] = x4.x; lv[4 * i + 1] = x4.y; lv[4 * i + 2] = x4.z; lv[4 * i + 3] = x4.w;
+      }
+    } else {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // half h: columns 32c + 8q + 4h + r'
-        float x[16];
-        bool pend = false;
+      for (int i = 0; i < 32; ++i) lv[i] = 32 * c + i < V ? l[32 * c + i] : NAN;
+    }
+  };
+  // the mask token is no candidate
+  auto unmask = [&](int c, float (&lv)[32]) {
+    if (c == cmask) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) lv[i] = i == imask ? NAN : lv[i];
+    }
+  };
+
+  int wd = 0;                            // this wave's deferred blocks
+  auto draw_chunk = [&](auto merged, int c, float (&lv)[32]) {
+    unmask(c, lv);
+    // candidates only: everything else as -inf (weight 0, never kept)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) lv[i] = fin(lv[i]) ? lv[i] : -INFINITY;
+    if (s1_in_draw) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s1 += fast_exp2(fmaf(lv[i], kLog2e, -ml));
+    }
+    uint32_t w[4];
+    philox_chunk(c, w);
+    const int dv = idb - 32 * c;
+    const bool mixed = dv >= 0 && dv < 31;         // ties on both sides of the boundary id
+    const float thr = dv < 0 ? xb : xb_below;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float S = 0.f;
+      bool pend = false;
+      if constexpr (decltype(merged)::value) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int r2 = 0; r2 < 4; ++r2) {
-            const int i = 8 * q + 4 * h + r2, v = 32 * c + i;
-            bool kept;
-            if (merged) {
-              const bool cd = cand(v, lv[i]);
-              const int bn = bin_of(lv[i]);
-              kept = cd & (bn < mbin);
-              if (cd & (bn == mbin)) {
-                pend = true;
-                const int k = atomicAdd(&s_n, 1);
-                if (k < kSfCap) s_g[k] = ((uint64_t)okey(lv[i]) << 32) | (uint32_t)~(uint32_t)v;
-              }
-            } else {
-              kept = keep(v, lv[i]);
-            }
-            x[4 * q + r2] = kept ? lv[i] * kLog2e : -INFINITY;
+            const int i = 8 * q + 4 * h + r2;
+            const float x = lv[i];
+            const bool kept = x > t_lo;
+            pend |= !kept & (x > t_hi);
+            S += kept ? fast_exp2(fmaf(x, c2, -mc2)) : 0.f;
           }
-        if (pend) {
-          const int k = atomicAdd(&s_ndef, 1);
-          if (k < kSfBins) s_def[k] = (uint32_t)(2 * c + h);
-          continue;
+        const uint64_t dbal = __ballot(pend);
+        if (dbal != 0ull) {
+          if (pend) {
+            const int slot = wd + lanes_below(dbal);
+            if (slot < kSfWaveDef) s_def[wave * kSfWaveDef + slot] = (uint32_t)(2 * c + h);
+            if (slot < kSfWaveStage) {
+              float x16[16];
+              half_of(lv, h, x16);
+              f32x4* st = reinterpret_cast<f32x4*>(s_stage + (wave * kSfWaveStage + slot) * 16);
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                st[q] = f32x4{x16[4 * q], x16[4 * q + 1], x16[4 * q + 2], x16[4 * q + 3]};
+            }
+          }
+          wd += (int)__popcll(dbal);
         }
-        draw_half(x, h ? w2 : w0, h ? w3 : w1, c, h);
+        if (pend) continue;
+      } else {
+        if (mixed) {
+          float x16[16];
+          half_of(lv, h, x16);
+          S = half_sum16(x16, c, h);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int r2 = 0; r2 < 4; ++r2) {
+              const float x = lv[8 * q + 4 * h + r2];
+              S += x > thr ? fast_exp2(fmaf(x, c2, -mc2)) : 0.f;
+            }
+        }
       }
+      consider(S, h ? w[3] : w[1], 2 * c + h);
     }
+  };
+  // every chunk once, one per thread at a time
+  auto draw = [&](auto merged) {
+    for (int c = tid; c < nchunk; c += kSfThreads) {
+      float lv[32];
+      load_chunk(c, lv);
+      draw_chunk(merged, c, lv);
+    }
+  };
+  // the 16 members of block (c, h) in member order, as the draw sees them
+  // (NaN past the row's end and at the mask token)
+  auto load_half = [&](int c, int h, float (&x)[16]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int v0 = 32 * c + 8 * q + 4 * h;
+      if (vec && v0 + 4 <= V) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(l + v0);
+        x[4 * q] = x4.x; x[4 * q + 1] = x4.y; x[4 * q + 2] = x4.z; x[4 * q + 3] = x4.w;
+      } else {
+#pragma unroll
+        for (int r2 = 0; r2 < 4; ++r2) x[4 * q + r2] = v0 + r2 < V ? l[v0 + r2] : NAN;
+      }
+#pragma unroll
+      for (int r2 = 0; r2 < 4; ++r2) x[4 * q + r2] = v0 + r2 == mask ? NAN : x[4 * q + r2];
+    }
+  };
+  // deferred block j of wave w: from LDS when it was staged
+  auto deferred_half = [&](int w, int j, int c, int h, float (&x)[16]) {
+    if (j < kSfWaveStage) {
+      const f32x4* st = reinterpret_cast<const f32x4*>(s_stage + (w * kSfWaveStage + j) * 16);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = st[q];
+        x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+      }
+    } else {
+      load_half(c, h, x);
+    }
+  };
+  // a deferred block, or one evaluated again, under the final test
+  auto half_G_final = [&](int c, int h, float& S) {
+    float x[16];
+    load_half(c, h, x);
+    uint32_t w[4];
+    philox_chunk(c, w);
+    S = half_sum16(x, c, h);
+    return h ? w[3] : w[1];
   };
 
   if (mbin < 0) {
-    draw(false);
+    draw(Tag<false>{});
   } else {
-    if (tid == 0) {
-      s_n = 0;
-      s_ndef = 0;
-    }
+    // the histogram's arrays become the deferred list and the staging
+    // area: every thread is done reading them
     __syncthreads();
-    draw(true);
+    draw(Tag<true>{});
+    if (lane == 0) s_wd[wave] = wd;
     __syncthreads();
-    const int n = s_n, nd = s_ndef;
-    if (n <= kSfCap && nd <= kSfBins) {
-      sort_list(n);
-      if (use_k) {                              // n >= mrank: the bin holds the top_k-th
-        const int e = max(min(mrank, n) - 1, 0);
-        kk = entry_key(e);
-        kid = entry_id(e);
-      } else {
-        select_sorted(n, mrem, pk, pid);
-      }
-      set_thr();
-      for (int j = tid; j < nd; j += kSfThreads) {
-        const int c = (int)(s_def[j] >> 1), h = (int)(s_def[j] & 1u);
-        uint32_t w0 = (uint32_t)c, w1 = rid, w2 = a.step, w3 = 0u;
-        sf_philox(w0, w1, w2, w3, a.key0, a.key1);
-        float x[16];
+    bool ovf = false;
+    for (int w = 0; w < kSfWaves; ++w) ovf |= s_wd[w] > kSfWaveDef;
+    if (!ovf) {
+      // every member of the boundary bin lies in a deferred block: gather
+      // them from those blocks' re-read logits, then ranking order
+      if (tid == 0) s_n = 0;
+      __syncthreads();
+      for (int w = 0; w < kSfWaves; ++w)
+        for (int j = tid; j < s_wd[w]; j += kSfThreads) {
+          const uint32_t k = s_def[w * kSfWaveDef + j];
+          const int c = (int)(k >> 1), h = (int)(k & 1u);
+          float x16[16];
+          deferred_half(w, j, c, h, x16);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int r2 = 0; r2 < 4; ++r2) {
-            const int v = 32 * c + 8 * q + 4 * h + r2;
-            const float xv = v < V ? l[v] : -INFINITY;
-            x[4 * q + r2] = keep(v, xv) ? xv * kLog2e : -INFINITY;
+          for (int jj = 0; jj < 16; ++jj) {
+            const float x = x16[jj];
+            if (fin(x) && !(x > t_lo) && x > t_hi) {
+              const int e = atomicAdd(&s_n, 1);
+              if (e < kSfCap) s_g[e] = rank_pair(x, 32 * c + 8 * (jj >> 2) + 4 * h + (jj & 3));
+            }
           }
-        draw_half(x, h ? w2 : w0, h ? w3 : w1, c, h);
+        }
+      __syncthreads();
+      const int n = s_n;
+      if (n <= kSfCap) {
+        sort_list(s_g, n);
+        if (use_k) {                            // n >= mrank: the bin holds the top_k-th
+          const int e = max(min(mrank, n) - 1, 0);
+          kk = entry_key(e);
+          kid = entry_id(e);
+        } else {
+          select_sorted(n, mrem, pk, pid);
+        }
+      } else if (use_k) {
+        radix([&](int, float x) { return bin_of(x) == mbin; }, false, (uint64_t)mrank, kk, kid);
+      } else {
+        radix([&](int, float x) { return bin_of(x) == mbin; }, true, mrem, pk, pid);
       }
+      set_final();
+      // the deferred blocks under the final test
+      for (int w = 0; w < kSfWaves; ++w)
+        for (int j = tid; j < s_wd[w]; j += kSfThreads) {
+          const uint32_t k = s_def[w * kSfWaveDef + j];
+          const int c = (int)(k >> 1), h = (int)(k & 1u);
+          float x16[16];
+          deferred_half(w, j, c, h, x16);
+          uint32_t wr[4];
+          philox_chunk(c, wr);
+          consider(half_sum16(x16, c, h), h ? wr[3] : wr[1], (int)k);
+        }
     } else {
-      // the boundary bin did not fit in LDS: resolve it as with top-k and
-      // draw the row again
+      // too many deferred blocks to list: resolve the boundary bin from the
+      // whole row and draw the row again
       const int n2 = gather_sort(mbin, [](int, float) { return true; });
       if (use_k) {
         if (n2 <= kSfCap) {
@@ -610,44 +873,85 @@ __global__ __launch_bounds__(1024) void sample_filtered_kernel(SampleArgs a) {
           kk = entry_key(e);
           kid = entry_id(e);
         } else {
-          radix([&](int v, float x) { return cand(v, x) && bin_of(x) == mbin; }, false, (uint64_t)mrank, kk,
-                kid);
+          radix([&](int, float x) { return bin_of(x) == mbin; }, false, (uint64_t)mrank, kk, kid);
         }
       } else if (n2 <= kSfCap) {
         select_sorted(n2, mrem, pk, pid);
       } else {
-        radix([&](int v, float x) { return cand(v, x) && bin_of(x) == mbin; }, true, mrem, pk, pid);
+        radix([&](int, float x) { return bin_of(x) == mbin; }, true, mrem, pk, pid);
       }
-      set_thr();
+      set_final();
       gbest = -INFINITY;
-      cbest = 0x7fffffff;
-      s1 = 0.f;
-      draw(false);
+      kbest = INT_MAX;
+      draw(Tag<false>{});
     }
   }
+
   const float S1 = block_reduce(s1, [](float x, float y) { return x + y; }, s_f);
-  // argmax of (G, lower candidate) over the workgroup
+  // the best (G, lower block index) over the workgroup
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     const float g2 = __shfl_xor(gbest, off, 64);
-    const int c2i = __shfl_xor(cbest, off, 64);
-    if (g2 > gbest || (g2 == gbest && c2i < cbest)) { gbest = g2; cbest = c2i; }
+    const int k2 = __shfl_xor(kbest, off, 64);
+    if (g2 > gbest || (g2 == gbest && k2 < kbest)) { gbest = g2; kbest = k2; }
   }
   if (lane == 0) {
     s_gbest[wave] = gbest;
-    s_cbest[wave] = cbest;
+    s_kbest[wave] = kbest;
   }
   __syncthreads();
   if (tid == 0) {
     for (int w = 1; w < kSfWaves; ++w)
-      if (s_gbest[w] > gbest || (s_gbest[w] == gbest && s_cbest[w] < cbest)) {
-        gbest = s_gbest[w]; cbest = s_cbest[w];
+      if (s_gbest[w] > gbest || (s_gbest[w] == gbest && s_kbest[w] < kbest)) {
+        gbest = s_gbest[w]; kbest = s_kbest[w];
       }
-    // the drawn token's own logit (a kept token always exists: the kept
-    // set holds at least the row maximum)
-    const float lb = cbest < V ? l[cbest] : -INFINITY;
-    a.token[rid] = cbest;
-    a.conf[rid] = __expf(lb - m) / S1;
+    // the inverse CDF inside block (c, h): the first member whose running
+    // sum reaches u S (the sums never decrease and u S > 0, so the members
+    // below it are a prefix and the first past it has weight); if rounding
+    // leaves none past it, the last member with weight
+    auto candidate = [&](int c, int h) {
+      float x[16];
+      load_half(c, h, x);
+      uint32_t w[4];
+      philox_chunk(c, w);
+      const int dv = idb - 32 * c;
+      float e[16], S = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int i = 8 * (j >> 2) + 4 * h + (j & 3);
+        e[j] = kept_final(x[j], i, dv) ? fast_exp2(fmaf(x[j], c2, -mc2)) : 0.f;
+        S += e[j];
+      }
+      const float target = sf_uniform(h ? w[2] : w[0]) * S;
+      float cum = 0.f;
+      int below = 0, last = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        cum += e[j];
+        below += cum < target ? 1 : 0;
+        last = e[j] > 0.f ? j : last;
+      }
+      const int j = below < 16 ? below : last;
+      return 32 * c + 8 * (j >> 2) + 4 * h + (j & 3);
+    };
+    // a kept token always exists (the kept set holds at least the row
+    // maximum, with weight 1), so the best block is set; the guards keep
+    // every read inside the row regardless
+    if (kbest < 0 || kbest >= 2 * nchunk) {
+      a.token[rid] = mask;
+      a.conf[rid] = 0.f;
+      return;
+    }
+    const int c = kbest >> 1, h = kbest & 1;
+    int tok = candidate(c, h);
+    if (h == 0 && 32 * c + 4 < V) {
+      // the chunk's other block at an equal G: the lower candidate wins
+      float S1b;
+      const uint32_t we = half_G_final(c, 1, S1b);
+      if (S1b > 0.f && gumbel(S1b, we) == gbest) tok = min(tok, candidate(c, 1));
+    }
+    a.token[rid] = tok;
+    a.conf[rid] = tok < V ? __expf(l[tok] - m) / S1 : 0.f;
   }
 }
 
