@@ -804,6 +804,25 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
     return h ? w[3] : w[1];
   };
 
+  // fn(w, j) for every deferred block, the waves' lists taken as one list
+  // of which each thread takes every kSfThreads-th entry
+  auto for_deferred = [&](auto fn) {
+    int pre[kSfWaves + 1];
+    pre[0] = 0;
+#pragma unroll
+    for (int w = 0; w < kSfWaves; ++w) pre[w + 1] = pre[w] + s_wd[w];
+    for (int f = tid; f < pre[kSfWaves]; f += kSfThreads) {
+      int w = 0, j = f;
+#pragma unroll
+      for (int ww = 1; ww < kSfWaves; ++ww)
+        if (f >= pre[ww]) {
+          w = ww;
+          j = f - pre[ww];
+        }
+      fn(w, j);
+    }
+  };
+
   if (mbin < 0) {
     draw(Tag<false>{});
   } else {
@@ -820,25 +839,38 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
       // them from those blocks' re-read logits, then ranking order
       if (tid == 0) s_n = 0;
       __syncthreads();
-      for (int w = 0; w < kSfWaves; ++w)
-        for (int j = tid; j < s_wd[w]; j += kSfThreads) {
-          const uint32_t k = s_def[w * kSfWaveDef + j];
-          const int c = (int)(k >> 1), h = (int)(k & 1u);
-          float x16[16];
-          deferred_half(w, j, c, h, x16);
+      for_deferred([&](int w, int j) {
+        const uint32_t k = s_def[w * kSfWaveDef + j];
+        const int c = (int)(k >> 1), h = (int)(k & 1u);
+        float x16[16];
+        deferred_half(w, j, c, h, x16);
 #pragma unroll
-          for (int jj = 0; jj < 16; ++jj) {
-            const float x = x16[jj];
-            if (fin(x) && !(x > t_lo) && x > t_hi) {
-              const int e = atomicAdd(&s_n, 1);
-              if (e < kSfCap) s_g[e] = rank_pair(x, 32 * c + 8 * (jj >> 2) + 4 * h + (jj & 3));
-            }
+        for (int jj = 0; jj < 16; ++jj) {
+          const float x = x16[jj];
+          if (fin(x) && !(x > t_lo) && x > t_hi) {
+            const int e = atomicAdd(&s_n, 1);
+            if (e < kSfCap) s_g[e] = rank_pair(x, 32 * c + 8 * (jj >> 2) + 4 * h + (jj & 3));
           }
         }
+      });
       __syncthreads();
       const int n = s_n;
-      if (n <= kSfCap) {
+      if (n <= kSfThreads) {
+        // ranking order by counting: each entry's position is the number of
+        // entries above it (the pairs are distinct)
+        uint64_t mine = 0ull;
+        int rank = 0;
+        if (tid < n) {
+          mine = s_g[tid];
+          for (int j = 0; j < n; ++j) rank += s_g[j] > mine ? 1 : 0;
+        }
+        __syncthreads();
+        if (tid < n) s_g[rank] = mine;
+        __syncthreads();
+      } else if (n <= kSfCap) {
         sort_list(s_g, n);
+      }
+      if (n <= kSfCap) {
         if (use_k) {                            // n >= mrank: the bin holds the top_k-th
           const int e = max(min(mrank, n) - 1, 0);
           kk = entry_key(e);
@@ -853,16 +885,15 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
       }
       set_final();
       // the deferred blocks under the final test
-      for (int w = 0; w < kSfWaves; ++w)
-        for (int j = tid; j < s_wd[w]; j += kSfThreads) {
-          const uint32_t k = s_def[w * kSfWaveDef + j];
-          const int c = (int)(k >> 1), h = (int)(k & 1u);
-          float x16[16];
-          deferred_half(w, j, c, h, x16);
-          uint32_t wr[4];
-          philox_chunk(c, wr);
-          consider(half_sum16(x16, c, h), h ? wr[3] : wr[1], (int)k);
-        }
+      for_deferred([&](int w, int j) {
+        const uint32_t k = s_def[w * kSfWaveDef + j];
+        const int c = (int)(k >> 1), h = (int)(k & 1u);
+        float x16[16];
+        deferred_half(w, j, c, h, x16);
+        uint32_t wr[4];
+        philox_chunk(c, wr);
+        consider(half_sum16(x16, c, h), h ? wr[3] : wr[1], (int)k);
+      });
     } else {
       // too many deferred blocks to list: resolve the boundary bin from the
       // whole row and draw the row again
@@ -905,24 +936,41 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
       if (s_gbest[w] > gbest || (s_gbest[w] == gbest && s_kbest[w] < kbest)) {
         gbest = s_gbest[w]; kbest = s_kbest[w];
       }
-    // the inverse CDF inside block (c, h): the first member whose running
-    // sum reaches u S (the sums never decrease and u S > 0, so the members
-    // below it are a prefix and the first past it has weight); if rounding
-    // leaves none past it, the last member with weight
-    auto candidate = [&](int c, int h) {
-      float x[16];
-      load_half(c, h, x);
-      uint32_t w[4];
-      philox_chunk(c, w);
+    // a kept token always exists (the kept set holds at least the row
+    // maximum, with weight 1), so the best block is set; the guard keeps
+    // every read inside the row regardless
+    if (kbest < 0 || kbest >= 2 * nchunk) {
+      a.token[rid] = mask;
+      a.conf[rid] = 0.f;
+      return;
+    }
+    const int c = kbest >> 1, h = kbest & 1;
+    // the winning chunk once: both blocks' members, as the draw saw them
+    float lv[32];
+    load_chunk(c, lv);
+    unmask(c, lv);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) lv[i] = fin(lv[i]) ? lv[i] : -INFINITY;
+    float x0[16], x1[16];
+    half_of(lv, 0, x0);
+    half_of(lv, 1, x1);
+    uint32_t w[4];
+    philox_chunk(c, w);
+    // the inverse CDF inside block hh of the chunk: the first member whose
+    // running sum reaches u S (the sums never decrease and u S > 0, so the
+    // members below it are a prefix and the first past it has weight); if
+    // rounding leaves none past it, the last member with weight.  Returns
+    // the member index.
+    auto icdf = [&](const float (&x)[16], int hh, uint32_t wu) {
       const int dv = idb - 32 * c;
       float e[16], S = 0.f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int i = 8 * (j >> 2) + 4 * h + (j & 3);
+        const int i = 8 * (j >> 2) + 4 * hh + (j & 3);
         e[j] = kept_final(x[j], i, dv) ? fast_exp2(fmaf(x[j], c2, -mc2)) : 0.f;
         S += e[j];
       }
-      const float target = sf_uniform(h ? w[2] : w[0]) * S;
+      const float target = sf_uniform(wu) * S;
       float cum = 0.f;
       int below = 0, last = 0;
 #pragma unroll
@@ -931,27 +979,28 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
         below += cum < target ? 1 : 0;
         last = e[j] > 0.f ? j : last;
       }
-      const int j = below < 16 ? below : last;
-      return 32 * c + 8 * (j >> 2) + 4 * h + (j & 3);
+      return below < 16 ? below : last;
     };
-    // a kept token always exists (the kept set holds at least the row
-    // maximum, with weight 1), so the best block is set; the guards keep
-    // every read inside the row regardless
-    if (kbest < 0 || kbest >= 2 * nchunk) {
-      a.token[rid] = mask;
-      a.conf[rid] = 0.f;
-      return;
-    }
-    const int c = kbest >> 1, h = kbest & 1;
-    int tok = candidate(c, h);
-    if (h == 0 && 32 * c + 4 < V) {
+    const int j0 = icdf(h ? x1 : x0, h, h ? w[2] : w[0]);
+    int tok = 32 * c + 8 * (j0 >> 2) + 4 * h + (j0 & 3);
+    float lt = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) lt = j == j0 ? (h ? x1[j] : x0[j]) : lt;
+    if (h == 0) {
       // the chunk's other block at an equal G: the lower candidate wins
-      float S1b;
-      const uint32_t we = half_G_final(c, 1, S1b);
-      if (S1b > 0.f && gumbel(S1b, we) == gbest) tok = min(tok, candidate(c, 1));
+      const float S1b = half_sum16(x1, c, 1);
+      if (S1b > 0.f && gumbel(S1b, w[3]) == gbest) {
+        const int j1 = icdf(x1, 1, w[2]);
+        const int tok1 = 32 * c + 8 * (j1 >> 2) + 4 + (j1 & 3);
+        if (tok1 < tok) {
+          tok = tok1;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) lt = j == j1 ? x1[j] : lt;
+        }
+      }
     }
     a.token[rid] = tok;
-    a.conf[rid] = tok < V ? __expf(l[tok] - m) / S1 : 0.f;
+    a.conf[rid] = __expf(lt - m) / S1;
   }
 }
 
