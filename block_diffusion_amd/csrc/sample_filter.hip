@@ -181,8 +181,10 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
 
   // every logit of the row once, the mask token's as NaN (no candidate);
   // with 16-byte aligned rows each thread keeps eight 16-byte loads in
-  // flight, the next four issued before the current four are used
-  auto each = [&](auto fn) {
+  // flight, the next four issued before the current four are used.  With
+  // rev the row is walked from its end: the histogram pass does, so that it
+  // starts on what the pass before it read last (still in the caches)
+  auto each = [&](auto fn, bool rev = false) {
     if (vec) {
       const f32x4* l4 = reinterpret_cast<const f32x4*>(l);
       const int n4 = V >> 2, qm = mask >> 2, jm = mask & 3;
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
       bool full = q + (U - 1) * kSfThreads < n4;
       if (full) {
 #pragma unroll
-        for (int j = 0; j < U; ++j) cur[j] = l4[q + j * kSfThreads];
+        for (int j = 0; j < U; ++j) cur[j] = l4[rev ? n4 - 1 - (q + j * kSfThreads) : q + j * kSfThreads];
       }
       while (full) {
         const int qn = q + U * kSfThreads;
@@ -209,16 +211,16 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
         f32x4 nx[U];
         if (nfull) {
 #pragma unroll
-          for (int j = 0; j < U; ++j) nx[j] = l4[qn + j * kSfThreads];
+          for (int j = 0; j < U; ++j) nx[j] = l4[rev ? n4 - 1 - (qn + j * kSfThreads) : qn + j * kSfThreads];
         }
 #pragma unroll
-        for (int j = 0; j < U; ++j) fn4(q + j * kSfThreads, cur[j]);
+        for (int j = 0; j < U; ++j) fn4(rev ? n4 - 1 - (q + j * kSfThreads) : q + j * kSfThreads, cur[j]);
 #pragma unroll
         for (int j = 0; j < U; ++j) cur[j] = nx[j];
         q = qn;
         full = nfull;
       }
-      for (; q < n4; q += kSfThreads) fn4(q, l4[q]);
+      for (; q < n4; q += kSfThreads) fn4(rev ? n4 - 1 - q : q, l4[rev ? n4 - 1 - q : q]);
     } else {
       for (int v = tid; v < V; v += kSfThreads) {
         const float x = l[v];
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(kSfThreads, 4) void sample_filtered_kernel(SampleAr
           tail_n += cd ? 1u : 0u;
           tail_m += u;
         }
-      });
+      }, true);
       if constexpr (decltype(with_k)::value)
         if (tail_n) atomicAdd(&s_bc[kSfBins - 1], tail_n);
       if constexpr (decltype(with_p)::value)
