@@ -138,8 +138,9 @@ def test_lmhead_logits_many_rows():
 def _direct_rows(V, mask, seed):
     """Logit rows that stress the boundary search: long runs of equal logits
     (6000 and 1500 tokens at one value), a plain spread, -inf tokens, an
-    all-equal row and a row with five tokens far above the rest; the mask
-    column is -inf as the LM head stores it."""
+    all-equal row, a row with five tokens far above the rest, and a row
+    whose top 3000 are 1600 tokens at +0 and 1600 at -0 (equal logits, so
+    ranked by id); the mask column is -inf as the LM head stores it."""
     g = np.random.default_rng(seed)
     rows = []
     for n_tie in (6000, 1500):
@@ -153,6 +154,11 @@ def _direct_rows(V, mask, seed):
     rows.append(np.zeros(V, np.float32))
     x = g.standard_normal(V).astype(np.float32)
     x[:5] = 12.0
+    rows.append(x)
+    x = -np.abs(g.standard_normal(V)).astype(np.float32) - 1.0
+    z = g.choice(V, 3200, replace=False)
+    x[z[:1600]] = 0.0
+    x[z[1600:]] = -0.0
     rows.append(x)
     lg = np.stack(rows)
     lg[:, mask] = -np.inf
