@@ -11,12 +11,14 @@
 // Work decomposition.  A segment is (sequence s, kv head g, row group rg); it
 // owns ceil(L_s/kKT) prefix tiles of kKT keys plus ceil(B/kKT) tiles of the
 // block's own keys.  All segments, in order, form one global tile stream,
-// which is cut into equal contiguous ranges, one per single-wave workgroup:
-// every wave streams the same number of tiles whatever the prefix lengths.
-// A wave finishes each segment it touches with (max, sum, unnormalised
-// output); a segment split over several waves leaves fp32 partials that
-// attn_combine_kernel merges, one that fits in one wave is written directly;
-// every piece records its segment's piece count for the combine launch.
+// which is cut into equal contiguous ranges, one per single-wave workgroup
+// (at least kMinTilesPerWave tiles each): every wave streams the same number
+// of tiles whatever the prefix lengths.  A wave finishes each segment it
+// touches with (max, sum, unnormalised output); a segment split over several
+// waves leaves fp32 partials that attn_combine_kernel merges, one that fits
+// in one wave is written directly.  A wave's range cuts at most two segments
+// (at its two ends), so the partials take two slots per wave; every piece
+// records its segment's piece count and first slot for the combine launch.
 // Each wave first turns the prefix lengths into tile prefix sums itself: a
 // separate planning launch would cost more than the few loads it saves.
 //
@@ -88,6 +90,9 @@ constexpr int kMaxWavesPerCU = ATTN_WAVES;
 constexpr int kCUs = 256;      // MI355X compute units
 constexpr int kLdsPerCU = 160 * 1024;
 constexpr int kSavingState = 3;   // sequence state SAVING
+// a wave streams at least this many tiles (a small launch uses fewer waves
+// rather than many waves with a handful of tiles each)
+constexpr int kMinTilesPerWave = 16;
 
 // chunk permutation of row r (D=128: 16 chunks per row; D=64: 8)
 template <int D>
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
   }
   const int start = incl - mine;                                    // plan(l*c)
   const long T = (long)NHG * __builtin_amdgcn_readfirstlane(__shfl(incl, 63, 64));
-  const long NWe = min((long)a.grid, max(1L, T / 64));
+  const long NWe = min((long)a.grid, max(1L, T / kMinTilesPerWave));
   const long w = blockIdx.x;
   if (w >= NWe) return;
   const long t0 = w * T / NWe, t1 = (w + 1) * T / NWe;
@@ -332,9 +337,13 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
     const long ts = (long)NHG * d.p + (long)d.hg * d.tiles;
     const long w0 = ((ts + 1) * NWe - 1) / T;
     const long w1 = ((ts + d.tiles) * NWe - 1) / T;
-    // every piece of a segment records how many there are (the same value),
-    // so the combine launch reads one word instead of re-deriving the split
-    if (lane == 0) a.seg_np[d.s * NHG + d.hg] = (int)(w1 - w0 + 1);
+    // A wave's range splits at most two segments: the one holding its first
+    // tile (partial slot 2w) and the one holding its last (slot 2w + 1).
+    // Every piece of a segment records the same word: its piece count, its
+    // first wave, and which of that wave's slots the first piece took (the
+    // others always take slot 2w), so the combine reads one word.
+    const int side0 = ts == w0 * T / NWe ? 0 : 1;
+    if (lane == 0) a.seg_np[d.s * NHG + d.hg] = (int)(w1 - w0 + 1) | (side0 << 11) | ((int)w0 << 12);
     if (w0 == w1) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
@@ -353,7 +362,7 @@ __global__ __launch_bounds__(64) void attn_stream_kernel(AttnArgs a) {
         }
       }
     } else {
-      const size_t slot = ((size_t)(d.s * NHG + d.hg) * a.maxp + (size_t)(w - w0)) * ROWS;
+      const size_t slot = (size_t)(2 * w + (ts <= t0 ? 0 : 1)) * ROWS;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const size_t row = slot + rt * 16 + lr;
@@ -579,26 +588,30 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
   if (a.gate != nullptr && *a.gate <= 0) return;
   const int NHG = a.Hkv * a.n_rg;
   const int seg = blockIdx.x;
-  const int pieces = a.seg_np[seg];
+  const int rec = a.seg_np[seg];
+  const int pieces = rec & 0x7FF;
   if (pieces <= 1) return;
+  const int side0 = (rec >> 11) & 1, w0 = rec >> 12;
+  // piece p came from wave w0 + p, slot 2(w0 + p) (+1 for the first piece
+  // when it was its wave's second split segment)
+  auto pslot = [&](int p) { return (size_t)(2 * (w0 + p) + (p == 0 ? side0 : 0)); };
   const int s = seg / NHG, hg = seg % NHG;
   const int g = hg / a.n_rg, rg = hg % a.n_rg;
   const int R = a.G * a.B;
-  const size_t base = (size_t)seg * a.maxp;
   for (int idx = threadIdx.x; idx < ROWS * (D / 8); idx += kCombineThreads) {
     const int row = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
     const int rr = rg * ROWS + row;
     if (rr >= R) continue;
     float M = -INFINITY;
-    for (int p = 0; p < pieces; ++p) M = fmaxf(M, a.part_ml[(base + p) * ROWS + row].x);
+    for (int p = 0; p < pieces; ++p) M = fmaxf(M, a.part_ml[pslot(p) * ROWS + row].x);
     float Ls = 0.f, o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = 0.f;
     for (int p = 0; p < pieces; ++p) {
-      const float2 ml = a.part_ml[(base + p) * ROWS + row];
+      const float2 ml = a.part_ml[pslot(p) * ROWS + row];
       const float wgt = fast_exp2(ml.x - M);
       Ls += ml.y * wgt;
-      const float* po = a.part_o + ((base + p) * ROWS + row) * D + d0;
+      const float* po = a.part_o + (pslot(p) * ROWS + row) * D + d0;
       const f32x4 lo4 = *reinterpret_cast<const f32x4*>(po);
       const f32x4 hi4 = *reinterpret_cast<const f32x4*>(po + 4);
       o[0] += wgt * lo4.x; o[1] += wgt * lo4.y; o[2] += wgt * lo4.z; o[3] += wgt * lo4.w;
@@ -623,12 +636,11 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
   const int R = G * B;
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   p.n_rg = (R + 16 * p.RT - 1) / (16 * p.RT);
-  const long max_seg_tiles = ((long)max_pages * page_size + kKT - 1) / kKT + (B + kKT - 1) / kKT;
-  p.maxp = (int)((max_seg_tiles + 63) / 64 + 1);
   const int slot_bytes = attn_slot_bytes(D, p.RT);
   const int waves_per_cu = std::max(1, std::min(kMaxWavesPerCU, kLdsPerCU / (kRing * slot_bytes)));
   p.grid = kCUs * waves_per_cu;
-  const size_t slots = (size_t)S * Hkv * p.n_rg * p.maxp * 16 * p.RT;
+  // two partial slots per wave (the segments its range cuts at either end)
+  const size_t slots = (size_t)2 * p.grid * 16 * p.RT;
   p.o_bytes = (slots * D * sizeof(float) + 255) & ~(size_t)255;
   p.ml_bytes = (slots * sizeof(float2) + 255) & ~(size_t)255;
   p.ws_bytes = p.o_bytes + p.ml_bytes + (size_t)S * Hkv * p.n_rg * sizeof(int32_t);

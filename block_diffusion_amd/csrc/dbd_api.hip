@@ -96,7 +96,7 @@ dbd_status enqueue_attn(int S, int B, int Hq, int Hkv, int D, int P, int max_pag
   a.part_ml = reinterpret_cast<float2*>(w + plan.o_bytes);
   a.seg_np = reinterpret_cast<int32_t*>(w + plan.o_bytes + plan.ml_bytes);
   a.S = S; a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.P = P; a.max_pages = max_pages;
-  a.n_rg = plan.n_rg; a.maxp = plan.maxp; a.grid = plan.grid;
+  a.n_rg = plan.n_rg; a.grid = plan.grid;
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)D);
   a.scale_log2 = sc * 1.4426950408889634f;
   a.save_state = save_state; a.k_cache_out = kc_out; a.v_cache_out = vc_out;

@@ -17,12 +17,13 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* prefix_len;
   uint16_t* out;
-  float* part_o;   // [S*NHG*maxp][rows][D] unnormalised sums of split segments
-  float2* part_ml; // [S*NHG*maxp][rows] (max, sum), log2 units
-  int32_t* seg_np; // [S*NHG] pieces of each segment in this launch (1: not split)
+  float* part_o;   // [2*grid][rows][D] unnormalised sums of split segments,
+                   // two slots per wave
+  float2* part_ml; // [2*grid][rows] (max, sum), log2 units
+  int32_t* seg_np; // [S*NHG] pieces of each segment in this launch (1: not
+                   // split) | first piece's slot side << 11 | first wave << 12
   int S, B, Hq, Hkv, G, P, max_pages;
   int n_rg;        // row groups per kv head (rows = G*B split in 16*RT)
-  int maxp;        // partial slots per segment
   int grid;        // workgroups (single waves) of the stream kernel
   float scale_log2;
   // SAVING forward: when save_state is set, the block keys and values of
@@ -38,7 +39,7 @@ struct AttnArgs {
 };
 
 struct AttnPlan {
-  int D, RT, n_rg, maxp, grid;
+  int D, RT, n_rg, grid;
   size_t o_bytes, ml_bytes, ws_bytes;  // workspace: part_o | part_ml | seg_np
 };
 
