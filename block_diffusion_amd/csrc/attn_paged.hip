@@ -602,20 +602,42 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
     const int row = idx / (D / 8), d0 = (idx % (D / 8)) * 8;
     const int rr = rg * ROWS + row;
     if (rr >= R) continue;
+    // the first kCombineFirst pieces' (m, l) and partial rows are loaded
+    // together (one round trip for the usual two pieces); any further piece
+    // is read in the loops.  The sums run in piece order either way.
+    constexpr int kCombineFirst = 4;
+    float2 mlf[kCombineFirst];
+    f32x4 lof[kCombineFirst], hif[kCombineFirst];
+#pragma unroll
+    for (int p = 0; p < kCombineFirst; ++p) {
+      if (p < pieces) {
+        mlf[p] = a.part_ml[pslot(p) * ROWS + row];
+        const float* po = a.part_o + (pslot(p) * ROWS + row) * D + d0;
+        lof[p] = *reinterpret_cast<const f32x4*>(po);
+        hif[p] = *reinterpret_cast<const f32x4*>(po + 4);
+      }
+    }
     float M = -INFINITY;
-    for (int p = 0; p < pieces; ++p) M = fmaxf(M, a.part_ml[pslot(p) * ROWS + row].x);
+#pragma unroll
+    for (int p = 0; p < kCombineFirst; ++p)
+      if (p < pieces) M = fmaxf(M, mlf[p].x);
+    for (int p = kCombineFirst; p < pieces; ++p) M = fmaxf(M, a.part_ml[pslot(p) * ROWS + row].x);
     float Ls = 0.f, o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = 0.f;
-    for (int p = 0; p < pieces; ++p) {
-      const float2 ml = a.part_ml[pslot(p) * ROWS + row];
+    auto add_piece = [&](float2 ml, f32x4 lo4, f32x4 hi4) {
       const float wgt = fast_exp2(ml.x - M);
       Ls += ml.y * wgt;
-      const float* po = a.part_o + (pslot(p) * ROWS + row) * D + d0;
-      const f32x4 lo4 = *reinterpret_cast<const f32x4*>(po);
-      const f32x4 hi4 = *reinterpret_cast<const f32x4*>(po + 4);
       o[0] += wgt * lo4.x; o[1] += wgt * lo4.y; o[2] += wgt * lo4.z; o[3] += wgt * lo4.w;
       o[4] += wgt * hi4.x; o[5] += wgt * hi4.y; o[6] += wgt * hi4.z; o[7] += wgt * hi4.w;
+    };
+#pragma unroll
+    for (int p = 0; p < kCombineFirst; ++p)
+      if (p < pieces) add_piece(mlf[p], lof[p], hif[p]);
+    for (int p = kCombineFirst; p < pieces; ++p) {
+      const float* po = a.part_o + (pslot(p) * ROWS + row) * D + d0;
+      add_piece(a.part_ml[pslot(p) * ROWS + row], *reinterpret_cast<const f32x4*>(po),
+                *reinterpret_cast<const f32x4*>(po + 4));
     }
     const float inv = 1.f / Ls;
     const int pos = rr / a.G, gi = rr % a.G;
