@@ -205,6 +205,16 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   const int wn = wave & 1, wm = wave >> 1;
   const int nk = a.Hd / TK;
   const int ntile = (v_hi - v_lo + NT - 1) / NT;
+  // Tile order.  The store mode's epilogue writes each tile's logits, and
+  // workgroups that finish tiles together queue on HBM writes together: odd
+  // teams take their partial last tile first, which offsets their
+  // epilogues from the even teams' by that tile's (shorter) time.  Every
+  // other mode keeps the plain order.
+#ifndef LM_ROT
+#define LM_ROT 1
+#endif
+  const bool rot = STO && LM_ROT != 0 && (team & 1) != 0 && ntile > 1;
+  auto tmap = [&](int t) { return rot ? (t == 0 ? ntile - 1 : t - 1) : t; };
   const uint32_t hdb = (uint32_t)a.Hd * 2;     // row bytes
 
   // Lane l of a 1 KB load fills LDS row 8*blk + l/8, physical chunk l%8,
@@ -236,7 +246,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
     constexpr int I0 = decltype(i0c)::value, I1 = decltype(i1c)::value;
     const char* kb = reinterpret_cast<const char*>(WL ? a.w : a.hidden) + (size_t)it_k * (TK * 2);
     if (WL) {
-      const int n0 = v_lo + min(it_t, ntile - 1) * NT;
+      const int n0 = v_lo + tmap(min(it_t, ntile - 1)) * NT;
       const char* tb = kb + (size_t)n0 * hdb;
       const int lim = v_hi - n0;                       // valid rows of this tile
       // rows past the range re-read a row of the tile's first 8
@@ -574,7 +584,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   // whose register budget has no room for more variants).  wofs: the
   // wave's first W row in the slot.
   auto tile_geom = [&](int t, int& wofs, int& nbw) {
-    const int wt = min(NT, v_hi - (v_lo + t * NT));
+    const int wt = min(NT, v_hi - (v_lo + tmap(t) * NT));
     const int h = wt >= NT ? 4 : ((wt + 31) / 32 + 1) / 2;
     wofs = wn * 32 * h;
     nbw = h;
@@ -587,7 +597,7 @@ __device__ __forceinline__ void lm_pass(const LmArgs& a, int m_base, int m_end, 
   read_frags(ws, hs, 0, fa0, fb0);
 
   for (int tile = 0; tile < ntile; ++tile) {
-    const int n0 = v_lo + tile * NT;
+    const int n0 = v_lo + tmap(tile) * NT;
     const int wofs = wofs_n, nbw = nbw_n;
     if constexpr (!SMP) {
       if (tile + 1 < ntile) tile_geom(tile + 1, wofs_n, nbw_n);
