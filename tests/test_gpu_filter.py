@@ -207,3 +207,30 @@ def test_sample_filtered_no_candidate():
     assert t[0] == mask and c[0] == 0.0
     ex = check_filtered_rows(lg_h[1:], np.array([1]), t, c, mask, 1.0, 10, 0.9, 5, 0)
     assert ex <= 1
+
+
+@pytest.mark.parametrize("T,k,p", [(1.0, 0, 0.5), (0.6, 0, 0.95), (1.0, 60000, 1.0), (1.0, 30000, 0.9)])
+def test_sample_filtered_full_vocab_overflow(T, k, p):
+    """Full-vocabulary rows whose boundary bin spans most of the row (all
+    logits equal; 60000 tied at the top of a spread), so that more blocks
+    are deferred than the draw can list: the boundary is then resolved from
+    the whole row (radix select) and the row drawn again."""
+    V, mask = 151936, 151669
+    g = np.random.default_rng(1207)
+    rows = [np.zeros(V, np.float32)]
+    x = (g.standard_normal(V) * 2 - 6).astype(np.float32)
+    x[g.choice(V, 60000, replace=False)] = 1.5
+    rows.append(x)
+    lg_h = np.stack(rows)
+    lg_h[:, mask] = -np.inf
+    M = lg_h.shape[0]
+    lg = torch.from_numpy(lg_h).to("cuda")
+    tok = torch.full((M,), -9, dtype=torch.int32, device="cuda")
+    conf = torch.full((M,), float("nan"), dtype=torch.float32, device="cuda")
+    seed, step = 31 + k, 2
+    api.dbd_sample_filtered(lg, dev_i32([M]), tok, conf, mask, T, k, p, seed, step)
+    torch.cuda.synchronize()
+    ex = check_filtered_rows(lg_h, np.arange(M), tok.cpu().numpy(), conf.cpu().numpy(), mask,
+                             T, k, p, seed, step)
+    print(f"T={T} k={k} p={p}: {M} rows, {ex} exempt", flush=True)
+    assert ex <= 1
