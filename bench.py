@@ -11,9 +11,10 @@ batch * block_length * rounds * steps / elapsed.  All inputs (prefix cache,
 LM-head weight, per-round queries/keys/values/hidden states) are seeded,
 synthetic and resident in HBM before the timed region.
 
-Prints one JSON line (rank 0).  Also times each entry point on its own with
-HIP events on the launch stream for the roofline object, and the CPU oracle
-on a bounded sample for the CPU baseline.
+Prints one JSON line (rank 0).  Also times each entry point with HIP events
+on the launch stream for the roofline object (the LM head between the
+attention and the remask, as a round launches it; the others back to back),
+and the CPU oracle on a bounded sample for the CPU baseline.
 """
 from __future__ import annotations
 
@@ -46,9 +47,11 @@ def parse():
                     help="the CPU oracle repeats whole blocks until this much time has passed")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-configuration entries (configs 0, 1, 3, 4)")
-    ap.add_argument("--only", choices=["attention", "lmhead", "remask", "logits", "filtered", "prefill"],
+    ap.add_argument("--only", choices=["attention", "lmhead", "lmhead_round", "remask", "logits", "filtered",
+                                       "prefill"],
                     help="launch only this entry point (warmup + steps times, round-1 inputs) and "
-                         "print its mean launch time: the run that rocprofv3 counters are taken on")
+                         "print its mean launch time: the run that rocprofv3 counters are taken on; "
+                         "lmhead_round runs attention, LM head and remask in turn and times the LM head")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="copy MIB MiB device-to-device (warmup + steps times) and exit: the plain "
                          "copy kernel of known size that scales FETCH_SIZE / WRITE_SIZE")
@@ -292,6 +295,19 @@ def main():
     ri, nr2 = torch.zeros(n, dtype=torch.int32, device=dev), torch.zeros(1, dtype=torch.int32, device=dev)
     t_remask = ev_time(lambda: api.dbd_remask_commit(tk, ss, arg_r, conf_r, ri, nr2, w.mask_id,
                                                      2.0))   # tau > 1: one commit each, no state change until full
+    # the LM head over the first round's rows inside a round's sequence
+    # (attention, LM head, remask): the launch the roofline reports
+    M1 = rows_per_round[0]
+    nr_m1 = torch.tensor([M1], dtype=torch.int32, device=dev)
+    t_lm_round = lm_in_round(
+        lambda: api.dbd_attn_paged(r1["q"], r1["k_blk"], r1["v_blk"], fixed["k_cache"], fixed["v_cache"],
+                                   fixed["page_table"], fixed["prefix_len"], attn_out, ws=bufs.workspace),
+        lambda: api.dbd_lmhead_conf(r1["hidden"], fixed["w_vocab"], nr_m1, bufs.argmax_tok, bufs.conf,
+                                    w.mask_id, row_index=lm_rows, max_rows=n, ws=bufs.workspace),
+        lambda: api.dbd_remask_commit(tk, ss, arg_r, conf_r, ri, nr2, w.mask_id, 2.0),
+        3, it)
+    log(f"LM head at M={M1} in a round's sequence (attention, LM head, remask): {t_lm_round:.1f} us; "
+        f"back to back alone: {lm_times[M1]:.1f} us")
     # the same two launches replayed from a captured graph (graph_time)
     tg_attn = graph_time(lambda: api.dbd_attn_paged(r1["q"], r1["k_blk"], r1["v_blk"],
                                                     fixed["k_cache"], fixed["v_cache"],
@@ -407,9 +423,8 @@ def main():
                      + 2 * w.S * w.B * w.Hq * w.D * 2              # q in, out
                      + 2 * w.S * w.B * w.Hkv * w.D * 2             # block K and V
                      + w.S * 4 + npages.sum() * 4)                 # prefix lengths, page ids
-    M1 = rows_per_round[0]
     lm_flops = 2.0 * M1 * w.Hd * w.V
-    t_lm1 = lm_times[M1]
+    t_lm1 = t_lm_round
     step_attn = t_attn * w.rounds
     step_lm = sum(lm_times.get(m, 0.0) for m in rows_per_round)
     attn_roof = dict(bound="hbm", achieved=attn_bytes / (t_attn * 1e-6) / 1e9, peak=PEAK_HBM_GBS,
@@ -454,6 +469,7 @@ def main():
         "roofline": roof,
         "breakdown_us": {"attention": round(t_attn, 2),
                          "lmhead": {str(m): round(t, 2) for m, t in lm_times.items()},
+                         "lmhead_in_round_M%d" % M1: round(t_lm_round, 2),
                          "remask": round(t_remask, 2),
                          "attention_kv_save": round(t_save, 2),
                          "per_round_eager_us": [round(t, 1) for t in round_us],
@@ -506,6 +522,32 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, fx, rins, args.cpu_seconds)
         out["breakdown_us"]["cpu_oracle_1thread"] = cpu_single_thread(synth)
     print(json.dumps(out), flush=True)
+
+
+def lm_in_round(attn_fn, lm_fn, remask_fn, warmup, reps):
+    """The LM head's launch time in the setting of a round: each repetition
+    launches the attention, the LM head between two HIP events, then the
+    remask, in order on one stream.  Returns the mean over reps in
+    microseconds.  Back-to-back launches of the LM head alone keep the matrix
+    cores busy without the attention's pauses and run at a lower clock; the
+    round is what the step runs."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        attn_fn()
+        lm_fn()
+        remask_fn()
+    pairs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        attn_fn()
+        e0.record(stream)
+        lm_fn()
+        e1.record(stream)
+        remask_fn()
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in pairs) * 1e3 / reps
 
 
 def graph_time(fn, n=20):
@@ -734,6 +776,24 @@ def only(args, w, api, fixed, r1, attn_out, bufs, tok0, st0):
         fn = lambda: api.dbd_lmhead_conf(r1["hidden"], fixed["w_vocab"], nr, bufs.argmax_tok,
                                          bufs.conf, w.mask_id, row_index=rows, max_rows=n,
                                          ws=bufs.workspace)
+    elif args.only == "lmhead_round":
+        rows = torch.arange(n, dtype=torch.int32, device=dev)
+        nr = torch.tensor([n], dtype=torch.int32, device=dev)
+        conf_r = torch.rand(n, device=dev)
+        arg_r = torch.zeros(n, dtype=torch.int32, device=dev)
+        tk, ss = tok0.clone(), st0.clone()
+        ri = torch.zeros(n, dtype=torch.int32, device=dev)
+        nr2 = torch.zeros(1, dtype=torch.int32, device=dev)
+        us = lm_in_round(
+            lambda: api.dbd_attn_paged(r1["q"], r1["k_blk"], r1["v_blk"], fixed["k_cache"], fixed["v_cache"],
+                                       fixed["page_table"], fixed["prefix_len"], attn_out, ws=bufs.workspace),
+            lambda: api.dbd_lmhead_conf(r1["hidden"], fixed["w_vocab"], nr, bufs.argmax_tok, bufs.conf,
+                                        w.mask_id, row_index=rows, max_rows=n, ws=bufs.workspace),
+            lambda: api.dbd_remask_commit(tk, ss, arg_r, conf_r, ri, nr2, w.mask_id, 2.0),
+            args.warmup, args.steps)
+        print(json.dumps({"only": args.only, "workload": w.name, "rows": n, "launches": args.steps,
+                          "us_per_launch": round(us, 2)}), flush=True)
+        return
     elif args.only in ("logits", "filtered"):
         rows = torch.arange(n, dtype=torch.int32, device=dev)
         nr = torch.tensor([n], dtype=torch.int32, device=dev)
