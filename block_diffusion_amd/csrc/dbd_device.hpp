@@ -62,13 +62,22 @@ __device__ __forceinline__ int shfl_xor_i(int v, int m) {
 // values of its own and its xor-16 partner in its two results (16-lane
 // groups 0,1 / 2,3 exchanged), and v_permlane32_swap those of it and its
 // xor-32 partner; either order, so max and sum are exact.
+// The maximum is one v_max_f32: fmaxf would first quiet each swapped value
+// (a v_max of the value with itself, two per call), since the compiler
+// cannot tell that a lane exchange leaves the bits of a quiet NaN as they
+// were.  v_max_f32 returns the other operand for a quiet NaN, as fmaxf does.
+__device__ __forceinline__ float vmax_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float max_xor16(float v) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Compiler-level ordering of LDS traffic among the lanes of one wave.  A

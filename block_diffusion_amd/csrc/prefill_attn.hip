@@ -220,19 +220,43 @@ __global__ __launch_bounds__(256, PF_OCC) void prefill_attn_kernel(PrefillArgs a
   const uint32_t rowb = (uint32_t)a.Hkv * D * 2;           // bytes between token rows
   const char* kbase = reinterpret_cast<const char*>(a.k + ((size_t)t0s * a.Hkv + g) * D);
   const char* vbase = reinterpret_cast<const char*>(a.v + ((size_t)t0s * a.Hkv + g) * D);
+  // load i of this wave fills stage row r = r0 + lane/LPR (r0 from the wave
+  // and i), physical chunk lane%LPR with logical chunk lc; loff[i] is the
+  // lane's byte offset from the stage's first key, the same in every stage
+  uint32_t loff[NLD];
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    const int ii = wave * NLD + i;                         // 0 .. 2*KT/RPI-1
+    const int r0 = (ii >= KT / RPI ? ii - KT / RPI : ii) * RPI;
+    const int r = r0 + lane / LPR;
+    loff[i] = (uint32_t)r * rowb + (uint32_t)((lane % LPR) ^ pswz<D>(r)) * 16;
+  }
   auto issue = [&](int st) {
     const int stc = st < nstage ? st : nstage - 1;         // past the end: repeat the last
     lds_u16* slot = ring + (st % NS) * 2 * KVE;
+    if ((stc + 1) * KT <= L) {
+      // every key of the stage is real: only the scalar base moves
+      const size_t sb = (size_t)stc * KT * rowb;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int ii = wave * NLD + i;                       // 0 .. 2*KT/RPI-1
-      const bool isv = ii >= KT / RPI;
-      const int r0 = (isv ? ii - KT / RPI : ii) * RPI;
-      const int r = r0 + lane / LPR;
-      const int lc = (lane % LPR) ^ pswz<D>(r);
-      const int key = min(stc * KT + r, L - 1);
-      pf_dma16(isv ? vbase : kbase, (uint32_t)key * rowb + (uint32_t)lc * 16,
-               slot + (isv ? KVE : 0) + r0 * D);
+      for (int i = 0; i < NLD; ++i) {
+        const int ii = wave * NLD + i;
+        const bool isv = ii >= KT / RPI;
+        const int r0 = (isv ? ii - KT / RPI : ii) * RPI;
+        pf_dma16((isv ? vbase : kbase) + sb, loff[i], slot + (isv ? KVE : 0) + r0 * D);
+      }
+    } else {
+      // the prompt's last stage: rows past L re-read row L-1
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        const int ii = wave * NLD + i;
+        const bool isv = ii >= KT / RPI;
+        const int r0 = (isv ? ii - KT / RPI : ii) * RPI;
+        const int r = r0 + lane / LPR;
+        const int lc = (lane % LPR) ^ pswz<D>(r);
+        const int key = min(stc * KT + r, L - 1);
+        pf_dma16(isv ? vbase : kbase, (uint32_t)key * rowb + (uint32_t)lc * 16,
+                 slot + (isv ? KVE : 0) + r0 * D);
+      }
     }
   };
 
