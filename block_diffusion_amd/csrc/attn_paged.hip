@@ -22,10 +22,13 @@
 // Each wave first turns the prefix lengths into tile prefix sums itself: a
 // separate planning launch would cost more than the few loads it saves.
 //
-// Per wave, tiles go straight from global memory into a ring of kRing LDS
+// Per wave, tiles go straight from global memory into a ring of NR LDS
 // slots (global_load_lds_dwordx4, non-temporal: kKT keys of K and of V in
-// runs of 16 that never cross a page), kRing-1 tiles in flight while one is
-// computed.  A 16-row segment's query rows ride along in a small region of
+// runs of 16 that never cross a page), NR-1 tiles in flight while one is
+// computed.  NR is 2 (four waves per CU), or 3 for 16-row segments in a
+// launch whose page tables can hold kDeepRingTiles tiles or more (two waves
+// per CU, two tiles in flight each: a long stream per wave takes fewer
+// pauses; a short one pays more for filling the deeper ring).  A 16-row segment's query rows ride along in a small region of
 // its first tile's slot and go from there into the MFMA operand registers
 // (a load from global memory at that point would drain the ring: the
 // compiler's wait for it counts every load before it); larger row groups
@@ -85,7 +88,8 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 #endif
 constexpr int kKT = ATTN_KT;   // keys per tile (a multiple of 32)
 static_assert(kKT % 32 == 0, "runs of 32 keys");
-constexpr int kRing = ATTN_RING;       // ring slots per wave
+constexpr int kRing = ATTN_RING;       // ring slots per wave (the deep ring: kRing + 1)
+constexpr int kDeepRingTiles = 65536;
 constexpr int kMaxWavesPerCU = ATTN_WAVES;
 constexpr int kCUs = 256;      // MI355X compute units
 constexpr int kLdsPerCU = 160 * 1024;
@@ -659,7 +663,11 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
   p.RT = R <= 16 ? 1 : (R <= 32 ? 2 : 4);
   p.n_rg = (R + 16 * p.RT - 1) / (16 * p.RT);
   const int slot_bytes = attn_slot_bytes(D, p.RT);
-  const int waves_per_cu = std::max(1, std::min(kMaxWavesPerCU, kLdsPerCU / (kRing * slot_bytes)));
+  // tiles the page tables can hold: an upper bound of the launch's stream
+  const size_t tiles_cap = (size_t)S * Hkv * p.n_rg *
+                           ((size_t)max_pages * page_size / kKT + (B + kKT - 1) / kKT);
+  p.ring = (p.RT == 1 && tiles_cap >= (size_t)kDeepRingTiles) ? kRing + 1 : kRing;
+  const int waves_per_cu = std::max(1, std::min(kMaxWavesPerCU, kLdsPerCU / (p.ring * slot_bytes)));
   p.grid = kCUs * waves_per_cu;
   // two partial slots per wave (the segments its range cuts at either end)
   const size_t slots = (size_t)2 * p.grid * 16 * p.RT;
@@ -671,10 +679,21 @@ AttnPlan attn_plan(int S, int B, int Hq, int Hkv, int D, int page_size, int max_
 
 template <int D, int RT>
 static hipError_t launch_dr(const AttnPlan& p, const AttnArgs& a, hipStream_t st) {
-  if (a.save_state != nullptr)
-    attn_stream_kernel<D, RT, kRing, true><<<p.grid, 64, 0, st>>>(a);
-  else
-    attn_stream_kernel<D, RT, kRing, false><<<p.grid, 64, 0, st>>>(a);
+  const bool deep = RT == 1 && p.ring != kRing;
+  if constexpr (RT == 1) {
+    if (deep) {
+      if (a.save_state != nullptr)
+        attn_stream_kernel<D, RT, kRing + 1, true><<<p.grid, 64, 0, st>>>(a);
+      else
+        attn_stream_kernel<D, RT, kRing + 1, false><<<p.grid, 64, 0, st>>>(a);
+    }
+  }
+  if (!deep) {
+    if (a.save_state != nullptr)
+      attn_stream_kernel<D, RT, kRing, true><<<p.grid, 64, 0, st>>>(a);
+    else
+      attn_stream_kernel<D, RT, kRing, false><<<p.grid, 64, 0, st>>>(a);
+  }
   attn_combine_kernel<D, RT><<<a.S * a.Hkv * p.n_rg, kCombineThreads, 0, st>>>(a);
   return hipGetLastError();
 }

@@ -39,7 +39,7 @@ struct AttnArgs {
 };
 
 struct AttnPlan {
-  int D, RT, n_rg, grid;
+  int D, RT, n_rg, grid, ring;   // ring: LDS slots per wave
   size_t o_bytes, ml_bytes, ws_bytes;  // workspace: part_o | part_ml | seg_np
 };
 
