@@ -13,7 +13,7 @@ import torch
 
 import oracle
 from block_diffusion_amd import api, synth
-from block_diffusion_amd.workloads import SDAR_1P7B, TINY, Workload
+from block_diffusion_amd.workloads import SDAR_1P7B, SDAR_4B, TINY, Workload
 from gpu_util import (ATTN_MAX_ABS, ATTN_REL_L2, RoundState, attn_errors, check_lm_rows,
                       dev_bf16, dev_i32, dev_u8, host_bits, round_inputs_dev, widen_bits)
 
@@ -47,6 +47,16 @@ def _save_case(name):
         w = Workload(name="save_rt4", seed_id=41, S=5, B=5, Hq=32, Hkv=2, D=64, P=32,
                      Hd=256, V=1024, mask_id=7, prefix_lo=0, prefix_hi=90, tau=0.9, rounds=5,
                      a_max=12.0, prefix_fixed=(30, 1, 90, 0, 63))
+    elif name == "deep_ring_ragged":
+        # page tables that can hold 66 K tiles (the attention takes its
+        # three-slot ring) over mostly short, empty and page-crossing
+        # prefixes: short tile streams per wave
+        lens = (0, 1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 300, 511, 512, 1000, 4000) * 4
+        w = Workload(name="save_deep_ring", seed_id=43, S=64, B=4, Hq=32, Hkv=8, D=128, P=256,
+                     Hd=256, V=1024, mask_id=7, prefix_lo=0, prefix_hi=4000, tau=0.9, rounds=4,
+                     a_max=12.0, prefix_fixed=lens)
+    elif name == "sdar4b":
+        w = SDAR_4B
     else:
         w = SDAR_1P7B
     fx = synth.make_fixed(w, with_w=False, reserve_tokens=2 * w.B)
@@ -54,7 +64,8 @@ def _save_case(name):
     return w, fx, rin
 
 
-@pytest.mark.parametrize("name", ["tiny", "ragged_d128", "rt4_d64", "llada_b64", "sdar1p7b"])
+@pytest.mark.parametrize("name", ["tiny", "ragged_d128", "rt4_d64", "llada_b64", "sdar1p7b",
+                                  "deep_ring_ragged", "sdar4b"])
 def test_attn_save_parity(name):
     w, fx, rin = _save_case(name)
     g = np.random.default_rng(w.seed_id + 77)
