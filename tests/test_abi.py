@@ -87,9 +87,14 @@ def test_attn_workspace_required():
     st = L.dbd_attn_paged(128, 4, 32, 8, 128, 256, 16, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, 16, need - 1, None)
     assert st == api.DBD_ERR_WORKSPACE
     # the tile plan and the split-segment partials always need some space
+    # (two partial slots per wave of the launch: the SDAR-4B launch above
+    # runs fewer, deeper-ringed waves than this small one, so the sizes are
+    # not ordered by the problem size)
     small = api.dbd_attn_workspace_size(2, 4, 4, 2, 64, 16, 3)
-    assert 0 < small < need
+    assert small > 0
     st = L.dbd_attn_paged(2, 4, 4, 2, 64, 16, 3, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, None, 0, None)
+    assert st == api.DBD_ERR_WORKSPACE
+    st = L.dbd_attn_paged(2, 4, 4, 2, 64, 16, 3, 16, 16, 16, 16, 16, 16, 16, 0.0, 16, 16, small - 1, None)
     assert st == api.DBD_ERR_WORKSPACE
 
 
