@@ -58,14 +58,15 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_table(workload):
+def traffic_table(workload, path=None):
     """HBM bytes per launch measured with rocprofv3 FETCH_SIZE/WRITE_SIZE
     (scaled by the copy calibration), keyed by entry point and row count.
     An entry counts only while the kernel source it was taken on is
     unchanged (sha256 recorded beside it); otherwise the figure is None."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
+    if path is None:
+        path = os.path.join(ROOT, "profiles", f"traffic_{workload}.md")
     table = {}
     if not os.path.exists(path):
         return table
