@@ -44,6 +44,13 @@ ATTN_SMALL = [
     # block of one token, D=64, 64 rows from G=64
     _custom("g64_b1", 105, S=2, B=1, Hq=64, Hkv=1, D=64, P=64,
             prefix_fixed=(64, 129), prefix_hi=129),
+    # page tables that hold 65568 tiles: the three-slot ring, with 9 rows per
+    # segment (padded to 16) and one 64 K-token prefix cut over many waves
+    _custom("deep_ring_rows9_d128", 106, S=4, B=3, Hq=24, Hkv=8, D=128, P=256,
+            prefix_fixed=(0, 5, 65536, 300), prefix_hi=65536),
+    # the same at D=64, where the three-slot ring still leaves four waves per CU
+    _custom("deep_ring_rows8_d64", 107, S=4, B=4, Hq=16, Hkv=8, D=64, P=256,
+            prefix_fixed=(0, 5, 65536, 300), prefix_hi=65536),
 ]
 
 
