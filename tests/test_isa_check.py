@@ -50,3 +50,18 @@ def test_branch_sources_are_followed():
     body = ("\tv_readlane_b32 s5, v255, 5\n\ts_nop 4\n\ts_cbranch_scc1 .LBB0_3\n\ts_branch .LBB0_9\n"
             ".LBB0_3:\n\tglobal_load_lds_dwordx4 v2, s[4:5]\n")
     assert _scan(body)[1] == []
+
+
+def test_stage_base_moved_by_scalar_arithmetic():
+    # the prefill's full-stage loads: the 64-bit base advanced by scalar
+    # multiply and add-with-carry (SALU writes need no wait states) ...
+    body = ("\ts_mul_hi_u32 s1, s55, s22\n\ts_mul_i32 s0, s55, s22\n\ts_lshl_b64 s[0:1], s[0:1], 5\n"
+            "\ts_add_u32 s0, s6, s0\n\ts_addc_u32 s1, s7, s1\n\ts_add_i32 m0, s53, s47\n"
+            "\ts_nop 4\n\tglobal_load_lds_dwordx4 v120, s[0:1]\n")
+    n, h = _scan(body)
+    assert n == 1 and h == []
+    # ... but the same base taken from a VALU lane read needs five
+    body = ("\tv_readfirstlane_b32 s1, v7\n\ts_add_i32 m0, s53, s47\n"
+            "\ts_nop 0\n\tglobal_load_lds_dwordx4 v120, s[0:1]\n")
+    n, h = _scan(body)
+    assert n == 1 and len(h) == 1 and h[0][3].startswith("v_readfirstlane_b32 s1")
