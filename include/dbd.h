@@ -479,7 +479,7 @@ size_t dbd_round_workspace_size(const dbd_round_args* a);
  * routine that allocates); its first call on a device looks up that
  * device's array address once.  Returns DBD_ERR_WORKSPACE, before any HIP
  * call, when dbd_round_workspace_size(a) exceeds the array (e.g. the
- * SDAR-8B and LLaDA shapes of block 16 and 64 need 104 and 149 MiB); the
+ * SDAR-8B and LLaDA shapes of block 16 and 64 need 71 and 68 MiB); the
  * other checks are dbd_round's.  The array's contents are not cleared and
  * need not be: every call writes what it reads.  All calls on one device
  * share that device's array, so calls that overlap in time on one device
