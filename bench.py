@@ -592,8 +592,9 @@ def config_entry(api, synth, w, dev, steps):
     """Workload w as whole blocks: the rounds from the initial state until
     no masked row is left (each round's inputs drawn as for the parity
     tests), captured as one graph and replayed `steps` times after a
-    warm-up; per-round eager times; attention, LM head (round-1 rows) and
-    remask per launch with their roofline fractions."""
+    warm-up, and again with the 256 MB MALL flushed before each replay (the
+    cold figure); per-round eager times; attention, LM head (round-1 rows)
+    and remask per launch with their roofline fractions."""
     import numpy as np
     import torch
 
@@ -659,8 +660,23 @@ def config_entry(api, synth, w, dev, steps):
         graph.launch()
     torch.cuda.synchronize()
     ms_block = (time.perf_counter() - t1) * 1e3 / steps
-    graph.close()
+    # the same block with the 256 MB MALL flushed before it (a 512 MB scratch
+    # write, untimed): the cold figure
     stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(max(steps // 2, 3)):
+        reset()
+        flush.fill_(1)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.launch()
+        e1.record(stream)
+        e1.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    del flush
+    ms_cold = float(np.median(cold))
+    graph.close()
     ra = [mk(pr) for pr in per_round]
     times = [[] for _ in ra]
     for _ in range(3):
@@ -709,6 +725,8 @@ def config_entry(api, synth, w, dev, steps):
     w_bytes = 2.0 * w.V * w.Hd
     ent = {"rounds": R, "rows_per_round": rows, "ms_per_block": round(ms_block, 4),
            "block_tokens_per_s": round(w.S * w.B * R / (ms_block * 1e-3), 1),
+           "cold_ms_per_block": round(ms_cold, 4),
+           "cold_block_tokens_per_s": round(w.S * w.B * R / (ms_cold * 1e-3), 1),
            "per_round_eager_us": [round(t, 1) for t in round_us],
            "attention_us": round(t_attn, 2), "attention_bytes": a_bytes,
            "attention_frac_hbm": round(a_bytes / (t_attn * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
@@ -720,7 +738,7 @@ def config_entry(api, synth, w, dev, steps):
            "lmhead_w_frac_hbm": round(w_bytes / (t_lm * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
            "remask_us": round(t_remask, 2)}
     log(f"{w.name}: {R} rounds (rows {rows[0]} -> {rows[-1]}), {ms_block:.3f} ms per block = "
-        f"{ent['block_tokens_per_s']:.0f} block-tokens/s; attention {t_attn:.1f} us "
+        f"{ent['block_tokens_per_s']:.0f} block-tokens/s (cold {ms_cold:.3f} ms); attention {t_attn:.1f} us "
         f"({ent['attention_frac_hbm']:.1%} of HBM), LM head {t_lm:.1f} us at {rows[0]} rows "
         f"({ent['lmhead_frac_mfma']:.1%} of bf16 MFMA), remask {t_remask:.1f} us "
         f"[{time.time() - t0:.1f} s]")
