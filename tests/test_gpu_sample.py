@@ -18,8 +18,8 @@ import torch
 import oracle
 from block_diffusion_amd import api, synth
 from block_diffusion_amd.workloads import SDAR_1P7B, TINY
-from gpu_util import (CONF_ABS, RoundState, check_filtered_rows, dev_bf16, dev_i32, round_inputs_dev,
-                      widen_bits)
+from gpu_util import (CONF_ABS, RoundState, check_filtered_rows, check_lm_rows, dev_bf16, dev_i32,
+                      round_inputs_dev, widen_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -203,3 +203,47 @@ def test_round_filtered_teacher_forced(w, k, p):
             break
     assert np.all(state == oracle.SAVING)
 
+
+
+@pytest.mark.parametrize("M", [1025, 1500, 2100])
+def test_lmhead_modes_many_rows(M):
+    """More than 1024 listed rows: the tile kernel runs passes of 1024 rows
+    with four-member teams, the last pass ragged.  The greedy head with the
+    entropy, and the temperature-sampling head, on sampled rows (the first
+    and last of each pass among them) against the oracle; every listed row
+    written, the other rows untouched."""
+    g = np.random.default_rng(M)
+    V, Hd, n, mask = 2003, 256, M + 100, 77     # V not a multiple of 32
+    wv = synth.normal_bf16(g, (V, Hd), std=1.0 / np.sqrt(Hd))
+    t = g.integers(0, V, n)
+    a = g.uniform(0, 14, n)
+    wt = widen_bits(wv[t])
+    wt /= np.linalg.norm(wt, axis=1, keepdims=True)
+    h = synth.f32_to_bf16((g.standard_normal((n, Hd)) + a[:, None] * wt).astype(np.float32))
+    rows = g.permutation(n)[:M].astype(np.int32)
+    ends = [0, 1023, 1024, M - 1] + ([2047, 2048] if M > 2048 else [])
+    samp = np.unique(np.concatenate([rows[g.choice(M, 30, replace=False)], rows[ends]]))
+    others = np.setdiff1d(np.arange(n), rows)
+    ri, nr = dev_i32(rows), dev_i32([M])
+
+    # greedy, with the entropy
+    arg = torch.full((n,), -7, dtype=torch.int32, device="cuda")
+    conf = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    ent = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+    api.dbd_lmhead_conf(dev_bf16(h), dev_bf16(wv), nr, arg, conf, mask, row_index=ri, max_rows=M, entropy=ent)
+    torch.cuda.synchronize()
+    arg, conf, ent = arg.cpu().numpy(), conf.cpu().numpy(), ent.cpu().numpy()
+    check_lm_rows(samp, arg, conf, h, wv, mask)
+    ref = oracle.lmhead_entropy(h[samp], wv, mask)
+    assert np.abs(ent[samp].astype(np.float64) - ref).max() <= ENT_TOL
+    assert np.all((arg[rows] >= 0) & (arg[rows] < V) & (arg[rows] != mask))
+    assert np.all(arg[others] == -7) and np.all(np.isnan(conf[others])) and np.all(np.isnan(ent[others]))
+
+    # temperature sampling
+    T, seed, step = 0.8, 0x5A17 + M, 3
+    tok, sconf, _ = _run(h, wv, mask, rows, T, seed, step)
+    ex = check_draws(samp, tok, sconf, h, wv, mask, T, seed, step)
+    print(f"M={M}: {len(samp)} sampled rows, {ex} draws exempt", flush=True)
+    assert ex <= 2
+    assert np.all((tok[rows] >= 0) & (tok[rows] < V) & (tok[rows] != mask))
+    assert np.all(tok[others] == -7)
