@@ -215,6 +215,10 @@ class RoundState:
                 max_pages_per_seq=self.maxp, Hd=w.Hd, V=w.V, mask_token_id=w.mask_id,
                 dynamic_threshold=w.tau, attn_out=attn_out, bufs=self.bufs, **rin_dev,
                 **self.fixed)
+        # the args hold raw pointers: keep the round's input tensors alive
+        # until the next round's args, so that no later allocation can take
+        # their memory before the round has run
+        self.inputs = (rin_dev, attn_out)
         return a
 
 

@@ -1,7 +1,8 @@
 """dbd_round_noalloc (the round with the library's static scratch as its
 workspace) against dbd_round with a caller workspace: bit-identical outputs
-on two calls in a row, the second with a smaller input; and the host-side
-rejection of a round whose workspace exceeds the scratch."""
+on two calls in a row, the second with a smaller input, greedy and with
+top-p filtered sampling; and the host-side rejection of a round whose
+workspace exceeds the scratch."""
 import numpy as np
 import pytest
 import torch
@@ -13,12 +14,18 @@ from gpu_util import RoundState, round_inputs_dev
 pytestmark = pytest.mark.gpu
 
 
-def _one(w, fx, rnd, noalloc):
-    """One round of workload w from its initial state; returns every output."""
+def _one(w, fx, rnd, noalloc, filtered=False):
+    """One round of workload w from its initial state; returns every output.
+    filtered: temperature 0.7, top_p 0.9 (stored logits, filtered draw)."""
     st = RoundState(w, fx)
     st.init_rows()
     attn_out = torch.full((w.S, w.B, w.Hq, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
     args = st.args(round_inputs_dev(synth.make_round(w, rnd, fx.w_vocab)), attn_out)
+    logits = None
+    if filtered:
+        logits = torch.full((w.S * w.B, w.V), float("nan"), dtype=torch.float32, device="cuda")
+        args.sample, args.temperature, args.seed, args.step = 1, 0.7, 0xA110C + rnd, rnd
+        args.filter, args.top_k, args.top_p, args.logits = 1, 0, 0.9, logits.data_ptr()
     if noalloc:
         # the workspace fields must not be read: point them at nothing
         args.workspace = None
@@ -40,20 +47,34 @@ def _same(x, y):
 
 
 def test_noalloc_matches_round_twice():
-    """The SDAR-1.7B shapes (6.8 MiB of workspace), then the tiny workload
-    (79 KiB): each equal bit for bit to dbd_round on the same inputs; the
+    """The SDAR-1.7B shapes (17.0 MiB of workspace), then the tiny workload
+    (8.3 MiB): each equal bit for bit to dbd_round on the same inputs; the
     second call finds the first call's data in the scratch."""
     for w, rnd in ((SDAR_1P7B, 1), (TINY, 2)):
         fx = synth.make_fixed(w)
         ref = _one(w, fx, rnd, noalloc=False)
         got = _one(w, fx, rnd, noalloc=True)
         _same(ref, got)
-        assert got["n"] < w.S * w.B or w is TINY
+        assert got["n"] <= w.S * (w.B - 1)      # every sequence committed
         print(f"{w.name} round {rnd}: equal, {got['n']} rows left", flush=True)
 
 
+def test_noalloc_filtered_matches_round():
+    """Rounds with top-p filtered sampling (the LM head stores the logits and
+    the filtered draw reads the row maxima it leaves in the workspace):
+    the SDAR-1.7B shapes, then the tiny workload, each equal bit for bit to
+    dbd_round."""
+    for w, rnd in ((SDAR_1P7B, 2), (TINY, 1)):
+        fx = synth.make_fixed(w)
+        ref = _one(w, fx, rnd, noalloc=False, filtered=True)
+        got = _one(w, fx, rnd, noalloc=True, filtered=True)
+        _same(ref, got)
+        assert got["n"] <= w.S * (w.B - 1)      # every sequence committed
+        print(f"{w.name} round {rnd} filtered: equal, {got['n']} rows left", flush=True)
+
+
 def test_noalloc_rejects_beyond_scratch():
-    """The SDAR-8B shapes need about 104 MiB of workspace: rejected with
+    """The SDAR-8B shapes need 71.0 MiB of workspace: rejected with
     DBD_ERR_WORKSPACE before anything is enqueued."""
     w = SDAR_8B
     n = w.S * w.B
