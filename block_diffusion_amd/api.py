@@ -181,6 +181,18 @@ def workspace(nbytes, device="cuda"):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _launch_ws(nbytes, device, stream):
+    """A workspace the binding allocates for one launch.  When the launch
+    goes to a stream the caller names, the allocator is told that stream
+    uses the buffer, so that its memory is not handed out again (to work on
+    torch's current stream) while the launch may still run."""
+    t = workspace(nbytes, device)
+    if stream is not None:
+        s = torch.cuda.ExternalStream(stream, device=t.device) if isinstance(stream, int) else stream
+        t.record_stream(s)
+    return t
+
+
 def dbd_attn_paged(q, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len, out,
                    softmax_scale=0.0, ws=None, stream=None):
     S, B, Hq, D = q.shape
@@ -199,7 +211,7 @@ def dbd_attn_paged(q, k_blk, v_blk, k_cache, v_cache, page_table, prefix_len, ou
     _need(prefix_len, torch.int32, (S,), "prefix_len")
     need = dbd_attn_workspace_size(S, B, Hq, Hkv, D, P, maxp)
     if ws is None and need:
-        ws = workspace(need, q.device)
+        ws = _launch_ws(need, q.device, stream)
     nbytes = ws.numel() if ws is not None else 0
     _check(lib().dbd_attn_paged(S, B, Hq, Hkv, D, P, maxp, _ptr(q), _ptr(k_blk), _ptr(v_blk),
                                 _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
@@ -228,7 +240,7 @@ def dbd_attn_paged_save(q, k_blk, v_blk, k_cache, v_cache, page_table, prefix_le
     _need(seq_state, torch.uint8, (S,), "seq_state")
     need = dbd_attn_workspace_size(S, B, Hq, Hkv, D, P, maxp)
     if ws is None and need:
-        ws = workspace(need, q.device)
+        ws = _launch_ws(need, q.device, stream)
     nbytes = ws.numel() if ws is not None else 0
     _check(lib().dbd_attn_paged_save(S, B, Hq, Hkv, D, P, maxp, npages, _ptr(q), _ptr(k_blk),
                                      _ptr(v_blk), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
@@ -271,7 +283,7 @@ def dbd_lmhead_conf(hidden, w_vocab, num_rows, argmax_tok, conf, mask_token_id,
             raise ValueError("row_index must be int32 with at least max_rows entries")
     need = dbd_lmhead_workspace_size(max_rows, V)
     if ws is None and need:
-        ws = workspace(need, hidden.device)
+        ws = _launch_ws(need, hidden.device, stream)
     nb = ws.numel() if ws is not None else 0
     if entropy is None:
         _check(lib().dbd_lmhead_conf(max_rows, Hd, V, int(mask_token_id), _ptr(hidden),
@@ -299,7 +311,7 @@ def dbd_lmhead_sample(hidden, w_vocab, num_rows, token, conf, mask_token_id, tem
     _need(num_rows, torch.int32, (1,), "num_rows")
     need = dbd_lmhead_workspace_size(max_rows, V)
     if ws is None and need:
-        ws = workspace(need, hidden.device)
+        ws = _launch_ws(need, hidden.device, stream)
     nb = ws.numel() if ws is not None else 0
     _check(lib().dbd_lmhead_sample(max_rows, Hd, V, int(mask_token_id), _ptr(hidden),
                                    _ptr(row_index), _ptr(num_rows), _ptr(w_vocab),
@@ -328,7 +340,7 @@ def dbd_prefill_attn(q, k, v, cu_seqlens, out, block_length, softmax_scale=0.0, 
         _need(page_table, torch.int32, (S, maxp), "page_table")
     need = lib().dbd_prefill_workspace_size(S)
     if ws is None:
-        ws = workspace(need, q.device)
+        ws = _launch_ws(need, q.device, stream)
     _check(lib().dbd_prefill_attn(S, T, Hq, Hkv, D, int(block_length), _ptr(q), _ptr(k), _ptr(v),
                                   _ptr(cu_seqlens), float(softmax_scale), _ptr(out), P, maxp,
                                   npages, _ptr(page_table), _ptr(k_cache), _ptr(v_cache),

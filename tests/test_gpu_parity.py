@@ -122,6 +122,42 @@ def test_attention_deterministic():
     assert np.array_equal(run_attn(fx, rin), run_attn(fx, rin))
 
 
+def test_side_stream_binding_workspace():
+    """Attention and the LM head launched on a stream the caller names (a
+    torch stream, then its raw handle), with the workspace the binding
+    allocates itself, while the current stream allocates and fills memory
+    right after each launch: the same bits as the launches on the current
+    stream."""
+    w = SDAR_1P7B
+    fx = synth.make_fixed(w)
+    rin = synth.make_round(w, 1, fx.w_vocab)
+    ref = run_attn(fx, rin)
+    rows = np.arange(w.S * w.B, dtype=np.int32)
+    arg_ref, conf_ref = _lm_run(rin.hidden, fx.w_vocab, w.mask_id, rows)
+    q, kb, vb = dev_bf16(rin.q), dev_bf16(rin.k_blk), dev_bf16(rin.v_blk)
+    kc, vc = dev_bf16(fx.k_cache), dev_bf16(fx.v_cache)
+    pt, pl = dev_i32(fx.page_table), dev_i32(fx.prefix_len)
+    h, wv, ri, nr = dev_bf16(rin.hidden), dev_bf16(fx.w_vocab), dev_i32(rows), dev_i32([rows.size])
+    side = torch.cuda.Stream()
+    for handle in (False, True):
+        st = side.cuda_stream if handle else side
+        out = torch.empty((w.S, w.B, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+        arg = torch.full((rows.size,), -7, dtype=torch.int32, device="cuda")
+        conf = torch.full((rows.size,), float("nan"), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        api.dbd_attn_paged(q, kb, vb, kc, vc, pt, pl, out, stream=st)
+        # sizes that fit the freed workspaces' blocks (the attention's in
+        # the large pool, the LM head's in the small one)
+        junk = [torch.full((n,), 7.0, device="cuda") for n in (1 << 19, 1 << 17) * 4]
+        api.dbd_lmhead_conf(h, wv, nr, arg, conf, w.mask_id, row_index=ri, max_rows=rows.size, stream=st)
+        junk += [torch.full((n,), 9.0, device="cuda") for n in (1 << 19, 1 << 17) * 4]
+        torch.cuda.synchronize()
+        del junk
+        assert np.array_equal(host_bits(out), ref), f"attention, handle={handle}"
+        assert np.array_equal(arg.cpu().numpy(), arg_ref[rows]), f"LM head tokens, handle={handle}"
+        assert np.array_equal(conf.cpu().numpy(), conf_ref[rows]), f"LM head conf, handle={handle}"
+
+
 @pytest.fixture(scope="module")
 def big_fixed():
     """Fixed inputs of the SDAR-8B (B=16) and LLaDA (B=64, 16K-32K prefix)
