@@ -441,8 +441,12 @@ def make_round_args(*, S, B, Hq, Hkv, D, page_size, max_pages_per_seq, Hd, V, ma
                     softmax_scale=0.0, rule=0, tokens_per_step=1, eb_threshold=0.0,
                     entropy=None, save_kv=False, token_stream=None,
                     end_len=None) -> dbd_round_args:
-    """save_kv: the round is a whole step for a batch with SAVING sequences
-    (their block K/V go into the cache, their blocks are committed)."""
+    """The C argument block of one round.  It holds the tensors' raw device
+    addresses, not the tensors: the caller keeps every tensor passed here
+    alive (and bufs.workspace unchanged) for as long as the block, or a
+    graph captured from it, can be launched.  save_kv: the round is a whole
+    step for a batch with SAVING sequences (their block K/V go into the
+    cache, their blocks are committed)."""
     a = dbd_round_args()
     a.S, a.B, a.Hq, a.Hkv, a.D = S, B, Hq, Hkv, D
     a.page_size, a.max_pages_per_seq, a.Hd, a.V = page_size, max_pages_per_seq, Hd, V
