@@ -489,7 +489,10 @@ def dbd_round_noalloc(args: dbd_round_args, stream=None):
 
 
 class Graph:
-    """n_rounds captured rounds replayed with one launch (dbd_graph_*)."""
+    """n_rounds captured rounds replayed with one launch (dbd_graph_*).  The
+    graph keeps the device addresses its rounds were captured with: every
+    tensor behind those argument blocks stays alive, at the same address,
+    until close()."""
 
     def __init__(self, args_list):
         arr = (dbd_round_args * len(args_list))(*args_list)
