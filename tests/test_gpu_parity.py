@@ -54,6 +54,49 @@ ATTN_SMALL = [
 ]
 
 
+def _random_attn_shapes(n, seed=2024):
+    """Seeded random shapes within the boundary's limits (B <= 64, D 64 or
+    128, page size a multiple of 16): GQA widths 1..16, several page sizes,
+    prefixes from empty through page-aligned to a few thousand tokens."""
+    g = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        D = int(g.choice([64, 128]))
+        Hkv = int(g.integers(1, 9))
+        G = int(g.choice([1, 2, 3, 4, 6, 8, 16]))
+        B = int(g.choice([1, 2, 3, 4, 5, 8, 16, 31, 64]))
+        while G * B > 256:
+            B = max(1, B // 2)
+        P = int(g.choice([16, 32, 64, 128, 256]))
+        S = int(g.integers(1, 12))
+        L = g.integers(0, 2500, S)
+        pick = g.integers(0, 4, S)            # 0: as drawn, 1: empty, 2: whole pages, 3: a page minus one
+        L = np.where(pick == 1, 0, np.where(pick == 2, (L // P) * P,
+                                            np.where(pick == 3, np.maximum(P - 1, (L // P) * P - 1), L)))
+        if L.max() == 0:
+            L[0] = P + 1                      # the cache needs a page; one prefix crosses into a second
+        shapes.append(_custom(f"rand{i}_s{S}_b{B}_g{G}x{Hkv}_d{D}_p{P}", 300 + i, S=S, B=B, Hq=G * Hkv,
+                              Hkv=Hkv, D=D, P=P, prefix_fixed=tuple(int(x) for x in L),
+                              prefix_hi=max(1, int(L.max()))))
+    return shapes
+
+
+@pytest.mark.parametrize("w", _random_attn_shapes(12), ids=lambda w: w.name)
+def test_attention_parity_random_shapes(w):
+    """Seeded random shapes: up to 8 (sequence, kv head) groups, among them
+    the first and the last, against the oracle."""
+    fx = synth.make_fixed(w, with_w=False)
+    rin = synth.make_round(w, 1, None)
+    out = run_attn(fx, rin)
+    allg = [(s, g) for s in range(w.S) for g in range(w.Hkv)]
+    rng = np.random.default_rng(w.seed_id)
+    idx = sorted(set([0, len(allg) - 1] + list(rng.choice(len(allg), min(6, len(allg)), replace=False))))
+    ref = oracle_attn_groups(fx, rin, [allg[i] for i in idx])
+    mx, rl2 = compare_attn(out, ref, w.G)
+    print(f"{w.name} prefixes {list(w.prefix_fixed)}: max abs {mx:.3e} rel L2 {rl2:.3e}", flush=True)
+    assert mx <= ATTN_MAX_ABS and rl2 <= ATTN_REL_L2
+
+
 @pytest.mark.parametrize("w", ATTN_SMALL, ids=lambda w: w.name)
 def test_attention_parity_small(w):
     fx = synth.make_fixed(w, with_w=False)
