@@ -145,3 +145,53 @@ def test_prefill_many_short_prompts():
     assert mx <= ATTN_MAX_ABS and rl <= ATTN_REL_L2, (mx, rl)
     ek, ev = oracle.prefill_store(store[1], store[2], store[0], k, v, cu)
     assert np.array_equal(kc, ek) and np.array_equal(vc, ev)
+
+
+def _random_prefill_shapes(n, seed=4242):
+    """Seeded random shapes within the boundary's limits: G a power of two
+    dividing the 128 query rows of a workgroup, D 64 or 128, blocks of 1 to
+    64 tokens, page sizes 16 to 256; prompt lengths from empty through one
+    token, a block minus one and whole blocks to about 1200 tokens."""
+    g = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        D = int(g.choice([64, 128]))
+        Hkv = int(g.integers(1, 9))
+        G = int(g.choice([1, 2, 4, 8, 16]))
+        B = int(g.choice([1, 2, 3, 4, 7, 16, 64]))
+        P = int(g.choice([16, 32, 64, 128, 256]))
+        S = int(g.integers(1, 9))
+        lens = g.integers(0, 1200, S)
+        pick = g.integers(0, 5, S)
+        lens = np.where(pick == 1, 0, np.where(pick == 2, 1, np.where(pick == 3, np.maximum(B - 1, 0),
+                                                                        np.where(pick == 4, (lens // B) * B, lens))))
+        shapes.append((f"rand{i}_s{S}_g{G}x{Hkv}_d{D}_b{B}_p{P}", tuple(int(x) for x in lens), G * Hkv, Hkv, D, B,
+                       P))
+    return shapes
+
+
+@pytest.mark.parametrize("case", _random_prefill_shapes(8), ids=lambda c: c[0])
+def test_prefill_random_shapes(case):
+    """Seeded random shapes: sampled rows (each prompt's first and last
+    among them) against the oracle, and the K/V store bit for bit."""
+    name, lens, Hq, Hkv, D, B, P = case
+    print(f"{name}: lens {lens}", flush=True)
+    q, k, v, cu = _prompts(sum(name.encode()), lens, Hq, Hkv, D)
+    store = _paged(7, lens, Hkv, D, P)
+    out, (kc, vc) = _run(q, k, v, cu, B, store)
+    g = np.random.default_rng(len(name))
+    picks = []
+    for s, L in enumerate(lens):
+        if L == 0:
+            continue
+        for i in {0, L - 1, int(g.integers(0, L)), int(g.integers(0, L))}:
+            picks.append((s, i, int(g.integers(0, Hq))))
+    if picks:
+        ref = _rows_ref(q, k, v, cu, B, picks)
+        got = np.stack([widen_bits(out[int(cu[s]) + i, h]) for s, i, h in picks])
+        mx, rl = attn_errors(got, ref)
+        print(f"  {len(picks)} rows: max abs {mx:.3g}, rel L2 {rl:.3g}", flush=True)
+        assert mx <= ATTN_MAX_ABS and rl <= ATTN_REL_L2
+    assert not np.any(np.isnan(widen_bits(out)))
+    ek, ev = oracle.prefill_store(store[1], store[2], store[0], k, v, cu)
+    assert np.array_equal(kc, ek) and np.array_equal(vc, ev)
