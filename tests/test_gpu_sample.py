@@ -247,3 +247,55 @@ def test_lmhead_modes_many_rows(M):
     assert ex <= 2
     assert np.all((tok[rows] >= 0) & (tok[rows] < V) & (tok[rows] != mask))
     assert np.all(tok[others] == -7)
+
+
+def _random_lm_shapes(n, seed=777):
+    """Seeded random LM-head shapes: hidden sizes 128..1024 (multiples of
+    128), vocabularies from 2 (one candidate) to 40000 (ragged ends), any
+    mask id, 1..1300 listed rows out of a larger buffer."""
+    g = np.random.default_rng(seed)
+    shapes = []
+    for i in range(n):
+        # vocabularies and row counts cycle through their lists, the rest is drawn
+        Hd = int(g.choice([128, 256, 384, 640, 1024]))
+        V = (2, 33, 257, 1000, 4099, 40000)[i % 6]
+        mask = int(g.integers(0, V))
+        M = (1, 1300, 64, 1025, 257, 600, 7, 255)[i % 8]
+        extra = int(g.integers(0, 40))
+        shapes.append((f"rand{i}_hd{Hd}_v{V}_m{M}", Hd, V, mask, M, M + extra))
+    return shapes
+
+
+@pytest.mark.parametrize("case", _random_lm_shapes(8), ids=lambda c: c[0])
+def test_lmhead_random_shapes(case):
+    """Seeded random shapes: greedy token and confidence, entropy, and the
+    temperature draw on sampled rows (the first and last listed among them)
+    against the oracle; rows outside the list untouched."""
+    name, Hd, V, mask, M, nbuf = case
+    g = np.random.default_rng(sum(name.encode()))
+    wv = synth.normal_bf16(g, (V, Hd), std=1.0 / np.sqrt(Hd))
+    t = g.integers(0, V, nbuf)
+    a = g.uniform(0, 14, nbuf)
+    wt = widen_bits(wv[t])
+    wt /= np.linalg.norm(wt, axis=1, keepdims=True)
+    h = synth.f32_to_bf16((g.standard_normal((nbuf, Hd)) + a[:, None] * wt).astype(np.float32))
+    rows = g.permutation(nbuf)[:M].astype(np.int32)
+    samp = np.unique(np.concatenate([rows[g.choice(M, min(M, 20), replace=False)], rows[[0, M - 1]]]))
+    others = np.setdiff1d(np.arange(nbuf), rows)
+    ri, nr = dev_i32(rows), dev_i32([M])
+    arg = torch.full((nbuf,), -7, dtype=torch.int32, device="cuda")
+    conf = torch.full((nbuf,), float("nan"), dtype=torch.float32, device="cuda")
+    ent = torch.full((nbuf,), float("nan"), dtype=torch.float32, device="cuda")
+    api.dbd_lmhead_conf(dev_bf16(h), dev_bf16(wv), nr, arg, conf, mask, row_index=ri, max_rows=M, entropy=ent)
+    torch.cuda.synchronize()
+    arg, conf, ent = arg.cpu().numpy(), conf.cpu().numpy(), ent.cpu().numpy()
+    check_lm_rows(samp, arg, conf, h, wv, mask)
+    ref = oracle.lmhead_entropy(h[samp], wv, mask)
+    assert np.abs(ent[samp].astype(np.float64) - ref).max() <= ENT_TOL
+    assert np.all(arg[others] == -7) and np.all(np.isnan(conf[others]))
+    T, seed, step = 0.9, 0x77 + M, 2
+    tok, sconf, _ = _run(h, wv, mask, rows, T, seed, step)
+    ex = check_draws(samp, tok, sconf, h, wv, mask, T, seed, step)
+    print(f"{name}: {len(samp)} rows, {ex} draws exempt", flush=True)
+    assert ex <= 2
+    assert np.all(tok[others] == -7)
