@@ -234,3 +234,46 @@ def test_sample_filtered_full_vocab_overflow(T, k, p):
                              T, k, p, seed, step)
     print(f"T={T} k={k} p={p}: {M} rows, {ex} exempt", flush=True)
     assert ex <= 1
+
+
+def _random_filter_cases(n, seed=909):
+    """Seeded random draws: vocabularies with ragged ends, 1..300 rows,
+    temperatures 0.2..3, top_k off or 1..V, top_p off or 0..1; logits as
+    Gaussians of random spread, some rows with ties and -inf entries."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        V = (997, 5003, 20000, 151936)[i % 4]
+        M = int(g.choice([1, 3, 17, 128, 300]))
+        T = float(np.round(g.uniform(0.2, 3.0), 3))
+        k = int(g.choice([0, 0, 1, 5, 200, V // 2]))
+        p = float(g.choice([1.0, 0.5, 0.9, 0.95, 0.999, 0.0]))
+        cases.append((f"rand{i}_v{V}_m{M}_t{T}_k{k}_p{p}", V, M, T, k, p))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_filter_cases(8), ids=lambda c: c[0])
+def test_sample_filtered_random(case):
+    name, V, M, T, k, p = case
+    g = np.random.default_rng(sum(name.encode()))
+    mask = int(g.integers(0, V))
+    spread = g.uniform(0.3, 4.0, M)[:, None]
+    lg_h = (g.standard_normal((M, V)) * spread).astype(np.float32)
+    for r in range(0, M, 3):                          # every third row: a run of ties and some -inf
+        lg_h[r, g.choice(V, max(2, V // 50), replace=False)] = np.float32(lg_h[r].max() * 0.5)
+        lg_h[r, g.choice(V, max(1, V // 100), replace=False)] = -np.inf
+    lg_h[:, mask] = -np.inf
+    rows = g.permutation(M + 5)[:M].astype(np.int32)
+    lg = torch.from_numpy(lg_h).to("cuda")
+    tok = torch.full((M + 5,), -9, dtype=torch.int32, device="cuda")
+    conf = torch.full((M + 5,), float("nan"), dtype=torch.float32, device="cuda")
+    seed, step = 0xF11 + M, 9
+    api.dbd_sample_filtered(lg, dev_i32([M]), tok, conf, mask, T, k, p, seed, step, row_index=dev_i32(rows),
+                            max_rows=M)
+    torch.cuda.synchronize()
+    t, c = tok.cpu().numpy(), conf.cpu().numpy()
+    samp = np.unique(np.concatenate([np.arange(min(M, 6)), [M - 1], g.choice(M, min(M, 10), replace=False)]))
+    ex = check_filtered_rows(lg_h[samp], rows[samp], t, c, mask, T, k, p, seed, step)
+    print(f"{name}: {len(samp)} rows checked, {ex} exempt", flush=True)
+    assert ex <= max(1, len(samp) // 10)
+    assert np.all(t[np.setdiff1d(np.arange(M + 5), rows)] == -9)
