@@ -175,3 +175,56 @@ def test_round_rule_teacher_forced(w, rule, k, eb):
         if not np.any(state == oracle.DENOISING):
             break
     assert np.all(state == oracle.SAVING)
+
+
+def _random_remask_cases(n, seed=31337):
+    """Seeded random remask inputs: every rule, batches of 1..2500 sequences,
+    block lengths 1..64 including odd ones (segments padded to the next power
+    of two), thresholds below 0 and above 1, the leftmost fallback, NaN
+    confidences and entropies, argmax tokens equal to the mask token."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        rule = i % 4
+        S = int(g.choice([1, 2, 5, 63, 300, 2500]))
+        B = int(g.choice([1, 2, 3, 5, 13, 16, 33, 47, 64]))
+        tau = float(np.float32(g.choice([-0.5, 0.0, 0.3, 0.9, 0.999, 1.5])))
+        flags = int(g.integers(0, 2)) if rule == 0 else 0
+        k = int(g.integers(1, 9))
+        eb = float(np.float32(g.choice([0.0, 0.35, 1.0, 5.0])))
+        cases.append((f"rand{i}_rule{rule}_s{S}_b{B}", rule, S, B, tau, flags, k, eb))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_remask_cases(16), ids=lambda c: c[0])
+def test_remask_random(case):
+    """Bit-exact tokens, states, row list and commit counts against the
+    oracle's rule on seeded random inputs."""
+    name, rule, S, B, tau, flags, k, eb = case
+    g = np.random.default_rng(sum(name.encode()))
+    mask = 151669
+    toks = np.where(g.random((S, B)) < 0.6, mask, g.integers(0, mask, (S, B))).astype(np.int32)
+    state = g.choice(np.array([2, 2, 2, 2, 3, 0, 4], np.uint8), size=S)
+    levels = np.array([0.1, 0.5, tau, tau, 0.3, 0.3, np.nan], dtype=np.float32)
+    conf = np.where(g.random(S * B) < 0.4, g.choice(levels, S * B), g.random(S * B)).astype(np.float32)
+    elev = np.array([0.05, 0.3, 0.3, 1.25, np.nan, 0.7], dtype=np.float32)
+    ent = np.where(g.random(S * B) < 0.4, g.choice(elev, S * B), 4 * g.random(S * B)).astype(np.float32)
+    argm = np.where(g.random(S * B) < 0.03, mask, g.integers(0, mask, S * B)).astype(np.int32)
+    t_d, s_d = dev_i32(toks), dev_u8(state)
+    ri = torch.full((S * B,), -1, dtype=torch.int32, device="cuda")
+    nr = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nc = torch.full((S,), -1, dtype=torch.int32, device="cuda")
+    api.dbd_remask_commit_rule(t_d, s_d, dev_i32(argm), torch.from_numpy(conf).cuda(), ri, nr, mask, rule,
+                               dynamic_threshold=tau, tokens_per_step=k, eb_threshold=eb,
+                               entropy=torch.from_numpy(ent).cuda(), flags=flags, num_committed=nc)
+    torch.cuda.synchronize()
+    et, es, com = oracle.remask_rule(toks, state, conf, argm, mask, rule, tau=tau, tokens_per_step=k, eb=eb,
+                                     entropy=ent, flags=flags)
+    assert np.array_equal(t_d.cpu().numpy(), et)
+    assert np.array_equal(s_d.cpu().numpy(), es)
+    rows = oracle.compact_rows(et, es, mask)
+    assert nr.item() == rows.size
+    assert np.array_equal(ri.cpu().numpy()[:rows.size], rows)
+    den = state == 2
+    assert np.array_equal(nc.cpu().numpy()[den], com.sum(1)[den])
+    print(f"{name}: {int(com.sum())} commits, {rows.size} rows left", flush=True)
