@@ -205,3 +205,66 @@ def test_multiblock_steps_teacher_forced(w):
     for s in range(w.S):
         assert np.all(ts[s, :L0[s]] == -1)
         assert np.all((ts[s, L0[s]:end[s]] >= 0) & (ts[s, L0[s]:end[s]] != w.mask_id))
+
+
+def _random_save_cases(n, seed=5150):
+    """Seeded random SAVING-step shapes: GQA widths 1..16, D 64/128, blocks
+    1..64, page sizes 16..256, prefixes empty, page-aligned (the block
+    starts a page), a page minus one (the block crosses into the next) or
+    drawn, with room for two blocks past each prefix."""
+    g = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        D = int(g.choice([64, 128]))
+        Hkv = int(g.integers(1, 9))
+        G = int(g.choice([1, 2, 4, 6, 16]))
+        B = int(g.choice([1, 3, 4, 16, 31, 64]))
+        while G * B > 256:
+            B = max(1, B // 2)
+        P = int(g.choice([16, 32, 64, 256]))
+        S = int(g.integers(1, 10))
+        L = g.integers(0, 1500, S)
+        pick = g.integers(0, 4, S)
+        L = np.where(pick == 1, 0, np.where(pick == 2, (L // P) * P,
+                                            np.where(pick == 3, np.maximum(P - 1, (L // P) * P - 1), L)))
+        cases.append(Workload(name=f"save_rand{i}_s{S}_b{B}_g{G}x{Hkv}_d{D}_p{P}", seed_id=500 + i, S=S, B=B,
+                              Hq=G * Hkv, Hkv=Hkv, D=D, P=P, Hd=256, V=1024, mask_id=7, prefix_lo=0,
+                              prefix_hi=max(1, int(L.max())), tau=0.9, rounds=B, a_max=12.0,
+                              prefix_fixed=tuple(int(x) for x in L)))
+    return cases
+
+
+@pytest.mark.parametrize("w", _random_save_cases(8), ids=lambda w: w.name)
+def test_attn_save_random(w):
+    """The K/V write of SAVING sequences bit for bit against the oracle, the
+    outputs bit for bit against dbd_attn_paged and within the attention
+    tolerances of the oracle on sampled groups."""
+    fx = synth.make_fixed(w, with_w=False, reserve_tokens=2 * w.B)
+    rin = synth.make_round(w, 1, None)
+    g = np.random.default_rng(w.seed_id)
+    state = _states(g, w.S)
+    q, kb, vb = dev_bf16(rin.q), dev_bf16(rin.k_blk), dev_bf16(rin.v_blk)
+    kc, vc = dev_bf16(fx.k_cache), dev_bf16(fx.v_cache)
+    pt, pl, st = dev_i32(fx.page_table), dev_i32(fx.prefix_len), dev_u8(state)
+    out = torch.empty((w.S, w.B, w.Hq, w.D), dtype=torch.bfloat16, device="cuda")
+    api.dbd_attn_paged_save(q, kb, vb, kc, vc, pt, pl, st, out)
+    torch.cuda.synchronize()
+    ek, ev = oracle.kv_save(fx.k_cache, fx.v_cache, fx.page_table, fx.prefix_len, state, rin.k_blk, rin.v_blk)
+    assert np.array_equal(host_bits(kc), ek) and np.array_equal(host_bits(vc), ev)
+    out2 = torch.empty_like(out)
+    api.dbd_attn_paged(q, kb, vb, dev_bf16(fx.k_cache), dev_bf16(fx.v_cache), pt, pl, out2)
+    torch.cuda.synchronize()
+    ob = host_bits(out)
+    assert np.array_equal(ob, host_bits(out2))
+    groups = [(s, gk) for s in range(w.S) for gk in range(w.Hkv)]
+    groups = [groups[i] for i in sorted(set([0, len(groups) - 1] + list(
+        g.choice(len(groups), min(6, len(groups)), replace=False))))]
+    got, ref = [], []
+    for s, gk in groups:
+        ref.append(oracle.attention_group(s, gk, rin.q, rin.k_blk, rin.v_blk, fx.k_cache, fx.v_cache,
+                                          fx.page_table, fx.prefix_len))
+        got.append(widen_bits(ob[s, :, gk * w.G:(gk + 1) * w.G, :]))
+    mx, rl = attn_errors(np.stack(got), np.stack(ref))
+    print(f"{w.name} prefixes {list(w.prefix_fixed)} states {state.tolist()}: max abs {mx:.3e} rel L2 {rl:.3e}",
+          flush=True)
+    assert mx <= ATTN_MAX_ABS and rl <= ATTN_REL_L2
