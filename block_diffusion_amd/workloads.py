@@ -4,7 +4,10 @@ model page run, as frozen records.
 
 Nothing here computes anything; it only names shapes.  Readings that the
 pages leave open (mask id where unstated, amplitude range, round caps) are
-fixed here and listed in the design doc.
+fixed here: the mask id of the model family's tokenizer where a shape names
+none, planted amplitudes up to 12 or 16 by shape (16 for the coverage
+variants, so that confidences cross the threshold at full vocabulary), and
+a round cap of one block's length.
 """
 from __future__ import annotations
 

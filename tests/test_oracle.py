@@ -49,7 +49,9 @@ def test_prefill_pins(check):
 
 def test_round_on_tiny_workload():
     """Whole rounds of the tiny workload through the oracle: the block fills
-    within its round cap, with the spec invariants each round."""
+    within its round cap; each round commits at least one masked position
+    per DENOISING sequence, never re-masks a committed one, and moves a
+    sequence to SAVING exactly when its block holds no mask."""
     import numpy as np
     from block_diffusion_amd import synth
     from block_diffusion_amd.workloads import TINY
@@ -64,6 +66,9 @@ def test_round_on_tiny_workload():
         den = state == oracle.DENOISING
         assert np.all(masked_after[den & (masked_before > 0)] < masked_before[den & (masked_before > 0)])
         assert np.all(res["committed"].sum(1)[den & (masked_before > 0)] >= 1)
+        kept = toks != TINY.mask_id                      # committed tokens are never re-masked or changed
+        assert np.array_equal(res["tokens"][kept], toks[kept])
+        assert np.array_equal(res["state"][den] == oracle.SAVING, masked_after[den] == 0)
         assert np.all(res["p1"][res["rows"]] > 0) and np.all(res["p1"][res["rows"]] <= 1)
         toks, state = res["tokens"], res["state"]
         if not np.any(state == oracle.DENOISING):
